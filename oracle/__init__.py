@@ -1,0 +1,193 @@
+"""Double-precision CPU oracle for the selective state-space scan.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call this package.  It shares
+no code with the HIP library: the arithmetic lives in ``ssm_oracle.c`` (plain C,
+fp64, sequential in time), and this module only marshals numpy arrays.
+
+Inputs are numpy arrays.  Sequence tensors (u, delta, z: [batch, dim, L];
+B, C: [batch, dstate, L]) are either ``float32`` or ``uint16`` holding bf16
+bit patterns; the C code widens them itself.  Per-channel parameters (A, D,
+delta_bias, h0) are widened to float64 here with ``astype`` (exact for float32).
+
+Each function cites the page passage it follows in ``ssm_oracle.c``.
+Parity status: every function here is pinned by ``tests/test_oracle_pins.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ssm_oracle.c")
+_SO = os.path.join(_HERE, "libssm_oracle.so")
+_LIB = None
+
+BBAR_MODES = {"delta": 0, "delta_b": 0, "zoh": 1, "zoh_exact": 1}
+
+
+def build(force: bool = False) -> str:
+    """Compile ssm_oracle.c into libssm_oracle.so with gcc (plain C, no GPU)."""
+    if force or not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(_SRC):
+        tmp = _SO + ".tmp%d" % os.getpid()
+        subprocess.check_call(
+            ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared",
+             "-o", tmp, _SRC, "-lm", "-lpthread"])
+        os.replace(tmp, _SO)
+    return _SO
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        build()
+        lib = ctypes.CDLL(_SO)
+        i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+        lib.ssm_oracle_selective_scan.argtypes = [
+            i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp,
+            i64, i64, i64, i64, vp, i64, vp, vp, i32]
+        lib.ssm_oracle_state_update.argtypes = [
+            i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32,
+            i64, i64, i64, vp, i64, vp, i32]
+        lib.ssm_oracle_lti_kernel.argtypes = [
+            vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, vp]
+        lib.ssm_oracle_causal_conv.argtypes = [vp, vp, ctypes.c_double, i64, vp]
+        for f in (lib.ssm_oracle_selective_scan, lib.ssm_oracle_state_update,
+                  lib.ssm_oracle_lti_kernel, lib.ssm_oracle_causal_conv):
+            f.restype = i32
+        _LIB = lib
+    return _LIB
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def _seq(x, name):
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.float32:
+        return x, 0
+    if x.dtype == np.uint16:
+        return x, 1
+    raise TypeError(f"{name}: expected float32 or uint16 (bf16 bits), got {x.dtype}")
+
+
+def _f64(x):
+    return None if x is None else np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _ptr(x):
+    return None if x is None else x.ctypes.data
+
+
+def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None,
+                   delta_softplus=False, bbar="delta", h0=None, channels=None,
+                   want_y=True, n_threads=None):
+    """Sequential fp64 selective scan.
+
+    Returns ``(y, final_state)`` with y float64 ``[n_sel, L]`` (or None) and
+    final_state float64 ``[n_sel, dstate]``, where the rows follow ``channels``
+    (flat ``b*dim + d``; None = every channel in order).  ``h0`` is
+    ``[n_sel, dstate]`` aligned with the same selection.
+    """
+    u, dt = _seq(u, "u")
+    delta, dt2 = _seq(delta, "delta")
+    B, dt3 = _seq(B, "B")
+    C, dt4 = _seq(C, "C")
+    if len({dt, dt2, dt3, dt4}) != 1:
+        raise TypeError("u, delta, B, C must share one dtype")
+    if z is not None:
+        z, dt5 = _seq(z, "z")
+        if dt5 != dt:
+            raise TypeError("z must share the io dtype")
+    batch, dim, L = u.shape
+    N = A.shape[1]
+    assert delta.shape == u.shape and B.shape == (batch, N, L) and C.shape == (batch, N, L)
+    assert A.shape == (dim, N)
+    if z is not None:
+        assert z.shape == u.shape
+    A64, D64, bias64 = _f64(A), _f64(D), _f64(delta_bias)
+    if channels is None:
+        sel = None
+        n_sel = batch * dim
+    else:
+        sel = np.ascontiguousarray(channels, dtype=np.int64)
+        n_sel = sel.size
+    h064 = None
+    if h0 is not None:
+        h064 = np.ascontiguousarray(h0, dtype=np.float64).reshape(n_sel, N)
+    y = np.empty((n_sel, L), dtype=np.float64) if want_y else None
+    fs = np.empty((n_sel, N), dtype=np.float64)
+    rc = _lib().ssm_oracle_selective_scan(
+        dt, _ptr(u), _ptr(delta), _ptr(B), _ptr(C), _ptr(z), _ptr(A64), _ptr(D64),
+        _ptr(bias64), int(bool(delta_softplus)), BBAR_MODES[bbar], _ptr(h064),
+        batch, dim, N, L, _ptr(sel), n_sel, _ptr(y), _ptr(fs),
+        int(n_threads or default_threads()))
+    if rc != 0:
+        raise RuntimeError(f"ssm_oracle_selective_scan failed ({rc})")
+    return y, fs
+
+
+def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None,
+                 delta_softplus=False, bbar="delta", channels=None, n_threads=None):
+    """One decode step.  ``state`` is float64 ``[n_sel, dstate]`` and is updated
+    in place; u, delta, z are ``[batch, dim]``; B, C ``[batch, dstate]``.
+    Returns y float64 ``[n_sel]``."""
+    if not (isinstance(state, np.ndarray) and state.dtype == np.float64
+            and state.flags.c_contiguous):
+        raise TypeError("state must be a C-contiguous float64 array")
+    u, dt = _seq(u, "u")
+    delta, _ = _seq(delta, "delta")
+    B, _ = _seq(B, "B")
+    C, _ = _seq(C, "C")
+    if z is not None:
+        z, _ = _seq(z, "z")
+    batch, dim = u.shape
+    N = A.shape[1]
+    sel = None if channels is None else np.ascontiguousarray(channels, dtype=np.int64)
+    n_sel = batch * dim if sel is None else sel.size
+    assert state.shape == (n_sel, N)
+    A64, D64, bias64 = _f64(A), _f64(D), _f64(delta_bias)
+    y = np.empty(n_sel, dtype=np.float64)
+    rc = _lib().ssm_oracle_state_update(
+        dt, _ptr(state), _ptr(u), _ptr(delta), _ptr(B), _ptr(C), _ptr(z), _ptr(A64),
+        _ptr(D64), _ptr(bias64), int(bool(delta_softplus)), BBAR_MODES[bbar],
+        batch, dim, N, _ptr(sel), n_sel, _ptr(y), int(n_threads or default_threads()))
+    if rc != 0:
+        raise RuntimeError(f"ssm_oracle_state_update failed ({rc})")
+    return y
+
+
+def lti_kernel(A, Bv, Cv, delta, L, bbar="delta", method="direct"):
+    """K[d, k] = sum_n C[d,n] Abar[d,n]^k Bbar[d,n] in fp64.  Bv/Cv may be
+    ``[dstate]`` (shared by every channel) or ``[dim, dstate]``."""
+    A64 = _f64(A)
+    dim, N = A64.shape
+    Bv64, Cv64, d64 = _f64(Bv), _f64(Cv), _f64(delta)
+    bs = 0 if Bv64.ndim == 1 else N
+    cs = 0 if Cv64.ndim == 1 else N
+    K = np.empty((dim, L), dtype=np.float64)
+    rc = _lib().ssm_oracle_lti_kernel(
+        _ptr(A64), _ptr(Bv64), _ptr(Cv64), _ptr(d64), dim, N, L, bs, cs,
+        BBAR_MODES[bbar], {"direct": 0, "powers": 1}[method], _ptr(K))
+    if rc != 0:
+        raise RuntimeError("ssm_oracle_lti_kernel failed")
+    return K
+
+
+def causal_conv(K, u, D=0.0):
+    """y[t] = sum_{k<=t} K[k] u[t-k] + D u[t], direct O(L^2) sum in fp64."""
+    K64, u64 = _f64(K), _f64(u)
+    L = u64.size
+    assert K64.size >= L
+    y = np.empty(L, dtype=np.float64)
+    rc = _lib().ssm_oracle_causal_conv(_ptr(K64), _ptr(u64), float(D), L, _ptr(y))
+    if rc != 0:
+        raise RuntimeError("ssm_oracle_causal_conv failed")
+    return y

@@ -1,0 +1,282 @@
+/*
+ * ssm_oracle.c -- plain, sequential, double-precision reference for the
+ * selective state-space scan.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file: it is used by the tests, by the smoke check and by the CPU
+ * baseline leg of the benchmark.  It shares no code, header, table or helper
+ * with the HIP library; it has its own bf16 widening and its own softplus.
+ *
+ * What it computes (sources are the five web pages on state-space models):
+ *
+ *  - discretization by zero-order hold, Abar = exp(delta*A) elementwise for
+ *    a diagonal A, with either the exact ZOH input matrix
+ *    Bbar = A^-1 (exp(delta*A) - 1) B  or the simplified Bbar = delta*B
+ *    ("State-space models", section "Discretization" (ZOH rule) and the
+ *    closing paragraph of "Implementation", which says the official
+ *    package uses Bbar = delta*B; "State Space Models: Mamba and Beyond",
+ *    section "Discretization: zero-order hold");
+ *  - the recurrence h_t = Abar_t h_{t-1} + Bbar_t u_t from h_{-1} = 0 (or a
+ *    caller-given h0) and the readout y_t = C_t . h_t + D u_t
+ *    ("State-space models", section "Recurrence and convolution";
+ *    "Structured State Space Models and Mamba ...", section "Discretization
+ *    Mechanics: Zero-Order Hold and Bilinear Transforms");
+ *  - selection: delta_t = softplus(raw_t + bias), B_t and C_t shared by all
+ *    channels of a sequence, A and delta per channel ("State-space models",
+ *    section "Mamba: selection"; "Structured State Space Models and Mamba
+ *    ...", section "The Linear Time-Invariance Bottleneck and the Selective
+ *    State Space (S6)", the delta_t formula with its bias parameter);
+ *  - the block's output gate y * silu(z) ("State-space models", section
+ *    "Mamba: selection", paragraph on the Mamba block);
+ *  - the time-invariant kernel K_k = C Abar^k Bbar and the causal convolution
+ *    y_t = sum_{k<=t} K_k u_{t-k} + D u_t ("State-space models", section
+ *    "Recurrence and convolution").
+ *
+ * The loop is the definition, in time order, one channel at a time.  The
+ * only parallelism is over independent channels (b, d), which does not
+ * change any channel's arithmetic.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { OR_F32 = 0, OR_BF16 = 1 };
+enum { OR_BBAR_DELTA_B = 0, OR_BBAR_ZOH_EXACT = 1 };
+
+/* bf16 is the upper half of an IEEE binary32; widening is exact. */
+static double or_widen(const void* p, int dtype, int64_t i) {
+  if (dtype == OR_F32) return (double)((const float*)p)[i];
+  uint32_t bits = (uint32_t)((const uint16_t*)p)[i] << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+/* softplus(x) = log(1 + e^x), written in the overflow-free form. */
+static double or_softplus(double x) {
+  return (x > 0.0 ? x : 0.0) + log1p(exp(-fabs(x)));
+}
+
+/* silu(z) = z * sigmoid(z). */
+static double or_silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* Input coefficient Bbar/B for one (delta, a) pair under the chosen rule. */
+static double or_bbar_factor(double dt, double a, int bbar_mode) {
+  if (bbar_mode == OR_BBAR_DELTA_B) return dt;
+  /* exact ZOH: (exp(dt*a) - 1) / a, whose limit at a = 0 is dt */
+  if (a == 0.0) return dt;
+  return expm1(dt * a) / a;
+}
+
+typedef struct {
+  int io_dtype;
+  const void *u, *delta, *Bm, *Cm, *z;
+  const double *A, *Dskip, *delta_bias;
+  int delta_softplus, bbar_mode;
+  const double* h0;
+  int64_t batch, dim, dstate, seqlen;
+  const int64_t* channels;
+  int64_t n_channels;
+  double *y, *final_state;
+  /* work distribution */
+  int64_t next;
+  pthread_mutex_t lock;
+  int status;
+} or_scan_job;
+
+/* The recurrence for one channel c = b*dim + d, written straight from the
+ * definition: discretize, update every state, read out, skip, gate. */
+static void or_scan_one(const or_scan_job* j, int64_t sel, double* h) {
+  const int64_t c = j->channels ? j->channels[sel] : sel;
+  const int64_t b = c / j->dim, d = c % j->dim;
+  const int64_t N = j->dstate, L = j->seqlen;
+  const int64_t row = c * L;            /* u, delta, z: [batch, dim, L] */
+  const int64_t bc_base = b * N * L;    /* B, C: [batch, N, L] */
+  for (int64_t n = 0; n < N; ++n) h[n] = j->h0 ? j->h0[sel * N + n] : 0.0;
+  const double bias = j->delta_bias ? j->delta_bias[d] : 0.0;
+  const double Dd = j->Dskip ? j->Dskip[d] : 0.0;
+  for (int64_t t = 0; t < L; ++t) {
+    const double ut = or_widen(j->u, j->io_dtype, row + t);
+    const double raw = or_widen(j->delta, j->io_dtype, row + t) + bias;
+    const double dt = j->delta_softplus ? or_softplus(raw) : raw;
+    double acc = 0.0;
+    for (int64_t n = 0; n < N; ++n) {
+      const double a = j->A[d * N + n];
+      const double abar = exp(dt * a);
+      const double bt = or_widen(j->Bm, j->io_dtype, bc_base + n * L + t);
+      const double ct = or_widen(j->Cm, j->io_dtype, bc_base + n * L + t);
+      h[n] = abar * h[n] + or_bbar_factor(dt, a, j->bbar_mode) * bt * ut;
+      acc += ct * h[n];
+    }
+    double yt = acc + Dd * ut;
+    if (j->z) yt *= or_silu(or_widen(j->z, j->io_dtype, row + t));
+    if (j->y) j->y[sel * L + t] = yt;
+  }
+  if (j->final_state)
+    for (int64_t n = 0; n < N; ++n) j->final_state[sel * N + n] = h[n];
+}
+
+static void* or_scan_worker(void* arg) {
+  or_scan_job* j = (or_scan_job*)arg;
+  double* h = (double*)malloc(sizeof(double) * (size_t)j->dstate);
+  if (!h) {
+    pthread_mutex_lock(&j->lock);
+    j->status = 2;
+    pthread_mutex_unlock(&j->lock);
+    return NULL;
+  }
+  for (;;) {
+    pthread_mutex_lock(&j->lock);
+    const int64_t sel = j->next++;
+    pthread_mutex_unlock(&j->lock);
+    if (sel >= j->n_channels) break;
+    or_scan_one(j, sel, h);
+  }
+  free(h);
+  return NULL;
+}
+
+/*
+ * Selective scan over the channels listed in `channels` (flat index
+ * b*dim + d; NULL means all batch*dim channels in order).
+ *
+ *   u, delta, z : [batch, dim, seqlen]   io_dtype (0 = float32, 1 = bf16 bits)
+ *   Bm, Cm      : [batch, dstate, seqlen] io_dtype
+ *   A           : [dim, dstate] double
+ *   Dskip, delta_bias : [dim] double or NULL (= 0)
+ *   z           : NULL = no gate
+ *   h0          : [n_channels, dstate] double or NULL (= 0); may equal
+ *                 final_state (each channel reads h0 before writing)
+ *   y           : [n_channels, seqlen] double out (may be NULL)
+ *   final_state : [n_channels, dstate] double out (may be NULL)
+ *
+ * Returns 0, or 1 on bad arguments, 2 on allocation failure.
+ */
+int ssm_oracle_selective_scan(int io_dtype, const void* u, const void* delta, const void* Bm,
+                              const void* Cm, const void* z, const double* A, const double* Dskip,
+                              const double* delta_bias, int delta_softplus, int bbar_mode,
+                              const double* h0, int64_t batch, int64_t dim, int64_t dstate,
+                              int64_t seqlen, const int64_t* channels, int64_t n_channels,
+                              double* y, double* final_state, int n_threads) {
+  if (!u || !delta || !Bm || !Cm || !A) return 1;
+  if (batch <= 0 || dim <= 0 || dstate <= 0 || seqlen <= 0) return 1;
+  if (io_dtype != OR_F32 && io_dtype != OR_BF16) return 1;
+  if (bbar_mode != OR_BBAR_DELTA_B && bbar_mode != OR_BBAR_ZOH_EXACT) return 1;
+  if (!channels) n_channels = batch * dim;
+  for (int64_t i = 0; channels && i < n_channels; ++i)
+    if (channels[i] < 0 || channels[i] >= batch * dim) return 1;
+  or_scan_job j;
+  memset(&j, 0, sizeof j);
+  j.io_dtype = io_dtype;
+  j.u = u;
+  j.delta = delta;
+  j.Bm = Bm;
+  j.Cm = Cm;
+  j.z = z;
+  j.A = A;
+  j.Dskip = Dskip;
+  j.delta_bias = delta_bias;
+  j.delta_softplus = delta_softplus;
+  j.bbar_mode = bbar_mode;
+  j.h0 = h0;
+  j.batch = batch;
+  j.dim = dim;
+  j.dstate = dstate;
+  j.seqlen = seqlen;
+  j.channels = channels;
+  j.n_channels = n_channels;
+  j.y = y;
+  j.final_state = final_state;
+  j.next = 0;
+  j.status = 0;
+  pthread_mutex_init(&j.lock, NULL);
+  if (n_threads < 1) n_threads = 1;
+  if (n_threads > 256) n_threads = 256;
+  if ((int64_t)n_threads > n_channels) n_threads = (int)n_channels;
+  pthread_t tid[256];
+  int started = 0;
+  for (int i = 1; i < n_threads; ++i)
+    if (pthread_create(&tid[started], NULL, or_scan_worker, &j) == 0) ++started;
+  or_scan_worker(&j);
+  for (int i = 0; i < started; ++i) pthread_join(tid[i], NULL);
+  pthread_mutex_destroy(&j.lock);
+  return j.status;
+}
+
+/*
+ * One decode step: the recurrence advanced by a single token per sequence
+ * ("State-space models", section "Recurrence and convolution": generation
+ * advances the N-dimensional state by one token at constant cost).
+ *
+ *   state : [n_channels, dstate] double, read and written in place
+ *   u, delta, z : [batch, dim] io_dtype;  Bm, Cm : [batch, dstate] io_dtype
+ *   y     : [n_channels] double out
+ *
+ * It is the scan above with seqlen = 1 and h0 = final_state = state.
+ */
+int ssm_oracle_state_update(int io_dtype, double* state, const void* u, const void* delta,
+                            const void* Bm, const void* Cm, const void* z, const double* A,
+                            const double* Dskip, const double* delta_bias, int delta_softplus,
+                            int bbar_mode, int64_t batch, int64_t dim, int64_t dstate,
+                            const int64_t* channels, int64_t n_channels, double* y,
+                            int n_threads) {
+  if (!state) return 1;
+  return ssm_oracle_selective_scan(io_dtype, u, delta, Bm, Cm, z, A, Dskip, delta_bias,
+                                   delta_softplus, bbar_mode, state, batch, dim, dstate, 1,
+                                   channels, n_channels, y, state, n_threads);
+}
+
+/*
+ * Time-invariant convolution kernel K[d, k] = sum_n C[d,n] Abar[d,n]^k Bbar[d,n]
+ * for k in [0, L) ("State-space models", section "Recurrence and
+ * convolution": K_k = C Abar^k Bbar; section "S4: a structured state matrix":
+ * with a diagonal A the powers are elementwise).
+ *
+ *   A : [dim, dstate];  Bv, Cv : rows of length dstate, row d at d*stride
+ *   (stride 0 = one row shared by every channel);  delta : [dim]
+ *   method 0 : Abar^k = exp(k * delta * A)      (direct)
+ *   method 1 : Abar^k by repeated multiplication (k successive products)
+ *   K : [dim, L] out
+ */
+int ssm_oracle_lti_kernel(const double* A, const double* Bv, const double* Cv,
+                          const double* delta, int64_t dim, int64_t dstate, int64_t L,
+                          int64_t b_row_stride, int64_t c_row_stride, int bbar_mode, int method,
+                          double* K) {
+  if (!A || !Bv || !Cv || !delta || !K || dim <= 0 || dstate <= 0 || L <= 0) return 1;
+  if (bbar_mode != OR_BBAR_DELTA_B && bbar_mode != OR_BBAR_ZOH_EXACT) return 1;
+  for (int64_t d = 0; d < dim; ++d) {
+    const double dt = delta[d];
+    for (int64_t k = 0; k < L; ++k) K[d * L + k] = 0.0;
+    for (int64_t n = 0; n < dstate; ++n) {
+      const double a = A[d * dstate + n];
+      const double abar = exp(dt * a);
+      const double bbar = or_bbar_factor(dt, a, bbar_mode) * Bv[d * b_row_stride + n];
+      const double cn = Cv[d * c_row_stride + n];
+      double p = 1.0; /* Abar^k for method 1 */
+      for (int64_t k = 0; k < L; ++k) {
+        const double pk = (method == 0) ? exp((double)k * dt * a) : p;
+        K[d * L + k] += cn * pk * bbar;
+        p *= abar;
+      }
+    }
+  }
+  return 0;
+}
+
+/*
+ * Causal linear convolution y[t] = sum_{k=0..t} K[k] u[t-k] + D u[t]: the
+ * output sees no future input ("State-space models", section "Recurrence and
+ * convolution", and the left-padded convolution in "Implementation").
+ * Direct O(L^2) sum.
+ */
+int ssm_oracle_causal_conv(const double* K, const double* u, double Dskip, int64_t L, double* y) {
+  if (!K || !u || !y || L <= 0) return 1;
+  for (int64_t t = 0; t < L; ++t) {
+    double acc = 0.0;
+    for (int64_t k = 0; k <= t; ++k) acc += K[k] * u[t - k];
+    y[t] = acc + Dskip * u[t];
+  }
+  return 0;
+}

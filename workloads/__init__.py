@@ -1,0 +1,216 @@
+"""Seeded synthetic inputs for the selective-scan workloads.
+
+This module only draws random numbers and rounds them to the storage dtype; it
+holds none of the scan's arithmetic and imports neither the HIP library nor the
+oracle, so both sides can consume the same bits.
+
+Every tensor row is drawn from its own PCG64 stream, keyed by
+``SeedSequence(seed, spawn_key=(tensor_id, row))``, so any row can be
+regenerated alone and rows can be drawn in parallel threads (numpy releases the
+GIL while filling).  Values are drawn in float32 and, for bf16 workloads,
+rounded to bf16 with round-to-nearest-even; both the GPU and the oracle read
+those exact bits.
+
+Workloads (shapes, dtypes and distributions of the Mamba-style scans):
+
+  tiny_fp32     batch 1, dim 16, N 4, L 256, fp32; u~N(0,1); raw delta~N(-2,0.5)
+                with softplus, no bias; A[d,n] = -(n+1); B,C~N(0,1); D~N(0,1);
+                no gate.
+  mamba130m     batch 8, dim 1536, N 16, L 2048, bf16 u/delta/B/C/z; fp32
+                A, D, bias; u,z~N(0,1); raw delta~N(0,1); delta_bias =
+                log(expm1(U[1e-3, 1e-1])); A = -exp(log(1..16)); B,C~N(0,1);
+                D~N(0,1); silu(z) gate.
+  mamba2p8b     as mamba130m at batch 4, dim 5120, N 16, L 8192.
+  long_context  batch 1, dim 2048, N 16, L 524288, bf16; u~N(0,1); raw
+                delta~N(-4,1) with softplus, no bias; A = -exp(U[ln 0.5, ln 16])
+                iid per (d, n); B,C~N(0,1); D~N(0,1); no gate.
+  decode        batch 256, dim 5120, N 16, one token per step, 1000 steps;
+                fp32 state ~N(0, 0.1); per step fresh bf16 u, raw delta, z ~N(0,1)
+                [256, 5120] and B, C ~N(0,1) [256, 16]; bias, A, D as mamba130m.
+
+N(mu, sigma) names the standard deviation as the second parameter.
+"""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass
+
+import numpy as np
+
+# tensor ids used in the per-row stream keys
+T_U, T_DELTA, T_Z, T_B, T_C, T_A, T_D, T_BIAS, T_STATE = range(9)
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    index: int            # position in the list of measured configurations (1-based)
+    batch: int
+    dim: int
+    dstate: int
+    seqlen: int           # tokens per sequence (1 for decode)
+    dtype: str            # "f32" or "bf16": dtype of u, delta, B, C, z, y
+    gate: bool            # silu(z) gate present
+    delta_mean: float
+    delta_std: float
+    bias: bool            # delta_bias = log(expm1(U[1e-3, 1e-1]))
+    a_init: str           # "s4d_real": A = -(n+1);  "loguniform": A = -exp(U[ln .5, ln 16])
+    steps: int = 0        # decode steps (decode workload only)
+
+    @property
+    def seed(self) -> int:
+        return 4300 + self.index
+
+    @property
+    def elements(self) -> int:
+        """Scan elements per pass, batch * dim * L * N."""
+        return self.batch * self.dim * self.seqlen * self.dstate
+
+    @property
+    def io_bytes(self) -> int:
+        """Bytes of u, delta, (z), B, C read once plus y written once."""
+        s = 2 if self.dtype == "bf16" else 4
+        seq = self.batch * self.dim * self.seqlen
+        return s * (seq * (2 + int(self.gate)) + 2 * self.batch * self.dstate * self.seqlen + seq)
+
+
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("tiny_fp32", 1, 1, 16, 4, 256, "f32", False, -2.0, 0.5, False, "s4d_real"),
+        Workload("mamba130m", 2, 8, 1536, 16, 2048, "bf16", True, 0.0, 1.0, True, "s4d_real"),
+        Workload("mamba2p8b", 3, 4, 5120, 16, 8192, "bf16", True, 0.0, 1.0, True, "s4d_real"),
+        Workload("long_context", 4, 1, 2048, 16, 524288, "bf16", False, -4.0, 1.0, False,
+                 "loguniform"),
+        Workload("decode", 5, 256, 5120, 16, 1, "bf16", True, 0.0, 1.0, True, "s4d_real",
+                 steps=1000),
+    ]
+}
+
+
+def threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def rng(seed: int, tensor_id: int, row: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=(tensor_id, row))))
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns (uint16), round to nearest, ties to even."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    rounded = b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))
+    return (rounded >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> float32 (exact)."""
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _store(x: np.ndarray, dtype: str) -> np.ndarray:
+    return to_bf16_bits(x) if dtype == "bf16" else x.astype(np.float32, copy=False)
+
+
+def _normal_rows(seed, tid, rows, n, mean, std, dtype, out):
+    """out[r] = stored(N(mean, std) draws of stream (tid, row0 + r))."""
+    def one(r):
+        x = rng(seed, tid, rows[r]).standard_normal(n, dtype=np.float32)
+        if std != 1.0:
+            x *= np.float32(std)
+        if mean != 0.0:
+            x += np.float32(mean)
+        out[r] = _store(x, dtype)
+    with ThreadPoolExecutor(threads()) as ex:
+        list(ex.map(one, range(len(rows))))
+    return out
+
+
+def seq_tensor(w: Workload, tid: int, mean: float, std: float, seed=None, step=None):
+    """A [batch, dim, L] (tid in u/delta/z) or [batch, N, L] (tid in B/C) tensor."""
+    seed = w.seed if seed is None else seed
+    inner = w.dim if tid in (T_U, T_DELTA, T_Z) else w.dstate
+    rows = w.batch * inner
+    np_dtype = np.uint16 if w.dtype == "bf16" else np.float32
+    out = np.empty((rows, w.seqlen), dtype=np_dtype)
+    base = 0 if step is None else (step + 1) * (1 << 32)
+    _normal_rows(seed, tid, [base + r for r in range(rows)], w.seqlen, mean, std, w.dtype, out)
+    return out.reshape(w.batch, inner, w.seqlen)
+
+
+def params(w: Workload, seed=None):
+    """A [dim, N], D [dim], delta_bias [dim] or None, all float32."""
+    seed = w.seed if seed is None else seed
+    if w.a_init == "s4d_real":
+        # A = -exp(log(1..N)), repeated over channels; in fp64 then rounded to fp32
+        a_row = (-np.exp(np.log(np.arange(1, w.dstate + 1, dtype=np.float64)))).astype(np.float32)
+        A = np.tile(a_row, (w.dim, 1))
+    else:
+        lo, hi = np.log(0.5), np.log(16.0)
+        A = np.empty((w.dim, w.dstate), dtype=np.float32)
+        for d in range(w.dim):
+            A[d] = (-np.exp(rng(seed, T_A, d).uniform(lo, hi, w.dstate))).astype(np.float32)
+    D = rng(seed, T_D, 0).standard_normal(w.dim, dtype=np.float32)
+    bias = None
+    if w.bias:
+        # inverse softplus of U[1e-3, 1e-1]: the initial step sizes of a Mamba layer
+        dt0 = rng(seed, T_BIAS, 0).uniform(1e-3, 1e-1, w.dim)
+        bias = np.log(np.expm1(dt0)).astype(np.float32)
+    return np.ascontiguousarray(A), D, bias
+
+
+def scan_inputs(w: Workload, seed=None):
+    """All inputs of one forward scan as numpy arrays (bf16 as uint16 bits)."""
+    A, D, bias = params(w, seed)
+    return dict(
+        u=seq_tensor(w, T_U, 0.0, 1.0, seed),
+        delta=seq_tensor(w, T_DELTA, w.delta_mean, w.delta_std, seed),
+        z=seq_tensor(w, T_Z, 0.0, 1.0, seed) if w.gate else None,
+        B=seq_tensor(w, T_B, 0.0, 1.0, seed),
+        C=seq_tensor(w, T_C, 0.0, 1.0, seed),
+        A=A, D=D, delta_bias=bias, delta_softplus=True)
+
+
+def decode_state(w: Workload, seed=None) -> np.ndarray:
+    """Initial fp32 decode state [batch, dim, N] ~ N(0, 0.1)."""
+    seed = w.seed if seed is None else seed
+    out = np.empty((w.batch * w.dim, w.dstate), dtype=np.float32)
+    _normal_rows(seed, T_STATE, list(range(w.batch * w.dim)), w.dstate, 0.0, 0.1, "f32", out)
+    return out.reshape(w.batch, w.dim, w.dstate)
+
+
+def decode_step(w: Workload, step: int, seed=None):
+    """Fresh per-step inputs: u, delta, z [batch, dim]; B, C [batch, N]."""
+    seed = w.seed if seed is None else seed
+
+    def t(tid, inner, mean, std):
+        np_dtype = np.uint16 if w.dtype == "bf16" else np.float32
+        out = np.empty((w.batch, inner), dtype=np_dtype)
+        base = (step + 1) << 32
+        x = rng(seed, tid, base).standard_normal(w.batch * inner, dtype=np.float32)
+        if std != 1.0:
+            x *= np.float32(std)
+        if mean != 0.0:
+            x += np.float32(mean)
+        out[:] = _store(x, w.dtype).reshape(w.batch, inner)
+        return out
+
+    return dict(u=t(T_U, w.dim, 0.0, 1.0),
+                delta=t(T_DELTA, w.dim, w.delta_mean, w.delta_std),
+                z=t(T_Z, w.dim, 0.0, 1.0) if w.gate else None,
+                B=t(T_B, w.dstate, 0.0, 1.0),
+                C=t(T_C, w.dstate, 0.0, 1.0))
+
+
+def custom(batch, dim, dstate, seqlen, dtype="bf16", gate=True, bias=True,
+           delta_mean=0.0, delta_std=1.0, a_init="s4d_real", seed=1234, name="custom"):
+    """A workload of any shape with the Mamba-layer distributions (for parity
+    sweeps over tiles and ragged tails)."""
+    w = Workload(name, 0, batch, dim, dstate, seqlen, dtype, gate, delta_mean, delta_std,
+                 bias, a_init)
+    return w, scan_inputs(w, seed)
