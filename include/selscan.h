@@ -1,0 +1,154 @@
+/*
+ * selscan.h -- C ABI of libselscan, the selective state-space scan for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operation is the selective (S6) state-space recurrence of Mamba as the
+ * pages on state-space models describe it:
+ *
+ *   delta_t = softplus(raw_t + bias)            (optional bias and softplus)
+ *   Abar_t  = exp(delta_t * A)                  (zero-order hold, diagonal A)
+ *   Bbar_t  = delta_t * B_t                     (default rule)   or
+ *             A^-1 (exp(delta_t * A) - 1) B_t   (exact zero-order hold)
+ *   h_t     = Abar_t h_{t-1} + Bbar_t u_t,   h_{-1} = h0 or 0
+ *   y_t     = (C_t . h_t + D u_t) * silu(z_t)   (gate optional)
+ *
+ * Sources: "State-space models" (rayaq.ca), sections "Discretization",
+ * "Recurrence and convolution", "Mamba: selection" and "The parallel scan";
+ * "State Space Models: Mamba and Beyond", section "Discretization:
+ * zero-order hold"; "Structured State Space Models and Mamba: Mathematical
+ * Foundations, Continuous Discretization, and Hardware-Aware Associative
+ * Scans", sections "The Linear Time-Invariance Bottleneck and the Selective
+ * State Space (S6)" (delta with bias) and "Hardware-Aware Parallel
+ * Associative Scan" (the pair-composition operator).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers are DEVICE pointers (memory of the current HIP device) unless a
+ *    comment says otherwise.  The caller allocates and owns every buffer;
+ *    the library allocates nothing, keeps no pointer after it returns and has
+ *    no mutable global state, so calls from several host threads are safe.
+ *  - Tensors are dense, row-major, innermost index last.  Sequence tensors
+ *    keep time innermost: u, delta, z, y are [batch, dim, seqlen] and the
+ *    selective B, C are [batch, dstate, seqlen] (shared by all channels of a
+ *    sequence).  A is [dim, dstate]; D and delta_bias are [dim]; states are
+ *    [batch, dim, dstate].
+ *  - io_dtype (ssm_dtype) is the element type of u, delta, B, C, z and y.
+ *    A, D, delta_bias and every state are float32.  All arithmetic is float32.
+ *  - Work is enqueued on `hip_stream` (a hipStream_t; NULL = the legacy
+ *    default stream) and the call returns without waiting.  Device-side
+ *    faults surface at the caller's next synchronization.
+ *  - Arguments are validated on the host before anything is enqueued.  On
+ *    error nothing is enqueued, the return value is the ssm_status code and
+ *    ssm_last_error() (thread-local) describes the argument at fault.
+ *  - Sequence-tensor base pointers must be 16-byte aligned (every torch
+ *    allocation is).  Any seqlen >= 1 is accepted; the fastest path needs
+ *    seqlen to be a multiple of 8 (bf16) or 4 (float32).
+ *  - Non-finite inputs are not trapped: NaN and Inf propagate.
+ */
+#ifndef SELSCAN_H
+#define SELSCAN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSM_ABI_VERSION 1
+
+typedef enum { SSM_DTYPE_F32 = 0, SSM_DTYPE_BF16 = 1 } ssm_dtype;
+
+/* Bbar rule: delta*B (Mamba's simplified input matrix, the default; the
+ * "Implementation" section of "State-space models" notes the official package
+ * uses it) or the exact zero-order-hold input matrix. */
+typedef enum { SSM_BBAR_DELTA_B = 0, SSM_BBAR_ZOH_EXACT = 1 } ssm_bbar_mode;
+
+typedef enum {
+  SSM_OK = 0,
+  SSM_E_NULL = 1,        /* a required pointer is NULL                         */
+  SSM_E_SHAPE = 2,       /* an extent is <= 0 or too large                      */
+  SSM_E_DTYPE = 3,       /* io_dtype or bbar_mode is not a known value          */
+  SSM_E_ALIGN = 4,       /* a sequence tensor is not 16-byte aligned            */
+  SSM_E_ALIAS = 5,       /* an output overlaps an input it must not overlap     */
+  SSM_E_UNSUPPORTED = 6, /* dstate outside 1..64                                */
+  SSM_E_HIP = 7          /* the HIP runtime refused the launch                  */
+} ssm_status;
+
+/*
+ * Forward selective scan over whole sequences (prefill / training forward).
+ *
+ *  u           [batch, dim, seqlen]     io_dtype   input x_t per channel
+ *  delta       [batch, dim, seqlen]     io_dtype   raw step; the step used is
+ *                                                  softplus(delta + delta_bias)
+ *                                                  if delta_softplus, else
+ *                                                  delta + delta_bias
+ *  A           [dim, dstate]            float32    diagonal of A (negative reals
+ *                                                  for a stable system)
+ *  Bm, Cm      [batch, dstate, seqlen]  io_dtype   input-dependent B_t and C_t
+ *  Dskip       [dim] float32 or NULL (= 0)         skip term D u_t
+ *  z           [batch, dim, seqlen] io_dtype or NULL: gate y * silu(z)
+ *  delta_bias  [dim] float32 or NULL (= 0)
+ *  h0          [batch, dim, dstate] float32 or NULL (= 0): initial state, so a
+ *              long sequence can be scanned in pieces (pass the previous
+ *              piece's final_state)
+ *  y           [batch, dim, seqlen] io_dtype, out.  Must not overlap any input.
+ *  final_state [batch, dim, dstate] float32 out, or NULL.  May be exactly h0
+ *              (in-place resume) but must not otherwise overlap it.
+ *
+ * The expanded state [batch, seqlen, dim, dstate] is never written to memory.
+ */
+int ssm_selective_scan_fwd(const void* u, const void* delta, const float* A, const void* Bm,
+                           const void* Cm, const float* Dskip, const void* z,
+                           const float* delta_bias, int delta_softplus, const float* h0, void* y,
+                           float* final_state, int64_t batch, int64_t dim, int64_t dstate,
+                           int64_t seqlen, int io_dtype, int bbar_mode, void* hip_stream);
+
+/*
+ * One decode step: every sequence advances by one token at constant cost,
+ * reading and writing its [dim, dstate] state in place ("State-space
+ * models", section "Recurrence and convolution": generation advances the
+ * state by one token).
+ *
+ *  state       [batch, dim, dstate] float32, in/out
+ *  u, delta, z [batch, dim]   io_dtype (z may be NULL)
+ *  Bm, Cm      [batch, dstate] io_dtype
+ *  A, Dskip, delta_bias, delta_softplus, bbar_mode: as for the forward scan
+ *  y           [batch, dim] io_dtype out; must not overlap any input or state
+ */
+int ssm_state_update(float* state, const void* u, const void* delta, const float* A,
+                     const void* Bm, const void* Cm, const float* Dskip, const void* z,
+                     const float* delta_bias, int delta_softplus, void* y, int64_t batch,
+                     int64_t dim, int64_t dstate, int io_dtype, int bbar_mode, void* hip_stream);
+
+/*
+ * Time-invariant convolution kernel K[d, k] = sum_n C[d,n] Abar[d,n]^k Bbar[d,n]
+ * for k in [0, L), with Abar = exp(delta[d] A[d,n]) and Bbar by bbar_mode.
+ * With delta, B and C fixed in time the recurrence equals the causal
+ * convolution y = K * u + D u ("State-space models", section "Recurrence and
+ * convolution"; "S4: a structured state matrix": with a diagonal A the powers
+ * are elementwise).  Used to check the scan against its time-invariant case.
+ *
+ *  A      [dim, dstate] float32
+ *  Bv, Cv rows of dstate float32; row d starts at Bv + d*b_row_stride
+ *         (stride 0: one row shared by every channel)
+ *  delta  [dim] float32: the step actually used (no softplus applied here)
+ *  K      [dim, L] float32 out
+ */
+int ssm_lti_kernel(const float* A, const float* Bv, const float* Cv, const float* delta, float* K,
+                   int64_t dim, int64_t dstate, int64_t L, int64_t b_row_stride,
+                   int64_t c_row_stride, int bbar_mode, void* hip_stream);
+
+/* Static description of a status code (never NULL). */
+const char* ssm_status_str(int status);
+
+/* Detail of the last error raised on the calling host thread ("" if none). */
+const char* ssm_last_error(void);
+
+/* SSM_ABI_VERSION of the loaded library. */
+int ssm_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SELSCAN_H */

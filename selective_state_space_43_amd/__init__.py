@@ -1,0 +1,33 @@
+"""Thin Python binding over libselscan's C ABI (include/selscan.h).
+
+Argument marshalling only: every step of the scan runs in the HIP kernels of
+``libselscan.so``.  PyTorch supplies device memory and the current stream.
+There is no CPU fallback: if the library is missing the first call raises.
+
+Entry points carry the C names:
+
+  ssm_selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
+                         delta_softplus=False, h0=None, bbar="delta",
+                         y=None, final_state=None, want_final_state=True)
+      -> (y, final_state)
+  ssm_state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None,
+                   delta_softplus=False, bbar="delta", y=None) -> y
+  ssm_lti_kernel(A, Bv, Cv, delta, L, bbar="delta", K=None) -> K
+
+Layouts: u, delta, z, y [batch, dim, L]; B, C [batch, dstate, L]; A
+[dim, dstate]; D, delta_bias [dim]; h0 / final_state / state
+[batch, dim, dstate].  Sequence tensors are torch.bfloat16 or torch.float32
+(one dtype for all of them); everything else is float32.
+"""
+from __future__ import annotations
+
+from ._lib import (SSM_BBAR_DELTA_B, SSM_BBAR_ZOH_EXACT, SSM_DTYPE_BF16, SSM_DTYPE_F32,
+                   SelscanError, library_path, lib, ssm_abi_version, ssm_last_error,
+                   ssm_status_str)
+from .binding import ssm_lti_kernel, ssm_selective_scan_fwd, ssm_state_update
+
+__all__ = [
+    "ssm_selective_scan_fwd", "ssm_state_update", "ssm_lti_kernel", "ssm_status_str",
+    "ssm_last_error", "ssm_abi_version", "SelscanError", "library_path", "lib",
+    "SSM_DTYPE_F32", "SSM_DTYPE_BF16", "SSM_BBAR_DELTA_B", "SSM_BBAR_ZOH_EXACT",
+]

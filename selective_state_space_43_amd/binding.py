@@ -1,0 +1,143 @@
+"""torch tensors -> C ABI calls.  Checks dtype, device, shape and contiguity,
+allocates outputs with torch when the caller did not pass them, and enqueues
+the library call on torch's current stream of the tensors' device."""
+from __future__ import annotations
+
+import torch
+
+from ._lib import SSM_DTYPE_BF16, SSM_DTYPE_F32, check, lib
+
+_IO = {torch.bfloat16: SSM_DTYPE_BF16, torch.float32: SSM_DTYPE_F32}
+_BBAR = {"delta": 0, "delta_b": 0, "zoh": 1, "zoh_exact": 1}
+
+
+def _dev(t, name, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _io(t, name, dtype, shape, device):
+    _dev(t, name, device)
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def _f32(t, name, shape, device):
+    if t is None:
+        return None
+    return _io(t, name, torch.float32, shape, device)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def ssm_selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
+                           delta_softplus=False, h0=None, bbar="delta", y=None,
+                           final_state=None, want_final_state=True):
+    """Forward selective scan; returns (y, final_state or None)."""
+    _dev(u, "u", None)
+    dev = u.device
+    if u.dim() != 3:
+        raise ValueError("u must be [batch, dim, L]")
+    if u.dtype not in _IO:
+        raise TypeError(f"u has dtype {u.dtype}; expected bfloat16 or float32")
+    batch, dim, L = u.shape
+    if A.dim() != 2:
+        raise ValueError("A must be [dim, dstate]")
+    N = A.shape[1]
+    io = u.dtype
+    _io(delta, "delta", io, (batch, dim, L), dev)
+    _io(A, "A", torch.float32, (dim, N), dev)
+    _io(B, "B", io, (batch, N, L), dev)
+    _io(C, "C", io, (batch, N, L), dev)
+    _f32(D, "D", (dim,), dev)
+    if z is not None:
+        _io(z, "z", io, (batch, dim, L), dev)
+    _f32(delta_bias, "delta_bias", (dim,), dev)
+    _f32(h0, "h0", (batch, dim, N), dev)
+    if y is None:
+        y = torch.empty((batch, dim, L), dtype=io, device=dev)
+    else:
+        _io(y, "y", io, (batch, dim, L), dev)
+    if final_state is None and want_final_state:
+        final_state = torch.empty((batch, dim, N), dtype=torch.float32, device=dev)
+    elif final_state is not None:
+        _f32(final_state, "final_state", (batch, dim, N), dev)
+    with torch.cuda.device(dev):
+        st = lib().ssm_selective_scan_fwd(
+            _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+            int(bool(delta_softplus)), _ptr(h0), _ptr(y), _ptr(final_state), batch, dim, N, L,
+            _IO[io], _BBAR[bbar], _stream(dev))
+    check(st, "ssm_selective_scan_fwd")
+    return y, final_state
+
+
+def ssm_state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None,
+                     delta_softplus=False, bbar="delta", y=None):
+    """One decode step; updates `state` in place and returns y [batch, dim]."""
+    _dev(state, "state", None)
+    dev = state.device
+    if state.dim() != 3 or state.dtype != torch.float32:
+        raise ValueError("state must be float32 [batch, dim, dstate]")
+    batch, dim, N = state.shape
+    if u.dtype not in _IO:
+        raise TypeError(f"u has dtype {u.dtype}; expected bfloat16 or float32")
+    io = u.dtype
+    _io(u, "u", io, (batch, dim), dev)
+    _io(delta, "delta", io, (batch, dim), dev)
+    _io(A, "A", torch.float32, (dim, N), dev)
+    _io(B, "B", io, (batch, N), dev)
+    _io(C, "C", io, (batch, N), dev)
+    _f32(D, "D", (dim,), dev)
+    if z is not None:
+        _io(z, "z", io, (batch, dim), dev)
+    _f32(delta_bias, "delta_bias", (dim,), dev)
+    if y is None:
+        y = torch.empty((batch, dim), dtype=io, device=dev)
+    else:
+        _io(y, "y", io, (batch, dim), dev)
+    with torch.cuda.device(dev):
+        st = lib().ssm_state_update(
+            _ptr(state), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+            _ptr(delta_bias), int(bool(delta_softplus)), _ptr(y), batch, dim, N, _IO[io],
+            _BBAR[bbar], _stream(dev))
+    check(st, "ssm_state_update")
+    return y
+
+
+def ssm_lti_kernel(A, Bv, Cv, delta, L, bbar="delta", K=None):
+    """K[d, k] = sum_n C Abar^k Bbar for k < L.  Bv/Cv are [dstate] (shared by
+    every channel) or [dim, dstate]."""
+    _dev(A, "A", None)
+    dev = A.device
+    dim, N = A.shape
+    _io(A, "A", torch.float32, (dim, N), dev)
+    bs = 0 if Bv.dim() == 1 else N
+    cs = 0 if Cv.dim() == 1 else N
+    _io(Bv, "Bv", torch.float32, (N,) if bs == 0 else (dim, N), dev)
+    _io(Cv, "Cv", torch.float32, (N,) if cs == 0 else (dim, N), dev)
+    _io(delta, "delta", torch.float32, (dim,), dev)
+    if K is None:
+        K = torch.empty((dim, L), dtype=torch.float32, device=dev)
+    else:
+        _io(K, "K", torch.float32, (dim, L), dev)
+    with torch.cuda.device(dev):
+        st = lib().ssm_lti_kernel(_ptr(A), _ptr(Bv), _ptr(Cv), _ptr(delta), _ptr(K), dim, N, L,
+                                  bs, cs, _BBAR[bbar], _stream(dev))
+    check(st, "ssm_lti_kernel")
+    return K

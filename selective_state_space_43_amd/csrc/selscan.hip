@@ -1,0 +1,734 @@
+// libselscan -- selective state-space scan for AMD Instinct MI355X (gfx950).
+//
+// The operation (see include/selscan.h for the ABI):
+//   delta_t = softplus(raw_t + bias),  Abar_t = exp(delta_t A),
+//   h_t = Abar_t h_{t-1} + Bbar_t u_t,  y_t = (C_t . h_t + D u_t) silu(z_t)
+// ("State-space models", sections "Discretization", "Recurrence and
+// convolution", "Mamba: selection", "The parallel scan").
+//
+// Forward-scan design (gfx950, wave64):
+//  * Lanes run along time.  A group of LPC lanes owns one channel (b, d); each
+//    lane owns K consecutive timesteps of a chunk of LPC*K timesteps.  A wave
+//    holds 64/LPC channels; a workgroup of W waves holds channels of one
+//    sequence b, so the selective B_t, C_t (shared by every channel of a
+//    sequence) are staged once per chunk in LDS as float32 and read by all
+//    of them.
+//  * Per state n each lane discretizes its K steps (one exp2 each), folds them
+//    into one pair (prod Abar, local state) with the composition
+//    (a1, b1) o (a2, b2) = (a1 a2, a2 b1 + b2) ("Structured State Space Models
+//    and Mamba ...", section "Hardware-Aware Parallel Associative Scan"),
+//    the LPC lane pairs are scanned with DPP row shifts/broadcasts, the
+//    channel's carry from the previous chunk is applied, and each lane
+//    replays its K steps from its exact incoming state, accumulating the
+//    readout C_t . h_t.  The expanded state never leaves registers.
+//  * The chunk carry lives in LDS ([channels of the block][dstate]), so dstate
+//    is a runtime value.  Step size, softplus, D skip and silu gate are fused.
+//  * Everything is float32; bf16 inputs are widened exactly, y is rounded to
+//    bf16 with round-to-nearest-even (v_cvt_pk_bf16_f32).
+#include <hip/hip_runtime.h>
+
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "selscan.h"
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------- math
+
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float lg2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// softplus(x) = log(1 + e^x).  Above 15 it equals x to within 2e-8 relative.
+// Below, log1p(e) is log(1 + e) with the rounding of 1 + e compensated to
+// first order, which keeps relative accuracy for tiny e.
+__device__ __forceinline__ float softplus_f(float x) {
+  const float e = ex2(x * kLog2e);
+  const float u = 1.0f + e;
+  const float l = lg2(u) * kLn2 - ((u - 1.0f) - e) * rcp(u);
+  return x > 15.0f ? x : l;
+}
+
+// silu(z) = z * sigmoid(z)
+__device__ __forceinline__ float silu_f(float z) { return z * rcp(1.0f + ex2(-z * kLog2e)); }
+
+// exp(r) - 1 for the exact zero-order-hold input rule; `e` is exp(r).
+__device__ __forceinline__ float expm1_f(float r, float e) {
+  const float p = r * (1.0f + r * (0.5f + r * (1.0f / 6 + r * (1.0f / 24 + r * (1.0f / 120)))));
+  return fabsf(r) < 0.03125f ? p : e - 1.0f;
+}
+
+// ---------------------------------------------------------------- io
+
+// bf16 is the upper half of an IEEE binary32.
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const __bf16 a = (__bf16)lo, b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+template <typename IO>
+struct Io;
+
+template <>
+struct Io<float> {
+  static constexpr int V = 4;  // elements per 16-byte access
+  __device__ static float ld1(const void* p, int64_t i) { return static_cast<const float*>(p)[i]; }
+  __device__ static void ldv(const void* p, int64_t i, float* o) {
+    const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+    o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+  }
+  __device__ static void st1(void* p, int64_t i, float v) { static_cast<float*>(p)[i] = v; }
+  __device__ static void stv(void* p, int64_t i, const float* v) {
+    *reinterpret_cast<float4*>(static_cast<float*>(p) + i) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+};
+
+template <>
+struct Io<uint16_t> {  // bf16 bit patterns
+  static constexpr int V = 8;
+  __device__ static float ld1(const void* p, int64_t i) {
+    return __uint_as_float((uint32_t) static_cast<const uint16_t*>(p)[i] << 16);
+  }
+  __device__ static void ldv(const void* p, int64_t i, float* o) {
+    const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p) + i);
+    o[0] = bf_lo(v.x); o[1] = bf_hi(v.x); o[2] = bf_lo(v.y); o[3] = bf_hi(v.y);
+    o[4] = bf_lo(v.z); o[5] = bf_hi(v.z); o[6] = bf_lo(v.w); o[7] = bf_hi(v.w);
+  }
+  __device__ static void st1(void* p, int64_t i, float v) {
+    const __bf16 h = (__bf16)v;
+    static_cast<uint16_t*>(p)[i] = __builtin_bit_cast(uint16_t, h);
+  }
+  __device__ static void stv(void* p, int64_t i, const float* v) {
+    uint4 w;
+    w.x = pack_bf16x2(v[0], v[1]); w.y = pack_bf16x2(v[2], v[3]);
+    w.z = pack_bf16x2(v[4], v[5]); w.w = pack_bf16x2(v[6], v[7]);
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p) + i) = w;
+  }
+};
+
+// K consecutive elements starting at p[base + t]; zero where t >= L.
+template <typename IO, int K>
+__device__ __forceinline__ void load_run(const void* p, int64_t base, int64_t t, int64_t L,
+                                         bool vec, bool valid, float* o) {
+  if (valid && vec && t + K <= L) {
+#pragma unroll
+    for (int i = 0; i < K; i += Io<IO>::V) Io<IO>::ldv(p, base + t + i, o + i);
+  } else {
+#pragma unroll
+    for (int i = 0; i < K; ++i) o[i] = (valid && t + i < L) ? Io<IO>::ld1(p, base + t + i) : 0.0f;
+  }
+}
+
+template <typename IO, int K>
+__device__ __forceinline__ void store_run(void* p, int64_t base, int64_t t, int64_t L, bool vec,
+                                          bool valid, const float* v) {
+  if (!valid) return;
+  if (vec && t + K <= L) {
+#pragma unroll
+    for (int i = 0; i < K; i += Io<IO>::V) Io<IO>::stv(p, base + t + i, v + i);
+  } else {
+#pragma unroll
+    for (int i = 0; i < K; ++i)
+      if (t + i < L) Io<IO>::st1(p, base + t + i, v[i]);
+  }
+}
+
+// ---------------------------------------------------------------- cross-lane
+
+// DPP move: lanes whose source is outside the pattern (or masked by row_mask)
+// receive `old`.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp(float old, float src) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src), CTRL,
+                                                    ROW_MASK, 0xf, false));
+}
+
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143, kWaveShr1 = 0x138;
+
+// One Hillis-Steele step: combine with the pair 2^s lanes earlier (identity
+// (1, 0) where there is none).  (A_prev, H_prev) then (A, H) composes to
+// (A_prev A, A H_prev + H).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void scan_step(float& A, float& H) {
+  const float As = dpp<CTRL, ROW_MASK>(1.0f, A);
+  const float Hs = dpp<CTRL, ROW_MASK>(0.0f, H);
+  H = fmaf(A, Hs, H);
+  A = A * As;
+}
+
+// Inclusive scan of (A, H) pairs over each group of LPC consecutive lanes.
+template <int LPC>
+__device__ __forceinline__ void group_scan(float& A, float& H) {
+  scan_step<kRowShr1, 0xf>(A, H);
+  scan_step<kRowShr2, 0xf>(A, H);
+  scan_step<kRowShr4, 0xf>(A, H);
+  scan_step<kRowShr8, 0xf>(A, H);
+  if constexpr (LPC >= 32) scan_step<kRowBcast15, 0xa>(A, H);
+  if constexpr (LPC >= 64) scan_step<kRowBcast31, 0xc>(A, H);
+}
+
+// Value of the previous lane of the group; `first` lanes get `id`.
+template <int LPC>
+__device__ __forceinline__ float group_prev(float id, float v, bool first) {
+  if constexpr (LPC == 16) {
+    return dpp<kRowShr1, 0xf>(id, v);
+  } else {
+    const float p = dpp<kWaveShr1, 0xf>(id, v);
+    return (LPC == 64 || !first) ? p : id;
+  }
+}
+
+// ---------------------------------------------------------------- forward scan
+
+struct ScanArgs {
+  const void* u;
+  const void* delta;
+  const float* A;
+  const void* Bm;
+  const void* Cm;
+  const float* Dskip;
+  const void* z;
+  const float* delta_bias;
+  const float* h0;
+  void* y;
+  float* final_state;
+  int64_t dim, dstate, seqlen;
+  int softplus;
+  int vec;  // every sequence row starts 16-byte aligned
+};
+
+template <typename IO, int LPC, int K, int W, int NT, bool ZOH, bool GATE>
+__global__ void __launch_bounds__(64 * W)
+    scan_fwd_kernel(const ScanArgs a) {
+  constexpr int CPW = 64 / LPC;  // channels per wave
+  constexpr int CPB = CPW * W;   // channels per workgroup
+  constexpr int T = LPC * K;     // timesteps per chunk
+  constexpr int KP = K + 4;      // padded per-lane run in LDS (spreads banks)
+  constexpr int V = Io<IO>::V;
+  static_assert(K % V == 0 && K % 4 == 0, "K must be a multiple of the vector width");
+  __shared__ float4 sB4[NT * LPC * KP / 4];
+  __shared__ float4 sC4[NT * LPC * KP / 4];
+  extern __shared__ float sDyn[];  // [CPB][dstate] carry, then [CPB][dstate] A
+  float* sB = reinterpret_cast<float*>(sB4);
+  float* sC = reinterpret_cast<float*>(sC4);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int seg = lane % LPC;
+  const int chb = wave * CPW + lane / LPC;
+  const int64_t b = blockIdx.y;
+  const int64_t d0 = (int64_t)blockIdx.x * CPB;
+  const int64_t d = d0 + chb;
+  const bool dvalid = d < a.dim;
+  const int64_t N = a.dstate, L = a.seqlen;
+  const int64_t row = (b * a.dim + (dvalid ? d : 0)) * L;
+  const int64_t bcrow = b * N * L;
+  const bool vec = a.vec != 0;
+
+  float* sCarry = sDyn;
+  float* sA = sDyn + CPB * N;
+  for (int64_t i = threadIdx.x; i < CPB * N; i += 64 * W) {
+    const int64_t c = i / N, n = i % N;
+    const bool ok = d0 + c < a.dim;
+    sCarry[i] = (a.h0 && ok) ? a.h0[(b * a.dim + d0 + c) * N + n] : 0.0f;
+    sA[i] = ok ? a.A[(d0 + c) * N + n] : 0.0f;
+  }
+  const float Dd = (a.Dskip && dvalid) ? a.Dskip[d] : 0.0f;
+  const float bias = (a.delta_bias && dvalid) ? a.delta_bias[d] : 0.0f;
+
+  for (int64_t t0 = 0; t0 < L; t0 += T) {
+    const int64_t tl = t0 + seg * K;
+    float dt[K], w[K], y[K], uu[K];
+    {
+      float raw[K];
+      load_run<IO, K>(a.u, row, tl, L, vec, dvalid, uu);
+      load_run<IO, K>(a.delta, row, tl, L, vec, dvalid, raw);
+#pragma unroll
+      for (int i = 0; i < K; ++i) {
+        const bool ok = dvalid && tl + i < L;
+        const float x = raw[i] + bias;
+        const float s = a.softplus ? softplus_f(x) : x;
+        dt[i] = ok ? s : 0.0f;  // identity step (Abar = 1, Bbar u = 0) past the end
+        w[i] = dt[i] * uu[i];
+        y[i] = Dd * uu[i];
+      }
+    }
+    float S = 0.0f;
+#pragma unroll
+    for (int i = 0; i < K; ++i) S += dt[i];
+
+    for (int64_t n0 = 0; n0 < N; n0 += NT) {
+      const int nt = (int)((N - n0) < NT ? (N - n0) : NT);
+      __syncthreads();
+      // stage B, C rows [n0, n0 + nt) x [t0, t0 + T) as float32
+      for (int item = threadIdx.x; item < 2 * nt * (T / V); item += 64 * W) {
+        const int tensor = item / (nt * (T / V));
+        const int r = item % (nt * (T / V));
+        const int nl = r / (T / V);
+        const int tloc = (r % (T / V)) * V;
+        const void* src = tensor ? a.Cm : a.Bm;
+        float* dst = (tensor ? sC : sB) + (nl * LPC + tloc / K) * KP + tloc % K;
+        float v[V];
+        load_run<IO, V>(src, bcrow + (n0 + nl) * L, t0 + tloc, L, vec, true, v);
+#pragma unroll
+        for (int q = 0; q < V; q += 4)
+          *reinterpret_cast<float4*>(dst + q) = make_float4(v[q], v[q + 1], v[q + 2], v[q + 3]);
+      }
+      __syncthreads();
+
+      for (int j = 0; j < nt; ++j) {
+        const int64_t n = n0 + j;
+        const float An = sA[chb * N + n];
+        const float A2 = An * kLog2e;
+        const float* pb = sB + (j * LPC + seg) * KP;
+        const float* pc = sC + (j * LPC + seg) * KP;
+        float av[K], xv[K];
+#pragma unroll
+        for (int i = 0; i < K; i += 4) {
+          const float4 bb = *reinterpret_cast<const float4*>(pb + i);
+          const float bq[4] = {bb.x, bb.y, bb.z, bb.w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            av[i + q] = ex2(dt[i + q] * A2);
+            if constexpr (ZOH) {
+              const float r = dt[i + q] * An;
+              const float coef = An != 0.0f ? expm1_f(r, av[i + q]) * rcp(An) : dt[i + q];
+              xv[i + q] = coef * bq[q] * uu[i + q];
+            } else {
+              xv[i + q] = w[i + q] * bq[q];
+            }
+          }
+        }
+        // local fold of the lane's K steps from a zero state
+        float H = xv[0];
+#pragma unroll
+        for (int i = 1; i < K; ++i) H = fmaf(av[i], H, xv[i]);
+        float Ag = ex2(A2 * S);
+        group_scan<LPC>(Ag, H);
+        const bool first = seg == 0;
+        const float Ae = group_prev<LPC>(1.0f, Ag, first);
+        const float He = group_prev<LPC>(0.0f, H, first);
+        float* carry = sCarry + chb * N + n;
+        const float c = *carry;
+        float h = fmaf(Ae, c, He);
+        if (seg == LPC - 1) *carry = fmaf(Ag, c, H);
+#pragma unroll
+        for (int i = 0; i < K; i += 4) {
+          const float4 cc = *reinterpret_cast<const float4*>(pc + i);
+          const float cq[4] = {cc.x, cc.y, cc.z, cc.w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            h = fmaf(av[i + q], h, xv[i + q]);
+            y[i + q] = fmaf(cq[q], h, y[i + q]);
+          }
+        }
+      }
+    }
+    if constexpr (GATE) {
+      float zz[K];
+      load_run<IO, K>(a.z, row, tl, L, vec, dvalid, zz);
+#pragma unroll
+      for (int i = 0; i < K; ++i) y[i] *= silu_f(zz[i]);
+    }
+    store_run<IO, K>(a.y, row, tl, L, vec, dvalid, y);
+  }
+  if (a.final_state && dvalid) {
+    // each channel's carry was written by its own wave; LDS is in order per wave
+    for (int64_t n = seg; n < N; n += LPC)
+      a.final_state[(b * a.dim + d) * N + n] = sCarry[chb * N + n];
+  }
+}
+
+// ---------------------------------------------------------------- decode step
+
+struct StepArgs {
+  float* state;
+  const void* u;
+  const void* delta;
+  const float* A;
+  const void* Bm;
+  const void* Cm;
+  const float* Dskip;
+  const void* z;
+  const float* delta_bias;
+  void* y;
+  int64_t batch, dim, dstate;
+  int softplus;
+};
+
+// Four lanes per channel; lane q of a channel updates states q*4 .. q*4+3 of
+// each block of 16, so a wave reads and writes 16 channels' states as one
+// contiguous run.  The readout is summed over the four lanes.
+template <typename IO, bool ZOH, bool GATE>
+__global__ void __launch_bounds__(256) state_update_kernel(const StepArgs a) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int q = threadIdx.x & 3;
+  const int64_t ch = gid >> 2;
+  const bool valid = ch < a.batch * a.dim;
+  const int64_t c = valid ? ch : 0;
+  const int64_t b = c / a.dim, d = c % a.dim;
+  const int64_t N = a.dstate;
+  const float uu = Io<IO>::ld1(a.u, c);
+  const float raw = Io<IO>::ld1(a.delta, c) + (a.delta_bias ? a.delta_bias[d] : 0.0f);
+  const float dt = a.softplus ? softplus_f(raw) : raw;
+  const float w = dt * uu;
+  float acc = 0.0f;
+  float* st = a.state + c * N;
+  const bool vec4 = (N & 3) == 0;
+  for (int64_t nb = 0; nb < N; nb += 16) {
+    const int64_t n = nb + q * 4;
+    if (n >= N) continue;
+    const int cnt = (int)((N - n) < 4 ? (N - n) : 4);
+    float h[4] = {0, 0, 0, 0};
+    if (valid) {
+      if (vec4) {
+        const float4 v = *reinterpret_cast<const float4*>(st + n);
+        h[0] = v.x; h[1] = v.y; h[2] = v.z; h[3] = v.w;
+      } else {
+        for (int k = 0; k < cnt; ++k) h[k] = st[n + k];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (k < cnt) {
+        const float An = a.A[d * N + n + k];
+        const float e = ex2(dt * An * kLog2e);
+        const float Bv = Io<IO>::ld1(a.Bm, b * N + n + k);
+        const float Cv = Io<IO>::ld1(a.Cm, b * N + n + k);
+        float x;
+        if constexpr (ZOH) {
+          const float coef = An != 0.0f ? expm1_f(dt * An, e) * rcp(An) : dt;
+          x = coef * Bv * uu;
+        } else {
+          x = w * Bv;
+        }
+        h[k] = fmaf(e, h[k], x);
+        acc = fmaf(Cv, h[k], acc);
+      }
+    }
+    if (valid) {
+      if (vec4) {
+        *reinterpret_cast<float4*>(st + n) = make_float4(h[0], h[1], h[2], h[3]);
+      } else {
+        for (int k = 0; k < cnt; ++k) st[n + k] = h[k];
+      }
+    }
+  }
+  // sum the four partial readouts of the channel (lanes 4c .. 4c+3)
+  acc += __shfl_xor(acc, 1);
+  acc += __shfl_xor(acc, 2);
+  if (valid && q == 0) {
+    float yv = acc + (a.Dskip ? a.Dskip[d] : 0.0f) * uu;
+    if constexpr (GATE) yv *= silu_f(Io<IO>::ld1(a.z, c));
+    Io<IO>::st1(a.y, c, yv);
+  }
+}
+
+// ---------------------------------------------------------------- LTI kernel
+
+template <bool ZOH>
+__global__ void __launch_bounds__(256)
+    lti_kernel_kernel(const float* A, const float* Bv, const float* Cv, const float* delta,
+                      float* K, int64_t dim, int64_t N, int64_t L, int64_t bs, int64_t cs) {
+  const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t d = blockIdx.y;
+  if (k >= L) return;
+  const float dt = delta[d];
+  float acc = 0.0f;
+  for (int64_t n = 0; n < N; ++n) {
+    const float An = A[d * N + n];
+    float bbar;
+    if constexpr (ZOH) {
+      bbar = An != 0.0f ? expm1_f(dt * An, ex2(dt * An * kLog2e)) * rcp(An) : dt;
+    } else {
+      bbar = dt;
+    }
+    bbar *= Bv[d * bs + n];
+    // Abar^k = exp(k dt A)
+    acc = fmaf(Cv[d * cs + n] * ex2((float)k * (dt * An * kLog2e)), bbar, acc);
+  }
+  K[d * L + k] = acc;
+}
+
+// ---------------------------------------------------------------- host side
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+struct Span {
+  const void* p;
+  int64_t bytes;
+  const char* name;
+};
+
+bool overlaps(const Span& x, const Span& y) {
+  if (!x.p || !y.p || x.bytes <= 0 || y.bytes <= 0) return false;
+  const uintptr_t a0 = (uintptr_t)x.p, a1 = a0 + (uintptr_t)x.bytes;
+  const uintptr_t b0 = (uintptr_t)y.p, b1 = b0 + (uintptr_t)y.bytes;
+  return a0 < b1 && b0 < a1;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+constexpr int64_t kMaxExtent = (int64_t)1 << 40;
+constexpr int64_t kMaxDstate = 64;
+
+int check_extent(const char* name, int64_t v) {
+  if (v <= 0 || v > kMaxExtent) return fail(SSM_E_SHAPE, "%s = %lld is out of range", name, (long long)v);
+  return SSM_OK;
+}
+
+// a * b * c * d <= 2^60 (byte sizes of every tensor stay far from overflow)
+bool product_ok(int64_t a, int64_t b, int64_t c = 1, int64_t d = 1) {
+  const int64_t lim = (int64_t)1 << 60;
+  int64_t p = a;
+  for (int64_t f : {b, c, d}) {
+    if (p > lim / f) return false;
+    p *= f;
+  }
+  return true;
+}
+
+int launch_status(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(SSM_E_HIP, "%s: %s", what, hipGetErrorString(e));
+  return SSM_OK;
+}
+
+template <typename IO, int LPC, int K, int W, int NT>
+int launch_fwd_cfg(const ScanArgs& a, int64_t batch, bool zoh, bool gate, hipStream_t s) {
+  constexpr int CPB = (64 / LPC) * W;
+  const dim3 grid((unsigned)((a.dim + CPB - 1) / CPB), (unsigned)batch);
+  const size_t shmem = 2 * (size_t)CPB * (size_t)a.dstate * sizeof(float);
+  if (zoh) {
+    if (gate) hipLaunchKernelGGL((scan_fwd_kernel<IO, LPC, K, W, NT, true, true>), grid, dim3(64 * W), shmem, s, a);
+    else hipLaunchKernelGGL((scan_fwd_kernel<IO, LPC, K, W, NT, true, false>), grid, dim3(64 * W), shmem, s, a);
+  } else {
+    if (gate) hipLaunchKernelGGL((scan_fwd_kernel<IO, LPC, K, W, NT, false, true>), grid, dim3(64 * W), shmem, s, a);
+    else hipLaunchKernelGGL((scan_fwd_kernel<IO, LPC, K, W, NT, false, false>), grid, dim3(64 * W), shmem, s, a);
+  }
+  return launch_status("ssm_selective_scan_fwd launch");
+}
+
+// Lane layout choice: 16 lanes per channel gives the shortest cross-lane scan;
+// a full wave per channel is used when there are too few channels to give
+// every SIMD of the 256 CUs several waves.
+template <typename IO>
+int launch_fwd(const ScanArgs& a, int64_t batch, bool zoh, bool gate, hipStream_t s) {
+  const int64_t channels = batch * a.dim;
+  if (channels >= 4 * 4096) return launch_fwd_cfg<IO, 16, 16, 4, 16>(a, batch, zoh, gate, s);
+  if (channels >= 2 * 4096) return launch_fwd_cfg<IO, 32, 16, 4, 8>(a, batch, zoh, gate, s);
+  return launch_fwd_cfg<IO, 64, 16, 4, 4>(a, batch, zoh, gate, s);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- C ABI
+
+extern "C" {
+
+int ssm_abi_version(void) { return SSM_ABI_VERSION; }
+
+const char* ssm_last_error(void) { return g_last_error; }
+
+const char* ssm_status_str(int status) {
+  switch (status) {
+    case SSM_OK: return "ok";
+    case SSM_E_NULL: return "required pointer is NULL";
+    case SSM_E_SHAPE: return "extent out of range";
+    case SSM_E_DTYPE: return "unknown io_dtype or bbar_mode";
+    case SSM_E_ALIGN: return "sequence tensor not 16-byte aligned";
+    case SSM_E_ALIAS: return "output overlaps an input";
+    case SSM_E_UNSUPPORTED: return "unsupported dstate";
+    case SSM_E_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int ssm_selective_scan_fwd(const void* u, const void* delta, const float* A, const void* Bm,
+                           const void* Cm, const float* Dskip, const void* z,
+                           const float* delta_bias, int delta_softplus, const float* h0, void* y,
+                           float* final_state, int64_t batch, int64_t dim, int64_t dstate,
+                           int64_t seqlen, int io_dtype, int bbar_mode, void* hip_stream) {
+  g_last_error[0] = 0;
+  if (!u) return fail(SSM_E_NULL, "u is NULL");
+  if (!delta) return fail(SSM_E_NULL, "delta is NULL");
+  if (!A) return fail(SSM_E_NULL, "A is NULL");
+  if (!Bm) return fail(SSM_E_NULL, "B is NULL");
+  if (!Cm) return fail(SSM_E_NULL, "C is NULL");
+  if (!y) return fail(SSM_E_NULL, "y is NULL");
+  int st;
+  if ((st = check_extent("batch", batch)) || (st = check_extent("dim", dim)) ||
+      (st = check_extent("dstate", dstate)) || (st = check_extent("seqlen", seqlen)))
+    return st;
+  if (batch > 65535) return fail(SSM_E_SHAPE, "batch = %lld exceeds 65535", (long long)batch);
+  if (dim > ((int64_t)1 << 30)) return fail(SSM_E_SHAPE, "dim = %lld exceeds 2^30", (long long)dim);
+  if (!product_ok(batch, dim, seqlen, 4) || !product_ok(batch, dim, dstate, 4))
+    return fail(SSM_E_SHAPE, "tensor sizes overflow");
+  if (io_dtype != SSM_DTYPE_F32 && io_dtype != SSM_DTYPE_BF16)
+    return fail(SSM_E_DTYPE, "io_dtype = %d is not SSM_DTYPE_F32 or SSM_DTYPE_BF16", io_dtype);
+  if (bbar_mode != SSM_BBAR_DELTA_B && bbar_mode != SSM_BBAR_ZOH_EXACT)
+    return fail(SSM_E_DTYPE, "bbar_mode = %d is not a known rule", bbar_mode);
+  if (dstate > kMaxDstate)
+    return fail(SSM_E_UNSUPPORTED, "dstate = %lld is outside 1..%lld", (long long)dstate,
+                (long long)kMaxDstate);
+  const int64_t es = io_dtype == SSM_DTYPE_BF16 ? 2 : 4;
+  const int64_t seq_bytes = batch * dim * seqlen * es;
+  const int64_t bc_bytes = batch * dstate * seqlen * es;
+  const int64_t st_bytes = batch * dim * dstate * 4;
+  const Span in[] = {{u, seq_bytes, "u"},
+                     {delta, seq_bytes, "delta"},
+                     {A, dim * dstate * 4, "A"},
+                     {Bm, bc_bytes, "B"},
+                     {Cm, bc_bytes, "C"},
+                     {Dskip, dim * 4, "D"},
+                     {z, z ? seq_bytes : 0, "z"},
+                     {delta_bias, dim * 4, "delta_bias"},
+                     {h0, st_bytes, "h0"}};
+  const void* seq_ptrs[] = {u, delta, Bm, Cm, z, y};
+  const char* seq_names[] = {"u", "delta", "B", "C", "z", "y"};
+  for (int i = 0; i < 6; ++i)
+    if (seq_ptrs[i] && !aligned16(seq_ptrs[i]))
+      return fail(SSM_E_ALIGN, "%s is not 16-byte aligned", seq_names[i]);
+  const Span ys{y, seq_bytes, "y"};
+  for (const Span& s : in)
+    if (overlaps(ys, s)) return fail(SSM_E_ALIAS, "y overlaps %s", s.name);
+  if (final_state) {
+    const Span fs{final_state, st_bytes, "final_state"};
+    if (overlaps(fs, ys)) return fail(SSM_E_ALIAS, "final_state overlaps y");
+    for (const Span& s : in) {
+      if (s.p == h0 && final_state == h0) continue;  // exact in-place resume
+      if (overlaps(fs, s)) return fail(SSM_E_ALIAS, "final_state overlaps %s", s.name);
+    }
+  }
+  ScanArgs a;
+  a.u = u; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm; a.Dskip = Dskip; a.z = z;
+  a.delta_bias = delta_bias; a.h0 = h0; a.y = y; a.final_state = final_state;
+  a.dim = dim; a.dstate = dstate; a.seqlen = seqlen;
+  a.softplus = delta_softplus ? 1 : 0;
+  a.vec = (seqlen % (io_dtype == SSM_DTYPE_BF16 ? 8 : 4)) == 0 ? 1 : 0;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  const bool zoh = bbar_mode == SSM_BBAR_ZOH_EXACT, gate = z != nullptr;
+  return io_dtype == SSM_DTYPE_BF16 ? launch_fwd<uint16_t>(a, batch, zoh, gate, s)
+                                    : launch_fwd<float>(a, batch, zoh, gate, s);
+}
+
+int ssm_state_update(float* state, const void* u, const void* delta, const float* A,
+                     const void* Bm, const void* Cm, const float* Dskip, const void* z,
+                     const float* delta_bias, int delta_softplus, void* y, int64_t batch,
+                     int64_t dim, int64_t dstate, int io_dtype, int bbar_mode, void* hip_stream) {
+  g_last_error[0] = 0;
+  if (!state) return fail(SSM_E_NULL, "state is NULL");
+  if (!u) return fail(SSM_E_NULL, "u is NULL");
+  if (!delta) return fail(SSM_E_NULL, "delta is NULL");
+  if (!A) return fail(SSM_E_NULL, "A is NULL");
+  if (!Bm) return fail(SSM_E_NULL, "B is NULL");
+  if (!Cm) return fail(SSM_E_NULL, "C is NULL");
+  if (!y) return fail(SSM_E_NULL, "y is NULL");
+  int st;
+  if ((st = check_extent("batch", batch)) || (st = check_extent("dim", dim)) ||
+      (st = check_extent("dstate", dstate)))
+    return st;
+  if (!product_ok(batch, dim, dstate, 4)) return fail(SSM_E_SHAPE, "tensor sizes overflow");
+  if (io_dtype != SSM_DTYPE_F32 && io_dtype != SSM_DTYPE_BF16)
+    return fail(SSM_E_DTYPE, "io_dtype = %d is not SSM_DTYPE_F32 or SSM_DTYPE_BF16", io_dtype);
+  if (bbar_mode != SSM_BBAR_DELTA_B && bbar_mode != SSM_BBAR_ZOH_EXACT)
+    return fail(SSM_E_DTYPE, "bbar_mode = %d is not a known rule", bbar_mode);
+  if (dstate > kMaxDstate)
+    return fail(SSM_E_UNSUPPORTED, "dstate = %lld is outside 1..%lld", (long long)dstate,
+                (long long)kMaxDstate);
+  if (!aligned16(state)) return fail(SSM_E_ALIGN, "state is not 16-byte aligned");
+  const int64_t es = io_dtype == SSM_DTYPE_BF16 ? 2 : 4;
+  const int64_t tok = batch * dim * es, bc = batch * dstate * es;
+  const Span st_span{state, batch * dim * dstate * 4, "state"}, ys{y, tok, "y"};
+  const Span in[] = {{u, tok, "u"},        {delta, tok, "delta"},   {A, dim * dstate * 4, "A"},
+                     {Bm, bc, "B"},        {Cm, bc, "C"},           {Dskip, dim * 4, "D"},
+                     {z, z ? tok : 0, "z"}, {delta_bias, dim * 4, "delta_bias"}};
+  if (overlaps(ys, st_span)) return fail(SSM_E_ALIAS, "y overlaps state");
+  for (const Span& s : in) {
+    if (overlaps(ys, s)) return fail(SSM_E_ALIAS, "y overlaps %s", s.name);
+    if (overlaps(st_span, s)) return fail(SSM_E_ALIAS, "state overlaps %s", s.name);
+  }
+  StepArgs a;
+  a.state = state; a.u = u; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm; a.Dskip = Dskip;
+  a.z = z; a.delta_bias = delta_bias; a.y = y; a.batch = batch; a.dim = dim; a.dstate = dstate;
+  a.softplus = delta_softplus ? 1 : 0;
+  const int64_t threads = batch * dim * 4;
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  if (grid.x == 0 || (threads + 255) / 256 > 0x7fffffff)
+    return fail(SSM_E_SHAPE, "batch * dim too large for one launch");
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  const bool zoh = bbar_mode == SSM_BBAR_ZOH_EXACT, gate = z != nullptr;
+#define SSM_STEP(IO)                                                                         \
+  do {                                                                                       \
+    if (zoh) {                                                                               \
+      if (gate) hipLaunchKernelGGL((state_update_kernel<IO, true, true>), grid, dim3(256), 0, s, a);   \
+      else hipLaunchKernelGGL((state_update_kernel<IO, true, false>), grid, dim3(256), 0, s, a);       \
+    } else {                                                                                 \
+      if (gate) hipLaunchKernelGGL((state_update_kernel<IO, false, true>), grid, dim3(256), 0, s, a);  \
+      else hipLaunchKernelGGL((state_update_kernel<IO, false, false>), grid, dim3(256), 0, s, a);      \
+    }                                                                                        \
+  } while (0)
+  if (io_dtype == SSM_DTYPE_BF16) SSM_STEP(uint16_t);
+  else SSM_STEP(float);
+#undef SSM_STEP
+  return launch_status("ssm_state_update launch");
+}
+
+int ssm_lti_kernel(const float* A, const float* Bv, const float* Cv, const float* delta, float* K,
+                   int64_t dim, int64_t dstate, int64_t L, int64_t b_row_stride,
+                   int64_t c_row_stride, int bbar_mode, void* hip_stream) {
+  g_last_error[0] = 0;
+  if (!A) return fail(SSM_E_NULL, "A is NULL");
+  if (!Bv) return fail(SSM_E_NULL, "B is NULL");
+  if (!Cv) return fail(SSM_E_NULL, "C is NULL");
+  if (!delta) return fail(SSM_E_NULL, "delta is NULL");
+  if (!K) return fail(SSM_E_NULL, "K is NULL");
+  int st;
+  if ((st = check_extent("dim", dim)) || (st = check_extent("dstate", dstate)) ||
+      (st = check_extent("L", L)))
+    return st;
+  if (dim > 65535) return fail(SSM_E_SHAPE, "dim = %lld exceeds 65535", (long long)dim);
+  if (!product_ok(dim, L, 4) || !product_ok(dim, dstate, 4) || L > ((int64_t)1 << 36))
+    return fail(SSM_E_SHAPE, "tensor sizes overflow");
+  if (b_row_stride < 0 || c_row_stride < 0)
+    return fail(SSM_E_SHAPE, "row strides must be >= 0");
+  if (bbar_mode != SSM_BBAR_DELTA_B && bbar_mode != SSM_BBAR_ZOH_EXACT)
+    return fail(SSM_E_DTYPE, "bbar_mode = %d is not a known rule", bbar_mode);
+  const Span ks{K, dim * L * 4, "K"};
+  const Span in[] = {{A, dim * dstate * 4, "A"},
+                     {Bv, ((dim - 1) * b_row_stride + dstate) * 4, "B"},
+                     {Cv, ((dim - 1) * c_row_stride + dstate) * 4, "C"},
+                     {delta, dim * 4, "delta"}};
+  for (const Span& s : in)
+    if (overlaps(ks, s)) return fail(SSM_E_ALIAS, "K overlaps %s", s.name);
+  const dim3 grid((unsigned)((L + 255) / 256), (unsigned)dim);
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  if (bbar_mode == SSM_BBAR_ZOH_EXACT)
+    hipLaunchKernelGGL(lti_kernel_kernel<true>, grid, dim3(256), 0, s, A, Bv, Cv, delta, K, dim,
+                       dstate, L, b_row_stride, c_row_stride);
+  else
+    hipLaunchKernelGGL(lti_kernel_kernel<false>, grid, dim3(256), 0, s, A, Bv, Cv, delta, K, dim,
+                       dstate, L, b_row_stride, c_row_stride);
+  return launch_status("ssm_lti_kernel launch");
+}
+
+}  // extern "C"

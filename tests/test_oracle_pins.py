@@ -388,9 +388,10 @@ def test_generators_are_seeded_and_row_addressable():
     _, x2 = wl.custom(2, 3, 4, 40, seed=99)
     for k in ("u", "delta", "z", "B", "C", "A", "D", "delta_bias"):
         assert np.array_equal(x1[k], x2[k])
-    # a row can be regenerated alone
-    row = wl.to_bf16_bits(wl.rng(99, wl.T_U, 4).standard_normal(40, dtype=np.float32))
-    assert np.array_equal(row, x1["u"].reshape(6, 40)[4])
+    # a stream block can be regenerated alone (here all six rows share block 0)
+    assert wl.rows_per_stream(40) >= 6
+    blk = wl.to_bf16_bits(wl.rng(99, wl.T_U, 0).standard_normal(6 * 40, dtype=np.float32))
+    assert np.array_equal(blk.reshape(6, 40), x1["u"].reshape(6, 40))
     A, D, bias = wl.params(wl.WORKLOADS["mamba130m"])
     assert np.array_equal(A[17], -np.arange(1, 17, dtype=np.float32))
     dt0 = np.log1p(np.exp(bias.astype(np.float64)))

@@ -1,0 +1,292 @@
+"""Parity of the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs.  Bound, elementwise: |gpu - oracle| <= tol * (1 + |oracle|)
+with tol = 1e-4 for float32 inputs and 2e-2 for bf16 inputs (the oracle reads
+the identical bf16 bits).  Final states use the same bound."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from helpers import TOL, norm_err, scan_gpu, scan_oracle, to_dev, to_np
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ssm():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import selective_state_space_43_amd as m
+    m.lib()  # loud failure if the library is missing
+    return m
+
+
+@pytest.fixture(scope="module")
+def dev(ssm):
+    return torch.device("cuda:0")
+
+
+def _check(ssm, dev, w, x, bbar="delta", label=""):
+    y, fs = scan_gpu(ssm, x, dev, bbar=bbar)
+    torch.cuda.synchronize()
+    yr, fr = scan_oracle(oracle, x, bbar=bbar)
+    ey = norm_err(to_np(y).reshape(yr.shape), yr)
+    es = norm_err(to_np(fs).reshape(fr.shape), fr)
+    print(f"{label or w.name}: max err y {ey:.3e} state {es:.3e}", flush=True)
+    assert ey <= TOL[w.dtype] and es <= TOL[w.dtype], (ey, es)
+    return y, fs
+
+
+# ---------------------------------------------------------------- the five workloads
+
+def test_tiny_fp32(ssm, dev):
+    w = wl.WORKLOADS["tiny_fp32"]
+    _check(ssm, dev, w, wl.scan_inputs(w))
+
+
+def test_mamba130m_full(ssm, dev):
+    w = wl.WORKLOADS["mamba130m"]
+    _check(ssm, dev, w, wl.scan_inputs(w))
+
+
+def _sampled(ssm, dev, w, x, channels):
+    y, fs = scan_gpu(ssm, x, dev)
+    torch.cuda.synchronize()
+    L, N = w.seqlen, w.dstate
+    yg = y.view(-1, L)[torch.as_tensor(channels, device=dev)]
+    fg = fs.view(-1, N)[torch.as_tensor(channels, device=dev)]
+    yr, fr = scan_oracle(oracle, x, channels=channels)
+    ey, es = norm_err(to_np(yg), yr), norm_err(to_np(fg), fr)
+    finite = bool(torch.isfinite(y.float()).all()) and bool(torch.isfinite(fs).all())
+    print(f"{w.name}: {len(channels)} sampled channels, max err y {ey:.3e} state {es:.3e}",
+          flush=True)
+    assert finite
+    assert ey <= TOL[w.dtype] and es <= TOL[w.dtype], (ey, es)
+
+
+def test_mamba2p8b_full_size_sampled(ssm, dev):
+    w = wl.WORKLOADS["mamba2p8b"]
+    x = wl.scan_inputs(w)
+    r = np.random.default_rng(0)
+    ch = np.concatenate([[0, w.dim - 1, w.batch * w.dim - 1],
+                         r.choice(w.batch * w.dim, 253, replace=False)])
+    _sampled(ssm, dev, w, x, ch)
+
+
+def test_long_context_full_size_sampled(ssm, dev):
+    w = wl.WORKLOADS["long_context"]
+    x = wl.scan_inputs(w)
+    r = np.random.default_rng(1)
+    ch = np.concatenate([[0, w.dim - 1], r.choice(w.dim, 22, replace=False)])
+    _sampled(ssm, dev, w, x, ch)
+
+
+def test_decode_1000_steps(ssm, dev):
+    """Full batch on the GPU; the oracle advances its own fp64 state for a
+    sample of channels and is never re-synchronised to the GPU."""
+    w = wl.WORKLOADS["decode"]
+    A, D, bias = wl.params(w)
+    s0 = wl.decode_state(w)
+    r = np.random.default_rng(2)
+    ch = np.sort(r.choice(w.batch * w.dim, 1024, replace=False))
+    ch_t = torch.as_tensor(ch, device=dev)
+    ref_state = s0.reshape(-1, w.dstate)[ch].astype(np.float64)
+    state = to_dev(s0, dev)
+    Ad, Dd, bd = to_dev(A, dev), to_dev(D, dev), to_dev(bias, dev)
+    worst = 0.0
+    for step in range(w.steps):
+        x = wl.decode_step(w, step)
+        y = ssm.ssm_state_update(state, to_dev(x["u"], dev), to_dev(x["delta"], dev), Ad,
+                                 to_dev(x["B"], dev), to_dev(x["C"], dev), D=Dd,
+                                 z=to_dev(x["z"], dev), delta_bias=bd, delta_softplus=True)
+        yr = oracle.state_update(ref_state, x["u"], x["delta"], A, x["B"], x["C"], D=D, z=x["z"],
+                                 delta_bias=bias, delta_softplus=True, channels=ch)
+        ey = norm_err(to_np(y.view(-1)[ch_t]), yr)
+        worst = max(worst, ey)
+        assert ey <= TOL["bf16"], (step, ey)
+        if step % 100 == 99 or step == w.steps - 1:
+            es = norm_err(to_np(state.view(-1, w.dstate)[ch_t]), ref_state)
+            print(f"decode step {step + 1}: max err y so far {worst:.3e}, state {es:.3e}",
+                  flush=True)
+            assert es <= TOL["bf16"], (step, es)
+
+
+# ---------------------------------------------------------------- shapes, tails, modes
+
+# (batch, dim, N, L, dtype, gate, bias): the channel counts select each lane
+# layout (>= 16384 channels: 16 lanes per channel, >= 8192: 32, else 64); the
+# lengths cover one step, partial chunks, exact chunks and ragged tails.
+CASES = [
+    (1, 3, 1, 1, "f32", False, False),
+    (2, 5, 4, 7, "f32", True, True),
+    (1, 37, 16, 255, "bf16", True, True),
+    (1, 40, 16, 256, "bf16", False, True),
+    (3, 21, 17, 1000, "bf16", True, False),
+    (2, 33, 33, 1025, "f32", True, True),
+    (1, 9, 64, 777, "bf16", True, True),
+    (1, 17, 8, 4099, "f32", False, False),
+    (2, 8192, 4, 72, "bf16", True, True),
+    (1, 16384, 2, 40, "bf16", True, True),
+    (4, 4100, 3, 33, "f32", True, True),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "b%d_d%d_n%d_l%d_%s%s%s" % (
+    c[0], c[1], c[2], c[3], c[4], "_z" if c[5] else "", "_bias" if c[6] else ""))
+def test_shapes_and_tails(ssm, dev, case):
+    b, d, n, L, dt, gate, bias = case
+    w, x = wl.custom(b, d, n, L, dtype=dt, gate=gate, bias=bias, seed=100 + L + d)
+    _check(ssm, dev, w, x, label=str(case))
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_exact_zoh_rule(ssm, dev, dt):
+    w, x = wl.custom(2, 24, 16, 600, dtype=dt, gate=True, seed=31)
+    _check(ssm, dev, w, x, bbar="zoh", label=f"zoh {dt}")
+
+
+def test_no_softplus_positive_raw_step(ssm, dev):
+    w, x = wl.custom(1, 20, 8, 300, dtype="f32", gate=False, bias=False, seed=41)
+    x["delta"] = np.abs(x["delta"]) * np.float32(0.1)
+    x["delta_softplus"] = False
+    _check(ssm, dev, w, x, label="raw step")
+
+
+def test_h0_resume_in_place_equals_full_scan(ssm, dev):
+    w, x = wl.custom(2, 40, 16, 2000, dtype="f32", gate=True, seed=51)
+    cut = 1100
+
+    def part(lo, hi):
+        return {k: (v[..., lo:hi] if isinstance(v, np.ndarray) and v.ndim == 3 else v)
+                for k, v in x.items()}
+
+    y1, f1 = scan_gpu(ssm, part(0, cut), dev)
+    # second piece resumes in place: final_state is the same buffer as h0
+    y2, f2 = scan_gpu(ssm, part(cut, 2000), dev, h0=f1, final_state=f1)
+    torch.cuda.synchronize()
+    yr, fr = scan_oracle(oracle, x)
+    y = np.concatenate([to_np(y1), to_np(y2)], axis=-1).reshape(yr.shape)
+    assert norm_err(y, yr) <= TOL["f32"]
+    assert norm_err(to_np(f2).reshape(fr.shape), fr) <= TOL["f32"]
+
+
+def test_h0_from_oracle_state(ssm, dev):
+    w, x = wl.custom(1, 30, 16, 500, dtype="bf16", gate=False, seed=61)
+    h0 = np.random.default_rng(3).normal(0, 0.5, (1, 30, 16)).astype(np.float32)
+    y, fs = scan_gpu(ssm, x, dev, h0=to_dev(h0, dev))
+    torch.cuda.synchronize()
+    yr, fr = scan_oracle(oracle, x, h0=h0.reshape(30, 16))
+    assert norm_err(to_np(y).reshape(yr.shape), yr) <= TOL["bf16"]
+    assert norm_err(to_np(fs).reshape(fr.shape), fr) <= TOL["bf16"]
+
+
+def test_repeat_runs_are_bitwise_identical(ssm, dev):
+    w, x = wl.custom(2, 512, 16, 2048, seed=71)
+    y1, f1 = scan_gpu(ssm, x, dev)
+    y2, f2 = scan_gpu(ssm, x, dev)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(f1.view(torch.int32), f2.view(torch.int32))
+
+
+def test_decode_steps_replay_the_scan(ssm, dev):
+    """L single-token steps on the GPU agree with the GPU scan of the same L tokens."""
+    w, x = wl.custom(2, 64, 16, 64, dtype="f32", gate=True, seed=81)
+    y, fs = scan_gpu(ssm, x, dev)
+    state = torch.zeros((2, 64, 16), dtype=torch.float32, device=dev)
+    ys = []
+    for t in range(64):
+        col = {k: np.ascontiguousarray(v[..., t]) for k, v in x.items()
+               if isinstance(v, np.ndarray) and v.ndim == 3}
+        ys.append(ssm.ssm_state_update(state, to_dev(col["u"], dev), to_dev(col["delta"], dev),
+                                       to_dev(x["A"], dev), to_dev(col["B"], dev),
+                                       to_dev(col["C"], dev), D=to_dev(x["D"], dev),
+                                       z=to_dev(col["z"], dev),
+                                       delta_bias=to_dev(x["delta_bias"], dev),
+                                       delta_softplus=True))
+    torch.cuda.synchronize()
+    yd = torch.stack(ys, dim=-1)
+    assert norm_err(to_np(yd), to_np(y)) <= TOL["f32"]
+    assert norm_err(to_np(state), to_np(fs)) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_state_update_small_shapes(ssm, dev, dt):
+    for (b, d, n) in [(1, 1, 1), (3, 7, 5), (2, 33, 16), (5, 19, 64)]:
+        w, x = wl.custom(b, d, n, 1, dtype=dt, gate=True, seed=90 + n)
+        col = {k: np.ascontiguousarray(v[..., 0]) for k, v in x.items()
+               if isinstance(v, np.ndarray) and v.ndim == 3}
+        s0 = np.random.default_rng(n).normal(0, 0.3, (b, d, n)).astype(np.float32)
+        state = to_dev(s0, dev)
+        y = ssm.ssm_state_update(state, to_dev(col["u"], dev), to_dev(col["delta"], dev),
+                                 to_dev(x["A"], dev), to_dev(col["B"], dev), to_dev(col["C"], dev),
+                                 D=to_dev(x["D"], dev), z=to_dev(col["z"], dev),
+                                 delta_bias=to_dev(x["delta_bias"], dev), delta_softplus=True)
+        torch.cuda.synchronize()
+        ref = s0.reshape(-1, n).astype(np.float64)
+        yr = oracle.state_update(ref, col["u"], col["delta"], x["A"], col["B"], col["C"],
+                                 D=x["D"], z=col["z"], delta_bias=x["delta_bias"],
+                                 delta_softplus=True)
+        assert norm_err(to_np(y).reshape(-1), yr) <= TOL[dt]
+        assert norm_err(to_np(state).reshape(ref.shape), ref) <= TOL[dt]
+
+
+# ---------------------------------------------------------------- LTI check path
+
+@pytest.mark.parametrize("bbar", ["delta", "zoh"])
+def test_lti_kernel_matches_oracle(ssm, dev, bbar):
+    r = np.random.default_rng(5)
+    dim, N, L = 12, 16, 700
+    A = -np.exp(r.uniform(np.log(0.5), np.log(16), (dim, N))).astype(np.float32)
+    Bv = r.standard_normal((dim, N)).astype(np.float32)
+    Cv = r.standard_normal(N).astype(np.float32)
+    dt = r.uniform(0.001, 0.1, dim).astype(np.float32)
+    K = ssm.ssm_lti_kernel(to_dev(A, dev), to_dev(Bv, dev), to_dev(Cv, dev), to_dev(dt, dev), L,
+                           bbar=bbar)
+    torch.cuda.synchronize()
+    Kr = oracle.lti_kernel(A, Bv, Cv, dt, L, bbar=bbar)
+    assert norm_err(to_np(K), Kr) <= 1e-4
+
+
+def test_time_invariant_scan_equals_kernel_convolution(ssm, dev):
+    """With delta, B, C fixed in time, the GPU scan equals the causal
+    convolution of u with the GPU kernel K (plus D u)."""
+    r = np.random.default_rng(6)
+    dim, N, L = 6, 16, 512
+    A = -np.exp(r.uniform(np.log(0.5), np.log(16), (dim, N))).astype(np.float32)
+    Bv = r.standard_normal(N).astype(np.float32)
+    Cv = r.standard_normal(N).astype(np.float32)
+    dt = r.uniform(0.01, 0.2, dim).astype(np.float32)
+    Dv = r.standard_normal(dim).astype(np.float32)
+    u = r.standard_normal((1, dim, L)).astype(np.float32)
+    x = dict(u=u, delta=np.repeat(dt[None, :, None], L, axis=2).copy(), A=A,
+             B=np.repeat(Bv[None, :, None], L, axis=2).copy(),
+             C=np.repeat(Cv[None, :, None], L, axis=2).copy(), D=Dv, z=None, delta_bias=None,
+             delta_softplus=False)
+    y, _ = scan_gpu(ssm, x, dev)
+    K = ssm.ssm_lti_kernel(to_dev(A, dev), to_dev(Bv, dev), to_dev(Cv, dev), to_dev(dt, dev), L)
+    torch.cuda.synchronize()
+    Kn = to_np(K)
+    for d in range(dim):
+        yc = oracle.causal_conv(Kn[d], u[0, d], float(Dv[d]))
+        assert norm_err(to_np(y[0, d]), yc) <= 1e-4
+
+
+# ---------------------------------------------------------------- ABI errors with real buffers
+
+def test_abi_rejects_misaligned_and_aliased_buffers(ssm, dev):
+    w, x = wl.custom(1, 8, 4, 64, dtype="f32", gate=False, seed=3)
+    keep = {k: to_dev(x[k], dev) for k in ("u", "delta", "A", "B", "C")}
+    lib = ssm.lib()
+    big = torch.zeros(1 + 8 * 64, dtype=torch.float32, device=dev)
+    y = torch.empty_like(keep["u"])
+    args = [big[1:].data_ptr(), keep["delta"].data_ptr(), keep["A"].data_ptr(),
+            keep["B"].data_ptr(), keep["C"].data_ptr(), None, None, None, 0,
+            None, y.data_ptr(), None, 1, 8, 4, 64, 0, 0, None]
+    assert lib.ssm_selective_scan_fwd(*args) == 4  # SSM_E_ALIGN
+    args[0] = keep["u"].data_ptr()
+    args[10] = keep["u"].data_ptr()  # y aliases u
+    assert lib.ssm_selective_scan_fwd(*args) == 5  # SSM_E_ALIAS
+    assert "overlaps" in ssm.ssm_last_error()

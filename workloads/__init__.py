@@ -4,10 +4,10 @@ This module only draws random numbers and rounds them to the storage dtype; it
 holds none of the scan's arithmetic and imports neither the HIP library nor the
 oracle, so both sides can consume the same bits.
 
-Every tensor row is drawn from its own PCG64 stream, keyed by
-``SeedSequence(seed, spawn_key=(tensor_id, row))``, so any row can be
-regenerated alone and rows can be drawn in parallel threads (numpy releases the
-GIL while filling).  Values are drawn in float32 and, for bf16 workloads,
+Rows of a tensor are drawn in blocks of about 2^19 values, each block from its
+own PCG64 stream keyed by ``SeedSequence(seed, spawn_key=(tensor_id, block))``,
+so any block can be regenerated alone and blocks are drawn in parallel threads
+(numpy releases the GIL while filling).  Values are drawn in float32 and, for bf16 workloads,
 rounded to bf16 with round-to-nearest-even; both the GPU and the oracle read
 those exact bits.
 
@@ -117,29 +117,42 @@ def _store(x: np.ndarray, dtype: str) -> np.ndarray:
     return to_bf16_bits(x) if dtype == "bf16" else x.astype(np.float32, copy=False)
 
 
-def _normal_rows(seed, tid, rows, n, mean, std, dtype, out):
-    """out[r] = stored(N(mean, std) draws of stream (tid, row0 + r))."""
-    def one(r):
-        x = rng(seed, tid, rows[r]).standard_normal(n, dtype=np.float32)
+def rows_per_stream(n: int, per_stream: int = 1 << 19) -> int:
+    """Rows of length n drawn from one stream (about per_stream values)."""
+    return max(1, per_stream // max(1, n))
+
+
+def _normal_rows(seed, tid, key0, out, mean, std, dtype, per_stream=1 << 19):
+    """Fill out[rows, n] with stored N(mean, std) draws.  Rows are grouped in
+    blocks of rows_per_stream(n, per_stream); block k is drawn from stream
+    (tid, key0 + k).  Blocks are spread over worker threads (numpy releases
+    the GIL while it fills large arrays)."""
+    rows, n = out.shape
+    rb = rows_per_stream(n, per_stream)
+    nblk = -(-rows // rb)
+
+    def one(k):
+        lo, hi = k * rb, min(rows, (k + 1) * rb)
+        x = rng(seed, tid, key0 + k).standard_normal((hi - lo) * n, dtype=np.float32)
         if std != 1.0:
             x *= np.float32(std)
         if mean != 0.0:
             x += np.float32(mean)
-        out[r] = _store(x, dtype)
+        out[lo:hi] = _store(x, dtype).reshape(hi - lo, n)
+
     with ThreadPoolExecutor(threads()) as ex:
-        list(ex.map(one, range(len(rows))))
+        list(ex.map(one, range(nblk)))
     return out
 
 
-def seq_tensor(w: Workload, tid: int, mean: float, std: float, seed=None, step=None):
+def seq_tensor(w: Workload, tid: int, mean: float, std: float, seed=None):
     """A [batch, dim, L] (tid in u/delta/z) or [batch, N, L] (tid in B/C) tensor."""
     seed = w.seed if seed is None else seed
     inner = w.dim if tid in (T_U, T_DELTA, T_Z) else w.dstate
     rows = w.batch * inner
     np_dtype = np.uint16 if w.dtype == "bf16" else np.float32
     out = np.empty((rows, w.seqlen), dtype=np_dtype)
-    base = 0 if step is None else (step + 1) * (1 << 32)
-    _normal_rows(seed, tid, [base + r for r in range(rows)], w.seqlen, mean, std, w.dtype, out)
+    _normal_rows(seed, tid, 0, out, mean, std, w.dtype)
     return out.reshape(w.batch, inner, w.seqlen)
 
 
@@ -177,27 +190,25 @@ def scan_inputs(w: Workload, seed=None):
 
 
 def decode_state(w: Workload, seed=None) -> np.ndarray:
-    """Initial fp32 decode state [batch, dim, N] ~ N(0, 0.1)."""
+    """Initial fp32 decode state [batch, dim, N] ~ N(0, 0.1), one stream per
+    sequence b."""
     seed = w.seed if seed is None else seed
-    out = np.empty((w.batch * w.dim, w.dstate), dtype=np.float32)
-    _normal_rows(seed, T_STATE, list(range(w.batch * w.dim)), w.dstate, 0.0, 0.1, "f32", out)
+    out = np.empty((w.batch, w.dim * w.dstate), dtype=np.float32)
+    _normal_rows(seed, T_STATE, 0, out, 0.0, 0.1, "f32")
     return out.reshape(w.batch, w.dim, w.dstate)
 
 
 def decode_step(w: Workload, step: int, seed=None):
-    """Fresh per-step inputs: u, delta, z [batch, dim]; B, C [batch, N]."""
+    """Fresh per-step inputs: u, delta, z [batch, dim]; B, C [batch, N].
+
+    Each tensor is drawn in blocks of about 2^16 values, one stream per
+    (tensor, step, block), so a step's inputs are generated in parallel."""
     seed = w.seed if seed is None else seed
+    np_dtype = np.uint16 if w.dtype == "bf16" else np.float32
 
     def t(tid, inner, mean, std):
-        np_dtype = np.uint16 if w.dtype == "bf16" else np.float32
         out = np.empty((w.batch, inner), dtype=np_dtype)
-        base = (step + 1) << 32
-        x = rng(seed, tid, base).standard_normal(w.batch * inner, dtype=np.float32)
-        if std != 1.0:
-            x *= np.float32(std)
-        if mean != 0.0:
-            x += np.float32(mean)
-        out[:] = _store(x, w.dtype).reshape(w.batch, inner)
+        _normal_rows(seed, tid, (step + 1) << 32, out, mean, std, w.dtype, per_stream=1 << 16)
         return out
 
     return dict(u=t(T_U, w.dim, 0.0, 1.0),
