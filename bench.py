@@ -1,0 +1,287 @@
+"""Benchmark of the selective-scan hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mamba2p8b]
+
+A step is one forward selective scan (ssm_selective_scan_fwd: load, step size,
+discretization, scan, readout, skip, gate, store) over the whole batch of the
+Mamba-2.8B-shaped layer (batch 4, dim 5120, N 16, L 8192, bf16 io, fp32
+arithmetic and state).  Inputs are generated once, uploaded, and resident in
+HBM before timing starts.  The one-token decode step (ssm_state_update) is
+timed separately on the decode workload and reported under "decode".
+
+Prints one JSON line: the metric (scan elements B*D*L*N per second), the
+roofline of the scan kernel (live HIP-event timing; HBM traffic from the
+committed rocprofv3 counter summary when it matches the current kernel
+source), the HBM view the metric asks for, and the fp64 oracle timed on host
+cores as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as wl  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0
+# VALU issue capacity: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz lane-slots/s.
+VALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
+# Minimal VALU lane-slots per scan element: Delta*A (1), exp (2: half rate on
+# gfx950), (Delta u)*B (1), state fma (1), readout fma (1).
+SLOTS_PER_ELEMENT = 6
+KERNEL_SRC = os.path.join(ROOT, "selective_state_space_43_amd", "csrc", "selscan.hip")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "scan_fwd_mamba2p8b_pmc.md")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def committed_traffic():
+    """HBM bytes per scan launch from the committed counter summary, or None if
+    the summary is missing or was taken on a different kernel source."""
+    try:
+        text = open(PMC_SUMMARY).read()
+    except OSError:
+        return None
+    m_src = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    m_tr = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not (m_src and m_tr) or m_src.group(1) != kernel_source_hash():
+        return None
+    return float(m_tr.group(1))
+
+
+def to_dev(a, dev):
+    import torch
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def host_threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))  # one GPU's share of the host
+
+
+def bench_scan(ssm, torch, w, x, dev, steps, warmup):
+    u, dl, A, B, C = (to_dev(x[k], dev) for k in ("u", "delta", "A", "B", "C"))
+    D, z, bias = to_dev(x["D"], dev), to_dev(x["z"], dev), to_dev(x["delta_bias"], dev)
+    y = torch.empty_like(u)
+    fs = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device=dev)
+
+    def step():
+        ssm.ssm_selective_scan_fwd(u, dl, A, B, C, D=D, z=z, delta_bias=bias,
+                                   delta_softplus=True, y=y, final_state=fs)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)  # the library launches on this stream
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    per_launch_ms = [a.elapsed_time(b) for a, b in ev]
+    total_ms = t_start.elapsed_time(t_end)
+    return total_ms / steps, float(np.mean(per_launch_ms)), float(np.min(per_launch_ms)), wall
+
+
+def bench_decode(ssm, torch, dev, steps, warmup):
+    w = wl.WORKLOADS["decode"]
+    A, D, bias = wl.params(w)
+    state = to_dev(wl.decode_state(w), dev)
+    pool = []
+    for i in range(4):  # a few distinct token batches, resident in HBM, used in turn
+        s = wl.decode_step(w, i)
+        pool.append({k: to_dev(v, dev) for k, v in s.items()})
+    Ad, Dd, bd = to_dev(A, dev), to_dev(D, dev), to_dev(bias, dev)
+    y = torch.empty((w.batch, w.dim), dtype=torch.bfloat16, device=dev)
+
+    def step(i):
+        p = pool[i % len(pool)]
+        ssm.ssm_state_update(state, p["u"], p["delta"], Ad, p["B"], p["C"], D=Dd, z=p["z"],
+                             delta_bias=bd, delta_softplus=True, y=y)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(steps):
+        step(i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / steps
+    state_bytes = 2 * w.batch * w.dim * w.dstate * 4  # read + write in place
+    io_bytes = w.batch * w.dim * 2 * 4 + 2 * w.batch * w.dstate * 2  # u, delta, z, y; B, C
+    gbps = (state_bytes + io_bytes) / (us * 1e-6) / 1e9
+    return {
+        "workload": f"decode: batch {w.batch}, dim {w.dim}, N {w.dstate}, one bf16 token, "
+                    "fp32 state in place",
+        "us_per_step": round(us, 3),
+        "tokens_per_s": round(w.batch / (us * 1e-6), 1),
+        "elements_per_s": float("%.4g" % (w.batch * w.dim * w.dstate / (us * 1e-6))),
+        "hbm_bytes_per_step": state_bytes + io_bytes,
+        "hbm_gbps": round(gbps, 1),
+        "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "steps": steps,
+    }
+
+
+def cpu_baseline(w, x, seconds_target=12.0):
+    """The fp64 oracle on host cores over whole channels of the same inputs:
+    as many channels (full length each) as fit the time target."""
+    import oracle
+    n_thr = host_threads()
+    total = w.batch * w.dim
+    probe = np.arange(0, total, max(1, total // (4 * n_thr)))[: 4 * n_thr]
+    t0 = time.perf_counter()
+    oracle.selective_scan(x["u"], x["delta"], x["A"], x["B"], x["C"], D=x["D"], z=x["z"],
+                          delta_bias=x["delta_bias"], delta_softplus=True, channels=probe,
+                          want_y=False, n_threads=n_thr)
+    per_ch = (time.perf_counter() - t0) / len(probe)
+    n_ch = int(min(total, max(len(probe), seconds_target / max(per_ch, 1e-9))))
+    chans = np.linspace(0, total - 1, n_ch).astype(np.int64)
+    t0 = time.perf_counter()
+    oracle.selective_scan(x["u"], x["delta"], x["A"], x["B"], x["C"], D=x["D"], z=x["z"],
+                          delta_bias=x["delta_bias"], delta_softplus=True, channels=chans,
+                          want_y=False, n_threads=n_thr)
+    dt = time.perf_counter() - t0
+    el = n_ch * w.seqlen * w.dstate
+    return {"value": float("%.4g" % (el / dt)), "unit": "elements/s", "cores": n_thr,
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"{n_ch} of {total} channels (b, d), full length {w.seqlen}, all "
+                      f"{w.dstate} states, same bf16 inputs; fp64 sequential recurrence"}
+
+
+def main(argv=None):
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="mamba2p8b",
+                   choices=[k for k in wl.WORKLOADS if k != "decode"])
+    p.add_argument("--decode-steps", type=int, default=200)
+    p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-check", type=int, default=0, metavar="BYTES",
+                   help="also run torch's plain copy of BYTES three times (counter calibration "
+                        "under rocprofv3)")
+    args = p.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the scan shards by batch and channel with no "
+              "communication, and this build runs on a single MI355X; use --gpus 1.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import selective_state_space_43_amd as ssm
+    ssm.lib()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+
+    w = wl.WORKLOADS[args.workload]
+    t0 = time.perf_counter()
+    x = wl.scan_inputs(w)
+    print(f"[bench] inputs for {w.name} generated in {time.perf_counter() - t0:.1f}s",
+          file=sys.stderr, flush=True)
+    ms_step, ms_kernel, ms_kernel_min, wall = bench_scan(ssm, torch, w, x, dev, args.steps,
+                                                        args.warmup)
+    print(f"[bench] scan: {ms_step:.4f} ms/step, kernel {ms_kernel:.4f} ms (min "
+          f"{ms_kernel_min:.4f})", file=sys.stderr, flush=True)
+    el = w.elements
+    value = el / (ms_step * 1e-3)
+    hbm_gbps = w.io_bytes / (ms_kernel * 1e-3) / 1e9
+    achieved_tslots = SLOTS_PER_ELEMENT * el / (ms_kernel * 1e-3) / 1e12
+    traffic = committed_traffic()
+
+    out = {
+        "metric": "selective-scan elements/sec (B*D*L*N)",
+        "value": float("%.5g" % value),
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: Mamba-2.8B-shaped selective scan" if w.name == "mamba2p8b"
+            else w.name,
+            "batch": w.batch, "dim": w.dim, "dstate": w.dstate, "seqlen": w.seqlen,
+            "io_dtype": w.dtype, "gate": w.gate, "delta_softplus": True,
+            "delta_bias": w.bias, "bbar": "delta*B", "parallelism": "single GPU",
+        },
+        "roofline": {
+            "kernel": "scan_fwd_kernel",
+            "bound": "alu",
+            "achieved": round(achieved_tslots, 3),
+            "peak": round(VALU_PEAK_TSLOTS, 3),
+            "unit": "T VALU lane-slots/s (6 slots per element)",
+            "frac": round(achieved_tslots / VALU_PEAK_TSLOTS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": w.io_bytes,
+            "kernel_ms": round(ms_kernel, 4),
+        },
+        "hbm": {
+            "achieved": round(hbm_gbps, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(hbm_gbps / HBM_PEAK_GBPS, 4),
+            "bytes_per_launch": w.io_bytes,
+        },
+    }
+    if args.copy_check:
+        src = torch.empty(args.copy_check // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_check_bytes"] = args.copy_check
+        del src, dst
+    if not args.no_decode:
+        out["decode"] = bench_decode(ssm, torch, dev, args.decode_steps, 10)
+        print(f"[bench] decode: {out['decode']['us_per_step']} us/step", file=sys.stderr,
+              flush=True)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, x)
+        print(f"[bench] cpu baseline: {out['cpu_baseline']['seconds']}s", file=sys.stderr,
+              flush=True)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

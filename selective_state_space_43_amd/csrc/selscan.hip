@@ -28,11 +28,26 @@
 #include <hip/hip_runtime.h>
 
 #include <stdarg.h>
+#include <type_traits>
 #include <stdint.h>
 #include <stdio.h>
 #include <string.h>
 
 #include "selscan.h"
+
+// Build-time tuning knobs of the forward scan (defaults are the tuned values).
+#ifndef SELSCAN_K
+#define SELSCAN_K 16  // timesteps per lane
+#endif
+#ifndef SELSCAN_W
+#define SELSCAN_W 4  // waves per workgroup
+#endif
+#ifndef SELSCAN_NT
+#define SELSCAN_NT 16  // states staged per LDS tile (16 lanes per channel)
+#endif
+#ifndef SELSCAN_WAVES_PER_EU
+#define SELSCAN_WAVES_PER_EU 0  // occupancy hint for the register allocator (0: none)
+#endif
 
 namespace {
 
@@ -53,6 +68,15 @@ __device__ __forceinline__ float softplus_f(float x) {
   const float u = 1.0f + e;
   const float l = lg2(u) * kLn2 - ((u - 1.0f) - e) * rcp(u);
   return x > 15.0f ? x : l;
+}
+
+// softplus(x) / ln 2, the step size in log2 units, with the same accuracy.
+__device__ __forceinline__ float softplus_log2(float x) {
+  const float xl = x * kLog2e;
+  const float e = ex2(xl);
+  const float u = 1.0f + e;
+  const float l = lg2(u) - ((u - 1.0f) - e) * rcp(u) * kLog2e;
+  return x > 15.0f ? xl : l;
 }
 
 // silu(z) = z * sigmoid(z)
@@ -115,24 +139,142 @@ struct Io<uint16_t> {  // bf16 bit patterns
   }
 };
 
-// K consecutive elements starting at p[base + t]; zero where t >= L.
-template <typename IO, int K>
-__device__ __forceinline__ void load_run(const void* p, int64_t base, int64_t t, int64_t L,
-                                         bool vec, bool valid, float* o) {
-  if (valid && vec && t + K <= L) {
-#pragma unroll
-    for (int i = 0; i < K; i += Io<IO>::V) Io<IO>::ldv(p, base + t + i, o + i);
+// ---------------------------------------------------------------- cross-lane
+
+// DPP move: lanes whose source lies outside the pattern, or whose row is
+// masked off, receive `old`.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp(float old, float src) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src), CTRL,
+                                                    ROW_MASK, 0xf, false));
+}
+
+// DPP move reading 0 where there is no source lane (bound_ctrl).
+template <int CTRL>
+__device__ __forceinline__ float dpp0(float src) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(src), CTRL, 0xf, 0xf, true));
+}
+
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143, kWaveShr1 = 0x138;
+
+// Inclusive scan of (A, H) pairs within each 16-lane row, where (A_prev,
+// H_prev) then (A, H) composes to (A_prev A, A H_prev + H).  Hillis-Steele
+// with the neighbour's H read through DPP inside the fma (v_fmac_f32_dpp);
+// a lane without a source reads H_prev = 0 and keeps H.  A lane without a
+// source also zeroes its A, which no later step of the row reads.  On return
+// H is exact on every lane (A is not returned).  Each s_nop 1 covers the
+// two wait states a DPP read needs after a VALU write of the same register,
+// including for code that follows the block.
+__device__ __forceinline__ void row_scan16(float A, float& H) {
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %0, %0, %1 row_shr:1 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_mul_f32_dpp %1, %1, %1 row_shr:1 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %0, %0, %1 row_shr:2 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_mul_f32_dpp %1, %1, %1 row_shr:2 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %0, %0, %1 row_shr:4 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_mul_f32_dpp %1, %1, %1 row_shr:4 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %0, %0, %1 row_shr:8 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "s_nop 1"
+      : "+v"(H), "+v"(A));
+}
+
+// Step across rows (row broadcast) for groups wider than a row: every lane of
+// the receiving rows uses its own A, so A keeps the identity where there is
+// no source.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void bcast_step(float& A, float& H) {
+  const float As = dpp<CTRL, ROW_MASK>(1.0f, A);
+  const float Hs = dpp<CTRL, ROW_MASK>(0.0f, H);
+  H = fmaf(A, Hs, H);
+  A = A * As;
+}
+
+// Inclusive scan of (A, H) pairs over each group of LPC consecutive lanes;
+// H is exact on every lane on return.
+template <int LPC>
+__device__ __forceinline__ void group_scan(float A, float& H) {
+  if constexpr (LPC == 16) {
+    row_scan16(A, H);
   } else {
-#pragma unroll
-    for (int i = 0; i < K; ++i) o[i] = (valid && t + i < L) ? Io<IO>::ld1(p, base + t + i) : 0.0f;
+    bcast_step<kRowShr1, 0xf>(A, H);
+    bcast_step<kRowShr2, 0xf>(A, H);
+    bcast_step<kRowShr4, 0xf>(A, H);
+    bcast_step<kRowShr8, 0xf>(A, H);
+    bcast_step<kRowBcast15, 0xa>(A, H);
+    if constexpr (LPC >= 64) bcast_step<kRowBcast31, 0xc>(A, H);
   }
 }
 
+// H of the previous lane of the group (0 on the group's first lane).
+template <int LPC>
+__device__ __forceinline__ float group_prev0(float v, bool first) {
+  if constexpr (LPC == 16) {
+    return dpp0<kRowShr1>(v);
+  } else {
+    const float p = dpp<kWaveShr1, 0xf>(0.0f, v);
+    return first ? 0.0f : p;
+  }
+}
+
+// ---------------------------------------------------------------- forward scan
+
+// Raw (undecoded) storage of K consecutive elements.
 template <typename IO, int K>
-__device__ __forceinline__ void store_run(void* p, int64_t base, int64_t t, int64_t L, bool vec,
+struct Run;
+template <int K>
+struct Run<uint16_t, K> {
+  uint4 v[K / 8];
+  __device__ void unpack(float* o) const {
+#pragma unroll
+    for (int i = 0; i < K / 8; ++i) {
+      o[8 * i + 0] = bf_lo(v[i].x); o[8 * i + 1] = bf_hi(v[i].x);
+      o[8 * i + 2] = bf_lo(v[i].y); o[8 * i + 3] = bf_hi(v[i].y);
+      o[8 * i + 4] = bf_lo(v[i].z); o[8 * i + 5] = bf_hi(v[i].z);
+      o[8 * i + 6] = bf_lo(v[i].w); o[8 * i + 7] = bf_hi(v[i].w);
+    }
+  }
+};
+template <int K>
+struct Run<float, K> {
+  float4 v[K / 4];
+  __device__ void unpack(float* o) const {
+#pragma unroll
+    for (int i = 0; i < K / 4; ++i) {
+      o[4 * i + 0] = v[i].x; o[4 * i + 1] = v[i].y; o[4 * i + 2] = v[i].z; o[4 * i + 3] = v[i].w;
+    }
+  }
+};
+
+// r <- p[base + t .. base + t + K), zero past L or when !valid.  VEC: rows
+// are 16-byte aligned, so whole runs load as 16-byte vectors.
+template <typename IO, int K, bool VEC>
+__device__ __forceinline__ void run_load(Run<IO, K>& r, const void* p, int64_t base, int64_t t,
+                                         int64_t L, bool valid) {
+  using VT = typename std::remove_reference<decltype(r.v[0])>::type;
+  constexpr int V = Io<IO>::V;
+  if (VEC && valid && t + K <= L) {
+    const VT* q = reinterpret_cast<const VT*>(static_cast<const IO*>(p) + base + t);
+#pragma unroll
+    for (int i = 0; i < K / V; ++i) r.v[i] = q[i];
+  } else {
+    IO e[K];
+#pragma unroll
+    for (int i = 0; i < K; ++i)
+      e[i] = (valid && t + i < L) ? static_cast<const IO*>(p)[base + t + i] : IO(0);
+    __builtin_memcpy(&r.v[0], e, sizeof e);
+  }
+}
+
+template <typename IO, int K, bool VEC>
+__device__ __forceinline__ void run_store(void* p, int64_t base, int64_t t, int64_t L,
                                           bool valid, const float* v) {
   if (!valid) return;
-  if (vec && t + K <= L) {
+  if (VEC && t + K <= L) {
 #pragma unroll
     for (int i = 0; i < K; i += Io<IO>::V) Io<IO>::stv(p, base + t + i, v + i);
   } else {
@@ -141,54 +283,6 @@ __device__ __forceinline__ void store_run(void* p, int64_t base, int64_t t, int6
       if (t + i < L) Io<IO>::st1(p, base + t + i, v[i]);
   }
 }
-
-// ---------------------------------------------------------------- cross-lane
-
-// DPP move: lanes whose source is outside the pattern (or masked by row_mask)
-// receive `old`.
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ float dpp(float old, float src) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src), CTRL,
-                                                    ROW_MASK, 0xf, false));
-}
-
-constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
-constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143, kWaveShr1 = 0x138;
-
-// One Hillis-Steele step: combine with the pair 2^s lanes earlier (identity
-// (1, 0) where there is none).  (A_prev, H_prev) then (A, H) composes to
-// (A_prev A, A H_prev + H).
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ void scan_step(float& A, float& H) {
-  const float As = dpp<CTRL, ROW_MASK>(1.0f, A);
-  const float Hs = dpp<CTRL, ROW_MASK>(0.0f, H);
-  H = fmaf(A, Hs, H);
-  A = A * As;
-}
-
-// Inclusive scan of (A, H) pairs over each group of LPC consecutive lanes.
-template <int LPC>
-__device__ __forceinline__ void group_scan(float& A, float& H) {
-  scan_step<kRowShr1, 0xf>(A, H);
-  scan_step<kRowShr2, 0xf>(A, H);
-  scan_step<kRowShr4, 0xf>(A, H);
-  scan_step<kRowShr8, 0xf>(A, H);
-  if constexpr (LPC >= 32) scan_step<kRowBcast15, 0xa>(A, H);
-  if constexpr (LPC >= 64) scan_step<kRowBcast31, 0xc>(A, H);
-}
-
-// Value of the previous lane of the group; `first` lanes get `id`.
-template <int LPC>
-__device__ __forceinline__ float group_prev(float id, float v, bool first) {
-  if constexpr (LPC == 16) {
-    return dpp<kRowShr1, 0xf>(id, v);
-  } else {
-    const float p = dpp<kWaveShr1, 0xf>(id, v);
-    return (LPC == 64 || !first) ? p : id;
-  }
-}
-
-// ---------------------------------------------------------------- forward scan
 
 struct ScanArgs {
   const void* u;
@@ -204,17 +298,22 @@ struct ScanArgs {
   float* final_state;
   int64_t dim, dstate, seqlen;
   int softplus;
-  int vec;  // every sequence row starts 16-byte aligned
 };
 
-template <typename IO, int LPC, int K, int W, int NT, bool ZOH, bool GATE>
+template <typename IO, int LPC, int K, int W, int NT, bool VEC, bool ZOH, bool GATE>
 __global__ void __launch_bounds__(64 * W)
+#if SELSCAN_WAVES_PER_EU
+    __attribute__((amdgpu_waves_per_eu(SELSCAN_WAVES_PER_EU, SELSCAN_WAVES_PER_EU)))
+#endif
     scan_fwd_kernel(const ScanArgs a) {
   constexpr int CPW = 64 / LPC;  // channels per wave
   constexpr int CPB = CPW * W;   // channels per workgroup
   constexpr int T = LPC * K;     // timesteps per chunk
   constexpr int KP = K + 4;      // padded per-lane run in LDS (spreads banks)
   constexpr int V = Io<IO>::V;
+  constexpr int TV = T / V;      // staged vectors per B/C row
+  constexpr int NTH = 64 * W;
+  constexpr int ITEMS = (2 * NT * TV + NTH - 1) / NTH;  // staged vectors per thread
   static_assert(K % V == 0 && K % 4 == 0, "K must be a multiple of the vector width");
   __shared__ float4 sB4[NT * LPC * KP / 4];
   __shared__ float4 sC4[NT * LPC * KP / 4];
@@ -225,127 +324,165 @@ __global__ void __launch_bounds__(64 * W)
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int seg = lane % LPC;
+  const bool first = seg == 0;
   const int chb = wave * CPW + lane / LPC;
   const int64_t b = blockIdx.y;
   const int64_t d0 = (int64_t)blockIdx.x * CPB;
   const int64_t d = d0 + chb;
+  // Lanes of a channel past `dim` compute on channel 0's data in their own
+  // lane group and store nothing.
   const bool dvalid = d < a.dim;
   const int64_t N = a.dstate, L = a.seqlen;
   const int64_t row = (b * a.dim + (dvalid ? d : 0)) * L;
   const int64_t bcrow = b * N * L;
-  const bool vec = a.vec != 0;
 
   float* sCarry = sDyn;
   float* sA = sDyn + CPB * N;
-  for (int64_t i = threadIdx.x; i < CPB * N; i += 64 * W) {
+  for (int64_t i = threadIdx.x; i < CPB * N; i += NTH) {
     const int64_t c = i / N, n = i % N;
     const bool ok = d0 + c < a.dim;
     sCarry[i] = (a.h0 && ok) ? a.h0[(b * a.dim + d0 + c) * N + n] : 0.0f;
     sA[i] = ok ? a.A[(d0 + c) * N + n] : 0.0f;
   }
-  const float Dd = (a.Dskip && dvalid) ? a.Dskip[d] : 0.0f;
+  // y accumulates D u with u kept as u ln 2 (see below)
+  const float Dl = ((a.Dskip && dvalid) ? a.Dskip[d] : 0.0f) * kLog2e;
   const float bias = (a.delta_bias && dvalid) ? a.delta_bias[d] : 0.0f;
+  float* carry_row = sCarry + chb * N;
+  const float* a_row = sA + chb * N;
 
-  for (int64_t t0 = 0; t0 < L; t0 += T) {
-    const int64_t tl = t0 + seg * K;
-    float dt[K], w[K], y[K], uu[K];
-    {
-      float raw[K];
-      load_run<IO, K>(a.u, row, tl, L, vec, dvalid, uu);
-      load_run<IO, K>(a.delta, row, tl, L, vec, dvalid, raw);
+  // B, C rows [n0, n0 + nt) x [t0, t0 + T) -> LDS as float32, laid out so
+  // that each lane reads its K steps as contiguous float4s.
+  auto stage_bc = [&](int64_t t0, int64_t n0, int nt) {
 #pragma unroll
-      for (int i = 0; i < K; ++i) {
-        const bool ok = dvalid && tl + i < L;
-        const float x = raw[i] + bias;
-        const float s = a.softplus ? softplus_f(x) : x;
-        dt[i] = ok ? s : 0.0f;  // identity step (Abar = 1, Bbar u = 0) past the end
-        w[i] = dt[i] * uu[i];
-        y[i] = Dd * uu[i];
-      }
-    }
-    float S = 0.0f;
-#pragma unroll
-    for (int i = 0; i < K; ++i) S += dt[i];
-
-    for (int64_t n0 = 0; n0 < N; n0 += NT) {
-      const int nt = (int)((N - n0) < NT ? (N - n0) : NT);
-      __syncthreads();
-      // stage B, C rows [n0, n0 + nt) x [t0, t0 + T) as float32
-      for (int item = threadIdx.x; item < 2 * nt * (T / V); item += 64 * W) {
-        const int tensor = item / (nt * (T / V));
-        const int r = item % (nt * (T / V));
-        const int nl = r / (T / V);
-        const int tloc = (r % (T / V)) * V;
-        const void* src = tensor ? a.Cm : a.Bm;
-        float* dst = (tensor ? sC : sB) + (nl * LPC + tloc / K) * KP + tloc % K;
+    for (int k = 0; k < ITEMS; ++k) {
+      const int item = threadIdx.x + k * NTH;
+      if (item < 2 * nt * TV) {
+        const int tensor = item / (nt * TV);
+        const int r = item % (nt * TV);
+        const int nl = r / TV, tloc = (r % TV) * V;
+        Run<IO, V> rv;
+        run_load<IO, V, VEC>(rv, tensor ? a.Cm : a.Bm, bcrow + (n0 + nl) * L, t0 + tloc, L, true);
         float v[V];
-        load_run<IO, V>(src, bcrow + (n0 + nl) * L, t0 + tloc, L, vec, true, v);
+        rv.unpack(v);
+        float* dst = (tensor ? sC : sB) + (nl * LPC + tloc / K) * KP + tloc % K;
 #pragma unroll
         for (int q = 0; q < V; q += 4)
           *reinterpret_cast<float4*>(dst + q) = make_float4(v[q], v[q + 1], v[q + 2], v[q + 3]);
       }
-      __syncthreads();
+    }
+  };
 
-      for (int j = 0; j < nt; ++j) {
-        const int64_t n = n0 + j;
-        const float An = sA[chb * N + n];
-        const float A2 = An * kLog2e;
-        const float* pb = sB + (j * LPC + seg) * KP;
-        const float* pc = sC + (j * LPC + seg) * KP;
-        float av[K], xv[K];
+  // One chunk of T timesteps.  FULL: the chunk lies inside [0, L) and N is a
+  // multiple of NT, so no step or state needs masking.
+  auto chunk = [&](int64_t t0, auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    const int64_t tl = t0 + seg * K;
+    // Step sizes are kept in log2 units, dl = delta / ln 2, so that
+    // Abar = exp(delta A) = exp2(dl A) with A in natural units, and u is
+    // kept as ul = u ln 2 so that delta u = dl ul.
+    float dl[K], w[K], y[K], ul[K];
+    float S = 0.0f;
+    // issue this chunk's sequence loads first: they complete while the first
+    // B/C tile is staged
+    Run<IO, K> ru, rd, rz;
+    run_load<IO, K, VEC>(ru, a.u, row, tl, L, dvalid);
+    run_load<IO, K, VEC>(rd, a.delta, row, tl, L, dvalid);
+    if constexpr (GATE) run_load<IO, K, VEC>(rz, a.z, row, tl, L, dvalid);
+    __syncthreads();  // every wave is done with the previous chunk's last tile
+    stage_bc(t0, 0, (int)(N < NT ? N : NT));
+    __syncthreads();
+    {
+      float raw[K];
+      ru.unpack(ul);
+      rd.unpack(raw);
 #pragma unroll
-        for (int i = 0; i < K; i += 4) {
-          const float4 bb = *reinterpret_cast<const float4*>(pb + i);
-          const float bq[4] = {bb.x, bb.y, bb.z, bb.w};
+      for (int i = 0; i < K; ++i) {
+        const float x = raw[i] + bias;
+        float v = a.softplus ? softplus_log2(x) : x * kLog2e;
+        if constexpr (!FULL) v = (tl + i < L) ? v : 0.0f;  // identity step past the end
+        ul[i] *= kLn2;
+        dl[i] = v;
+        w[i] = v * ul[i];
+        y[i] = Dl * ul[i];
+        S += v;
+      }
+    }
+
+    // one state n: discretize, fold, scan, apply, read out
+    auto state = [&](int j, int64_t n) {
+      const float An = a_row[n];
+      const float c = carry_row[n];  // state at the chunk start
+      const float* pb = sB + (j * LPC + seg) * KP;
+      const float* pc = sC + (j * LPC + seg) * KP;
+      float av[K], xv[K];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            av[i + q] = ex2(dt[i + q] * A2);
-            if constexpr (ZOH) {
-              const float r = dt[i + q] * An;
-              const float coef = An != 0.0f ? expm1_f(r, av[i + q]) * rcp(An) : dt[i + q];
-              xv[i + q] = coef * bq[q] * uu[i + q];
-            } else {
-              xv[i + q] = w[i + q] * bq[q];
-            }
-          }
-        }
-        // local fold of the lane's K steps from a zero state
-        float H = xv[0];
+      for (int i = 0; i < K; i += 4) {
+        const float4 bb = *reinterpret_cast<const float4*>(pb + i);
+        const float bq[4] = {bb.x, bb.y, bb.z, bb.w};
 #pragma unroll
-        for (int i = 1; i < K; ++i) H = fmaf(av[i], H, xv[i]);
-        float Ag = ex2(A2 * S);
-        group_scan<LPC>(Ag, H);
-        const bool first = seg == 0;
-        const float Ae = group_prev<LPC>(1.0f, Ag, first);
-        const float He = group_prev<LPC>(0.0f, H, first);
-        float* carry = sCarry + chb * N + n;
-        const float c = *carry;
-        float h = fmaf(Ae, c, He);
-        if (seg == LPC - 1) *carry = fmaf(Ag, c, H);
-#pragma unroll
-        for (int i = 0; i < K; i += 4) {
-          const float4 cc = *reinterpret_cast<const float4*>(pc + i);
-          const float cq[4] = {cc.x, cc.y, cc.z, cc.w};
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            h = fmaf(av[i + q], h, xv[i + q]);
-            y[i + q] = fmaf(cq[q], h, y[i + q]);
+        for (int q = 0; q < 4; ++q) {
+          av[i + q] = ex2(dl[i + q] * An);
+          if constexpr (ZOH) {
+            const float r = dl[i + q] * An * kLn2;  // delta * A
+            const float coef = An != 0.0f ? expm1_f(r, av[i + q]) * rcp(An) : dl[i + q] * kLn2;
+            xv[i + q] = coef * bq[q] * (ul[i + q] * kLog2e);
+          } else {
+            xv[i + q] = w[i + q] * bq[q];
           }
         }
       }
+      // fold the lane's K steps into one pair; the channel's first lane starts
+      // from the carried state, the others from zero, so the scan below hands
+      // every lane its exact incoming state
+      float H = fmaf(av[0], first ? c : 0.0f, xv[0]);
+#pragma unroll
+      for (int i = 1; i < K; ++i) H = fmaf(av[i], H, xv[i]);
+      const float Al = ex2(An * S);  // product of the lane's K decays
+      group_scan<LPC>(Al, H);
+      const float He = group_prev0<LPC>(H, first);
+      float h = first ? c : He;
+      if (seg == LPC - 1) carry_row[n] = H;
+#pragma unroll
+      for (int i = 0; i < K; i += 4) {
+        const float4 cc = *reinterpret_cast<const float4*>(pc + i);
+        const float cq[4] = {cc.x, cc.y, cc.z, cc.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          h = fmaf(av[i + q], h, xv[i + q]);
+          y[i + q] = fmaf(cq[q], h, y[i + q]);
+        }
+      }
+    };
+
+    for (int64_t n0 = 0; n0 < N; n0 += NT) {
+      if (n0 > 0) {
+        __syncthreads();  // every wave is done with the previous tile
+        stage_bc(t0, n0, (int)((N - n0) < NT ? (N - n0) : NT));
+        __syncthreads();
+      }
+      const int nt = FULL ? NT : (int)((N - n0) < NT ? (N - n0) : NT);
+#pragma unroll 1
+      for (int j = 0; j < nt; ++j) state(j, n0 + j);
     }
     if constexpr (GATE) {
       float zz[K];
-      load_run<IO, K>(a.z, row, tl, L, vec, dvalid, zz);
+      rz.unpack(zz);
 #pragma unroll
       for (int i = 0; i < K; ++i) y[i] *= silu_f(zz[i]);
     }
-    store_run<IO, K>(a.y, row, tl, L, vec, dvalid, y);
+    run_store<IO, K, VEC>(a.y, row, tl, L, dvalid, y);
+  };
+
+  int64_t t0 = 0;
+  if (N % NT == 0) {
+    for (; t0 + T <= L; t0 += T) chunk(t0, std::true_type{});
   }
+  for (; t0 < L; t0 += T) chunk(t0, std::false_type{});
+
   if (a.final_state && dvalid) {
     // each channel's carry was written by its own wave; LDS is in order per wave
     for (int64_t n = seg; n < N; n += LPC)
-      a.final_state[(b * a.dim + d) * N + n] = sCarry[chb * N + n];
+      a.final_state[(b * a.dim + d) * N + n] = carry_row[n];
   }
 }
 
@@ -513,30 +650,37 @@ int launch_status(const char* what) {
   return SSM_OK;
 }
 
-template <typename IO, int LPC, int K, int W, int NT>
+template <typename IO, int LPC, int K, int W, int NT, bool VEC>
 int launch_fwd_cfg(const ScanArgs& a, int64_t batch, bool zoh, bool gate, hipStream_t s) {
   constexpr int CPB = (64 / LPC) * W;
   const dim3 grid((unsigned)((a.dim + CPB - 1) / CPB), (unsigned)batch);
   const size_t shmem = 2 * (size_t)CPB * (size_t)a.dstate * sizeof(float);
   if (zoh) {
-    if (gate) hipLaunchKernelGGL((scan_fwd_kernel<IO, LPC, K, W, NT, true, true>), grid, dim3(64 * W), shmem, s, a);
-    else hipLaunchKernelGGL((scan_fwd_kernel<IO, LPC, K, W, NT, true, false>), grid, dim3(64 * W), shmem, s, a);
+    if (gate) hipLaunchKernelGGL((scan_fwd_kernel<IO, LPC, K, W, NT, VEC, true, true>), grid, dim3(64 * W), shmem, s, a);
+    else hipLaunchKernelGGL((scan_fwd_kernel<IO, LPC, K, W, NT, VEC, true, false>), grid, dim3(64 * W), shmem, s, a);
   } else {
-    if (gate) hipLaunchKernelGGL((scan_fwd_kernel<IO, LPC, K, W, NT, false, true>), grid, dim3(64 * W), shmem, s, a);
-    else hipLaunchKernelGGL((scan_fwd_kernel<IO, LPC, K, W, NT, false, false>), grid, dim3(64 * W), shmem, s, a);
+    if (gate) hipLaunchKernelGGL((scan_fwd_kernel<IO, LPC, K, W, NT, VEC, false, true>), grid, dim3(64 * W), shmem, s, a);
+    else hipLaunchKernelGGL((scan_fwd_kernel<IO, LPC, K, W, NT, VEC, false, false>), grid, dim3(64 * W), shmem, s, a);
   }
   return launch_status("ssm_selective_scan_fwd launch");
 }
 
 // Lane layout choice: 16 lanes per channel gives the shortest cross-lane scan;
-// a full wave per channel is used when there are too few channels to give
-// every SIMD of the 256 CUs several waves.
-template <typename IO>
-int launch_fwd(const ScanArgs& a, int64_t batch, bool zoh, bool gate, hipStream_t s) {
+// wider groups are used when there are too few channels to give every SIMD of
+// the 256 CUs several waves.
+template <typename IO, bool VEC>
+int launch_fwd_vec(const ScanArgs& a, int64_t batch, bool zoh, bool gate, hipStream_t s) {
+  constexpr int K = SELSCAN_K, W = SELSCAN_W, NT = SELSCAN_NT;
   const int64_t channels = batch * a.dim;
-  if (channels >= 4 * 4096) return launch_fwd_cfg<IO, 16, 16, 4, 16>(a, batch, zoh, gate, s);
-  if (channels >= 2 * 4096) return launch_fwd_cfg<IO, 32, 16, 4, 8>(a, batch, zoh, gate, s);
-  return launch_fwd_cfg<IO, 64, 16, 4, 4>(a, batch, zoh, gate, s);
+  if (channels >= 4 * 4096) return launch_fwd_cfg<IO, 16, K, W, NT, VEC>(a, batch, zoh, gate, s);
+  if (channels >= 2 * 4096) return launch_fwd_cfg<IO, 32, K, W, NT / 2, VEC>(a, batch, zoh, gate, s);
+  return launch_fwd_cfg<IO, 64, K, W, NT / 4, VEC>(a, batch, zoh, gate, s);
+}
+
+template <typename IO>
+int launch_fwd(const ScanArgs& a, int64_t batch, bool zoh, bool gate, bool vec, hipStream_t s) {
+  return vec ? launch_fwd_vec<IO, true>(a, batch, zoh, gate, s)
+             : launch_fwd_vec<IO, false>(a, batch, zoh, gate, s);
 }
 
 }  // namespace
@@ -624,11 +768,11 @@ int ssm_selective_scan_fwd(const void* u, const void* delta, const float* A, con
   a.delta_bias = delta_bias; a.h0 = h0; a.y = y; a.final_state = final_state;
   a.dim = dim; a.dstate = dstate; a.seqlen = seqlen;
   a.softplus = delta_softplus ? 1 : 0;
-  a.vec = (seqlen % (io_dtype == SSM_DTYPE_BF16 ? 8 : 4)) == 0 ? 1 : 0;
+  const bool vec = (seqlen % (io_dtype == SSM_DTYPE_BF16 ? 8 : 4)) == 0;
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   const bool zoh = bbar_mode == SSM_BBAR_ZOH_EXACT, gate = z != nullptr;
-  return io_dtype == SSM_DTYPE_BF16 ? launch_fwd<uint16_t>(a, batch, zoh, gate, s)
-                                    : launch_fwd<float>(a, batch, zoh, gate, s);
+  return io_dtype == SSM_DTYPE_BF16 ? launch_fwd<uint16_t>(a, batch, zoh, gate, vec, s)
+                                    : launch_fwd<float>(a, batch, zoh, gate, vec, s);
 }
 
 int ssm_state_update(float* state, const void* u, const void* delta, const float* A,
