@@ -49,6 +49,7 @@
 #define SELSCAN_WAVES_PER_EU 0  // occupancy hint for the register allocator (0: none)
 #endif
 
+
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -89,6 +90,8 @@ __device__ __forceinline__ float expm1_f(float r, float e) {
 }
 
 // ---------------------------------------------------------------- io
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // bf16 is the upper half of an IEEE binary32.
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -503,72 +506,80 @@ struct StepArgs {
   int softplus;
 };
 
-// Four lanes per channel; lane q of a channel updates states q*4 .. q*4+3 of
-// each block of 16, so a wave reads and writes 16 channels' states as one
-// contiguous run.  The readout is summed over the four lanes.
+// One lane per channel: the lane streams its channel's whole state row
+// (N floats, 16-byte vectors) in and out, so a wave keeps 64 rows in flight
+// and neighbouring lanes read neighbouring rows.  A is read as float4s; B and
+// C (one row per sequence, shared by the wave's channels) as 16-byte vectors.
 template <typename IO, bool ZOH, bool GATE>
 __global__ void __launch_bounds__(256) state_update_kernel(const StepArgs a) {
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int q = threadIdx.x & 3;
-  const int64_t ch = gid >> 2;
-  const bool valid = ch < a.batch * a.dim;
-  const int64_t c = valid ? ch : 0;
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= a.batch * a.dim) return;
   const int64_t b = c / a.dim, d = c % a.dim;
   const int64_t N = a.dstate;
   const float uu = Io<IO>::ld1(a.u, c);
   const float raw = Io<IO>::ld1(a.delta, c) + (a.delta_bias ? a.delta_bias[d] : 0.0f);
-  const float dt = a.softplus ? softplus_f(raw) : raw;
-  const float w = dt * uu;
-  float acc = 0.0f;
+  const float dl = a.softplus ? softplus_log2(raw) : raw * kLog2e;  // delta / ln 2
+  const float w = dl * kLn2 * uu;                                   // delta u
   float* st = a.state + c * N;
-  const bool vec4 = (N & 3) == 0;
-  for (int64_t nb = 0; nb < N; nb += 16) {
-    const int64_t n = nb + q * 4;
-    if (n >= N) continue;
-    const int cnt = (int)((N - n) < 4 ? (N - n) : 4);
-    float h[4] = {0, 0, 0, 0};
-    if (valid) {
-      if (vec4) {
-        const float4 v = *reinterpret_cast<const float4*>(st + n);
-        h[0] = v.x; h[1] = v.y; h[2] = v.z; h[3] = v.w;
-      } else {
-        for (int k = 0; k < cnt; ++k) h[k] = st[n + k];
+  const float* Ar = a.A + d * N;
+  const int64_t bc = b * N;
+  float acc = 0.0f;
+  // 16 states at a time with vector accesses when rows allow it
+  const bool vec = (N % 16) == 0;
+  for (int64_t n0 = 0; n0 < N; n0 += 16) {
+    const int cnt = (int)((N - n0) < 16 ? (N - n0) : 16);
+    float h[16], An[16], Bv[16], Cv[16];
+    if (vec) {
+#pragma unroll
+      for (int k = 0; k < 16; k += 4) {
+        const f32x4 s4 = *reinterpret_cast<const f32x4*>(st + n0 + k);
+        const float4 a4 = *reinterpret_cast<const float4*>(Ar + n0 + k);
+        h[k] = s4.x; h[k + 1] = s4.y; h[k + 2] = s4.z; h[k + 3] = s4.w;
+        An[k] = a4.x; An[k + 1] = a4.y; An[k + 2] = a4.z; An[k + 3] = a4.w;
+      }
+#pragma unroll
+      for (int k = 0; k < 16; k += Io<IO>::V) {
+        Io<IO>::ldv(a.Bm, bc + n0 + k, Bv + k);
+        Io<IO>::ldv(a.Cm, bc + n0 + k, Cv + k);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const bool ok = k < cnt;
+        h[k] = ok ? st[n0 + k] : 0.0f;
+        An[k] = ok ? Ar[n0 + k] : 0.0f;
+        Bv[k] = ok ? Io<IO>::ld1(a.Bm, bc + n0 + k) : 0.0f;
+        Cv[k] = ok ? Io<IO>::ld1(a.Cm, bc + n0 + k) : 0.0f;
       }
     }
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if (k < cnt) {
-        const float An = a.A[d * N + n + k];
-        const float e = ex2(dt * An * kLog2e);
-        const float Bv = Io<IO>::ld1(a.Bm, b * N + n + k);
-        const float Cv = Io<IO>::ld1(a.Cm, b * N + n + k);
-        float x;
-        if constexpr (ZOH) {
-          const float coef = An != 0.0f ? expm1_f(dt * An, e) * rcp(An) : dt;
-          x = coef * Bv * uu;
-        } else {
-          x = w * Bv;
-        }
-        h[k] = fmaf(e, h[k], x);
-        acc = fmaf(Cv, h[k], acc);
-      }
-    }
-    if (valid) {
-      if (vec4) {
-        *reinterpret_cast<float4*>(st + n) = make_float4(h[0], h[1], h[2], h[3]);
+    for (int k = 0; k < 16; ++k) {
+      const float e = ex2(dl * An[k]);
+      float x;
+      if constexpr (ZOH) {
+        const float coef = An[k] != 0.0f ? expm1_f(dl * kLn2 * An[k], e) * rcp(An[k]) : dl * kLn2;
+        x = coef * Bv[k] * uu;
       } else {
-        for (int k = 0; k < cnt; ++k) st[n + k] = h[k];
+        x = w * Bv[k];
       }
+      h[k] = fmaf(e, h[k], x);
+      acc = fmaf(Cv[k], h[k], acc);
+    }
+    if (vec) {
+#pragma unroll
+      for (int k = 0; k < 16; k += 4) {
+        const f32x4 v = {h[k], h[k + 1], h[k + 2], h[k + 3]};
+        *reinterpret_cast<f32x4*>(st + n0 + k) = v;
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        if (k < cnt) st[n0 + k] = h[k];
     }
   }
-  // sum the four partial readouts of the channel (lanes 4c .. 4c+3)
-  acc += __shfl_xor(acc, 1);
-  acc += __shfl_xor(acc, 2);
-  if (valid && q == 0) {
-    float yv = acc + (a.Dskip ? a.Dskip[d] : 0.0f) * uu;
-    if constexpr (GATE) yv *= silu_f(Io<IO>::ld1(a.z, c));
-    Io<IO>::st1(a.y, c, yv);
-  }
+  float yv = acc + (a.Dskip ? a.Dskip[d] : 0.0f) * uu;
+  if constexpr (GATE) yv *= silu_f(Io<IO>::ld1(a.z, c));
+  Io<IO>::st1(a.y, c, yv);
 }
 
 // ---------------------------------------------------------------- LTI kernel
@@ -815,7 +826,7 @@ int ssm_state_update(float* state, const void* u, const void* delta, const float
   a.state = state; a.u = u; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm; a.Dskip = Dskip;
   a.z = z; a.delta_bias = delta_bias; a.y = y; a.batch = batch; a.dim = dim; a.dstate = dstate;
   a.softplus = delta_softplus ? 1 : 0;
-  const int64_t threads = batch * dim * 4;
+  const int64_t threads = batch * dim;
   const dim3 grid((unsigned)((threads + 255) / 256));
   if (grid.x == 0 || (threads + 255) / 256 > 0x7fffffff)
     return fail(SSM_E_SHAPE, "batch * dim too large for one launch");

@@ -290,3 +290,35 @@ def test_abi_rejects_misaligned_and_aliased_buffers(ssm, dev):
     args[10] = keep["u"].data_ptr()  # y aliases u
     assert lib.ssm_selective_scan_fwd(*args) == 5  # SSM_E_ALIAS
     assert "overlaps" in ssm.ssm_last_error()
+
+
+def test_decode_steps_in_a_hip_graph_match_eager(ssm, dev):
+    """Decode steps captured in a HIP graph: every replay (with eager work and
+    synchronisation between replays) matches the same steps run eagerly."""
+    w, x = wl.custom(4, 96, 16, 6, dtype="bf16", gate=True, seed=123)
+    cols = [{k: to_dev(np.ascontiguousarray(v[..., t]), dev) for k, v in x.items()
+             if isinstance(v, np.ndarray) and v.ndim == 3} for t in range(6)]
+    A, D, bias = to_dev(x["A"], dev), to_dev(x["D"], dev), to_dev(x["delta_bias"], dev)
+    s0 = torch.randn((4, 96, 16), dtype=torch.float32, device=dev) * 0.1
+    state = s0.clone()
+    y = torch.empty((4, 96), dtype=torch.bfloat16, device=dev)
+
+    def steps(st, out):
+        for c in cols:
+            ssm.ssm_state_update(st, c["u"], c["delta"], A, c["B"], c["C"], D=D, z=c["z"],
+                                 delta_bias=bias, delta_softplus=True, y=out)
+
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        steps(state, y)
+    ref_state = s0.clone()
+    ref_y = torch.empty_like(y)
+    state.copy_(s0)
+    for rep in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        steps(ref_state, ref_y)  # eager, between replays
+        torch.cuda.synchronize()
+        assert torch.equal(state.view(torch.int32), ref_state.view(torch.int32)), rep
+        assert torch.equal(y.view(torch.int16), ref_y.view(torch.int16)), rep
