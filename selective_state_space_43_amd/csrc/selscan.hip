@@ -72,11 +72,14 @@ __device__ __forceinline__ float softplus_f(float x) {
 }
 
 // softplus(x) / ln 2, the step size in log2 units, with the same accuracy.
+// The rounding error of u = 1 + e is corrected to first order with 1/u
+// replaced by 2 - u, which is exact enough wherever the correction matters
+// (u near 1) and negligible where it does not.
 __device__ __forceinline__ float softplus_log2(float x) {
   const float xl = x * kLog2e;
   const float e = ex2(xl);
   const float u = 1.0f + e;
-  const float l = lg2(u) - ((u - 1.0f) - e) * rcp(u) * kLog2e;
+  const float l = fmaf(((u - 1.0f) - e) * kLog2e, u - 2.0f, lg2(u));
   return x > 15.0f ? xl : l;
 }
 

@@ -141,6 +141,14 @@ def test_shapes_and_tails(ssm, dev, case):
     _check(ssm, dev, w, x, label=str(case))
 
 
+def test_tiny_steps_long_memory_fp32(ssm, dev):
+    """Very negative raw steps (softplus far below 1e-3) over a long sequence:
+    the step's relative accuracy decides the decay over thousands of steps."""
+    w, x = wl.custom(1, 32, 16, 6000, dtype="f32", gate=True, bias=False, delta_mean=-11.0,
+                     delta_std=2.0, a_init="loguniform", seed=77)
+    _check(ssm, dev, w, x, label="tiny steps")
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_exact_zoh_rule(ssm, dev, dt):
     w, x = wl.custom(2, 24, 16, 600, dtype=dt, gate=True, seed=31)
