@@ -7,11 +7,13 @@ fp64, sequential in time), and this module only marshals numpy arrays.
 
 Inputs are numpy arrays.  Sequence tensors (u, delta, z: [batch, dim, L];
 B, C: [batch, dstate, L]) are either ``float32`` or ``uint16`` holding bf16
-bit patterns; the C code widens them itself.  Per-channel parameters (A, D,
+bit patterns, or ``float64`` (used by the finite-difference pins); the C code
+widens them itself.  Per-channel parameters (A, D,
 delta_bias, h0) are widened to float64 here with ``astype`` (exact for float32).
 
 Each function cites the page passage it follows in ``ssm_oracle.c``.
-Parity status: every function here is pinned by ``tests/test_oracle_pins.py``.
+Parity status: every function here is pinned by ``tests/test_oracle_pins.py`` (forward,
+decode, LTI) and ``tests/test_oracle_bwd_pins.py`` (backward, by finite differences).
 """
 from __future__ import annotations
 
@@ -55,8 +57,12 @@ def _lib():
         lib.ssm_oracle_lti_kernel.argtypes = [
             vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, vp]
         lib.ssm_oracle_causal_conv.argtypes = [vp, vp, ctypes.c_double, i64, vp]
+        lib.ssm_oracle_selective_scan_bwd.argtypes = [
+            i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp,
+            i64, i64, i64, i64, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32]
         for f in (lib.ssm_oracle_selective_scan, lib.ssm_oracle_state_update,
-                  lib.ssm_oracle_lti_kernel, lib.ssm_oracle_causal_conv):
+                  lib.ssm_oracle_lti_kernel, lib.ssm_oracle_causal_conv,
+                  lib.ssm_oracle_selective_scan_bwd):
             f.restype = i32
         _LIB = lib
     return _LIB
@@ -75,7 +81,9 @@ def _seq(x, name):
         return x, 0
     if x.dtype == np.uint16:
         return x, 1
-    raise TypeError(f"{name}: expected float32 or uint16 (bf16 bits), got {x.dtype}")
+    if x.dtype == np.float64:
+        return x, 2
+    raise TypeError(f"{name}: expected float32, float64 or uint16 (bf16 bits), got {x.dtype}")
 
 
 def _f64(x):
@@ -191,3 +199,42 @@ def causal_conv(K, u, D=0.0):
     if rc != 0:
         raise RuntimeError("ssm_oracle_causal_conv failed")
     return y
+
+
+def selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None,
+                       delta_softplus=False, bbar="delta", h0=None, dfinal=None, channels=None,
+                       n_threads=None):
+    """Gradients of the fp64 selective scan for the loss sum(dy * y) +
+    sum(dfinal * final_state).  Returns a dict of float64 arrays: per selected
+    channel du, ddelta (raw step), dz (if z), dh0 ([n_sel, dstate]); summed over
+    the selected channels dA [dim, dstate], dB, dC [batch, dstate, L], dD,
+    ddelta_bias [dim]."""
+    u, dt = _seq(u, "u")
+    delta, _ = _seq(delta, "delta")
+    B, _ = _seq(B, "B")
+    C, _ = _seq(C, "C")
+    if z is not None:
+        z, _ = _seq(z, "z")
+    batch, dim, L = u.shape
+    N = A.shape[1]
+    sel = None if channels is None else np.ascontiguousarray(channels, dtype=np.int64)
+    n_sel = batch * dim if sel is None else sel.size
+    dy64 = np.ascontiguousarray(dy, dtype=np.float64)
+    assert dy64.shape == (batch, dim, L)
+    h064 = None if h0 is None else np.ascontiguousarray(h0, dtype=np.float64).reshape(n_sel, N)
+    df64 = None if dfinal is None else np.ascontiguousarray(dfinal, dtype=np.float64).reshape(n_sel, N)
+    out = dict(du=np.empty((n_sel, L)), ddelta=np.empty((n_sel, L)),
+               dz=np.empty((n_sel, L)) if z is not None else None,
+               dh0=np.empty((n_sel, N)),
+               dA=np.empty((dim, N)), dB=np.empty((batch, N, L)), dC=np.empty((batch, N, L)),
+               dD=np.empty(dim), ddelta_bias=np.empty(dim))
+    rc = _lib().ssm_oracle_selective_scan_bwd(
+        dt, _ptr(u), _ptr(delta), _ptr(B), _ptr(C), _ptr(z), _ptr(_f64(A)), _ptr(_f64(D)),
+        _ptr(_f64(delta_bias)), int(bool(delta_softplus)), BBAR_MODES[bbar], _ptr(h064),
+        _ptr(dy64), _ptr(df64), batch, dim, N, L, _ptr(sel), n_sel,
+        _ptr(out["du"]), _ptr(out["ddelta"]), _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]),
+        _ptr(out["dD"]), _ptr(out["dz"]), _ptr(out["ddelta_bias"]), _ptr(out["dh0"]),
+        int(n_threads or default_threads()))
+    if rc != 0:
+        raise RuntimeError(f"ssm_oracle_selective_scan_bwd failed ({rc})")
+    return out

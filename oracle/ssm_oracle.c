@@ -42,11 +42,12 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { OR_F32 = 0, OR_BF16 = 1 };
+enum { OR_F32 = 0, OR_BF16 = 1, OR_F64 = 2 };
 enum { OR_BBAR_DELTA_B = 0, OR_BBAR_ZOH_EXACT = 1 };
 
 /* bf16 is the upper half of an IEEE binary32; widening is exact. */
 static double or_widen(const void* p, int dtype, int64_t i) {
+  if (dtype == OR_F64) return ((const double*)p)[i];
   if (dtype == OR_F32) return (double)((const float*)p)[i];
   uint32_t bits = (uint32_t)((const uint16_t*)p)[i] << 16;
   float f;
@@ -162,7 +163,7 @@ int ssm_oracle_selective_scan(int io_dtype, const void* u, const void* delta, co
                               double* y, double* final_state, int n_threads) {
   if (!u || !delta || !Bm || !Cm || !A) return 1;
   if (batch <= 0 || dim <= 0 || dstate <= 0 || seqlen <= 0) return 1;
-  if (io_dtype != OR_F32 && io_dtype != OR_BF16) return 1;
+  if (io_dtype != OR_F32 && io_dtype != OR_BF16 && io_dtype != OR_F64) return 1;
   if (bbar_mode != OR_BBAR_DELTA_B && bbar_mode != OR_BBAR_ZOH_EXACT) return 1;
   if (!channels) n_channels = batch * dim;
   for (int64_t i = 0; channels && i < n_channels; ++i)
@@ -279,4 +280,241 @@ int ssm_oracle_causal_conv(const double* K, const double* u, double Dskip, int64
     y[t] = acc + Dskip * u[t];
   }
   return 0;
+}
+
+/* ------------------------------------------------------------------ backward
+ *
+ * Gradients of the selective scan by reverse-mode differentiation of the
+ * recurrence above (the backward pass that the fused kernel recomputes the
+ * state for: "State-space models", section "The parallel scan").  With
+ * g = dL/dy and the final-state gradient dL/dh_{L-1}:
+ *
+ *   yc_t = C_t . h_t + D u_t,  y_t = yc_t s_t,  s_t = silu(z_t)
+ *   dyc_t = g_t s_t,  dz_t = g_t yc_t silu'(z_t)
+ *   lambda_t = dyc_t C_t + Abar_{t+1} lambda_{t+1}   (dL/dh_t; the final-state
+ *                                                    gradient enters at L-1)
+ *   dC_t += dyc_t h_t,  dAbar_t = lambda_t h_{t-1},  dBbar_t = lambda_t B_t u_t
+ *   dB_t += lambda_t bbar_t u_t,  du_t = dyc_t D + sum_n lambda_t bbar_t B_t
+ *   ddt_t = sum_n [dAbar_t Abar_t A + dBbar_t dbbar/ddt]
+ *   dA += dAbar_t Abar_t dt_t + dBbar_t dbbar/dA
+ *   draw_t = ddt_t softplus'(raw_t + bias) = ddt_t sigmoid(raw_t + bias)
+ *   dh0 = Abar_0 lambda_0
+ *
+ * with bbar = dt (delta*B rule: dbbar/ddt = 1, dbbar/dA = 0) or
+ * bbar = (exp(dt A) - 1)/A (exact ZOH: dbbar/ddt = Abar,
+ * dbbar/dA = (dt Abar - bbar)/A, limit dt^2/2 at A = 0).
+ */
+
+static double or_sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+typedef struct {
+  int io_dtype;
+  const void *u, *delta, *Bm, *Cm, *z;
+  const double *A, *Dskip, *delta_bias, *h0, *dy, *dfinal;
+  int delta_softplus, bbar_mode;
+  int64_t batch, dim, dstate, seqlen;
+  const int64_t* channels;
+  int64_t n_channels;
+  double *du, *ddelta, *dz, *dh0;            /* per selected channel */
+  double *dA, *dB, *dC, *dD, *dbias;         /* shared sums (per-thread copies) */
+  int64_t next;
+  pthread_mutex_t lock;
+  int status;
+} or_bwd_job;
+
+typedef struct {
+  double *dA, *dB, *dC, *dD, *dbias;
+} or_bwd_acc;
+
+static void or_bwd_one(const or_bwd_job* j, int64_t sel, double* hs, double* lam, or_bwd_acc* acc) {
+  const int64_t c = j->channels ? j->channels[sel] : sel;
+  const int64_t b = c / j->dim, d = c % j->dim;
+  const int64_t N = j->dstate, L = j->seqlen;
+  const int64_t row = c * L, bc_base = b * N * L;
+  const double bias = j->delta_bias ? j->delta_bias[d] : 0.0;
+  const double Dd = j->Dskip ? j->Dskip[d] : 0.0;
+  /* forward: hs[(t + 1) * N + n] = h_t, hs[n] = h_{-1} */
+  for (int64_t n = 0; n < N; ++n) hs[n] = j->h0 ? j->h0[sel * N + n] : 0.0;
+  for (int64_t t = 0; t < L; ++t) {
+    const double ut = or_widen(j->u, j->io_dtype, row + t);
+    const double raw = or_widen(j->delta, j->io_dtype, row + t) + bias;
+    const double dt = j->delta_softplus ? or_softplus(raw) : raw;
+    for (int64_t n = 0; n < N; ++n) {
+      const double a = j->A[d * N + n];
+      const double bt = or_widen(j->Bm, j->io_dtype, bc_base + n * L + t);
+      hs[(t + 1) * N + n] =
+          exp(dt * a) * hs[t * N + n] + or_bbar_factor(dt, a, j->bbar_mode) * bt * ut;
+    }
+  }
+  /* reverse: lam[n] holds Abar_{t+1} lambda_{t+1} (the final-state gradient at t = L-1) */
+  for (int64_t n = 0; n < N; ++n) lam[n] = j->dfinal ? j->dfinal[sel * N + n] : 0.0;
+  for (int64_t t = L - 1; t >= 0; --t) {
+    const double ut = or_widen(j->u, j->io_dtype, row + t);
+    const double raw = or_widen(j->delta, j->io_dtype, row + t) + bias;
+    const double dt = j->delta_softplus ? or_softplus(raw) : raw;
+    double yc = Dd * ut;
+    for (int64_t n = 0; n < N; ++n)
+      yc += or_widen(j->Cm, j->io_dtype, bc_base + n * L + t) * hs[(t + 1) * N + n];
+    const double g = j->dy[row + t];
+    double dyc = g;
+    if (j->z) {
+      const double zz = or_widen(j->z, j->io_dtype, row + t);
+      const double sg = or_sigmoid(zz);
+      dyc = g * zz * sg;
+      if (j->dz) j->dz[sel * L + t] = g * yc * sg * (1.0 + zz * (1.0 - sg));
+    }
+    acc->dD[d] += dyc * ut;
+    double du = dyc * Dd, ddt = 0.0;
+    for (int64_t n = 0; n < N; ++n) {
+      const double a = j->A[d * N + n];
+      const double abar = exp(dt * a);
+      const double bbar = or_bbar_factor(dt, a, j->bbar_mode);
+      const double bt = or_widen(j->Bm, j->io_dtype, bc_base + n * L + t);
+      const double ct = or_widen(j->Cm, j->io_dtype, bc_base + n * L + t);
+      const double l = dyc * ct + lam[n];
+      const double dabar = l * hs[t * N + n];
+      const double dbbar = l * bt * ut;
+      acc->dC[bc_base + n * L + t] += dyc * hs[(t + 1) * N + n];
+      acc->dB[bc_base + n * L + t] += l * bbar * ut;
+      du += l * bbar * bt;
+      double dbbar_ddt, dbbar_dA;
+      if (j->bbar_mode == OR_BBAR_DELTA_B) {
+        dbbar_ddt = 1.0;
+        dbbar_dA = 0.0;
+      } else {
+        dbbar_ddt = abar;
+        dbbar_dA = a != 0.0 ? (dt * abar - bbar) / a : 0.5 * dt * dt;
+      }
+      ddt += dabar * abar * a + dbbar * dbbar_ddt;
+      acc->dA[d * N + n] += dabar * abar * dt + dbbar * dbbar_dA;
+      lam[n] = abar * l;
+    }
+    const double dr = j->delta_softplus ? ddt * or_sigmoid(raw) : ddt;
+    j->du[sel * L + t] = du;
+    j->ddelta[sel * L + t] = dr;
+    acc->dbias[d] += dr;
+  }
+  if (j->dh0)
+    for (int64_t n = 0; n < N; ++n) j->dh0[sel * N + n] = lam[n];
+}
+
+static void* or_bwd_worker(void* arg) {
+  or_bwd_job* j = (or_bwd_job*)arg;
+  const int64_t N = j->dstate, L = j->seqlen, D = j->dim, Bt = j->batch;
+  double* hs = (double*)malloc(sizeof(double) * (size_t)((L + 1) * N));
+  double* lam = (double*)malloc(sizeof(double) * (size_t)N);
+  or_bwd_acc acc;
+  acc.dA = (double*)calloc((size_t)(D * N), sizeof(double));
+  acc.dD = (double*)calloc((size_t)D, sizeof(double));
+  acc.dbias = (double*)calloc((size_t)D, sizeof(double));
+  acc.dB = (double*)calloc((size_t)(Bt * N * L), sizeof(double));
+  acc.dC = (double*)calloc((size_t)(Bt * N * L), sizeof(double));
+  int ok = hs && lam && acc.dA && acc.dD && acc.dbias && acc.dB && acc.dC;
+  for (; ok;) {
+    pthread_mutex_lock(&j->lock);
+    const int64_t sel = j->next++;
+    pthread_mutex_unlock(&j->lock);
+    if (sel >= j->n_channels) break;
+    or_bwd_one(j, sel, hs, lam, &acc);
+  }
+  pthread_mutex_lock(&j->lock);
+  if (!ok) {
+    j->status = 2;
+  } else {
+    for (int64_t i = 0; i < D * N; ++i) j->dA[i] += acc.dA[i];
+    for (int64_t i = 0; i < D; ++i) j->dD[i] += acc.dD[i];
+    for (int64_t i = 0; i < D; ++i) j->dbias[i] += acc.dbias[i];
+    for (int64_t i = 0; i < Bt * N * L; ++i) j->dB[i] += acc.dB[i];
+    for (int64_t i = 0; i < Bt * N * L; ++i) j->dC[i] += acc.dC[i];
+  }
+  pthread_mutex_unlock(&j->lock);
+  free(hs);
+  free(lam);
+  free(acc.dA);
+  free(acc.dD);
+  free(acc.dbias);
+  free(acc.dB);
+  free(acc.dC);
+  return NULL;
+}
+
+/*
+ * Backward of ssm_oracle_selective_scan over the selected channels.
+ *   dy          : [batch, dim, seqlen] double, gradient of y
+ *   dfinal      : [n_channels, dstate] double or NULL, gradient of the final state
+ *   h0          : [n_channels, dstate] double or NULL
+ * Outputs (double; the sums add the selected channels' contributions):
+ *   du, ddelta  : [n_channels, seqlen] (ddelta is the gradient of the raw step)
+ *   dz          : [n_channels, seqlen] or NULL
+ *   dh0         : [n_channels, dstate] or NULL
+ *   dA          : [dim, dstate];  dB, dC : [batch, dstate, seqlen];  dD, dbias : [dim]
+ * The sums are overwritten (zeroed first).  Returns 0, 1 on bad arguments,
+ * 2 on allocation failure.
+ */
+int ssm_oracle_selective_scan_bwd(int io_dtype, const void* u, const void* delta, const void* Bm,
+                                  const void* Cm, const void* z, const double* A,
+                                  const double* Dskip, const double* delta_bias,
+                                  int delta_softplus, int bbar_mode, const double* h0,
+                                  const double* dy, const double* dfinal, int64_t batch,
+                                  int64_t dim, int64_t dstate, int64_t seqlen,
+                                  const int64_t* channels, int64_t n_channels, double* du,
+                                  double* ddelta, double* dA, double* dB, double* dC, double* dD,
+                                  double* dz, double* dbias, double* dh0, int n_threads) {
+  if (!u || !delta || !Bm || !Cm || !A || !dy || !du || !ddelta || !dA || !dB || !dC || !dD ||
+      !dbias)
+    return 1;
+  if (batch <= 0 || dim <= 0 || dstate <= 0 || seqlen <= 0) return 1;
+  if (io_dtype != OR_F32 && io_dtype != OR_BF16 && io_dtype != OR_F64) return 1;
+  if (bbar_mode != OR_BBAR_DELTA_B && bbar_mode != OR_BBAR_ZOH_EXACT) return 1;
+  if (!channels) n_channels = batch * dim;
+  for (int64_t i = 0; channels && i < n_channels; ++i)
+    if (channels[i] < 0 || channels[i] >= batch * dim) return 1;
+  memset(dA, 0, sizeof(double) * (size_t)(dim * dstate));
+  memset(dD, 0, sizeof(double) * (size_t)dim);
+  memset(dbias, 0, sizeof(double) * (size_t)dim);
+  memset(dB, 0, sizeof(double) * (size_t)(batch * dstate * seqlen));
+  memset(dC, 0, sizeof(double) * (size_t)(batch * dstate * seqlen));
+  or_bwd_job j;
+  memset(&j, 0, sizeof j);
+  j.io_dtype = io_dtype;
+  j.u = u;
+  j.delta = delta;
+  j.Bm = Bm;
+  j.Cm = Cm;
+  j.z = z;
+  j.A = A;
+  j.Dskip = Dskip;
+  j.delta_bias = delta_bias;
+  j.h0 = h0;
+  j.dy = dy;
+  j.dfinal = dfinal;
+  j.delta_softplus = delta_softplus;
+  j.bbar_mode = bbar_mode;
+  j.batch = batch;
+  j.dim = dim;
+  j.dstate = dstate;
+  j.seqlen = seqlen;
+  j.channels = channels;
+  j.n_channels = n_channels;
+  j.du = du;
+  j.ddelta = ddelta;
+  j.dz = dz;
+  j.dh0 = dh0;
+  j.dA = dA;
+  j.dB = dB;
+  j.dC = dC;
+  j.dD = dD;
+  j.dbias = dbias;
+  pthread_mutex_init(&j.lock, NULL);
+  if (n_threads < 1) n_threads = 1;
+  if (n_threads > 256) n_threads = 256;
+  if ((int64_t)n_threads > n_channels) n_threads = (int)n_channels;
+  pthread_t tid[256];
+  int started = 0;
+  for (int i = 1; i < n_threads; ++i)
+    if (pthread_create(&tid[started], NULL, or_bwd_worker, &j) == 0) ++started;
+  or_bwd_worker(&j);
+  for (int i = 0; i < started; ++i) pthread_join(tid[i], NULL);
+  pthread_mutex_destroy(&j.lock);
+  return j.status;
 }
