@@ -223,14 +223,16 @@ def selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None,
     assert dy64.shape == (batch, dim, L)
     h064 = None if h0 is None else np.ascontiguousarray(h0, dtype=np.float64).reshape(n_sel, N)
     df64 = None if dfinal is None else np.ascontiguousarray(dfinal, dtype=np.float64).reshape(n_sel, N)
+    # held in locals: the C call reads them through raw addresses
+    A64, D64, bias64 = _f64(A), _f64(D), _f64(delta_bias)
     out = dict(du=np.empty((n_sel, L)), ddelta=np.empty((n_sel, L)),
                dz=np.empty((n_sel, L)) if z is not None else None,
                dh0=np.empty((n_sel, N)),
                dA=np.empty((dim, N)), dB=np.empty((batch, N, L)), dC=np.empty((batch, N, L)),
                dD=np.empty(dim), ddelta_bias=np.empty(dim))
     rc = _lib().ssm_oracle_selective_scan_bwd(
-        dt, _ptr(u), _ptr(delta), _ptr(B), _ptr(C), _ptr(z), _ptr(_f64(A)), _ptr(_f64(D)),
-        _ptr(_f64(delta_bias)), int(bool(delta_softplus)), BBAR_MODES[bbar], _ptr(h064),
+        dt, _ptr(u), _ptr(delta), _ptr(B), _ptr(C), _ptr(z), _ptr(A64), _ptr(D64),
+        _ptr(bias64), int(bool(delta_softplus)), BBAR_MODES[bbar], _ptr(h064),
         _ptr(dy64), _ptr(df64), batch, dim, N, L, _ptr(sel), n_sel,
         _ptr(out["du"]), _ptr(out["ddelta"]), _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]),
         _ptr(out["dD"]), _ptr(out["dz"]), _ptr(out["ddelta_bias"]), _ptr(out["dh0"]),

@@ -89,3 +89,32 @@ def test_backward_channel_selection_and_zero_gradients():
     for k, v in z0.items():
         if v is not None:
             assert np.all(v == 0), k
+
+
+def test_backward_float32_parameters_marshalled_like_float64():
+    """A, D and delta_bias stored as float32 (as the workloads hold them) give
+    the same gradients as their exact float64 copies: the float64 buffers the
+    wrapper makes must stay alive through the C call."""
+    r = np.random.default_rng(21)
+    Bt, Dm, N, L = 1, 16, 16, 128
+    u = r.standard_normal((Bt, Dm, L)).astype(np.float32)
+    delta = r.standard_normal((Bt, Dm, L)).astype(np.float32)
+    B = r.standard_normal((Bt, N, L)).astype(np.float32)
+    C = r.standard_normal((Bt, N, L)).astype(np.float32)
+    A = -np.tile(np.arange(1, N + 1, dtype=np.float32), (Dm, 1))
+    D = r.standard_normal(Dm).astype(np.float32)
+    bias = r.normal(-1, 0.5, Dm).astype(np.float32)
+    dy = r.standard_normal((Bt, Dm, L))
+    dfinal = r.standard_normal((Bt * Dm, N))
+    for bbar in ("delta", "zoh"):
+        g32 = oracle.selective_scan_bwd(u, delta, A, B, C, dy, D=D, delta_bias=bias,
+                                        delta_softplus=True, bbar=bbar, dfinal=dfinal,
+                                        n_threads=1)
+        g64 = oracle.selective_scan_bwd(u, delta, A.astype(np.float64), B, C, dy,
+                                        D=D.astype(np.float64),
+                                        delta_bias=bias.astype(np.float64),
+                                        delta_softplus=True, bbar=bbar, dfinal=dfinal,
+                                        n_threads=1)
+        for k, v in g64.items():
+            if v is not None:
+                assert np.array_equal(g32[k], v), (bbar, k)
