@@ -7,7 +7,8 @@ discretization, scan, readout, skip, gate, store) over the whole batch of the
 Mamba-2.8B-shaped layer (batch 4, dim 5120, N 16, L 8192, bf16 io, fp32
 arithmetic and state).  Inputs are generated once, uploaded, and resident in
 HBM before timing starts.  The one-token decode step (ssm_state_update) is
-timed separately on the decode workload and reported under "decode".
+timed separately on the decode workload and reported under "decode", and the
+backward pass (ssm_selective_scan_bwd) on the same workload under "backward".
 
 Prints one JSON line: the metric (scan elements B*D*L*N per second), the
 roofline of the scan kernel (live HIP-event timing; HBM traffic from the
@@ -166,6 +167,53 @@ def bench_decode(ssm, torch, dev, steps, warmup):
     }
 
 
+def bench_bwd(ssm, torch, w, x, dev, steps, warmup):
+    """The backward pass (ssm_selective_scan_bwd: checkpointed forward, adjoint
+    carries, gradients) on the same inputs with a seeded upstream gradient.
+    Every gradient is produced; the workspace is allocated once outside the
+    timed region."""
+    g = wl.grad_inputs(w)
+    u, dl, A, B, C = (to_dev(x[k], dev) for k in ("u", "delta", "A", "B", "C"))
+    D, z, bias = to_dev(x["D"], dev), to_dev(x["z"], dev), to_dev(x["delta_bias"], dev)
+    dy = to_dev(g["dy"], dev)
+    ws = torch.empty(ssm.ssm_selective_scan_bwd_workspace_size(w.batch, w.dim, w.dstate,
+                                                               w.seqlen),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        return ssm.ssm_selective_scan_bwd(u, dl, A, B, C, dy, D=D, z=z, delta_bias=bias,
+                                          delta_softplus=True, workspace=ws, want_dh0=True)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        step()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    es = 2 if w.dtype == "bf16" else 4
+    seq = w.batch * w.dim * w.seqlen * es
+    bc = w.batch * w.dstate * w.seqlen * es
+    n_seq_in = 4 if w.gate else 3      # u, delta, dy (, z)
+    n_seq_out = 3 if w.gate else 2     # du, ddelta (, dz)
+    algo = (n_seq_in + n_seq_out) * seq + 4 * bc  # B, C read; dB, dC written
+    gbps = algo / (ms * 1e-3) / 1e9
+    return {
+        "workload": f"{w.name} backward: every gradient (du, ddelta, dz, dA, dB, dC, dD, "
+                    "ddelta_bias, dh0)",
+        "ms_per_call": round(ms, 4),
+        "elements_per_s": float("%.4g" % (w.elements / (ms * 1e-3))),
+        "algorithmic_bytes": algo,
+        "hbm_gbps": round(gbps, 1),
+        "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "steps": steps,
+    }
+
+
 def cpu_baseline(w, x, seconds_target=12.0):
     """The fp64 oracle on host cores over whole channels of the same inputs:
     as many channels (full length each) as fit the time target."""
@@ -202,6 +250,8 @@ def main(argv=None):
     p.add_argument("--decode-steps", type=int, default=200)
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-backward", action="store_true")
+    p.add_argument("--backward-steps", type=int, default=5)
     p.add_argument("--copy-check", type=int, default=0, metavar="BYTES",
                    help="also run torch's plain copy of BYTES three times (counter calibration "
                         "under rocprofv3)")
@@ -287,6 +337,10 @@ def main(argv=None):
     if not args.no_decode:
         out["decode"] = bench_decode(ssm, torch, dev, args.decode_steps, 10)
         print(f"[bench] decode: {out['decode']['us_per_step']} us/step", file=sys.stderr,
+              flush=True)
+    if not args.no_backward and w.dstate <= 16:
+        out["backward"] = bench_bwd(ssm, torch, w, x, dev, args.backward_steps, 1)
+        print(f"[bench] backward: {out['backward']['ms_per_call']} ms/call", file=sys.stderr,
               flush=True)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, x)

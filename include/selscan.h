@@ -138,6 +138,52 @@ int ssm_lti_kernel(const float* A, const float* Bv, const float* Cv, const float
                    int64_t dim, int64_t dstate, int64_t L, int64_t b_row_stride,
                    int64_t c_row_stride, int bbar_mode, void* hip_stream);
 
+/*
+ * Backward of ssm_selective_scan_fwd: gradients of the loss
+ * sum(dy * y) + sum(dfinal_state * final_state) with respect to every input,
+ * by reverse-mode differentiation of the recurrence with the states
+ * recomputed rather than stored ("State-space models", section "The
+ * parallel scan": the fused kernel recomputes the expanded state in the
+ * backward pass).  The adjoint lambda_t = dL/dh_t obeys the same recurrence
+ * run backwards, lambda_t = dyc_t C_t + Abar_{t+1} lambda_{t+1}, and is
+ * scanned the same way.
+ *
+ * Inputs: the forward's inputs (same layouts, dtypes and rules; y and the
+ * final state are not needed), and
+ *  dy           [batch, dim, seqlen] io_dtype: gradient of y
+ *  dfinal_state [batch, dim, dstate] float32 or NULL (= 0)
+ * Outputs (overwritten; none may overlap an input or another output):
+ *  du, ddelta   [batch, dim, seqlen] io_dtype; ddelta is the gradient of the
+ *               raw step (before bias and softplus)
+ *  dA           [dim, dstate] float32
+ *  dB, dC       [batch, dstate, seqlen] io_dtype (summed over channels)
+ *  dD           [dim] float32 or NULL (not computed)
+ *  dz           [batch, dim, seqlen] io_dtype; required when z is given
+ *  ddelta_bias  [dim] float32 or NULL (not computed)
+ *  dh0          [batch, dim, dstate] float32 or NULL (not computed)
+ *  workspace    device memory of at least
+ *               ssm_selective_scan_bwd_workspace_size(batch, dim, dstate, seqlen)
+ *               bytes, 16-byte aligned, owned by the caller; its contents on
+ *               entry do not matter.  Calls that share a workspace must not
+ *               run concurrently.
+ * dstate must be 1..16 (SSM_E_UNSUPPORTED otherwise).  dA, dD, ddelta_bias,
+ * dB and dC are sums accumulated in float32 with atomic adds, so they can
+ * differ in the last bits from run to run.
+ */
+int ssm_selective_scan_bwd(const void* u, const void* delta, const float* A, const void* Bm,
+                           const void* Cm, const float* Dskip, const void* z,
+                           const float* delta_bias, int delta_softplus, const float* h0,
+                           const void* dy, const float* dfinal_state, void* du, void* ddelta,
+                           float* dA, void* dB, void* dC, float* dD, void* dz,
+                           float* ddelta_bias, float* dh0, void* workspace,
+                           int64_t workspace_bytes, int64_t batch, int64_t dim, int64_t dstate,
+                           int64_t seqlen, int io_dtype, int bbar_mode, void* hip_stream);
+
+/* Bytes of workspace ssm_selective_scan_bwd needs for these extents (-1 if
+ * an extent is out of range).  Host-only, enqueues nothing. */
+int64_t ssm_selective_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
+                                              int64_t seqlen);
+
 /* Static description of a status code (never NULL). */
 const char* ssm_status_str(int status);
 

@@ -13,6 +13,9 @@ Entry points carry the C names:
   ssm_state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None,
                    delta_softplus=False, bbar="delta", y=None) -> y
   ssm_lti_kernel(A, Bv, Cv, delta, L, bbar="delta", K=None) -> K
+  ssm_selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None,
+                         delta_softplus=False, h0=None, dfinal_state=None,
+                         bbar="delta", workspace=None) -> dict of gradients
 
 Layouts: u, delta, z, y [batch, dim, L]; B, C [batch, dstate, L]; A
 [dim, dstate]; D, delta_bias [dim]; h0 / final_state / state
@@ -24,10 +27,13 @@ from __future__ import annotations
 from ._lib import (SSM_BBAR_DELTA_B, SSM_BBAR_ZOH_EXACT, SSM_DTYPE_BF16, SSM_DTYPE_F32,
                    SelscanError, library_path, lib, ssm_abi_version, ssm_last_error,
                    ssm_status_str)
-from .binding import ssm_lti_kernel, ssm_selective_scan_fwd, ssm_state_update
+from .binding import (ssm_lti_kernel, ssm_selective_scan_bwd,
+                      ssm_selective_scan_bwd_workspace_size, ssm_selective_scan_fwd,
+                      ssm_state_update)
 
 __all__ = [
-    "ssm_selective_scan_fwd", "ssm_state_update", "ssm_lti_kernel", "ssm_status_str",
+    "ssm_selective_scan_fwd", "ssm_state_update", "ssm_lti_kernel", "ssm_selective_scan_bwd",
+    "ssm_selective_scan_bwd_workspace_size", "ssm_status_str",
     "ssm_last_error", "ssm_abi_version", "SelscanError", "library_path", "lib",
     "SSM_DTYPE_F32", "SSM_DTYPE_BF16", "SSM_BBAR_DELTA_B", "SSM_BBAR_ZOH_EXACT",
 ]

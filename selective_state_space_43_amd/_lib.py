@@ -41,7 +41,13 @@ def lib() -> ctypes.CDLL:
         L.ssm_state_update.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp,
                                        i64, i64, i64, i32, i32, vp]
         L.ssm_lti_kernel.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
-        for f in (L.ssm_selective_scan_fwd, L.ssm_state_update, L.ssm_lti_kernel):
+        L.ssm_selective_scan_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp,
+                                             vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64,
+                                             i64, i64, i64, i64, i32, i32, vp]
+        L.ssm_selective_scan_bwd_workspace_size.argtypes = [i64, i64, i64, i64]
+        L.ssm_selective_scan_bwd_workspace_size.restype = i64
+        for f in (L.ssm_selective_scan_fwd, L.ssm_state_update, L.ssm_lti_kernel,
+                  L.ssm_selective_scan_bwd):
             f.restype = i32
         L.ssm_status_str.argtypes = [i32]
         L.ssm_status_str.restype = ctypes.c_char_p

@@ -141,3 +141,59 @@ def ssm_lti_kernel(A, Bv, Cv, delta, L, bbar="delta", K=None):
                                   bs, cs, _BBAR[bbar], _stream(dev))
     check(st, "ssm_lti_kernel")
     return K
+
+
+def ssm_selective_scan_bwd_workspace_size(batch, dim, dstate, seqlen):
+    n = lib().ssm_selective_scan_bwd_workspace_size(batch, dim, dstate, seqlen)
+    if n < 0:
+        raise ValueError("extents out of range")
+    return int(n)
+
+
+def ssm_selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None,
+                           delta_softplus=False, h0=None, dfinal_state=None, bbar="delta",
+                           workspace=None, want_dh0=None):
+    """Gradients of sum(dy * y) + sum(dfinal_state * final_state).  Returns a
+    dict with du, ddelta (raw step), dA, dB, dC, and dD / dz / ddelta_bias /
+    dh0 when D / z / delta_bias / h0 (or want_dh0) are given."""
+    _dev(u, "u", None)
+    dev = u.device
+    if u.dim() != 3 or u.dtype not in _IO:
+        raise TypeError("u must be [batch, dim, L] bfloat16 or float32")
+    batch, dim, L = u.shape
+    N = A.shape[1]
+    io = u.dtype
+    for t, n, shp in ((delta, "delta", (batch, dim, L)), (dy, "dy", (batch, dim, L)),
+                      (B, "B", (batch, N, L)), (C, "C", (batch, N, L))):
+        _io(t, n, io, shp, dev)
+    _io(A, "A", torch.float32, (dim, N), dev)
+    _f32(D, "D", (dim,), dev)
+    if z is not None:
+        _io(z, "z", io, (batch, dim, L), dev)
+    _f32(delta_bias, "delta_bias", (dim,), dev)
+    _f32(h0, "h0", (batch, dim, N), dev)
+    _f32(dfinal_state, "dfinal_state", (batch, dim, N), dev)
+    need = ssm_selective_scan_bwd_workspace_size(batch, dim, N, L)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    elif workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace needs {need} bytes")
+    g = dict(du=torch.empty_like(u), ddelta=torch.empty_like(u),
+             dA=torch.empty((dim, N), dtype=torch.float32, device=dev),
+             dB=torch.empty_like(B), dC=torch.empty_like(C),
+             dD=torch.empty(dim, dtype=torch.float32, device=dev) if D is not None else None,
+             dz=torch.empty_like(u) if z is not None else None,
+             ddelta_bias=(torch.empty(dim, dtype=torch.float32, device=dev)
+                          if delta_bias is not None else None),
+             dh0=(torch.empty((batch, dim, N), dtype=torch.float32, device=dev)
+                  if (h0 is not None or want_dh0) else None))
+    with torch.cuda.device(dev):
+        st = lib().ssm_selective_scan_bwd(
+            _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+            int(bool(delta_softplus)), _ptr(h0), _ptr(dy), _ptr(dfinal_state), _ptr(g["du"]),
+            _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]),
+            _ptr(g["dz"]), _ptr(g["ddelta_bias"]), _ptr(g["dh0"]), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), batch, dim, N, L, _IO[io],
+            _BBAR[bbar], _stream(dev))
+    check(st, "ssm_selective_scan_bwd")
+    return g

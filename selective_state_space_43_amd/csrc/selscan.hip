@@ -189,6 +189,28 @@ __device__ __forceinline__ void row_scan16(float A, float& H) {
       : "+v"(H), "+v"(A));
 }
 
+// The same scan run towards lower lanes (row_shl): on return H on lane l
+// composes the pairs of lanes l..15 of its row, i.e. the suffix scan used by
+// the adjoint recurrence, which runs backwards in time.
+__device__ __forceinline__ void row_scan16_rev(float A, float& H) {
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %0, %0, %1 row_shl:1 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_mul_f32_dpp %1, %1, %1 row_shl:1 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %0, %0, %1 row_shl:2 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_mul_f32_dpp %1, %1, %1 row_shl:2 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %0, %0, %1 row_shl:4 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_mul_f32_dpp %1, %1, %1 row_shl:4 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "s_nop 1\n\t"
+      "v_fmac_f32_dpp %0, %0, %1 row_shl:8 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "s_nop 1"
+      : "+v"(H), "+v"(A));
+}
+
+constexpr int kRowShl1 = 0x101;
+
 // Step across rows (row broadcast) for groups wider than a row: every lane of
 // the receiving rows uses its own A, so A keeps the identity where there is
 // no source.
@@ -304,9 +326,13 @@ struct ScanArgs {
   float* final_state;
   int64_t dim, dstate, seqlen;
   int softplus;
+  float* ckpt;  // checkpoint mode: state at each chunk start, [batch, dim, chunks, dstate]
 };
 
-template <typename IO, int LPC, int K, int W, int NT, bool VEC, bool ZOH, bool GATE>
+// CKPT: the pass that the backward recomputes from: it writes the state at
+// the start of every chunk to a.ckpt and computes no output.
+template <typename IO, int LPC, int K, int W, int NT, bool VEC, bool ZOH, bool GATE,
+          bool CKPT = false>
 __global__ void __launch_bounds__(64 * W)
 #if SELSCAN_WAVES_PER_EU
     __attribute__((amdgpu_waves_per_eu(SELSCAN_WAVES_PER_EU, SELSCAN_WAVES_PER_EU)))
@@ -455,11 +481,16 @@ __global__ void __launch_bounds__(64 * W)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           h = fmaf(av[i + q], h, xv[i + q]);
-          y[i + q] = fmaf(cq[q], h, y[i + q]);
+          if constexpr (!CKPT) y[i + q] = fmaf(cq[q], h, y[i + q]);
         }
       }
     };
 
+    if constexpr (CKPT) {
+      if (dvalid)
+        for (int64_t n = seg; n < N; n += LPC)
+          a.ckpt[((b * a.dim + d) * ((L + T - 1) / T) + t0 / T) * N + n] = carry_row[n];
+    }
     for (int64_t n0 = 0; n0 < N; n0 += NT) {
       if (n0 > 0) {
         __syncthreads();  // every wave is done with the previous tile
@@ -470,6 +501,7 @@ __global__ void __launch_bounds__(64 * W)
 #pragma unroll 1
       for (int j = 0; j < nt; ++j) state(j, n0 + j);
     }
+    if constexpr (CKPT) return;
     if constexpr (GATE) {
       float zz[K];
       rz.unpack(zz);
@@ -490,6 +522,410 @@ __global__ void __launch_bounds__(64 * W)
     for (int64_t n = seg; n < N; n += LPC)
       a.final_state[(b * a.dim + d) * N + n] = carry_row[n];
   }
+}
+
+// ---------------------------------------------------------------- backward
+//
+// Gradients of the forward scan for the loss sum(dy * y) + sum(dfinal * h_L)
+// by reverse-mode differentiation of the recurrence, with the states
+// recomputed instead of stored ("State-space models", section "The parallel
+// scan": the fused kernel recomputes the expanded state in the backward
+// pass).  With s = silu(z), dyc = dy s and lambda_t = dL/dh_t:
+//
+//   lambda_t = dyc_t C_t + Abar_{t+1} lambda_{t+1}        (adjoint, backwards in t)
+//   dC_t += dyc_t h_t,  dB_t += lambda_t bbar_t u_t,  du_t = dyc_t D + sum_n lambda_t bbar_t B_t
+//   ddelta_t = sum_n [lambda_t h_{t-1} Abar_t A + lambda_t B_t u_t dbbar/ddelta]
+//   dA += lambda_t h_{t-1} Abar_t delta_t + lambda_t B_t u_t dbbar/dA
+//   draw_t = ddelta_t sigmoid(raw_t + bias),  dz_t = dy_t yc_t silu'(z_t),  dh0 = Abar_0 lambda_0
+//
+// The adjoint is the same linear recurrence run backwards, so it scans with
+// the same pair composition.  Three passes over chunks of T = 16 K steps:
+//  1. the forward kernel in checkpoint mode stores the state at every chunk
+//     start;
+//  2. scan_bwd_carry_kernel runs the adjoint backwards over the chunks of
+//     each channel, keeping only mu = Abar lambda at every chunk end (the
+//     adjoint that enters the chunk from its future);
+//  3. scan_bwd_main_kernel treats every (sequence, chunk) independently,
+//     for a run of channel groups: it recomputes the chunk's states from the
+//     checkpoint, runs the adjoint from the stored carry and accumulates the
+//     gradients; dB and dC, which sum over the channels of a sequence, are
+//     reduced in LDS before one global atomic add per value.
+
+struct BwdArgs {
+  const void* u;
+  const void* delta;
+  const float* A;
+  const void* Bm;
+  const void* Cm;
+  const float* Dskip;
+  const void* z;
+  const float* delta_bias;
+  const void* dy;
+  const float* dfinal;
+  void* du;
+  void* ddelta;
+  float* dA;
+  float* dD;
+  void* dz;
+  float* ddelta_bias;
+  float* dh0;
+  const float* ckpt;  // [batch, dim, chunks, N]: state at each chunk start
+  float* carry;       // [batch, dim, chunks, N]: Abar lambda entering each chunk from its end
+  float* accB;        // [batch, N, L] float32 sums over channels
+  float* accC;
+  int64_t dim, dstate, seqlen, chunks;
+  int softplus;
+  int groups_per_block;  // channel groups of 16 per workgroup in the main pass
+};
+
+// sum over the 16 lanes of a row; the row's last lane holds the total
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp0<kRowShr1>(v);
+  v += dpp0<kRowShr2>(v);
+  v += dpp0<kRowShr4>(v);
+  v += dpp0<kRowShr8>(v);
+  return v;
+}
+
+// Sum over the four 16-lane rows of a wave (four channels) of eight values
+// per lane.  permlane32_swap trades the upper half of its first operand for
+// the lower half of its second, permlane16_swap the odd rows of the first for
+// the even rows of the second; adding each swapped pair halves the rows to sum
+// while packing two values into one register.  On return row r of lo holds
+// the four-row sum of v[red_step(r)] and row r of hi that of v[4 + red_step(r)].
+__device__ __forceinline__ int red_step(int row) { return ((row & 1) << 1) | (row >> 1); }
+
+__device__ __forceinline__ void rows_sum8(const float* v, float& lo, float& hi) {
+  float s[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[2 * p]),
+                                                    __float_as_uint(v[2 * p + 1]), false, false);
+    s[p] = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+  }
+  const auto y0 = __builtin_amdgcn_permlane16_swap(__float_as_uint(s[0]), __float_as_uint(s[1]),
+                                                   false, false);
+  const auto y1 = __builtin_amdgcn_permlane16_swap(__float_as_uint(s[2]), __float_as_uint(s[3]),
+                                                   false, false);
+  lo = __uint_as_float(y0[0]) + __uint_as_float(y0[1]);
+  hi = __uint_as_float(y1[0]) + __uint_as_float(y1[1]);
+}
+
+template <typename IO, int K, bool VEC, bool GATE>
+__global__ void __launch_bounds__(256) scan_bwd_carry_kernel(const BwdArgs a) {
+  constexpr int LPC = 16, CPB = 16, T = LPC * K, KP = K + 4, V = Io<IO>::V, TV = T / V;
+  constexpr int NT = 16, NTH = 256, ITEMS = (NT * TV + NTH - 1) / NTH;
+  __shared__ float4 sC4[NT * LPC * KP / 4];
+  __shared__ float sMu[CPB * NT], sA[CPB * NT];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int seg = lane % LPC;
+  const int chb = wave * 4 + lane / LPC;
+  const int64_t b = blockIdx.y, d0 = (int64_t)blockIdx.x * CPB, d = d0 + chb;
+  const bool dvalid = d < a.dim;
+  const int64_t N = a.dstate, L = a.seqlen;
+  const int64_t row = (b * a.dim + (dvalid ? d : 0)) * L, bcrow = b * N * L;
+  for (int i = threadIdx.x; i < CPB * N; i += NTH) {
+    const int64_t c = i / N, n = i % N;
+    const bool ok = d0 + c < a.dim;
+    sMu[i] = (a.dfinal && ok) ? a.dfinal[(b * a.dim + d0 + c) * N + n] : 0.0f;
+    sA[i] = ok ? a.A[(d0 + c) * N + n] : 0.0f;
+  }
+  for (int64_t ci = a.chunks - 1; ci >= 0; --ci) {
+    const int64_t t0 = ci * T, tl = t0 + seg * K;
+    Run<IO, K> rdy, rd, rz;
+    run_load<IO, K, VEC>(rdy, a.dy, row, tl, L, dvalid);
+    run_load<IO, K, VEC>(rd, a.delta, row, tl, L, dvalid);
+    if constexpr (GATE) run_load<IO, K, VEC>(rz, a.z, row, tl, L, dvalid);
+    __syncthreads();  // previous chunk's tile is no longer read; sMu/sA visible
+    if (dvalid && seg < N) a.carry[((b * a.dim + d) * a.chunks + ci) * N + seg] = sMu[chb * N + seg];
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k) {
+      const int item = threadIdx.x + k * NTH;
+      if (item < N * TV) {
+        const int nl = item / TV, tloc = (item % TV) * V;
+        Run<IO, V> rv;
+        run_load<IO, V, VEC>(rv, a.Cm, bcrow + nl * L, t0 + tloc, L, true);
+        float v[V];
+        rv.unpack(v);
+        float* dst = reinterpret_cast<float*>(sC4) + (nl * LPC + tloc / K) * KP + tloc % K;
+#pragma unroll
+        for (int q = 0; q < V; q += 4)
+          *reinterpret_cast<float4*>(dst + q) = make_float4(v[q], v[q + 1], v[q + 2], v[q + 3]);
+      }
+    }
+    __syncthreads();
+    float dl[K], dyc[K], S = 0.0f;
+    {
+      float raw[K], g[K], zz[K];
+      rd.unpack(raw);
+      rdy.unpack(g);
+      if constexpr (GATE) rz.unpack(zz);
+      const float bias = (a.delta_bias && dvalid) ? a.delta_bias[d] : 0.0f;
+#pragma unroll
+      for (int i = 0; i < K; ++i) {
+        const float x = raw[i] + bias;
+        const float v = a.softplus ? softplus_log2(x) : x * kLog2e;
+        dl[i] = (tl + i < L) ? v : 0.0f;
+        dyc[i] = GATE ? g[i] * silu_f(zz[i]) : g[i];
+        S += dl[i];
+      }
+    }
+#pragma unroll 1
+    for (int64_t n = 0; n < N; ++n) {
+      const float An = sA[chb * N + n];
+      const float mu = sMu[chb * N + n];
+      const float* pc = reinterpret_cast<const float*>(sC4) + (n * LPC + seg) * KP;
+      float av[K], gv[K];
+#pragma unroll
+      for (int i = 0; i < K; i += 4) {
+        const float4 cc = *reinterpret_cast<const float4*>(pc + i);
+        const float cq[4] = {cc.x, cc.y, cc.z, cc.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          av[i + q] = ex2(dl[i + q] * An);
+          gv[i + q] = dyc[i + q] * cq[q];
+        }
+      }
+      // fold the lane's steps backwards; the row's last lane starts from the
+      // adjoint entering the chunk
+      float Lam = gv[K - 1] + (seg == LPC - 1 ? mu : 0.0f);
+#pragma unroll
+      for (int i = K - 2; i >= 0; --i) Lam = fmaf(av[i + 1], Lam, gv[i]);
+      float H = av[0] * Lam;
+      row_scan16_rev(ex2(An * S), H);
+      if (seg == 0) sMu[chb * N + n] = H;  // Abar lambda at the chunk's first step
+    }
+  }
+}
+
+template <typename IO, int K, bool VEC, bool ZOH, bool GATE>
+__global__ void __launch_bounds__(256) scan_bwd_main_kernel(const BwdArgs a) {
+  static_assert(K == 8, "the channel reduction of dB and dC handles eight steps per lane");
+  constexpr int LPC = 16, CPB = 16, T = LPC * K, KP = K + 4, V = Io<IO>::V, TV = T / V;
+  constexpr int NT = 16, NTH = 256, ITEMS = (2 * NT * TV + NTH - 1) / NTH;
+  __shared__ float4 sB4[NT * LPC * KP / 4];
+  __shared__ float4 sC4[NT * LPC * KP / 4];
+  __shared__ float sdB[NT * T], sdC[NT * T];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int seg = lane % LPC;
+  const bool first = seg == 0, last = seg == LPC - 1;
+  const int chb = wave * 4 + lane / LPC;
+  const int64_t b = blockIdx.z, ci = blockIdx.y;
+  const int64_t N = a.dstate, L = a.seqlen;
+  const int64_t t0 = ci * T, tl = t0 + seg * K, bcrow = b * N * L;
+  for (int i = threadIdx.x; i < N * T; i += NTH) {
+    sdB[i] = 0.0f;
+    sdC[i] = 0.0f;
+  }
+#pragma unroll
+  for (int k = 0; k < ITEMS; ++k) {
+    const int item = threadIdx.x + k * NTH;
+    if (item < 2 * N * TV) {
+      const int tensor = item / (N * TV);
+      const int r = item % (N * TV);
+      const int nl = r / TV, tloc = (r % TV) * V;
+      Run<IO, V> rv;
+      run_load<IO, V, VEC>(rv, tensor ? a.Cm : a.Bm, bcrow + nl * L, t0 + tloc, L, true);
+      float v[V];
+      rv.unpack(v);
+      float* dst = reinterpret_cast<float*>(tensor ? sC4 : sB4) + (nl * LPC + tloc / K) * KP + tloc % K;
+#pragma unroll
+      for (int q = 0; q < V; q += 4)
+        *reinterpret_cast<float4*>(dst + q) = make_float4(v[q], v[q + 1], v[q + 2], v[q + 3]);
+    }
+  }
+  __syncthreads();
+
+  const int64_t ngroups = (a.dim + CPB - 1) / CPB;
+  const int64_t g_end = min((int64_t)(blockIdx.x + 1) * a.groups_per_block, ngroups);
+  for (int64_t g = (int64_t)blockIdx.x * a.groups_per_block; g < g_end; ++g) {
+    const int64_t d = g * CPB + chb;
+    const bool dvalid = d < a.dim;
+    const int64_t ch = b * a.dim + (dvalid ? d : 0);
+    const int64_t row = ch * L;
+    Run<IO, K> ru, rd, rz, rdy;
+    run_load<IO, K, VEC>(ru, a.u, row, tl, L, dvalid);
+    run_load<IO, K, VEC>(rd, a.delta, row, tl, L, dvalid);
+    run_load<IO, K, VEC>(rdy, a.dy, row, tl, L, dvalid);
+    if constexpr (GATE) run_load<IO, K, VEC>(rz, a.z, row, tl, L, dvalid);
+    const float bias = (a.delta_bias && dvalid) ? a.delta_bias[d] : 0.0f;
+    const float Dd = (a.Dskip && dvalid) ? a.Dskip[d] : 0.0f;
+    // per-step values: dl = delta / ln 2, dt = delta, uu = u, w = delta u,
+    // dyc = dy silu(z); accumulators yc (readout), ddt, du
+    float dl[K], uu[K], w[K], dyc[K], yc[K], ddt[K], du[K];
+    float S = 0.0f;
+    {
+      float raw[K], g[K], zz[K];
+      ru.unpack(uu);
+      rd.unpack(raw);
+      rdy.unpack(g);
+      if constexpr (GATE) rz.unpack(zz);
+#pragma unroll
+      for (int i = 0; i < K; ++i) {
+        const float x = raw[i] + bias;
+        const float v = a.softplus ? softplus_log2(x) : x * kLog2e;
+        dl[i] = (tl + i < L) ? v : 0.0f;
+        w[i] = dl[i] * kLn2 * uu[i];
+        dyc[i] = GATE ? g[i] * silu_f(zz[i]) : g[i];
+        yc[i] = Dd * uu[i];
+        ddt[i] = 0.0f;
+        du[i] = 0.0f;
+        S += dl[i];
+      }
+    }
+    const int64_t cbase = (ch * a.chunks + ci) * N;
+    const float* Arow = a.A + (dvalid ? d : 0) * N;
+    // the next state's per-channel values load one iteration ahead
+    float An_next = Arow[0], hs_next = a.ckpt[cbase], mu_next = a.carry[cbase];
+#pragma unroll 1
+    for (int64_t n = 0; n < N; ++n) {
+      const float An = An_next;
+      const float hs = hs_next;  // state before the chunk
+      const float mu_end = mu_next;
+      if (n + 1 < N) {
+        An_next = Arow[n + 1];
+        hs_next = a.ckpt[cbase + n + 1];
+        mu_next = a.carry[cbase + n + 1];
+      }
+      const float* pb = reinterpret_cast<const float*>(sB4) + (n * LPC + seg) * KP;
+      const float* pc = reinterpret_cast<const float*>(sC4) + (n * LPC + seg) * KP;
+      float av[K], xv[K], hp[K], bq[K], cq[K];
+#pragma unroll
+      for (int i = 0; i < K; i += 4) {
+        const float4 bb = *reinterpret_cast<const float4*>(pb + i);
+        const float4 cc = *reinterpret_cast<const float4*>(pc + i);
+        bq[i] = bb.x; bq[i + 1] = bb.y; bq[i + 2] = bb.z; bq[i + 3] = bb.w;
+        cq[i] = cc.x; cq[i + 1] = cc.y; cq[i + 2] = cc.z; cq[i + 3] = cc.w;
+      }
+#pragma unroll
+      for (int i = 0; i < K; ++i) {
+        av[i] = ex2(dl[i] * An);
+        if constexpr (ZOH) {
+          const float coef = An != 0.0f ? expm1_f(dl[i] * kLn2 * An, av[i]) * rcp(An) : dl[i] * kLn2;
+          xv[i] = coef * bq[i] * uu[i];
+        } else {
+          xv[i] = w[i] * bq[i];
+        }
+      }
+      // ---- forward: the states of the chunk, from the checkpoint
+      const float Al = ex2(An * S);
+      float H = fmaf(av[0], first ? hs : 0.0f, xv[0]);
+#pragma unroll
+      for (int i = 1; i < K; ++i) H = fmaf(av[i], H, xv[i]);
+      row_scan16(Al, H);
+      const float He = dpp0<kRowShr1>(H);
+      float h = first ? hs : He;
+#pragma unroll
+      for (int i = 0; i < K; ++i) {
+        hp[i] = h;
+        h = fmaf(av[i], h, xv[i]);
+        yc[i] = fmaf(cq[i], h, yc[i]);
+      }
+      // ---- adjoint: backwards over the chunk from the stored carry
+      float Lam = dyc[K - 1] * cq[K - 1] + (last ? mu_end : 0.0f);
+#pragma unroll
+      for (int i = K - 2; i >= 0; --i) Lam = fmaf(av[i + 1], Lam, dyc[i] * cq[i]);
+      float H2 = av[0] * Lam;
+      row_scan16_rev(Al, H2);
+      const float Hn = dpp0<kRowShl1>(H2);
+      float mu = last ? mu_end : Hn;
+      float dAacc = 0.0f, gB[K], gC[K];
+#pragma unroll
+      for (int i = K - 1; i >= 0; --i) {
+        const float lam = fmaf(dyc[i], cq[i], mu);
+        const float hi = fmaf(av[i], hp[i], xv[i]);
+        const float daa = lam * hp[i] * av[i];
+        const float dt = dl[i] * kLn2;
+        float dbv;
+        if constexpr (ZOH) {
+          const float coef = An != 0.0f ? expm1_f(dt * An, av[i]) * rcp(An) : dt;
+          const float dbeta = lam * bq[i] * uu[i];
+          ddt[i] = fmaf(daa, An, fmaf(dbeta, av[i], ddt[i]));
+          const float dcoef_dA = An != 0.0f ? (dt * av[i] - coef) * rcp(An) : 0.5f * dt * dt;
+          dAacc = fmaf(daa, dt, fmaf(dbeta, dcoef_dA, dAacc));
+          dbv = lam * coef * uu[i];
+          du[i] = fmaf(lam, coef * bq[i], du[i]);
+        } else {
+          ddt[i] = fmaf(daa, An, fmaf(lam, bq[i] * uu[i], ddt[i]));
+          dAacc = fmaf(daa, dt, dAacc);
+          dbv = lam * w[i];
+          du[i] = fmaf(lam, dt * bq[i], du[i]);
+        }
+        gC[i] = dyc[i] * hi;
+        gB[i] = dbv;
+        mu = av[i] * lam;
+      }
+      // dB, dC: sum the wave's four channels, then one LDS add per value;
+      // the tiles are laid out [n][step in lane][lane] so the adds of a
+      // wave fall in distinct banks
+      {
+        float lo, hi;
+        const int row = lane >> 4, st = red_step(row);
+        rows_sum8(gC, lo, hi);
+        atomicAdd(&sdC[n * T + st * LPC + seg], lo);
+        atomicAdd(&sdC[n * T + (4 + st) * LPC + seg], hi);
+        rows_sum8(gB, lo, hi);
+        atomicAdd(&sdB[n * T + st * LPC + seg], lo);
+        atomicAdd(&sdB[n * T + (4 + st) * LPC + seg], hi);
+      }
+      dAacc = row_sum16(dAacc);
+      if (last && dvalid) unsafeAtomicAdd(&a.dA[d * N + n], dAacc);
+      if (ci == 0 && first && dvalid && a.dh0) a.dh0[ch * N + n] = mu;
+    }
+    // ---- per-step gradients
+    float dDacc = 0.0f, dbacc = 0.0f;
+    {
+      float raw[K], g[K], zz[K], outz[K], outr[K];
+      rd.unpack(raw);
+      rdy.unpack(g);
+      if constexpr (GATE) rz.unpack(zz);
+#pragma unroll
+      for (int i = 0; i < K; ++i) {
+        const bool ok = tl + i < L;
+        const float x = raw[i] + bias;
+        const float sig = a.softplus ? rcp(1.0f + ex2(-x * kLog2e)) : 1.0f;
+        const float dr = ok ? ddt[i] * sig : 0.0f;
+        outr[i] = dr;
+        dbacc += dr;
+        dDacc += ok ? dyc[i] * uu[i] : 0.0f;
+        du[i] = fmaf(dyc[i], Dd, du[i]);
+        if constexpr (GATE) {
+          const float sz = rcp(1.0f + ex2(-zz[i] * kLog2e));
+          outz[i] = g[i] * yc[i] * sz * fmaf(zz[i], 1.0f - sz, 1.0f);
+        }
+      }
+      run_store<IO, K, VEC>(a.du, row, tl, L, dvalid, du);
+      run_store<IO, K, VEC>(a.ddelta, row, tl, L, dvalid, outr);
+      if constexpr (GATE) run_store<IO, K, VEC>(a.dz, row, tl, L, dvalid, outz);
+    }
+    dDacc = row_sum16(dDacc);
+    dbacc = row_sum16(dbacc);
+    if (last && dvalid) {
+      if (a.dD) unsafeAtomicAdd(&a.dD[d], dDacc);
+      if (a.ddelta_bias) unsafeAtomicAdd(&a.ddelta_bias[d], dbacc);
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < N * T; i += NTH) {
+    const int n = i / T, tt = i % T;
+    const int64_t t = t0 + tt;
+    const int li = n * T + (tt % K) * LPC + tt / K;
+    if (t < L) {
+      unsafeAtomicAdd(&a.accB[(b * N + n) * L + t], sdB[li]);
+      unsafeAtomicAdd(&a.accC[(b * N + n) * L + t], sdC[li]);
+    }
+  }
+}
+
+__global__ void __launch_bounds__(256) fill_zero_kernel(float* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    p[i] = 0.0f;
+}
+
+template <typename IO>
+__global__ void __launch_bounds__(256) store_io_kernel(const float* src, void* dst, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    Io<IO>::st1(dst, i, src[i]);
 }
 
 // ---------------------------------------------------------------- decode step
@@ -697,6 +1133,72 @@ int launch_fwd(const ScanArgs& a, int64_t batch, bool zoh, bool gate, bool vec, 
              : launch_fwd_vec<IO, false>(a, batch, zoh, gate, s);
 }
 
+// Backward: chunks of T = 16 * kBwdK steps.
+constexpr int kBwdK = 8;
+constexpr int64_t kBwdMaxDstate = 16;
+
+struct BwdLayout {
+  int64_t chunks, ckpt_off, carry_off, accB_off, accC_off, bytes;
+};
+
+BwdLayout bwd_layout(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen) {
+  auto up = [](int64_t x) { return (x + 255) & ~(int64_t)255; };
+  BwdLayout l;
+  const int64_t T = 16 * kBwdK;
+  l.chunks = (seqlen + T - 1) / T;
+  const int64_t states = batch * dim * l.chunks * dstate * 4;
+  const int64_t acc = batch * dstate * seqlen * 4;
+  l.ckpt_off = 0;
+  l.carry_off = up(states);
+  l.accB_off = l.carry_off + up(states);
+  l.accC_off = l.accB_off + up(acc);
+  l.bytes = l.accC_off + up(acc);
+  return l;
+}
+
+template <typename IO, bool VEC, bool ZOH, bool GATE>
+int launch_bwd_typed(const ScanArgs& fa, BwdArgs ba, int64_t batch, hipStream_t s) {
+  constexpr int K = kBwdK;
+  const dim3 grid16((unsigned)((ba.dim + 15) / 16), (unsigned)batch);
+  // 1. checkpoints: the state at every chunk start
+  hipLaunchKernelGGL((scan_fwd_kernel<IO, 16, K, 4, 16, VEC, ZOH, false, true>), grid16, dim3(256),
+                     2 * 16 * (size_t)ba.dstate * sizeof(float), s, fa);
+  // 2. adjoint carries at every chunk end
+  hipLaunchKernelGGL((scan_bwd_carry_kernel<IO, K, VEC, GATE>), grid16, dim3(256), 0, s, ba);
+  // 3. gradients, every (sequence, chunk) independently
+  const int64_t ngroups = (ba.dim + 15) / 16;
+  const int64_t cells = ngroups * ba.chunks * batch;
+  int64_t gpb = cells / 4096;  // a few thousand workgroups in total
+  if (gpb < 1) gpb = 1;
+  if (gpb > ngroups) gpb = ngroups;
+  ba.groups_per_block = (int)gpb;
+  const dim3 gridm((unsigned)((ngroups + gpb - 1) / gpb), (unsigned)ba.chunks, (unsigned)batch);
+  hipLaunchKernelGGL((scan_bwd_main_kernel<IO, K, VEC, ZOH, GATE>), gridm, dim3(256), 0, s, ba);
+  return SSM_OK;
+}
+
+template <typename IO>
+int launch_bwd(const ScanArgs& fa, const BwdArgs& ba, int64_t batch, bool vec, bool zoh, bool gate,
+               hipStream_t s) {
+  if (vec) {
+    if (zoh) return gate ? launch_bwd_typed<IO, true, true, true>(fa, ba, batch, s)
+                         : launch_bwd_typed<IO, true, true, false>(fa, ba, batch, s);
+    return gate ? launch_bwd_typed<IO, true, false, true>(fa, ba, batch, s)
+                : launch_bwd_typed<IO, true, false, false>(fa, ba, batch, s);
+  }
+  if (zoh) return gate ? launch_bwd_typed<IO, false, true, true>(fa, ba, batch, s)
+                       : launch_bwd_typed<IO, false, true, false>(fa, ba, batch, s);
+  return gate ? launch_bwd_typed<IO, false, false, true>(fa, ba, batch, s)
+              : launch_bwd_typed<IO, false, false, false>(fa, ba, batch, s);
+}
+
+void zero_fill(float* p, int64_t n, hipStream_t s) {
+  if (!p || n <= 0) return;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n);
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------- C ABI
@@ -887,6 +1389,115 @@ int ssm_lti_kernel(const float* A, const float* Bv, const float* Cv, const float
     hipLaunchKernelGGL(lti_kernel_kernel<false>, grid, dim3(256), 0, s, A, Bv, Cv, delta, K, dim,
                        dstate, L, b_row_stride, c_row_stride);
   return launch_status("ssm_lti_kernel launch");
+}
+
+int64_t ssm_selective_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
+                                              int64_t seqlen) {
+  if (batch <= 0 || dim <= 0 || dstate <= 0 || seqlen <= 0) return -1;
+  if (!product_ok(batch, dim, seqlen, 4) || !product_ok(batch, dim, dstate, seqlen)) return -1;
+  return bwd_layout(batch, dim, dstate, seqlen).bytes;
+}
+
+int ssm_selective_scan_bwd(const void* u, const void* delta, const float* A, const void* Bm,
+                           const void* Cm, const float* Dskip, const void* z,
+                           const float* delta_bias, int delta_softplus, const float* h0,
+                           const void* dy, const float* dfinal_state, void* du, void* ddelta,
+                           float* dA, void* dB, void* dC, float* dD, void* dz,
+                           float* ddelta_bias, float* dh0, void* workspace,
+                           int64_t workspace_bytes, int64_t batch, int64_t dim, int64_t dstate,
+                           int64_t seqlen, int io_dtype, int bbar_mode, void* hip_stream) {
+  g_last_error[0] = 0;
+  const struct { const void* p; const char* name; } req[] = {
+      {u, "u"}, {delta, "delta"}, {A, "A"}, {Bm, "B"}, {Cm, "C"}, {dy, "dy"}, {du, "du"},
+      {ddelta, "ddelta"}, {dA, "dA"}, {dB, "dB"}, {dC, "dC"}, {workspace, "workspace"}};
+  for (const auto& r : req)
+    if (!r.p) return fail(SSM_E_NULL, "%s is NULL", r.name);
+  if (z && !dz) return fail(SSM_E_NULL, "dz is NULL while z is given");
+  int st;
+  if ((st = check_extent("batch", batch)) || (st = check_extent("dim", dim)) ||
+      (st = check_extent("dstate", dstate)) || (st = check_extent("seqlen", seqlen)))
+    return st;
+  if (batch > 65535) return fail(SSM_E_SHAPE, "batch = %lld exceeds 65535", (long long)batch);
+  if (dim > ((int64_t)1 << 30)) return fail(SSM_E_SHAPE, "dim = %lld exceeds 2^30", (long long)dim);
+  if (!product_ok(batch, dim, seqlen, 4) || !product_ok(batch, dim, dstate, seqlen))
+    return fail(SSM_E_SHAPE, "tensor sizes overflow");
+  if (io_dtype != SSM_DTYPE_F32 && io_dtype != SSM_DTYPE_BF16)
+    return fail(SSM_E_DTYPE, "io_dtype = %d is not SSM_DTYPE_F32 or SSM_DTYPE_BF16", io_dtype);
+  if (bbar_mode != SSM_BBAR_DELTA_B && bbar_mode != SSM_BBAR_ZOH_EXACT)
+    return fail(SSM_E_DTYPE, "bbar_mode = %d is not a known rule", bbar_mode);
+  if (dstate > kBwdMaxDstate)
+    return fail(SSM_E_UNSUPPORTED, "backward supports dstate 1..%lld, got %lld",
+                (long long)kBwdMaxDstate, (long long)dstate);
+  const BwdLayout lay = bwd_layout(batch, dim, dstate, seqlen);
+  if (lay.chunks > 65535) return fail(SSM_E_SHAPE, "seqlen = %lld is too long", (long long)seqlen);
+  if (workspace_bytes < lay.bytes)
+    return fail(SSM_E_SHAPE, "workspace holds %lld bytes, needs %lld", (long long)workspace_bytes,
+                (long long)lay.bytes);
+  const int64_t es = io_dtype == SSM_DTYPE_BF16 ? 2 : 4;
+  const int64_t seq = batch * dim * seqlen * es, bc = batch * dstate * seqlen * es;
+  const int64_t stb = batch * dim * dstate * 4;
+  const void* seq_ptrs[] = {u, delta, Bm, Cm, z, dy, du, ddelta, dB, dC, dz, workspace};
+  const char* seq_names[] = {"u", "delta", "B", "C", "z", "dy", "du", "ddelta", "dB", "dC", "dz",
+                             "workspace"};
+  for (int i = 0; i < 12; ++i)
+    if (seq_ptrs[i] && !aligned16(seq_ptrs[i]))
+      return fail(SSM_E_ALIGN, "%s is not 16-byte aligned", seq_names[i]);
+  const Span ins[] = {{u, seq, "u"},           {delta, seq, "delta"},     {A, dim * dstate * 4, "A"},
+                      {Bm, bc, "B"},           {Cm, bc, "C"},             {Dskip, dim * 4, "D"},
+                      {z, z ? seq : 0, "z"},   {delta_bias, dim * 4, "delta_bias"},
+                      {h0, stb, "h0"},         {dy, seq, "dy"},           {dfinal_state, stb, "dfinal_state"}};
+  const Span outs[] = {{du, seq, "du"},          {ddelta, seq, "ddelta"},  {dA, dim * dstate * 4, "dA"},
+                       {dB, bc, "dB"},           {dC, bc, "dC"},           {dD, dim * 4, "dD"},
+                       {dz, z ? seq : 0, "dz"},  {ddelta_bias, dim * 4, "ddelta_bias"},
+                       {dh0, stb, "dh0"},        {workspace, lay.bytes, "workspace"}};
+  for (const Span& o : outs) {
+    for (const Span& i : ins)
+      if (overlaps(o, i)) return fail(SSM_E_ALIAS, "%s overlaps %s", o.name, i.name);
+    for (const Span& o2 : outs)
+      if (&o2 != &o && overlaps(o, o2)) return fail(SSM_E_ALIAS, "%s overlaps %s", o.name, o2.name);
+  }
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  char* ws = static_cast<char*>(workspace);
+  ScanArgs fa;
+  memset(&fa, 0, sizeof fa);
+  fa.u = u; fa.delta = delta; fa.A = A; fa.Bm = Bm; fa.Cm = Cm; fa.Dskip = Dskip; fa.z = nullptr;
+  fa.delta_bias = delta_bias; fa.h0 = h0; fa.y = nullptr; fa.final_state = nullptr;
+  fa.dim = dim; fa.dstate = dstate; fa.seqlen = seqlen; fa.softplus = delta_softplus ? 1 : 0;
+  fa.ckpt = reinterpret_cast<float*>(ws + lay.ckpt_off);
+  BwdArgs ba;
+  memset(&ba, 0, sizeof ba);
+  ba.u = u; ba.delta = delta; ba.A = A; ba.Bm = Bm; ba.Cm = Cm; ba.Dskip = Dskip; ba.z = z;
+  ba.delta_bias = delta_bias; ba.dy = dy; ba.dfinal = dfinal_state; ba.du = du; ba.ddelta = ddelta;
+  ba.dA = dA; ba.dD = dD; ba.dz = dz; ba.ddelta_bias = ddelta_bias; ba.dh0 = dh0;
+  ba.ckpt = fa.ckpt;
+  ba.carry = reinterpret_cast<float*>(ws + lay.carry_off);
+  ba.accB = reinterpret_cast<float*>(ws + lay.accB_off);
+  ba.accC = reinterpret_cast<float*>(ws + lay.accC_off);
+  ba.dim = dim; ba.dstate = dstate; ba.seqlen = seqlen; ba.chunks = lay.chunks;
+  ba.softplus = delta_softplus ? 1 : 0;
+  const int64_t nacc = batch * dstate * seqlen;
+  zero_fill(ba.accB, nacc, s);
+  zero_fill(ba.accC, nacc, s);
+  zero_fill(dA, dim * dstate, s);
+  zero_fill(dD, dim, s);
+  zero_fill(ddelta_bias, dim, s);
+  const bool vec = (seqlen % (io_dtype == SSM_DTYPE_BF16 ? 8 : 4)) == 0;
+  const bool zoh = bbar_mode == SSM_BBAR_ZOH_EXACT, gate = z != nullptr;
+  if (io_dtype == SSM_DTYPE_BF16) {
+    launch_bwd<uint16_t>(fa, ba, batch, vec, zoh, gate, s);
+  } else {
+    launch_bwd<float>(fa, ba, batch, vec, zoh, gate, s);
+  }
+  int64_t blocks = (nacc + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (io_dtype == SSM_DTYPE_BF16) {
+    hipLaunchKernelGGL(store_io_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, s, ba.accB, dB, nacc);
+    hipLaunchKernelGGL(store_io_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, s, ba.accC, dC, nacc);
+  } else {
+    hipLaunchKernelGGL(store_io_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, s, ba.accB, dB, nacc);
+    hipLaunchKernelGGL(store_io_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, s, ba.accC, dC, nacc);
+  }
+  return launch_status("ssm_selective_scan_bwd launch");
 }
 
 }  // extern "C"

@@ -26,6 +26,7 @@ def declared_functions():
 def test_library_exports_every_declared_function(lib):
     names = declared_functions()
     assert {"ssm_selective_scan_fwd", "ssm_state_update", "ssm_lti_kernel", "ssm_status_str",
+            "ssm_selective_scan_bwd", "ssm_selective_scan_bwd_workspace_size",
             "ssm_last_error", "ssm_abi_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -112,3 +113,42 @@ def test_no_cpu_fallback_in_product_path():
         if fn.endswith(".py"):
             src = open(os.path.join(pkg, fn)).read()
             assert "oracle" not in src, fn
+
+
+BWD_KEYS = ("u", "delta", "A", "B", "C", "D", "z", "bias", "softplus", "h0", "dy", "dfinal",
+            "du", "ddelta", "dA", "dB", "dC", "dD", "dz", "dbias", "dh0", "ws", "ws_bytes",
+            "batch", "dim", "N", "L", "io", "bbar", "stream")
+
+
+def bwd_args(**over):
+    a = dict(u=1 * P, delta=2 * P, A=3 * P, B=4 * P, C=5 * P, D=None, z=None, bias=None,
+             softplus=1, h0=None, dy=6 * P, dfinal=None, du=7 * P, ddelta=8 * P, dA=9 * P,
+             dB=10 * P, dC=11 * P, dD=None, dz=None, dbias=None, dh0=None, ws=12 * P,
+             ws_bytes=P, batch=2, dim=8, N=4, L=16, io=1, bbar=0, stream=None)
+    a.update(over)
+    return [a[k] for k in BWD_KEYS]
+
+
+def test_bwd_workspace_size(lib):
+    f = lib.ssm_selective_scan_bwd_workspace_size
+    assert f(0, 8, 4, 16) == -1 and f(2, 8, 4, -1) == -1
+    small, big = f(2, 8, 4, 16), f(2, 8, 4, 1000)
+    assert 0 < small < big and small % 256 == 0
+    # two state checkpoints per 128-step chunk plus two float32 [batch, N, L] sums
+    assert big >= 2 * (2 * 8 * 8 * 4 * 4) + 2 * (2 * 4 * 1000 * 4)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(u=None), 1), (dict(dy=None), 1), (dict(du=None), 1), (dict(dB=None), 1),
+    (dict(ws=None), 1), (dict(z=13 * P, dz=None), 1),
+    (dict(L=0), 2), (dict(batch=70000), 2), (dict(ws_bytes=64), 2),
+    (dict(io=2), 3), (dict(bbar=5), 3),
+    (dict(du=7 * P + 2), 4), (dict(ws=12 * P + 8), 4),
+    (dict(du=1 * P), 5), (dict(dA=3 * P), 5), (dict(dB=10 * P + 64, dC=10 * P + 64), 5),
+    (dict(ws=6 * P), 5), (dict(dh0=9 * P), 5),
+    (dict(N=17), 6), (dict(N=64), 6),
+])
+def test_bwd_validation(lib, over, status):
+    assert lib.ssm_selective_scan_bwd(*bwd_args(**over)) == status
+    import selective_state_space_43_amd as ssm
+    assert ssm.ssm_last_error() != ""

@@ -39,7 +39,7 @@ from dataclasses import dataclass
 import numpy as np
 
 # tensor ids used in the per-row stream keys
-T_U, T_DELTA, T_Z, T_B, T_C, T_A, T_D, T_BIAS, T_STATE = range(9)
+T_U, T_DELTA, T_Z, T_B, T_C, T_A, T_D, T_BIAS, T_STATE, T_DY, T_DFINAL = range(11)
 
 
 @dataclass(frozen=True)
@@ -148,7 +148,7 @@ def _normal_rows(seed, tid, key0, out, mean, std, dtype, per_stream=1 << 19):
 def seq_tensor(w: Workload, tid: int, mean: float, std: float, seed=None):
     """A [batch, dim, L] (tid in u/delta/z) or [batch, N, L] (tid in B/C) tensor."""
     seed = w.seed if seed is None else seed
-    inner = w.dim if tid in (T_U, T_DELTA, T_Z) else w.dstate
+    inner = w.dim if tid in (T_U, T_DELTA, T_Z, T_DY) else w.dstate
     rows = w.batch * inner
     np_dtype = np.uint16 if w.dtype == "bf16" else np.float32
     out = np.empty((rows, w.seqlen), dtype=np_dtype)
@@ -187,6 +187,16 @@ def scan_inputs(w: Workload, seed=None):
         B=seq_tensor(w, T_B, 0.0, 1.0, seed),
         C=seq_tensor(w, T_C, 0.0, 1.0, seed),
         A=A, D=D, delta_bias=bias, delta_softplus=True)
+
+
+def grad_inputs(w: Workload, seed=None):
+    """Upstream gradients for the backward pass: dy [batch, dim, L] ~N(0,1) in
+    the workload's storage dtype and dfinal [batch, dim, N] ~N(0,1) float32."""
+    seed = w.seed if seed is None else seed
+    dfinal = np.empty((w.batch * w.dim, w.dstate), dtype=np.float32)
+    _normal_rows(seed, T_DFINAL, 0, dfinal, 0.0, 1.0, "f32")
+    return dict(dy=seq_tensor(w, T_DY, 0.0, 1.0, seed),
+                dfinal=dfinal.reshape(w.batch, w.dim, w.dstate))
 
 
 def decode_state(w: Workload, seed=None) -> np.ndarray:
