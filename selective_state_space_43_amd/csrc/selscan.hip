@@ -698,25 +698,49 @@ __global__ void __launch_bounds__(256) scan_bwd_carry_kernel(const BwdArgs a) {
   }
 }
 
+// Two consecutive elements starting at an even index (4- or 8-byte aligned).
+template <typename IO>
+struct Pair;
+template <>
+struct Pair<float> {
+  float2 v;
+  __device__ void load(const void* p, int64_t i) { v = *reinterpret_cast<const float2*>(static_cast<const float*>(p) + i); }
+  __device__ float get(int k) const { return k ? v.y : v.x; }
+};
+template <>
+struct Pair<uint16_t> {
+  uint32_t v;
+  __device__ void load(const void* p, int64_t i) { v = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p) + i); }
+  __device__ float get(int k) const { return k ? bf_hi(v) : bf_lo(v); }
+};
+
 template <typename IO, int K, bool VEC, bool ZOH, bool GATE>
 __global__ void __launch_bounds__(256) scan_bwd_main_kernel(const BwdArgs a) {
   static_assert(K == 8, "the channel reduction of dB and dC handles eight steps per lane");
-  constexpr int LPC = 16, CPB = 16, T = LPC * K, KP = K + 4, V = Io<IO>::V, TV = T / V;
+  constexpr int LPC = 16, T = LPC * K, KP = K + 4, V = Io<IO>::V, TV = T / V;
   constexpr int NT = 16, NTH = 256, ITEMS = (2 * NT * TV + NTH - 1) / NTH;
+  constexpr int CPG = 4;  // channels per group: one per 16-lane row
+  constexpr int NW = 4;   // waves sharing a group
+  // Work split inside a group: wave w runs the recurrences for states
+  // w, w + 4, w + 8, w + 12 over all steps, and the per-step work (step
+  // size, gate, output gradients) for steps 2w and 2w + 1 of every lane.
   __shared__ float4 sB4[NT * LPC * KP / 4];
   __shared__ float4 sC4[NT * LPC * KP / 4];
-  __shared__ float sdB[NT * T], sdC[NT * T];
+  __shared__ float4 sRed4[NW * 3 * 64 * K / 4];  // [wave][ddt, du, yc][lane][step] partial sums
+  __shared__ float4 sPrep4[3 * 64 * K / 4];      // [delta, u, dy silu(z)][lane][step]
+  __shared__ float sPar[NW * 3 * CPG * NT];      // per wave: A, state at chunk start, carry
+  float* sRed = reinterpret_cast<float*>(sRed4);
+  float* sPrep = reinterpret_cast<float*>(sPrep4);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int seg = lane % LPC;
+  const int seg = lane % LPC, row = lane / LPC;
   const bool first = seg == 0, last = seg == LPC - 1;
-  const int chb = wave * 4 + lane / LPC;
+  const int red_row = red_step(row);
   const int64_t b = blockIdx.z, ci = blockIdx.y;
   const int64_t N = a.dstate, L = a.seqlen;
   const int64_t t0 = ci * T, tl = t0 + seg * K, bcrow = b * N * L;
-  for (int i = threadIdx.x; i < N * T; i += NTH) {
-    sdB[i] = 0.0f;
-    sdC[i] = 0.0f;
-  }
+  const int s0 = 2 * wave;               // this wave's two steps
+  const int64_t ts = tl + s0;            // their time index
+  const bool ok0 = ts < L, ok1 = ts + 1 < L;
 #pragma unroll
   for (int k = 0; k < ITEMS; ++k) {
     const int item = threadIdx.x + k * NTH;
@@ -734,185 +758,292 @@ __global__ void __launch_bounds__(256) scan_bwd_main_kernel(const BwdArgs a) {
         *reinterpret_cast<float4*>(dst + q) = make_float4(v[q], v[q + 1], v[q + 2], v[q + 3]);
     }
   }
-  __syncthreads();
 
-  const int64_t ngroups = (a.dim + CPB - 1) / CPB;
-  const int64_t g_end = min((int64_t)(blockIdx.x + 1) * a.groups_per_block, ngroups);
-  for (int64_t g = (int64_t)blockIdx.x * a.groups_per_block; g < g_end; ++g) {
-    const int64_t d = g * CPB + chb;
+  // dB and dC of this chunk for states wave + 4j and steps seg K + red_row
+  // (lo) and seg K + 4 + red_row (hi), summed over every channel visited
+  float acc[4][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[j][q] = 0.0f;
+
+  const int64_t ngroups = (a.dim + CPG - 1) / CPG;
+  const int64_t g_begin = (int64_t)blockIdx.x * a.groups_per_block;
+  const int64_t g_end = min(g_begin + a.groups_per_block, ngroups);
+  float* par = sPar + wave * 3 * CPG * NT;
+  // loads of group g + 1 are issued while group g computes
+  Pair<IO> nu, nd, ndy, nz;
+  float npar[3];
+  auto fetch = [&](int64_t g) {
+    const int64_t d = g * CPG + row;
+    const bool okd = d < a.dim;
+    const int64_t ch = b * a.dim + (okd ? d : 0);
+    // the pair is read whole when it starts inside the row (L is even on
+    // the vectorised path); otherwise element by element
+    const int64_t base = ch * L + ts;
+    if (okd && VEC && ok1) {
+      nu.load(a.u, base);
+      nd.load(a.delta, base);
+      ndy.load(a.dy, base);
+      if constexpr (GATE) nz.load(a.z, base);
+    } else {
+      float e[4][2];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const bool okk = okd && ts + k < L;
+        e[0][k] = okk ? Io<IO>::ld1(a.u, base + k) : 0.0f;
+        e[1][k] = okk ? Io<IO>::ld1(a.delta, base + k) : 0.0f;
+        e[2][k] = okk ? Io<IO>::ld1(a.dy, base + k) : 0.0f;
+        e[3][k] = (GATE && okk) ? Io<IO>::ld1(a.z, base + k) : 0.0f;
+      }
+      if constexpr (std::is_same<IO, float>::value) {
+        nu.v = make_float2(e[0][0], e[0][1]); nd.v = make_float2(e[1][0], e[1][1]);
+        ndy.v = make_float2(e[2][0], e[2][1]); nz.v = make_float2(e[3][0], e[3][1]);
+      } else {
+        nu.v = pack_bf16x2(e[0][0], e[0][1]); nd.v = pack_bf16x2(e[1][0], e[1][1]);
+        ndy.v = pack_bf16x2(e[2][0], e[2][1]); nz.v = pack_bf16x2(e[3][0], e[3][1]);
+      }
+    }
+    const int64_t cb = (ch * a.chunks + ci) * N + seg;
+    const bool own = okd && seg < N;
+    npar[0] = own ? a.A[(okd ? d : 0) * N + seg] : 0.0f;
+    npar[1] = own ? a.ckpt[cb] : 0.0f;
+    npar[2] = own ? a.carry[cb] : 0.0f;
+  };
+  if (g_begin < g_end) fetch(g_begin);
+  for (int64_t g = g_begin; g < g_end; ++g) {
+    const int64_t d = g * CPG + row;
     const bool dvalid = d < a.dim;
     const int64_t ch = b * a.dim + (dvalid ? d : 0);
-    const int64_t row = ch * L;
-    Run<IO, K> ru, rd, rz, rdy;
-    run_load<IO, K, VEC>(ru, a.u, row, tl, L, dvalid);
-    run_load<IO, K, VEC>(rd, a.delta, row, tl, L, dvalid);
-    run_load<IO, K, VEC>(rdy, a.dy, row, tl, L, dvalid);
-    if constexpr (GATE) run_load<IO, K, VEC>(rz, a.z, row, tl, L, dvalid);
+    const Pair<IO> pu = nu, pd = nd, pdy = ndy, pz = nz;
+    if (seg < N) {
+      par[row * N + seg] = npar[0];
+      par[(CPG + row) * N + seg] = npar[1];
+      par[(2 * CPG + row) * N + seg] = npar[2];
+    }
+    if (g + 1 < g_end) fetch(g + 1);
     const float bias = (a.delta_bias && dvalid) ? a.delta_bias[d] : 0.0f;
-    const float Dd = (a.Dskip && dvalid) ? a.Dskip[d] : 0.0f;
-    // per-step values: dl = delta / ln 2, dt = delta, uu = u, w = delta u,
-    // dyc = dy silu(z); accumulators yc (readout), ddt, du
-    float dl[K], uu[K], w[K], dyc[K], yc[K], ddt[K], du[K];
-    float S = 0.0f;
+    // ---- per-step inputs of this wave's two steps, shared through LDS
+    float xs[2], us[2], gs[2], zs[2], dycs[2];
     {
-      float raw[K], g[K], zz[K];
-      ru.unpack(uu);
-      rd.unpack(raw);
-      rdy.unpack(g);
-      if constexpr (GATE) rz.unpack(zz);
+      float2 dtp, dyp;
 #pragma unroll
-      for (int i = 0; i < K; ++i) {
-        const float x = raw[i] + bias;
-        const float v = a.softplus ? softplus_log2(x) : x * kLog2e;
-        dl[i] = (tl + i < L) ? v : 0.0f;
-        w[i] = dl[i] * kLn2 * uu[i];
-        dyc[i] = GATE ? g[i] * silu_f(zz[i]) : g[i];
-        yc[i] = Dd * uu[i];
-        ddt[i] = 0.0f;
-        du[i] = 0.0f;
-        S += dl[i];
+      for (int k = 0; k < 2; ++k) {
+        xs[k] = pd.get(k) + bias;
+        us[k] = pu.get(k);
+        gs[k] = pdy.get(k);
+        zs[k] = GATE ? pz.get(k) : 0.0f;
+        const float v = a.softplus ? softplus_log2(xs[k]) : xs[k] * kLog2e;
+        const float dtk = (k ? ok1 : ok0) ? v * kLn2 : 0.0f;
+        dycs[k] = GATE ? gs[k] * silu_f(zs[k]) : gs[k];
+        if (k) { dtp.y = dtk; dyp.y = dycs[k]; } else { dtp.x = dtk; dyp.x = dycs[k]; }
+      }
+      *reinterpret_cast<float2*>(sPrep + (0 * 64 + lane) * K + s0) = dtp;
+      *reinterpret_cast<float2*>(sPrep + (1 * 64 + lane) * K + s0) = make_float2(us[0], us[1]);
+      *reinterpret_cast<float2*>(sPrep + (2 * 64 + lane) * K + s0) = dyp;
+    }
+    __syncthreads();  // every wave's steps are in; the previous group's sums are read
+    float dt[K], uu[K], w[K], dyc[K], yc[K], ddt[K], du[K];
+    float S = 0.0f;  // sum of the lane's steps, in log2 units
+#pragma unroll
+    for (int i = 0; i < K; i += 4) {
+      const float4 q0 = *reinterpret_cast<const float4*>(sPrep + (0 * 64 + lane) * K + i);
+      const float4 q1 = *reinterpret_cast<const float4*>(sPrep + (1 * 64 + lane) * K + i);
+      const float4 q2 = *reinterpret_cast<const float4*>(sPrep + (2 * 64 + lane) * K + i);
+      dt[i] = q0.x; dt[i + 1] = q0.y; dt[i + 2] = q0.z; dt[i + 3] = q0.w;
+      uu[i] = q1.x; uu[i + 1] = q1.y; uu[i + 2] = q1.z; uu[i + 3] = q1.w;
+      dyc[i] = q2.x; dyc[i + 1] = q2.y; dyc[i + 2] = q2.z; dyc[i + 3] = q2.w;
+    }
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      S += dt[i];
+      w[i] = dt[i] * uu[i];
+      yc[i] = 0.0f;
+      ddt[i] = 0.0f;
+      du[i] = 0.0f;
+    }
+    S *= kLog2e;
+    const float* pA = par + row * N;
+    const float* pH = par + (CPG + row) * N;
+    const float* pM = par + (2 * CPG + row) * N;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = wave + NW * j;
+      if (n < N) {
+        const float An = pA[n];
+        const float hs = pH[n];      // state before the chunk
+        const float mu_end = pM[n];  // Abar lambda entering from the chunk's end
+        const float Anl = An * kLog2e;
+        const float* pb = reinterpret_cast<const float*>(sB4) + (n * LPC + seg) * KP;
+        const float* pc = reinterpret_cast<const float*>(sC4) + (n * LPC + seg) * KP;
+        float av[K], xv[K], cf[K], hh[K + 1], bq[K], cq[K];
+#pragma unroll
+        for (int i = 0; i < K; i += 4) {
+          const float4 bb = *reinterpret_cast<const float4*>(pb + i);
+          const float4 cc = *reinterpret_cast<const float4*>(pc + i);
+          bq[i] = bb.x; bq[i + 1] = bb.y; bq[i + 2] = bb.z; bq[i + 3] = bb.w;
+          cq[i] = cc.x; cq[i + 1] = cc.y; cq[i + 2] = cc.z; cq[i + 3] = cc.w;
+        }
+#pragma unroll
+        for (int i = 0; i < K; ++i) {
+          av[i] = ex2(dt[i] * Anl);
+          if constexpr (ZOH) {
+            cf[i] = An != 0.0f ? expm1_f(dt[i] * An, av[i]) * rcp(An) : dt[i];
+            xv[i] = cf[i] * uu[i] * bq[i];
+          } else {
+            xv[i] = w[i] * bq[i];
+          }
+        }
+        // ---- forward: the states of the chunk, from the checkpoint
+        const float Al = ex2(An * S);
+        float H = fmaf(av[0], first ? hs : 0.0f, xv[0]);
+#pragma unroll
+        for (int i = 1; i < K; ++i) H = fmaf(av[i], H, xv[i]);
+        row_scan16(Al, H);
+        const float He = dpp0<kRowShr1>(H);
+        hh[0] = first ? hs : He;
+#pragma unroll
+        for (int i = 0; i < K; ++i) {
+          hh[i + 1] = fmaf(av[i], hh[i], xv[i]);
+          if constexpr (GATE) yc[i] = fmaf(cq[i], hh[i + 1], yc[i]);
+        }
+        // ---- adjoint: backwards over the chunk from the stored carry
+        float Lam = fmaf(dyc[K - 1], cq[K - 1], last ? mu_end : 0.0f);
+#pragma unroll
+        for (int i = K - 2; i >= 0; --i) Lam = fmaf(av[i + 1], Lam, dyc[i] * cq[i]);
+        float H2 = av[0] * Lam;
+        row_scan16_rev(Al, H2);
+        const float Hn = dpp0<kRowShl1>(H2);
+        float mu = last ? mu_end : Hn;
+        float dAacc = 0.0f, gB[K], gC[K];
+#pragma unroll
+        for (int i = K - 1; i >= 0; --i) {
+          const float lam = fmaf(dyc[i], cq[i], mu);  // lambda_t
+          const float mun = av[i] * lam;               // Abar_t lambda_t
+          const float daa = mun * hh[i];               // lambda_t Abar_t h_{t-1}
+          const float lb = lam * bq[i];
+          ddt[i] = fmaf(daa, An, ddt[i]);
+          dAacc = fmaf(daa, dt[i], dAacc);
+          if constexpr (ZOH) {
+            const float dbeta = lb * uu[i];  // lambda B u
+            ddt[i] = fmaf(dbeta, av[i], ddt[i]);
+            const float dcf = An != 0.0f ? (dt[i] * av[i] - cf[i]) * rcp(An) : 0.5f * dt[i] * dt[i];
+            dAacc = fmaf(dbeta, dcf, dAacc);
+            gB[i] = lam * cf[i] * uu[i];
+            du[i] = fmaf(lb, cf[i], du[i]);
+          } else {
+            ddt[i] = fmaf(lb, uu[i], ddt[i]);
+            gB[i] = lam * w[i];
+            du[i] = fmaf(lb, dt[i], du[i]);
+          }
+          gC[i] = dyc[i] * hh[i + 1];
+          mu = mun;
+        }
+        float lo, hi;
+        rows_sum8(gB, lo, hi);
+        acc[j][0] += lo;
+        acc[j][1] += hi;
+        rows_sum8(gC, lo, hi);
+        acc[j][2] += lo;
+        acc[j][3] += hi;
+        dAacc = row_sum16(dAacc);
+        if (last && dvalid) unsafeAtomicAdd(&a.dA[d * N + n], dAacc);
+        if (ci == 0 && first && dvalid && a.dh0) a.dh0[ch * N + n] = mu;
       }
     }
-    const int64_t cbase = (ch * a.chunks + ci) * N;
-    const float* Arow = a.A + (dvalid ? d : 0) * N;
-    // the next state's per-channel values load one iteration ahead
-    float An_next = Arow[0], hs_next = a.ckpt[cbase], mu_next = a.carry[cbase];
-#pragma unroll 1
-    for (int64_t n = 0; n < N; ++n) {
-      const float An = An_next;
-      const float hs = hs_next;  // state before the chunk
-      const float mu_end = mu_next;
-      if (n + 1 < N) {
-        An_next = Arow[n + 1];
-        hs_next = a.ckpt[cbase + n + 1];
-        mu_next = a.carry[cbase + n + 1];
-      }
-      const float* pb = reinterpret_cast<const float*>(sB4) + (n * LPC + seg) * KP;
-      const float* pc = reinterpret_cast<const float*>(sC4) + (n * LPC + seg) * KP;
-      float av[K], xv[K], hp[K], bq[K], cq[K];
+    // ---- per-step gradients: sum the four waves' partials for this wave's
+    // two steps
+    {
+      float* red = sRed + wave * 3 * 64 * K;
 #pragma unroll
       for (int i = 0; i < K; i += 4) {
-        const float4 bb = *reinterpret_cast<const float4*>(pb + i);
-        const float4 cc = *reinterpret_cast<const float4*>(pc + i);
-        bq[i] = bb.x; bq[i + 1] = bb.y; bq[i + 2] = bb.z; bq[i + 3] = bb.w;
-        cq[i] = cc.x; cq[i + 1] = cc.y; cq[i + 2] = cc.z; cq[i + 3] = cc.w;
+        *reinterpret_cast<float4*>(red + (0 * 64 + lane) * K + i) = make_float4(ddt[i], ddt[i + 1], ddt[i + 2], ddt[i + 3]);
+        *reinterpret_cast<float4*>(red + (1 * 64 + lane) * K + i) = make_float4(du[i], du[i + 1], du[i + 2], du[i + 3]);
+        if constexpr (GATE)
+          *reinterpret_cast<float4*>(red + (2 * 64 + lane) * K + i) = make_float4(yc[i], yc[i + 1], yc[i + 2], yc[i + 3]);
       }
-#pragma unroll
-      for (int i = 0; i < K; ++i) {
-        av[i] = ex2(dl[i] * An);
-        if constexpr (ZOH) {
-          const float coef = An != 0.0f ? expm1_f(dl[i] * kLn2 * An, av[i]) * rcp(An) : dl[i] * kLn2;
-          xv[i] = coef * bq[i] * uu[i];
-        } else {
-          xv[i] = w[i] * bq[i];
-        }
-      }
-      // ---- forward: the states of the chunk, from the checkpoint
-      const float Al = ex2(An * S);
-      float H = fmaf(av[0], first ? hs : 0.0f, xv[0]);
-#pragma unroll
-      for (int i = 1; i < K; ++i) H = fmaf(av[i], H, xv[i]);
-      row_scan16(Al, H);
-      const float He = dpp0<kRowShr1>(H);
-      float h = first ? hs : He;
-#pragma unroll
-      for (int i = 0; i < K; ++i) {
-        hp[i] = h;
-        h = fmaf(av[i], h, xv[i]);
-        yc[i] = fmaf(cq[i], h, yc[i]);
-      }
-      // ---- adjoint: backwards over the chunk from the stored carry
-      float Lam = dyc[K - 1] * cq[K - 1] + (last ? mu_end : 0.0f);
-#pragma unroll
-      for (int i = K - 2; i >= 0; --i) Lam = fmaf(av[i + 1], Lam, dyc[i] * cq[i]);
-      float H2 = av[0] * Lam;
-      row_scan16_rev(Al, H2);
-      const float Hn = dpp0<kRowShl1>(H2);
-      float mu = last ? mu_end : Hn;
-      float dAacc = 0.0f, gB[K], gC[K];
-#pragma unroll
-      for (int i = K - 1; i >= 0; --i) {
-        const float lam = fmaf(dyc[i], cq[i], mu);
-        const float hi = fmaf(av[i], hp[i], xv[i]);
-        const float daa = lam * hp[i] * av[i];
-        const float dt = dl[i] * kLn2;
-        float dbv;
-        if constexpr (ZOH) {
-          const float coef = An != 0.0f ? expm1_f(dt * An, av[i]) * rcp(An) : dt;
-          const float dbeta = lam * bq[i] * uu[i];
-          ddt[i] = fmaf(daa, An, fmaf(dbeta, av[i], ddt[i]));
-          const float dcoef_dA = An != 0.0f ? (dt * av[i] - coef) * rcp(An) : 0.5f * dt * dt;
-          dAacc = fmaf(daa, dt, fmaf(dbeta, dcoef_dA, dAacc));
-          dbv = lam * coef * uu[i];
-          du[i] = fmaf(lam, coef * bq[i], du[i]);
-        } else {
-          ddt[i] = fmaf(daa, An, fmaf(lam, bq[i] * uu[i], ddt[i]));
-          dAacc = fmaf(daa, dt, dAacc);
-          dbv = lam * w[i];
-          du[i] = fmaf(lam, dt * bq[i], du[i]);
-        }
-        gC[i] = dyc[i] * hi;
-        gB[i] = dbv;
-        mu = av[i] * lam;
-      }
-      // dB, dC: sum the wave's four channels, then one LDS add per value;
-      // the tiles are laid out [n][step in lane][lane] so the adds of a
-      // wave fall in distinct banks
-      {
-        float lo, hi;
-        const int row = lane >> 4, st = red_step(row);
-        rows_sum8(gC, lo, hi);
-        atomicAdd(&sdC[n * T + st * LPC + seg], lo);
-        atomicAdd(&sdC[n * T + (4 + st) * LPC + seg], hi);
-        rows_sum8(gB, lo, hi);
-        atomicAdd(&sdB[n * T + st * LPC + seg], lo);
-        atomicAdd(&sdB[n * T + (4 + st) * LPC + seg], hi);
-      }
-      dAacc = row_sum16(dAacc);
-      if (last && dvalid) unsafeAtomicAdd(&a.dA[d * N + n], dAacc);
-      if (ci == 0 && first && dvalid && a.dh0) a.dh0[ch * N + n] = mu;
     }
-    // ---- per-step gradients
-    float dDacc = 0.0f, dbacc = 0.0f;
+    __syncthreads();
     {
-      float raw[K], g[K], zz[K], outz[K], outr[K];
-      rd.unpack(raw);
-      rdy.unpack(g);
-      if constexpr (GATE) rz.unpack(zz);
+      float2 sddt = make_float2(0.0f, 0.0f), sdu = sddt, syc = sddt;
 #pragma unroll
-      for (int i = 0; i < K; ++i) {
-        const bool ok = tl + i < L;
-        const float x = raw[i] + bias;
-        const float sig = a.softplus ? rcp(1.0f + ex2(-x * kLog2e)) : 1.0f;
-        const float dr = ok ? ddt[i] * sig : 0.0f;
-        outr[i] = dr;
-        dbacc += dr;
-        dDacc += ok ? dyc[i] * uu[i] : 0.0f;
-        du[i] = fmaf(dyc[i], Dd, du[i]);
+      for (int ww = 0; ww < NW; ++ww) {
+        const float* rr = sRed + ww * 3 * 64 * K + lane * K + s0;
+        const float2 p0 = *reinterpret_cast<const float2*>(rr);
+        const float2 p1 = *reinterpret_cast<const float2*>(rr + 64 * K);
+        sddt.x += p0.x; sddt.y += p0.y;
+        sdu.x += p1.x; sdu.y += p1.y;
         if constexpr (GATE) {
-          const float sz = rcp(1.0f + ex2(-zz[i] * kLog2e));
-          outz[i] = g[i] * yc[i] * sz * fmaf(zz[i], 1.0f - sz, 1.0f);
+          const float2 p2 = *reinterpret_cast<const float2*>(rr + 2 * 64 * K);
+          syc.x += p2.x; syc.y += p2.y;
         }
       }
-      run_store<IO, K, VEC>(a.du, row, tl, L, dvalid, du);
-      run_store<IO, K, VEC>(a.ddelta, row, tl, L, dvalid, outr);
-      if constexpr (GATE) run_store<IO, K, VEC>(a.dz, row, tl, L, dvalid, outz);
-    }
-    dDacc = row_sum16(dDacc);
-    dbacc = row_sum16(dbacc);
-    if (last && dvalid) {
-      if (a.dD) unsafeAtomicAdd(&a.dD[d], dDacc);
-      if (a.ddelta_bias) unsafeAtomicAdd(&a.ddelta_bias[d], dbacc);
+      const float Dd = (a.Dskip && dvalid) ? a.Dskip[d] : 0.0f;
+      float o_du[2], o_dr[2], o_dz[2];
+      float dbacc = 0.0f, dDacc = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const bool okk = k ? ok1 : ok0;
+        const float s_ddt = k ? sddt.y : sddt.x, s_du = k ? sdu.y : sdu.x, s_yc = k ? syc.y : syc.x;
+        const float sig = a.softplus ? rcp(1.0f + ex2(-xs[k] * kLog2e)) : 1.0f;
+        o_dr[k] = okk ? s_ddt * sig : 0.0f;
+        dbacc += o_dr[k];
+        dDacc += okk ? dycs[k] * us[k] : 0.0f;
+        o_du[k] = fmaf(dycs[k], Dd, s_du);
+        if constexpr (GATE) {
+          const float sz = rcp(1.0f + ex2(-zs[k] * kLog2e));
+          o_dz[k] = gs[k] * fmaf(Dd, us[k], s_yc) * sz * fmaf(zs[k], 1.0f - sz, 1.0f);
+        }
+      }
+      if (dvalid) {
+        const int64_t base = ch * L + ts;
+        if (VEC && ok1) {
+          if constexpr (std::is_same<IO, float>::value) {
+            *reinterpret_cast<float2*>(static_cast<float*>(a.du) + base) = make_float2(o_du[0], o_du[1]);
+            *reinterpret_cast<float2*>(static_cast<float*>(a.ddelta) + base) = make_float2(o_dr[0], o_dr[1]);
+            if constexpr (GATE)
+              *reinterpret_cast<float2*>(static_cast<float*>(a.dz) + base) = make_float2(o_dz[0], o_dz[1]);
+          } else {
+            *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.du) + base) = pack_bf16x2(o_du[0], o_du[1]);
+            *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.ddelta) + base) = pack_bf16x2(o_dr[0], o_dr[1]);
+            if constexpr (GATE)
+              *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.dz) + base) = pack_bf16x2(o_dz[0], o_dz[1]);
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            if (k ? ok1 : ok0) {
+              Io<IO>::st1(a.du, base + k, o_du[k]);
+              Io<IO>::st1(a.ddelta, base + k, o_dr[k]);
+              if constexpr (GATE) Io<IO>::st1(a.dz, base + k, o_dz[k]);
+            }
+          }
+        }
+      }
+      dbacc = row_sum16(dbacc);
+      dDacc = row_sum16(dDacc);
+      if (last && dvalid) {
+        if (a.ddelta_bias) unsafeAtomicAdd(&a.ddelta_bias[d], dbacc);
+        if (a.dD) unsafeAtomicAdd(&a.dD[d], dDacc);
+      }
     }
   }
-  __syncthreads();
-  for (int i = threadIdx.x; i < N * T; i += NTH) {
-    const int n = i / T, tt = i % T;
-    const int64_t t = t0 + tt;
-    const int li = n * T + (tt % K) * LPC + tt / K;
-    if (t < L) {
-      unsafeAtomicAdd(&a.accB[(b * N + n) * L + t], sdB[li]);
-      unsafeAtomicAdd(&a.accC[(b * N + n) * L + t], sdC[li]);
+  // ---- this chunk's dB and dC from every channel the block visited
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = wave + NW * j;
+    const int64_t t = t0 + seg * K + red_row;
+    if (n < N) {
+      float* pBn = a.accB + (b * N + n) * L;
+      float* pCn = a.accC + (b * N + n) * L;
+      if (t < L) {
+        unsafeAtomicAdd(pBn + t, acc[j][0]);
+        unsafeAtomicAdd(pCn + t, acc[j][2]);
+      }
+      if (t + 4 < L) {
+        unsafeAtomicAdd(pBn + t + 4, acc[j][1]);
+        unsafeAtomicAdd(pCn + t + 4, acc[j][3]);
+      }
     }
   }
 }
@@ -1165,8 +1296,8 @@ int launch_bwd_typed(const ScanArgs& fa, BwdArgs ba, int64_t batch, hipStream_t 
                      2 * 16 * (size_t)ba.dstate * sizeof(float), s, fa);
   // 2. adjoint carries at every chunk end
   hipLaunchKernelGGL((scan_bwd_carry_kernel<IO, K, VEC, GATE>), grid16, dim3(256), 0, s, ba);
-  // 3. gradients, every (sequence, chunk) independently
-  const int64_t ngroups = (ba.dim + 15) / 16;
+  // 3. gradients, every (sequence, chunk) independently; groups of 4 channels
+  const int64_t ngroups = (ba.dim + 3) / 4;
   const int64_t cells = ngroups * ba.chunks * batch;
   int64_t gpb = cells / 4096;  // a few thousand workgroups in total
   if (gpb < 1) gpb = 1;
