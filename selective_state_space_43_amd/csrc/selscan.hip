@@ -326,11 +326,14 @@ struct ScanArgs {
   float* final_state;
   int64_t dim, dstate, seqlen;
   int softplus;
-  float* ckpt;  // checkpoint mode: state at each chunk start, [batch, dim, chunks, dstate]
+  float* ckpt;  // checkpoint mode: state every kCkptT steps, [batch, dim, ceil(L / kCkptT), dstate]
 };
 
-// CKPT: the pass that the backward recomputes from: it writes the state at
-// the start of every chunk to a.ckpt and computes no output.
+// Steps between the states that the checkpoint pass keeps for the backward.
+constexpr int kCkptT = 128;
+
+// CKPT: the pass that the backward recomputes from: it writes the state
+// entering every kCkptT-step block to a.ckpt and computes no output.
 template <typename IO, int LPC, int K, int W, int NT, bool VEC, bool ZOH, bool GATE,
           bool CKPT = false>
 __global__ void __launch_bounds__(64 * W)
@@ -474,6 +477,11 @@ __global__ void __launch_bounds__(64 * W)
       const float He = group_prev0<LPC>(H, first);
       float h = first ? c : He;
       if (seg == LPC - 1) carry_row[n] = H;
+      if constexpr (CKPT) {
+        static_assert(kCkptT % K == 0 && T % kCkptT == 0, "checkpoints fall on lane starts");
+        if (dvalid && (seg * K) % kCkptT == 0 && tl < L)
+          a.ckpt[((b * a.dim + d) * ((L + kCkptT - 1) / kCkptT) + tl / kCkptT) * N + n] = h;
+      }
 #pragma unroll
       for (int i = 0; i < K; i += 4) {
         const float4 cc = *reinterpret_cast<const float4*>(pc + i);
@@ -486,11 +494,6 @@ __global__ void __launch_bounds__(64 * W)
       }
     };
 
-    if constexpr (CKPT) {
-      if (dvalid)
-        for (int64_t n = seg; n < N; n += LPC)
-          a.ckpt[((b * a.dim + d) * ((L + T - 1) / T) + t0 / T) * N + n] = carry_row[n];
-    }
     for (int64_t n0 = 0; n0 < N; n0 += NT) {
       if (n0 > 0) {
         __syncthreads();  // every wave is done with the previous tile
@@ -630,14 +633,21 @@ __global__ void __launch_bounds__(256) scan_bwd_carry_kernel(const BwdArgs a) {
     sMu[i] = (a.dfinal && ok) ? a.dfinal[(b * a.dim + d0 + c) * N + n] : 0.0f;
     sA[i] = ok ? a.A[(d0 + c) * N + n] : 0.0f;
   }
-  for (int64_t ci = a.chunks - 1; ci >= 0; --ci) {
+  // carries are kept per kCkptT-step block: the adjoint entering block k
+  // from its end, Abar lambda at step (k + 1) kCkptT
+  static_assert(T % kCkptT == 0 && kCkptT % K == 0, "carry blocks fall on lane starts");
+  float* carry_ch = a.carry + (b * a.dim + d) * a.chunks * N;
+  for (int64_t ci = (L + T - 1) / T - 1; ci >= 0; --ci) {
     const int64_t t0 = ci * T, tl = t0 + seg * K;
     Run<IO, K> rdy, rd, rz;
     run_load<IO, K, VEC>(rdy, a.dy, row, tl, L, dvalid);
     run_load<IO, K, VEC>(rd, a.delta, row, tl, L, dvalid);
     if constexpr (GATE) run_load<IO, K, VEC>(rz, a.z, row, tl, L, dvalid);
     __syncthreads();  // previous chunk's tile is no longer read; sMu/sA visible
-    if (dvalid && seg < N) a.carry[((b * a.dim + d) * a.chunks + ci) * N + seg] = sMu[chb * N + seg];
+    {
+      const int64_t cend = ((t0 + T < L ? t0 + T : L) - 1) / kCkptT;  // last block of the chunk
+      if (dvalid && seg < N) carry_ch[cend * N + seg] = sMu[chb * N + seg];
+    }
 #pragma unroll
     for (int k = 0; k < ITEMS; ++k) {
       const int item = threadIdx.x + k * NTH;
@@ -694,6 +704,9 @@ __global__ void __launch_bounds__(256) scan_bwd_carry_kernel(const BwdArgs a) {
       float H = av[0] * Lam;
       row_scan16_rev(ex2(An * S), H);
       if (seg == 0) sMu[chb * N + n] = H;  // Abar lambda at the chunk's first step
+      // lanes that start a block inside the chunk hand the block before it its carry
+      if (seg > 0 && (seg * K) % kCkptT == 0 && tl < L && dvalid)
+        carry_ch[(tl / kCkptT - 1) * N + n] = H;
     }
   }
 }
@@ -726,8 +739,9 @@ __global__ void __launch_bounds__(256) scan_bwd_main_kernel(const BwdArgs a) {
   // size, gate, output gradients) for steps 2w and 2w + 1 of every lane.
   __shared__ float4 sB4[NT * LPC * KP / 4];
   __shared__ float4 sC4[NT * LPC * KP / 4];
-  __shared__ float4 sRed4[NW * 3 * 64 * K / 4];  // [wave][ddt, du, yc][lane][step] partial sums
-  __shared__ float4 sPrep4[3 * 64 * K / 4];      // [delta, u, dy silu(z)][lane][step]
+  constexpr int SP = K + 4;  // padded per-lane row: 16-byte reads of a wave hit distinct banks
+  __shared__ float4 sRed4[NW * 3 * 64 * SP / 4];  // [wave][ddt, du, yc][lane][step] partial sums
+  __shared__ float4 sPrep4[3 * 64 * SP / 4];      // [delta, u, dy silu(z)][lane][step]
   __shared__ float sPar[NW * 3 * CPG * NT];      // per wave: A, state at chunk start, carry
   float* sRed = reinterpret_cast<float*>(sRed4);
   float* sPrep = reinterpret_cast<float*>(sPrep4);
@@ -838,18 +852,18 @@ __global__ void __launch_bounds__(256) scan_bwd_main_kernel(const BwdArgs a) {
         dycs[k] = GATE ? gs[k] * silu_f(zs[k]) : gs[k];
         if (k) { dtp.y = dtk; dyp.y = dycs[k]; } else { dtp.x = dtk; dyp.x = dycs[k]; }
       }
-      *reinterpret_cast<float2*>(sPrep + (0 * 64 + lane) * K + s0) = dtp;
-      *reinterpret_cast<float2*>(sPrep + (1 * 64 + lane) * K + s0) = make_float2(us[0], us[1]);
-      *reinterpret_cast<float2*>(sPrep + (2 * 64 + lane) * K + s0) = dyp;
+      *reinterpret_cast<float2*>(sPrep + (0 * 64 + lane) * SP + s0) = dtp;
+      *reinterpret_cast<float2*>(sPrep + (1 * 64 + lane) * SP + s0) = make_float2(us[0], us[1]);
+      *reinterpret_cast<float2*>(sPrep + (2 * 64 + lane) * SP + s0) = dyp;
     }
     __syncthreads();  // every wave's steps are in; the previous group's sums are read
     float dt[K], uu[K], w[K], dyc[K], yc[K], ddt[K], du[K];
     float S = 0.0f;  // sum of the lane's steps, in log2 units
 #pragma unroll
     for (int i = 0; i < K; i += 4) {
-      const float4 q0 = *reinterpret_cast<const float4*>(sPrep + (0 * 64 + lane) * K + i);
-      const float4 q1 = *reinterpret_cast<const float4*>(sPrep + (1 * 64 + lane) * K + i);
-      const float4 q2 = *reinterpret_cast<const float4*>(sPrep + (2 * 64 + lane) * K + i);
+      const float4 q0 = *reinterpret_cast<const float4*>(sPrep + (0 * 64 + lane) * SP + i);
+      const float4 q1 = *reinterpret_cast<const float4*>(sPrep + (1 * 64 + lane) * SP + i);
+      const float4 q2 = *reinterpret_cast<const float4*>(sPrep + (2 * 64 + lane) * SP + i);
       dt[i] = q0.x; dt[i + 1] = q0.y; dt[i + 2] = q0.z; dt[i + 3] = q0.w;
       uu[i] = q1.x; uu[i + 1] = q1.y; uu[i + 2] = q1.z; uu[i + 3] = q1.w;
       dyc[i] = q2.x; dyc[i + 1] = q2.y; dyc[i + 2] = q2.z; dyc[i + 3] = q2.w;
@@ -954,13 +968,13 @@ __global__ void __launch_bounds__(256) scan_bwd_main_kernel(const BwdArgs a) {
     // ---- per-step gradients: sum the four waves' partials for this wave's
     // two steps
     {
-      float* red = sRed + wave * 3 * 64 * K;
+      float* red = sRed + wave * 3 * 64 * SP;
 #pragma unroll
       for (int i = 0; i < K; i += 4) {
-        *reinterpret_cast<float4*>(red + (0 * 64 + lane) * K + i) = make_float4(ddt[i], ddt[i + 1], ddt[i + 2], ddt[i + 3]);
-        *reinterpret_cast<float4*>(red + (1 * 64 + lane) * K + i) = make_float4(du[i], du[i + 1], du[i + 2], du[i + 3]);
+        *reinterpret_cast<float4*>(red + (0 * 64 + lane) * SP + i) = make_float4(ddt[i], ddt[i + 1], ddt[i + 2], ddt[i + 3]);
+        *reinterpret_cast<float4*>(red + (1 * 64 + lane) * SP + i) = make_float4(du[i], du[i + 1], du[i + 2], du[i + 3]);
         if constexpr (GATE)
-          *reinterpret_cast<float4*>(red + (2 * 64 + lane) * K + i) = make_float4(yc[i], yc[i + 1], yc[i + 2], yc[i + 3]);
+          *reinterpret_cast<float4*>(red + (2 * 64 + lane) * SP + i) = make_float4(yc[i], yc[i + 1], yc[i + 2], yc[i + 3]);
       }
     }
     __syncthreads();
@@ -968,13 +982,13 @@ __global__ void __launch_bounds__(256) scan_bwd_main_kernel(const BwdArgs a) {
       float2 sddt = make_float2(0.0f, 0.0f), sdu = sddt, syc = sddt;
 #pragma unroll
       for (int ww = 0; ww < NW; ++ww) {
-        const float* rr = sRed + ww * 3 * 64 * K + lane * K + s0;
+        const float* rr = sRed + ww * 3 * 64 * SP + lane * SP + s0;
         const float2 p0 = *reinterpret_cast<const float2*>(rr);
-        const float2 p1 = *reinterpret_cast<const float2*>(rr + 64 * K);
+        const float2 p1 = *reinterpret_cast<const float2*>(rr + 64 * SP);
         sddt.x += p0.x; sddt.y += p0.y;
         sdu.x += p1.x; sdu.y += p1.y;
         if constexpr (GATE) {
-          const float2 p2 = *reinterpret_cast<const float2*>(rr + 2 * 64 * K);
+          const float2 p2 = *reinterpret_cast<const float2*>(rr + 2 * 64 * SP);
           syc.x += p2.x; syc.y += p2.y;
         }
       }
@@ -1264,8 +1278,9 @@ int launch_fwd(const ScanArgs& a, int64_t batch, bool zoh, bool gate, bool vec, 
              : launch_fwd_vec<IO, false>(a, batch, zoh, gate, s);
 }
 
-// Backward: chunks of T = 16 * kBwdK steps.
+// Backward: the gradient pass works on chunks of T = 16 * kBwdK = kCkptT steps.
 constexpr int kBwdK = 8;
+static_assert(16 * kBwdK == kCkptT, "gradient chunks are the checkpoint blocks");
 constexpr int64_t kBwdMaxDstate = 16;
 
 struct BwdLayout {
@@ -1291,11 +1306,12 @@ template <typename IO, bool VEC, bool ZOH, bool GATE>
 int launch_bwd_typed(const ScanArgs& fa, BwdArgs ba, int64_t batch, hipStream_t s) {
   constexpr int K = kBwdK;
   const dim3 grid16((unsigned)((ba.dim + 15) / 16), (unsigned)batch);
-  // 1. checkpoints: the state at every chunk start
-  hipLaunchKernelGGL((scan_fwd_kernel<IO, 16, K, 4, 16, VEC, ZOH, false, true>), grid16, dim3(256),
+  // 1. checkpoints: the state entering every kCkptT-step block (a forward
+  // pass over 256-step chunks)
+  hipLaunchKernelGGL((scan_fwd_kernel<IO, 16, 16, 4, 16, VEC, ZOH, false, true>), grid16, dim3(256),
                      2 * 16 * (size_t)ba.dstate * sizeof(float), s, fa);
-  // 2. adjoint carries at every chunk end
-  hipLaunchKernelGGL((scan_bwd_carry_kernel<IO, K, VEC, GATE>), grid16, dim3(256), 0, s, ba);
+  // 2. adjoint carries at every block end (a reverse pass over 256-step chunks)
+  hipLaunchKernelGGL((scan_bwd_carry_kernel<IO, 16, VEC, GATE>), grid16, dim3(256), 0, s, ba);
   // 3. gradients, every (sequence, chunk) independently; groups of 4 channels
   const int64_t ngroups = (ba.dim + 3) / 4;
   const int64_t cells = ngroups * ba.chunks * batch;
