@@ -13,7 +13,9 @@ delta_bias, h0) are widened to float64 here with ``astype`` (exact for float32).
 
 Each function cites the page passage it follows in ``ssm_oracle.c``.
 Parity status: every function here is pinned by ``tests/test_oracle_pins.py`` (forward,
-decode, LTI) and ``tests/test_oracle_bwd_pins.py`` (backward, by finite differences).
+decode, LTI), ``tests/test_oracle_bwd_pins.py`` (backward, by finite differences) and
+``tests/test_oracle_conv_pins.py`` (causal conv1d: torch's conv1d, closed forms, finite
+differences).
 """
 from __future__ import annotations
 
@@ -60,9 +62,13 @@ def _lib():
         lib.ssm_oracle_selective_scan_bwd.argtypes = [
             i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp,
             i64, i64, i64, i64, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32]
+        lib.ssm_oracle_conv1d.argtypes = [i32, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp, vp]
+        lib.ssm_oracle_conv1d_bwd.argtypes = [i32, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32,
+                                              vp, vp, vp, vp]
         for f in (lib.ssm_oracle_selective_scan, lib.ssm_oracle_state_update,
                   lib.ssm_oracle_lti_kernel, lib.ssm_oracle_causal_conv,
-                  lib.ssm_oracle_selective_scan_bwd):
+                  lib.ssm_oracle_selective_scan_bwd, lib.ssm_oracle_conv1d,
+                  lib.ssm_oracle_conv1d_bwd):
             f.restype = i32
         _LIB = lib
     return _LIB
@@ -240,3 +246,43 @@ def selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None,
     if rc != 0:
         raise RuntimeError(f"ssm_oracle_selective_scan_bwd failed ({rc})")
     return out
+
+
+def conv1d(x, w, bias=None, state_in=None, silu=True):
+    """Depthwise causal convolution (width W = w.shape[1]) with optional silu.
+    x: [batch, dim, L] float32 / bf16 bits / float64; w: [dim, W]; bias: [dim];
+    state_in: [batch, dim, W-1] (the inputs before t = 0, oldest first) or None.
+    Returns (out float64 [batch, dim, L], state_out float64 [batch, dim, W-1])."""
+    x, dt = _seq(x, "x")
+    batch, dim, L = x.shape
+    w64 = _f64(w)
+    W = w64.shape[1]
+    b64, s64 = _f64(bias), _f64(state_in)
+    out = np.empty((batch, dim, L), dtype=np.float64)
+    st = np.empty((batch, dim, W - 1), dtype=np.float64)
+    rc = _lib().ssm_oracle_conv1d(dt, _ptr(x), _ptr(w64), _ptr(b64), _ptr(s64), batch, dim, L,
+                                  W, int(bool(silu)), _ptr(out), _ptr(st) if W > 1 else None)
+    if rc != 0:
+        raise RuntimeError(f"ssm_oracle_conv1d failed ({rc})")
+    return out, st
+
+
+def conv1d_bwd(x, w, dout, bias=None, state_in=None, silu=True):
+    """Gradients of conv1d for the loss sum(dout * out): dict of float64 dx
+    [batch, dim, L], dw [dim, W], dbias [dim], dstate_in [batch, dim, W-1]."""
+    x, dt = _seq(x, "x")
+    batch, dim, L = x.shape
+    w64 = _f64(w)
+    W = w64.shape[1]
+    b64, s64 = _f64(bias), _f64(state_in)
+    d64 = np.ascontiguousarray(dout, dtype=np.float64)
+    assert d64.shape == (batch, dim, L)
+    g = dict(dx=np.empty((batch, dim, L)), dw=np.empty((dim, W)), dbias=np.empty(dim),
+             dstate_in=np.empty((batch, dim, W - 1)))
+    rc = _lib().ssm_oracle_conv1d_bwd(dt, _ptr(x), _ptr(w64), _ptr(b64), _ptr(s64), _ptr(d64),
+                                      batch, dim, L, W, int(bool(silu)), _ptr(g["dx"]),
+                                      _ptr(g["dw"]), _ptr(g["dbias"]),
+                                      _ptr(g["dstate_in"]) if W > 1 else None)
+    if rc != 0:
+        raise RuntimeError(f"ssm_oracle_conv1d_bwd failed ({rc})")
+    return g

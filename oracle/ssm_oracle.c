@@ -518,3 +518,94 @@ int ssm_oracle_selective_scan_bwd(int io_dtype, const void* u, const void* delta
   pthread_mutex_destroy(&j.lock);
   return j.status;
 }
+
+/*
+ * Depthwise causal convolution of width W with an optional silu, the step in
+ * front of the scan in the Mamba block ("State-space models", section
+ * "Mamba: selection", the paragraph on the block: a depthwise causal
+ * convolution of width 4 and a silu on one half of the projection).  Per
+ * sequence b and channel d:
+ *
+ *   pre_t = bias_d + sum_{k=0}^{W-1} w_{d,k} x_{t-(W-1)+k},   out_t = silu(pre_t) or pre_t
+ *
+ * i.e. the cross-correlation of the sequence padded on the left, as the
+ * page's F.conv1d snippet computes it ("State-space models", section
+ * "Implementation": left padding so that no output sees the future).  The
+ * W-1 inputs before t = 0 come from state_in ([batch, dim, W-1], oldest
+ * first) or are zero.  state_out (optional) receives the last W-1 inputs of
+ * the extended sequence, oldest first: with L = 1 this is the one-token
+ * decode step.  Inputs are io dtype bits (0 f32, 1 bf16, 2 f64); weights,
+ * bias and states are double; out is double [batch, dim, L].
+ */
+static double or_conv_x(const void* x, int io_dtype, const double* st, int64_t row, int64_t sbase,
+                        int64_t W, int64_t t) {
+  if (t >= 0) return or_widen(x, io_dtype, row + t);
+  return st ? st[sbase + (W - 1) + t] : 0.0; /* t in [-(W-1), -1] */
+}
+
+int ssm_oracle_conv1d(int io_dtype, const void* x, const double* w, const double* bias,
+                      const double* state_in, int64_t batch, int64_t dim, int64_t L, int64_t W,
+                      int silu, double* out, double* state_out) {
+  if (!x || !w || !out || batch <= 0 || dim <= 0 || L <= 0 || W <= 0) return 1;
+  for (int64_t c = 0; c < batch * dim; ++c) {
+    const int64_t d = c % dim, row = c * L, sb = c * (W - 1);
+    for (int64_t t = 0; t < L; ++t) {
+      double pre = bias ? bias[d] : 0.0;
+      for (int64_t k = 0; k < W; ++k)
+        pre += w[d * W + k] * or_conv_x(x, io_dtype, state_in, row, sb, W, t - (W - 1) + k);
+      out[row + t] = silu ? or_silu(pre) : pre;
+    }
+    if (state_out)
+      for (int64_t j = 0; j < W - 1; ++j)
+        state_out[sb + j] = or_conv_x(x, io_dtype, state_in, row, sb, W, L - (W - 1) + j);
+  }
+  return 0;
+}
+
+/*
+ * Gradients of ssm_oracle_conv1d for the loss sum(dout * out): with
+ * g_t = dout_t silu'(pre_t) (or dout_t without the silu),
+ *   dx_s     = sum_k w_k g_{s+(W-1)-k}          (terms with 0 <= s+(W-1)-k < L)
+ *   dw_{d,k} = sum_{b,t} g_t x_{t-(W-1)+k}      dbias_d = sum_{b,t} g_t
+ *   dstate_j = the dx of the pre-start input at time j-(W-1).
+ * dx and dout are double [batch, dim, L]; dw [dim, W], dbias [dim] are
+ * overwritten; dstate_in [batch, dim, W-1] may be NULL.
+ */
+int ssm_oracle_conv1d_bwd(int io_dtype, const void* x, const double* w, const double* bias,
+                          const double* state_in, const double* dout, int64_t batch, int64_t dim,
+                          int64_t L, int64_t W, int silu, double* dx, double* dw, double* dbias,
+                          double* dstate_in) {
+  if (!x || !w || !dout || !dx || !dw || !dbias || batch <= 0 || dim <= 0 || L <= 0 || W <= 0)
+    return 1;
+  memset(dw, 0, sizeof(double) * (size_t)(dim * W));
+  memset(dbias, 0, sizeof(double) * (size_t)dim);
+  double* g = (double*)malloc(sizeof(double) * (size_t)L);
+  if (!g) return 2;
+  for (int64_t c = 0; c < batch * dim; ++c) {
+    const int64_t d = c % dim, row = c * L, sb = c * (W - 1);
+    for (int64_t t = 0; t < L; ++t) {
+      double pre = bias ? bias[d] : 0.0;
+      for (int64_t k = 0; k < W; ++k)
+        pre += w[d * W + k] * or_conv_x(x, io_dtype, state_in, row, sb, W, t - (W - 1) + k);
+      const double s = or_sigmoid(pre);
+      g[t] = silu ? dout[row + t] * s * (1.0 + pre * (1.0 - s)) : dout[row + t];
+      dbias[d] += g[t];
+      for (int64_t k = 0; k < W; ++k)
+        dw[d * W + k] += g[t] * or_conv_x(x, io_dtype, state_in, row, sb, W, t - (W - 1) + k);
+    }
+    /* input at time s (s >= -(W-1)) feeds outputs t = s + (W-1) - k */
+    for (int64_t s = -(W - 1); s < L; ++s) {
+      double acc = 0.0;
+      for (int64_t k = 0; k < W; ++k) {
+        const int64_t t = s + (W - 1) - k;
+        if (t >= 0 && t < L) acc += w[d * W + k] * g[t];
+      }
+      if (s >= 0)
+        dx[row + s] = acc;
+      else if (dstate_in)
+        dstate_in[sb + (W - 1) + s] = acc;
+    }
+  }
+  free(g);
+  return 0;
+}
