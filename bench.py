@@ -8,7 +8,9 @@ Mamba-2.8B-shaped layer (batch 4, dim 5120, N 16, L 8192, bf16 io, fp32
 arithmetic and state).  Inputs are generated once, uploaded, and resident in
 HBM before timing starts.  The one-token decode step (ssm_state_update) is
 timed separately on the decode workload and reported under "decode", and the
-backward pass (ssm_selective_scan_bwd) on the same workload under "backward".
+backward pass (ssm_selective_scan_bwd) on the same workload under "backward",
+and the causal conv1d in front of the scan (forward and backward) under
+"conv1d".
 
 Prints one JSON line: the metric (scan elements B*D*L*N per second), the
 roofline of the scan kernel (live HIP-event timing; HBM traffic from the
@@ -214,6 +216,38 @@ def bench_bwd(ssm, torch, w, x, dev, steps, warmup):
     }
 
 
+def bench_conv(ssm, torch, w, dev, steps, warmup):
+    """The causal conv1d + silu in front of the scan (width 4, bias) at the
+    workload's [batch, dim, L] shape: forward and backward, HBM-bound."""
+    c = wl.conv_inputs(w, width=4)
+    x, wt, b, dout = (to_dev(c[k], dev) for k in ("x", "weight", "bias", "dout"))
+    out = torch.empty_like(x)
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(steps):
+            fn()
+        e.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(e) / steps
+
+    ms_f = timed(lambda: ssm.ssm_causal_conv1d_fwd(x, wt, b, out=out))
+    ms_b = timed(lambda: ssm.ssm_causal_conv1d_bwd(x, wt, dout, b))
+    seq = x.numel() * x.element_size()
+    res = {"workload": f"{w.name} conv1d: x [{w.batch}, {w.dim}, {w.seqlen}] {w.dtype}, width 4, "
+                       "bias, silu"}
+    for name, ms, nbytes in (("fwd", ms_f, 2 * seq), ("bwd", ms_b, 3 * seq)):
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        res[name] = {"ms": round(ms, 4), "algorithmic_bytes": nbytes, "hbm_gbps": round(gbps, 1),
+                     "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
+    return res
+
+
 def cpu_baseline(w, x, seconds_target=12.0):
     """The fp64 oracle on host cores over whole channels of the same inputs:
     as many channels (full length each) as fit the time target."""
@@ -251,6 +285,7 @@ def main(argv=None):
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-backward", action="store_true")
+    p.add_argument("--no-conv", action="store_true")
     p.add_argument("--backward-steps", type=int, default=5)
     p.add_argument("--copy-check", type=int, default=0, metavar="BYTES",
                    help="also run torch's plain copy of BYTES three times (counter calibration "
@@ -342,6 +377,10 @@ def main(argv=None):
         out["backward"] = bench_bwd(ssm, torch, w, x, dev, args.backward_steps, 1)
         print(f"[bench] backward: {out['backward']['ms_per_call']} ms/call", file=sys.stderr,
               flush=True)
+    if not args.no_conv:
+        out["conv1d"] = bench_conv(ssm, torch, w, dev, 10, 2)
+        print(f"[bench] conv1d: fwd {out['conv1d']['fwd']['ms']} ms, bwd "
+              f"{out['conv1d']['bwd']['ms']} ms", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, x)
         print(f"[bench] cpu baseline: {out['cpu_baseline']['seconds']}s", file=sys.stderr,

@@ -184,6 +184,57 @@ int ssm_selective_scan_bwd(const void* u, const void* delta, const float* A, con
 int64_t ssm_selective_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
                                               int64_t seqlen);
 
+/*
+ * Depthwise causal convolution of width W (1..4) with an optional silu, the
+ * step in front of the scan in the Mamba block ("State-space models",
+ * section "Mamba: selection": a depthwise causal convolution of width 4 and
+ * a silu on one half of the projection).  Per sequence b and channel d:
+ *
+ *   pre_t = bias_d + sum_{k<W} weight_{d,k} x_{t-(W-1)+k},  out_t = silu(pre_t) or pre_t
+ *
+ * the cross-correlation of the sequence padded on the left, the convention of
+ * the page's F.conv1d snippet ("State-space models", section
+ * "Implementation").  The W-1 inputs before t = 0 are state_in or zero.
+ *
+ *  x, out      [batch, dim, seqlen] io_dtype, 16-byte aligned
+ *  weight      [dim, W] float32;  bias [dim] float32 or NULL
+ *  state_in    [batch, dim, W-1] float32 (oldest first) or NULL (zeros)
+ *  state_out   [batch, dim, W-1] float32 or NULL: the last W-1 inputs of the
+ *              extended sequence, what ssm_causal_conv1d_update or a later
+ *              call continues from; it may be state_in itself
+ * Outputs must not overlap inputs (except state_out == state_in).  Returns
+ * SSM_E_UNSUPPORTED for W outside 1..4.  Arithmetic in float32.
+ */
+int ssm_causal_conv1d_fwd(const void* x, const float* weight, const float* bias,
+                          const float* state_in, void* out, float* state_out, int64_t batch,
+                          int64_t dim, int64_t seqlen, int64_t width, int apply_silu,
+                          int io_dtype, void* hip_stream);
+
+/*
+ * One token per (sequence, channel): out = act(bias + sum_k weight_k
+ * [conv_state, x]_k), then conv_state (float32 [batch, dim, W-1], updated in
+ * place) drops its oldest input and appends x.  x, out are [batch, dim].
+ * Equal to ssm_causal_conv1d_fwd with seqlen 1 and state_out = state_in.
+ */
+int ssm_causal_conv1d_update(const void* x, float* conv_state, const float* weight,
+                             const float* bias, void* out, int64_t batch, int64_t dim,
+                             int64_t width, int apply_silu, int io_dtype, void* hip_stream);
+
+/*
+ * Backward of ssm_causal_conv1d_fwd for the loss sum(dout * out):
+ *  dx        [batch, dim, seqlen] io_dtype
+ *  dweight   [dim, W] float32, overwritten (sum over sequences and steps)
+ *  dbias     [dim] float32 or NULL, overwritten
+ *  dstate_in [batch, dim, W-1] float32 or NULL: gradient of state_in
+ * pre is recomputed from x.  dweight and dbias are float32 sums with atomic
+ * adds, so they can differ in the last bits from run to run.
+ */
+int ssm_causal_conv1d_bwd(const void* x, const float* weight, const float* bias,
+                          const float* state_in, const void* dout, void* dx, float* dweight,
+                          float* dbias, float* dstate_in, int64_t batch, int64_t dim,
+                          int64_t seqlen, int64_t width, int apply_silu, int io_dtype,
+                          void* hip_stream);
+
 /* Static description of a status code (never NULL). */
 const char* ssm_status_str(int status);
 

@@ -16,6 +16,12 @@ Entry points carry the C names:
   ssm_selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None,
                          delta_softplus=False, h0=None, dfinal_state=None,
                          bbar="delta", workspace=None) -> dict of gradients
+  ssm_causal_conv1d_fwd(x, weight, bias=None, state_in=None, silu=True,
+                        out=None, state_out=None, want_state_out=False)
+      -> (out, state_out)
+  ssm_causal_conv1d_update(x, conv_state, weight, bias=None, silu=True) -> out
+  ssm_causal_conv1d_bwd(x, weight, dout, bias=None, state_in=None, silu=True)
+      -> dict of gradients
 
 Layouts: u, delta, z, y [batch, dim, L]; B, C [batch, dstate, L]; A
 [dim, dstate]; D, delta_bias [dim]; h0 / final_state / state
@@ -27,13 +33,15 @@ from __future__ import annotations
 from ._lib import (SSM_BBAR_DELTA_B, SSM_BBAR_ZOH_EXACT, SSM_DTYPE_BF16, SSM_DTYPE_F32,
                    SelscanError, library_path, lib, ssm_abi_version, ssm_last_error,
                    ssm_status_str)
-from .binding import (ssm_lti_kernel, ssm_selective_scan_bwd,
+from .binding import (ssm_causal_conv1d_bwd, ssm_causal_conv1d_fwd, ssm_causal_conv1d_update,
+                      ssm_lti_kernel, ssm_selective_scan_bwd,
                       ssm_selective_scan_bwd_workspace_size, ssm_selective_scan_fwd,
                       ssm_state_update)
 
 __all__ = [
     "ssm_selective_scan_fwd", "ssm_state_update", "ssm_lti_kernel", "ssm_selective_scan_bwd",
-    "ssm_selective_scan_bwd_workspace_size", "ssm_status_str",
+    "ssm_selective_scan_bwd_workspace_size", "ssm_causal_conv1d_fwd", "ssm_causal_conv1d_update",
+    "ssm_causal_conv1d_bwd", "ssm_status_str",
     "ssm_last_error", "ssm_abi_version", "SelscanError", "library_path", "lib",
     "SSM_DTYPE_F32", "SSM_DTYPE_BF16", "SSM_BBAR_DELTA_B", "SSM_BBAR_ZOH_EXACT",
 ]

@@ -197,3 +197,84 @@ def ssm_selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=Non
             _BBAR[bbar], _stream(dev))
     check(st, "ssm_selective_scan_bwd")
     return g
+
+
+def _conv_params(x, weight, bias, dev):
+    if x.dim() != 3 or x.dtype not in _IO:
+        raise TypeError("x must be [batch, dim, L] bfloat16 or float32")
+    batch, dim, L = x.shape
+    if weight.dim() != 2 or weight.shape[0] != dim:
+        raise ValueError("weight must be [dim, width]")
+    W = weight.shape[1]
+    _io(weight, "weight", torch.float32, (dim, W), dev)
+    _f32(bias, "bias", (dim,), dev)
+    return batch, dim, L, W
+
+
+def ssm_causal_conv1d_fwd(x, weight, bias=None, state_in=None, silu=True, out=None,
+                          state_out=None, want_state_out=False):
+    """Depthwise causal conv1d (+ silu); returns (out, state_out or None)."""
+    _dev(x, "x", None)
+    dev = x.device
+    batch, dim, L, W = _conv_params(x, weight, bias, dev)
+    _f32(state_in, "state_in", (batch, dim, W - 1), dev)
+    if out is None:
+        out = torch.empty_like(x)
+    else:
+        _io(out, "out", x.dtype, (batch, dim, L), dev)
+    if state_out is None and want_state_out:
+        state_out = torch.empty((batch, dim, W - 1), dtype=torch.float32, device=dev)
+    elif state_out is not None:
+        _f32(state_out, "state_out", (batch, dim, W - 1), dev)
+    with torch.cuda.device(dev):
+        st = lib().ssm_causal_conv1d_fwd(_ptr(x), _ptr(weight), _ptr(bias), _ptr(state_in),
+                                         _ptr(out), _ptr(state_out), batch, dim, L, W,
+                                         int(bool(silu)), _IO[x.dtype], _stream(dev))
+    check(st, "ssm_causal_conv1d_fwd")
+    return out, state_out
+
+
+def ssm_causal_conv1d_update(x, conv_state, weight, bias=None, silu=True, out=None):
+    """One token: x [batch, dim]; conv_state [batch, dim, W-1] updated in place."""
+    _dev(x, "x", None)
+    dev = x.device
+    if x.dim() != 2 or x.dtype not in _IO:
+        raise TypeError("x must be [batch, dim] bfloat16 or float32")
+    batch, dim = x.shape
+    W = weight.shape[1]
+    _io(weight, "weight", torch.float32, (dim, W), dev)
+    _f32(bias, "bias", (dim,), dev)
+    _f32(conv_state, "conv_state", (batch, dim, W - 1), dev)
+    if out is None:
+        out = torch.empty_like(x)
+    else:
+        _io(out, "out", x.dtype, (batch, dim), dev)
+    with torch.cuda.device(dev):
+        st = lib().ssm_causal_conv1d_update(_ptr(x), _ptr(conv_state), _ptr(weight), _ptr(bias),
+                                            _ptr(out), batch, dim, W, int(bool(silu)),
+                                            _IO[x.dtype], _stream(dev))
+    check(st, "ssm_causal_conv1d_update")
+    return out
+
+
+def ssm_causal_conv1d_bwd(x, weight, dout, bias=None, state_in=None, silu=True,
+                          want_dstate_in=False):
+    """Gradients of ssm_causal_conv1d_fwd: dict dx, dweight, dbias (if bias),
+    dstate_in (if state_in or want_dstate_in)."""
+    _dev(x, "x", None)
+    dev = x.device
+    batch, dim, L, W = _conv_params(x, weight, bias, dev)
+    _io(dout, "dout", x.dtype, (batch, dim, L), dev)
+    _f32(state_in, "state_in", (batch, dim, W - 1), dev)
+    g = dict(dx=torch.empty_like(x),
+             dweight=torch.empty((dim, W), dtype=torch.float32, device=dev),
+             dbias=torch.empty(dim, dtype=torch.float32, device=dev) if bias is not None else None,
+             dstate_in=(torch.empty((batch, dim, W - 1), dtype=torch.float32, device=dev)
+                        if (state_in is not None or want_dstate_in) else None))
+    with torch.cuda.device(dev):
+        st = lib().ssm_causal_conv1d_bwd(_ptr(x), _ptr(weight), _ptr(bias), _ptr(state_in),
+                                         _ptr(dout), _ptr(g["dx"]), _ptr(g["dweight"]),
+                                         _ptr(g["dbias"]), _ptr(g["dstate_in"]), batch, dim, L,
+                                         W, int(bool(silu)), _IO[x.dtype], _stream(dev))
+    check(st, "ssm_causal_conv1d_bwd")
+    return g

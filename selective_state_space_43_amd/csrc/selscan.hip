@@ -1073,6 +1073,250 @@ __global__ void __launch_bounds__(256) store_io_kernel(const float* src, void* d
     Io<IO>::st1(dst, i, src[i]);
 }
 
+// ---------------------------------------------------------------- causal conv1d
+//
+// Depthwise causal convolution of width W with an optional silu, the step in
+// front of the scan in the Mamba block ("State-space models", section
+// "Mamba: selection"): pre_t = bias + sum_k w_k x_{t-(W-1)+k} on a sequence
+// padded on the left (by zeros or a carried state of the W-1 previous
+// inputs), out_t = silu(pre_t).  HBM-bound: one read of x and one write of
+// out.  A thread owns one 16-byte vector of V consecutive steps of a row; the
+// W-1 inputs before its vector come from the neighbouring lane by a DPP
+// wave shift, the first lane of each wave loads them itself.
+
+struct ConvArgs {
+  const void* x;
+  const float* w;       // [dim, W]
+  const float* bias;    // [dim] or null
+  const float* state_in;  // [batch, dim, W-1] or null (zeros)
+  void* out;
+  const void* dout;     // backward
+  void* dx;
+  float* dw;
+  float* dbias;
+  float* dstate_in;
+  int64_t rows, dim, seqlen;
+  int silu;
+};
+
+template <int CTRL>
+__device__ __forceinline__ float wave_dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+constexpr int kWaveShl1 = 0x130;
+
+// x of row r at step t, t in [-(W-1), L): the carried state before t = 0.
+template <typename IO, int W>
+__device__ __forceinline__ float conv_x_at(const ConvArgs& a, int64_t r, int64_t t) {
+  if (t >= 0) return t < a.seqlen ? Io<IO>::ld1(a.x, r * a.seqlen + t) : 0.0f;
+  return a.state_in ? a.state_in[r * (W - 1) + (W - 1) + t] : 0.0f;
+}
+
+// the V steps of this thread (zero past L)
+template <typename IO, bool VEC>
+__device__ __forceinline__ void conv_load_run(const void* p, int64_t base, int64_t t0, int64_t L,
+                                              float* v) {
+  constexpr int V = Io<IO>::V;
+  if (VEC && t0 + V <= L) {
+    Io<IO>::ldv(p, base + t0, v);
+  } else {
+#pragma unroll
+    for (int i = 0; i < V; ++i) v[i] = t0 + i < L ? Io<IO>::ld1(p, base + t0 + i) : 0.0f;
+  }
+}
+
+template <typename IO, bool VEC>
+__device__ __forceinline__ void conv_store_run(void* p, int64_t base, int64_t t0, int64_t L,
+                                               const float* v) {
+  constexpr int V = Io<IO>::V;
+  if (VEC && t0 + V <= L) {
+    Io<IO>::stv(p, base + t0, v);
+  } else {
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+      if (t0 + i < L) Io<IO>::st1(p, base + t0 + i, v[i]);
+  }
+}
+
+template <typename IO, int W, bool VEC>
+__global__ void __launch_bounds__(256) conv1d_fwd_kernel(const ConvArgs a) {
+  constexpr int V = Io<IO>::V, H = W - 1;
+  const int lane = threadIdx.x & 63;
+  const int64_t L = a.seqlen;
+  const int64_t t0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * V;
+  for (int64_t r = blockIdx.y; r < a.rows; r += gridDim.y) {
+    const int64_t d = r % a.dim, base = r * L;
+    float xe[H + V];  // the H inputs before this run, then the run
+    conv_load_run<IO, VEC>(a.x, base, t0, L, xe + H);
+#pragma unroll
+    for (int j = 0; j < H; ++j) xe[j] = wave_dpp<kWaveShr1>(xe[V + j]);
+    if (lane == 0) {
+#pragma unroll
+      for (int j = 0; j < H; ++j) xe[j] = conv_x_at<IO, W>(a, r, t0 - H + j);
+    }
+    float wk[W];
+#pragma unroll
+    for (int k = 0; k < W; ++k) wk[k] = a.w[d * W + k];
+    const float b = a.bias ? a.bias[d] : 0.0f;
+    float o[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      float pre = b;
+#pragma unroll
+      for (int k = 0; k < W; ++k) pre = fmaf(wk[k], xe[i + k], pre);
+      o[i] = a.silu ? silu_f(pre) : pre;
+    }
+    if (t0 < L) conv_store_run<IO, VEC>(a.out, base, t0, L, o);
+  }
+}
+
+// The W-1 inputs that end the extended sequence (the state a later call or
+// the decode step continues from); one thread per row.  Reads everything it
+// needs before writing, so state_out may be state_in.
+template <typename IO, int W>
+__global__ void __launch_bounds__(256) conv1d_state_kernel(const ConvArgs a, float* state_out) {
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (r >= a.rows || W == 1) return;
+  float v[W > 1 ? W - 1 : 1];
+#pragma unroll
+  for (int j = 0; j < W - 1; ++j) v[j] = conv_x_at<IO, W>(a, r, a.seqlen - (W - 1) + j);
+#pragma unroll
+  for (int j = 0; j < W - 1; ++j) state_out[r * (W - 1) + j] = v[j];
+}
+
+// One token per row: out = act(bias + sum_k w_k [state, x]_k), state shifted
+// in place by one input.  One thread per row.
+template <typename IO, int W>
+__global__ void __launch_bounds__(256) conv1d_update_kernel(const void* x, float* state,
+                                                            const float* w, const float* bias,
+                                                            void* out, int64_t rows, int64_t dim,
+                                                            int silu) {
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (r >= rows) return;
+  const int64_t d = r % dim;
+  float xe[W];
+#pragma unroll
+  for (int j = 0; j < W - 1; ++j) xe[j] = state[r * (W - 1) + j];
+  xe[W - 1] = Io<IO>::ld1(x, r);
+  float pre = bias ? bias[d] : 0.0f;
+#pragma unroll
+  for (int k = 0; k < W; ++k) pre = fmaf(w[d * W + k], xe[k], pre);
+  Io<IO>::st1(out, r, silu ? silu_f(pre) : pre);
+#pragma unroll
+  for (int j = 0; j < W - 1; ++j) state[r * (W - 1) + j] = xe[j + 1];
+}
+
+// Backward.  g_t = dout_t silu'(pre_t); dx_s = sum_k w_k g_{s+(W-1)-k};
+// dw_k = sum g_t x_{t-(W-1)+k}; dbias = sum g_t; dstate_in from the first
+// W-1 outputs.  A thread recomputes pre and g for its V steps and the W-1
+// after them (taken from the next lane by a DPP shift, the last lane of the
+// wave computes them itself).  dw and dbias are reduced over the workgroup
+// (one row per workgroup) and added with one atomic per value.
+template <typename IO, int W, bool VEC>
+__global__ void __launch_bounds__(256) conv1d_bwd_kernel(const ConvArgs a) {
+  constexpr int V = Io<IO>::V, H = W - 1;
+  __shared__ float sRed[4][W + 1];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t L = a.seqlen;
+  const int64_t t0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * V;
+  for (int64_t r = blockIdx.y; r < a.rows; r += gridDim.y) {
+    const int64_t d = r % a.dim, base = r * L;
+    float wk[W];
+#pragma unroll
+    for (int k = 0; k < W; ++k) wk[k] = a.w[d * W + k];
+    const float b = a.bias ? a.bias[d] : 0.0f;
+    // inputs t0-H .. t0+V+H-1 and output gradients t0 .. t0+V+H-1
+    float xe[H + V + H], ge[V + H];
+    conv_load_run<IO, VEC>(a.x, base, t0, L, xe + H);
+    conv_load_run<IO, VEC>(a.dout, base, t0, L, ge);
+#pragma unroll
+    for (int j = 0; j < H; ++j) {
+      xe[j] = wave_dpp<kWaveShr1>(xe[V + j]);
+      xe[H + V + j] = wave_dpp<kWaveShl1>(xe[H + j]);
+      ge[V + j] = wave_dpp<kWaveShl1>(ge[j]);
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int j = 0; j < H; ++j) xe[j] = conv_x_at<IO, W>(a, r, t0 - H + j);
+    }
+    if (lane == 63) {
+#pragma unroll
+      for (int j = 0; j < H; ++j) {
+        const int64_t t = t0 + V + j;
+        xe[H + V + j] = t < L ? Io<IO>::ld1(a.x, base + t) : 0.0f;
+        ge[V + j] = t < L ? Io<IO>::ld1(a.dout, base + t) : 0.0f;
+      }
+    }
+    // g for steps t0 .. t0+V+H-1 (zero past L, where dout is zero)
+#pragma unroll
+    for (int i = 0; i < V + H; ++i) {
+      float pre = b;
+#pragma unroll
+      for (int k = 0; k < W; ++k) pre = fmaf(wk[k], xe[i + k], pre);
+      if (a.silu) {
+        const float s = rcp(1.0f + ex2(-pre * kLog2e));
+        ge[i] *= s * fmaf(pre, 1.0f - s, 1.0f);
+      }
+    }
+    float dwp[W + 1];
+#pragma unroll
+    for (int k = 0; k <= W; ++k) dwp[k] = 0.0f;
+    float dxo[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      // own outputs feed dw, dbias
+#pragma unroll
+      for (int k = 0; k < W; ++k) dwp[k] = fmaf(ge[i], xe[i + k], dwp[k]);
+      dwp[W] += ge[i];
+      // input t0+i feeds outputs t0+i+H-k
+      float acc = 0.0f;
+#pragma unroll
+      for (int k = 0; k < W; ++k) acc = fmaf(wk[k], ge[i + H - k], acc);
+      dxo[i] = acc;
+    }
+    if (t0 < L) conv_store_run<IO, VEC>(a.dx, base, t0, L, dxo);
+    // the carried inputs before t = 0 feed outputs 0 .. H-1 (first thread of the row)
+    if (t0 == 0 && a.dstate_in) {
+#pragma unroll
+      for (int j = 0; j < H; ++j) {  // input at time j - H
+        float acc = 0.0f;
+#pragma unroll
+        for (int k = 0; k < W; ++k) {
+          const int t = j - k;  // output index j - H + H - k
+          if (t >= 0) acc = fmaf(wk[k], ge[t], acc);
+        }
+        a.dstate_in[r * H + j] = acc;
+      }
+    }
+    // workgroup sums of dw and dbias
+#pragma unroll
+    for (int k = 0; k <= W; ++k) {
+      float v = dwp[k];
+      v += wave_dpp<kRowShr1>(v);
+      v += dpp0<kRowShr2>(v);
+      v += dpp0<kRowShr4>(v);
+      v += dpp0<kRowShr8>(v);
+      v += dpp<kRowBcast15, 0xa>(0.0f, v);
+      v += dpp<kRowBcast31, 0xc>(0.0f, v);
+      dwp[k] = v;  // lane 63 holds the wave's sum
+    }
+    if (lane == 63) {
+#pragma unroll
+      for (int k = 0; k <= W; ++k) sRed[wave][k] = dwp[k];
+    }
+    __syncthreads();
+    if (threadIdx.x <= W) {
+      const float s = sRed[0][threadIdx.x] + sRed[1][threadIdx.x] + sRed[2][threadIdx.x] +
+                      sRed[3][threadIdx.x];
+      if (threadIdx.x < W)
+        unsafeAtomicAdd(&a.dw[d * W + threadIdx.x], s);
+      else if (a.dbias)
+        unsafeAtomicAdd(&a.dbias[d], s);
+    }
+    __syncthreads();
+  }
+}
+
 // ---------------------------------------------------------------- decode step
 
 struct StepArgs {
@@ -1344,6 +1588,57 @@ void zero_fill(float* p, int64_t n, hipStream_t s) {
   int64_t blocks = (n + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n);
+}
+
+
+// ---------------------------------------------------------------- causal conv1d: launch
+
+template <typename IO, int W>
+void launch_conv_fwd(const ConvArgs& a, bool vec, float* state_out, hipStream_t s) {
+  constexpr int V = Io<IO>::V;
+  const int64_t nvec = (a.seqlen + V - 1) / V;
+  const dim3 grid((unsigned)((nvec + 255) / 256), (unsigned)(a.rows < 65535 ? a.rows : 65535));
+  if (vec)
+    hipLaunchKernelGGL((conv1d_fwd_kernel<IO, W, true>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((conv1d_fwd_kernel<IO, W, false>), grid, dim3(256), 0, s, a);
+  if (state_out && W > 1)
+    hipLaunchKernelGGL((conv1d_state_kernel<IO, W>), dim3((unsigned)((a.rows + 255) / 256)),
+                       dim3(256), 0, s, a, state_out);
+}
+
+template <typename IO, int W>
+void launch_conv_bwd(const ConvArgs& a, bool vec, hipStream_t s) {
+  constexpr int V = Io<IO>::V;
+  const int64_t nvec = (a.seqlen + V - 1) / V;
+  const dim3 grid((unsigned)((nvec + 255) / 256), (unsigned)(a.rows < 65535 ? a.rows : 65535));
+  if (vec)
+    hipLaunchKernelGGL((conv1d_bwd_kernel<IO, W, true>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((conv1d_bwd_kernel<IO, W, false>), grid, dim3(256), 0, s, a);
+}
+
+template <typename F>
+void with_width(int64_t width, F&& f) {
+  switch (width) {
+    case 1: f(std::integral_constant<int, 1>{}); break;
+    case 2: f(std::integral_constant<int, 2>{}); break;
+    case 3: f(std::integral_constant<int, 3>{}); break;
+    default: f(std::integral_constant<int, 4>{}); break;
+  }
+}
+
+int conv_common_checks(int64_t batch, int64_t dim, int64_t seqlen, int64_t width, int io_dtype) {
+  int st;
+  if ((st = check_extent("batch", batch)) || (st = check_extent("dim", dim)) ||
+      (st = check_extent("seqlen", seqlen)))
+    return st;
+  if (width < 1 || width > 4)
+    return fail(SSM_E_UNSUPPORTED, "width = %lld: supported widths are 1..4", (long long)width);
+  if (!product_ok(batch, dim, seqlen, 4)) return fail(SSM_E_SHAPE, "tensor sizes overflow");
+  if (io_dtype != SSM_DTYPE_F32 && io_dtype != SSM_DTYPE_BF16)
+    return fail(SSM_E_DTYPE, "io_dtype = %d is not SSM_DTYPE_F32 or SSM_DTYPE_BF16", io_dtype);
+  return SSM_OK;
 }
 
 }  // namespace
@@ -1645,6 +1940,127 @@ int ssm_selective_scan_bwd(const void* u, const void* delta, const float* A, con
     hipLaunchKernelGGL(store_io_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, s, ba.accC, dC, nacc);
   }
   return launch_status("ssm_selective_scan_bwd launch");
+}
+
+int ssm_causal_conv1d_fwd(const void* x, const float* weight, const float* bias,
+                          const float* state_in, void* out, float* state_out, int64_t batch,
+                          int64_t dim, int64_t seqlen, int64_t width, int apply_silu,
+                          int io_dtype, void* hip_stream) {
+  g_last_error[0] = 0;
+  if (!x) return fail(SSM_E_NULL, "x is NULL");
+  if (!weight) return fail(SSM_E_NULL, "weight is NULL");
+  if (!out) return fail(SSM_E_NULL, "out is NULL");
+  int st = conv_common_checks(batch, dim, seqlen, width, io_dtype);
+  if (st) return st;
+  if (!aligned16(x) || !aligned16(out))
+    return fail(SSM_E_ALIGN, "x and out must be 16-byte aligned");
+  const int64_t es = io_dtype == SSM_DTYPE_BF16 ? 2 : 4;
+  const int64_t seq = batch * dim * seqlen * es, stb = batch * dim * (width - 1) * 4;
+  const Span ins[] = {{x, seq, "x"}, {weight, dim * width * 4, "weight"}, {bias, dim * 4, "bias"},
+                      {state_in, stb, "state_in"}};
+  const Span o{out, seq, "out"}, so{state_out, stb, "state_out"};
+  for (const Span& i : ins) {
+    if (overlaps(o, i)) return fail(SSM_E_ALIAS, "out overlaps %s", i.name);
+    // state_out may be state_in itself (the state is read before it is written)
+    if (i.p != state_in && overlaps(so, i)) return fail(SSM_E_ALIAS, "state_out overlaps %s", i.name);
+  }
+  if (overlaps(o, so)) return fail(SSM_E_ALIAS, "state_out overlaps out");
+  if (state_out && state_in && state_out != state_in && overlaps(so, Span{state_in, stb, ""}))
+    return fail(SSM_E_ALIAS, "state_out partly overlaps state_in");
+  ConvArgs a;
+  memset(&a, 0, sizeof a);
+  a.x = x; a.w = weight; a.bias = bias; a.state_in = state_in; a.out = out;
+  a.rows = batch * dim; a.dim = dim; a.seqlen = seqlen; a.silu = apply_silu ? 1 : 0;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  const bool vec = seqlen % (io_dtype == SSM_DTYPE_BF16 ? 8 : 4) == 0;
+  with_width(width, [&](auto wt) {
+    constexpr int W = decltype(wt)::value;
+    if (io_dtype == SSM_DTYPE_BF16)
+      launch_conv_fwd<uint16_t, W>(a, vec, state_out, s);
+    else
+      launch_conv_fwd<float, W>(a, vec, state_out, s);
+  });
+  return launch_status("ssm_causal_conv1d_fwd launch");
+}
+
+int ssm_causal_conv1d_update(const void* x, float* conv_state, const float* weight,
+                             const float* bias, void* out, int64_t batch, int64_t dim,
+                             int64_t width, int apply_silu, int io_dtype, void* hip_stream) {
+  g_last_error[0] = 0;
+  if (!x) return fail(SSM_E_NULL, "x is NULL");
+  if (!weight) return fail(SSM_E_NULL, "weight is NULL");
+  if (!out) return fail(SSM_E_NULL, "out is NULL");
+  if (!conv_state && width > 1) return fail(SSM_E_NULL, "conv_state is NULL");
+  int st = conv_common_checks(batch, dim, 1, width, io_dtype);
+  if (st) return st;
+  const int64_t es = io_dtype == SSM_DTYPE_BF16 ? 2 : 4;
+  const Span o{out, batch * dim * es, "out"}, cs{conv_state, batch * dim * (width - 1) * 4, "conv_state"};
+  const Span ins[] = {{x, batch * dim * es, "x"}, {weight, dim * width * 4, "weight"},
+                      {bias, dim * 4, "bias"}};
+  for (const Span& i : ins) {
+    if (overlaps(o, i)) return fail(SSM_E_ALIAS, "out overlaps %s", i.name);
+    if (overlaps(cs, i)) return fail(SSM_E_ALIAS, "conv_state overlaps %s", i.name);
+  }
+  if (overlaps(o, cs)) return fail(SSM_E_ALIAS, "out overlaps conv_state");
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  const int64_t rows = batch * dim;
+  const dim3 grid((unsigned)((rows + 255) / 256));
+  with_width(width, [&](auto wt) {
+    constexpr int W = decltype(wt)::value;
+    if (io_dtype == SSM_DTYPE_BF16)
+      hipLaunchKernelGGL((conv1d_update_kernel<uint16_t, W>), grid, dim3(256), 0, s, x,
+                         conv_state, weight, bias, out, rows, dim, apply_silu ? 1 : 0);
+    else
+      hipLaunchKernelGGL((conv1d_update_kernel<float, W>), grid, dim3(256), 0, s, x, conv_state,
+                         weight, bias, out, rows, dim, apply_silu ? 1 : 0);
+  });
+  return launch_status("ssm_causal_conv1d_update launch");
+}
+
+int ssm_causal_conv1d_bwd(const void* x, const float* weight, const float* bias,
+                          const float* state_in, const void* dout, void* dx, float* dweight,
+                          float* dbias, float* dstate_in, int64_t batch, int64_t dim,
+                          int64_t seqlen, int64_t width, int apply_silu, int io_dtype,
+                          void* hip_stream) {
+  g_last_error[0] = 0;
+  if (!x) return fail(SSM_E_NULL, "x is NULL");
+  if (!weight) return fail(SSM_E_NULL, "weight is NULL");
+  if (!dout) return fail(SSM_E_NULL, "dout is NULL");
+  if (!dx) return fail(SSM_E_NULL, "dx is NULL");
+  if (!dweight) return fail(SSM_E_NULL, "dweight is NULL");
+  int st = conv_common_checks(batch, dim, seqlen, width, io_dtype);
+  if (st) return st;
+  if (!aligned16(x) || !aligned16(dout) || !aligned16(dx))
+    return fail(SSM_E_ALIGN, "x, dout and dx must be 16-byte aligned");
+  const int64_t es = io_dtype == SSM_DTYPE_BF16 ? 2 : 4;
+  const int64_t seq = batch * dim * seqlen * es, stb = batch * dim * (width - 1) * 4;
+  const Span ins[] = {{x, seq, "x"}, {weight, dim * width * 4, "weight"}, {bias, dim * 4, "bias"},
+                      {state_in, stb, "state_in"}, {dout, seq, "dout"}};
+  const Span outs[] = {{dx, seq, "dx"}, {dweight, dim * width * 4, "dweight"},
+                       {dbias, dim * 4, "dbias"}, {dstate_in, stb, "dstate_in"}};
+  for (const Span& o : outs) {
+    for (const Span& i : ins)
+      if (overlaps(o, i)) return fail(SSM_E_ALIAS, "%s overlaps %s", o.name, i.name);
+    for (const Span& o2 : outs)
+      if (&o2 != &o && overlaps(o, o2)) return fail(SSM_E_ALIAS, "%s overlaps %s", o.name, o2.name);
+  }
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  zero_fill(dweight, dim * width, s);
+  zero_fill(dbias, dim, s);
+  ConvArgs a;
+  memset(&a, 0, sizeof a);
+  a.x = x; a.w = weight; a.bias = bias; a.state_in = state_in; a.dout = dout; a.dx = dx;
+  a.dw = dweight; a.dbias = dbias; a.dstate_in = dstate_in;
+  a.rows = batch * dim; a.dim = dim; a.seqlen = seqlen; a.silu = apply_silu ? 1 : 0;
+  const bool vec = seqlen % (io_dtype == SSM_DTYPE_BF16 ? 8 : 4) == 0;
+  with_width(width, [&](auto wt) {
+    constexpr int W = decltype(wt)::value;
+    if (io_dtype == SSM_DTYPE_BF16)
+      launch_conv_bwd<uint16_t, W>(a, vec, s);
+    else
+      launch_conv_bwd<float, W>(a, vec, s);
+  });
+  return launch_status("ssm_causal_conv1d_bwd launch");
 }
 
 }  // extern "C"

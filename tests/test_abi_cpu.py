@@ -152,3 +152,51 @@ def test_bwd_validation(lib, over, status):
     assert lib.ssm_selective_scan_bwd(*bwd_args(**over)) == status
     import selective_state_space_43_amd as ssm
     assert ssm.ssm_last_error() != ""
+
+
+def conv_args(**over):
+    a = dict(x=1 * P, w=2 * P, bias=None, st_in=None, out=3 * P, st_out=None, batch=2, dim=8,
+             L=16, W=4, silu=1, io=1, stream=None)
+    a.update(over)
+    return [a[k] for k in ("x", "w", "bias", "st_in", "out", "st_out", "batch", "dim", "L", "W",
+                           "silu", "io", "stream")]
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(x=None), 1), (dict(w=None), 1), (dict(out=None), 1),
+    (dict(L=0), 2), (dict(dim=-3), 2),
+    (dict(io=4), 3),
+    (dict(x=1 * P + 2), 4), (dict(out=3 * P + 8), 4),
+    (dict(out=1 * P), 5), (dict(out=2 * P), 5), (dict(st_out=1 * P), 5),
+    (dict(st_in=4 * P, st_out=4 * P + 4), 5),
+    (dict(W=0), 6), (dict(W=5), 6),
+])
+def test_conv1d_fwd_validation(lib, over, status):
+    assert lib.ssm_causal_conv1d_fwd(*conv_args(**over)) == status
+
+
+def test_conv1d_fwd_state_out_may_be_state_in(lib):
+    # validation passes (a GPU call would follow): only checked up to the launch here
+    import selective_state_space_43_amd as ssm
+    st = lib.ssm_causal_conv1d_fwd(*conv_args(st_in=4 * P, st_out=4 * P, batch=0))
+    assert st == 2 and "batch" in ssm.ssm_last_error()
+
+
+def test_conv1d_update_and_bwd_validation(lib):
+    up = lib.ssm_causal_conv1d_update
+    assert up(None, 2 * P, 3 * P, None, 4 * P, 2, 8, 4, 1, 1, None) == 1
+    assert up(1 * P, None, 3 * P, None, 4 * P, 2, 8, 4, 1, 1, None) == 1
+    assert up(1 * P, 2 * P, 3 * P, None, 4 * P, 2, 8, 7, 1, 1, None) == 6
+    assert up(1 * P, 2 * P, 3 * P, None, 1 * P, 2, 8, 4, 1, 1, None) == 5
+    bwd = lib.ssm_causal_conv1d_bwd
+    args = [1 * P, 2 * P, None, None, 3 * P, 4 * P, 5 * P, None, None, 2, 8, 16, 4, 1, 1, None]
+    for i in (0, 1, 4, 5, 6):
+        a = list(args)
+        a[i] = None
+        assert bwd(*a) == 1, i
+    a = list(args)
+    a[5] = 3 * P  # dx overlaps dout
+    assert bwd(*a) == 5
+    a = list(args)
+    a[12] = 9
+    assert bwd(*a) == 6

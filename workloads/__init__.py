@@ -40,6 +40,7 @@ import numpy as np
 
 # tensor ids used in the per-row stream keys
 T_U, T_DELTA, T_Z, T_B, T_C, T_A, T_D, T_BIAS, T_STATE, T_DY, T_DFINAL = range(11)
+T_CX, T_CW, T_CB, T_CSTATE, T_CDOUT = range(11, 16)
 
 
 @dataclass(frozen=True)
@@ -197,6 +198,29 @@ def grad_inputs(w: Workload, seed=None):
     _normal_rows(seed, T_DFINAL, 0, dfinal, 0.0, 1.0, "f32")
     return dict(dy=seq_tensor(w, T_DY, 0.0, 1.0, seed),
                 dfinal=dfinal.reshape(w.batch, w.dim, w.dstate))
+
+
+def conv_inputs(w: Workload, width=4, seed=None):
+    """Inputs of the causal conv1d in front of the scan, at the workload's
+    [batch, dim, L] shape: x ~ N(0,1) and dout ~ N(0,1) in the storage dtype;
+    weight ~ U(-1/sqrt(W), 1/sqrt(W)) and bias ~ U(-1/sqrt(W), 1/sqrt(W))
+    float32 (the default init of a depthwise Conv1d, fan-in W); state_in
+    [batch, dim, W-1] ~ N(0,1) float32."""
+    seed = w.seed if seed is None else seed
+    rows = w.batch * w.dim
+    np_dtype = np.uint16 if w.dtype == "bf16" else np.float32
+    x = np.empty((rows, w.seqlen), dtype=np_dtype)
+    _normal_rows(seed, T_CX, 0, x, 0.0, 1.0, w.dtype)
+    dout = np.empty((rows, w.seqlen), dtype=np_dtype)
+    _normal_rows(seed, T_CDOUT, 0, dout, 0.0, 1.0, w.dtype)
+    bound = 1.0 / np.sqrt(width)
+    weight = rng(seed, T_CW, 0).uniform(-bound, bound, (w.dim, width)).astype(np.float32)
+    bias = rng(seed, T_CB, 0).uniform(-bound, bound, w.dim).astype(np.float32)
+    state = np.empty((rows, max(width - 1, 1)), dtype=np.float32)
+    _normal_rows(seed, T_CSTATE, 0, state, 0.0, 1.0, "f32")
+    return dict(x=x.reshape(w.batch, w.dim, w.seqlen), weight=weight, bias=bias,
+                state_in=state[:, :width - 1].reshape(w.batch, w.dim, width - 1).copy(),
+                dout=dout.reshape(w.batch, w.dim, w.seqlen))
 
 
 def decode_state(w: Workload, seed=None) -> np.ndarray:
