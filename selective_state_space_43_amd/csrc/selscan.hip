@@ -1138,6 +1138,53 @@ __device__ __forceinline__ void conv_store_run(void* p, int64_t base, int64_t t0
   }
 }
 
+// Loads of one thread's run and of the wave's halo, issued without waiting:
+// addresses are clamped into bounds and out-of-range values are replaced
+// only after the loads (a branch around a load would wait for it at once).
+template <typename IO, int W, bool VEC>
+struct ConvRun {
+  static constexpr int V = Io<IO>::V, H = W - 1;
+  using Raw = typename std::conditional<std::is_same<IO, float>::value, float4, uint4>::type;
+  Raw raw;
+  float hx[H > 0 ? H : 1], hs[H > 0 ? H : 1];
+  __device__ void load(const ConvArgs& a, const void* p, int64_t r, int64_t base, int64_t t0,
+                       bool first_lane, bool want_halo) {
+    const int64_t L = a.seqlen;
+    if constexpr (VEC) {
+      const int64_t tc = t0 < L ? t0 : L - V;  // L is a multiple of V here
+      raw = *reinterpret_cast<const Raw*>(static_cast<const IO*>(p) + base + tc);
+    }
+    if (want_halo && first_lane) {
+#pragma unroll
+      for (int j = 0; j < H; ++j) {
+        const int64_t t = t0 - H + j;
+        hx[j] = Io<IO>::ld1(p, base + (t > 0 ? t : 0));
+        const int64_t si = H + t < 0 ? 0 : (H + t > H - 1 ? H - 1 : H + t);
+        hs[j] = a.state_in ? a.state_in[r * H + si] : 0.0f;
+      }
+    }
+  }
+  // the run's V values, zero past L
+  __device__ void values(const void* p, int64_t base, int64_t t0, int64_t L, float* v) const {
+    if constexpr (VEC) {
+      float u[V];
+      if constexpr (std::is_same<IO, float>::value) {
+        u[0] = raw.x; u[1] = raw.y; u[2] = raw.z; u[3] = raw.w;
+      } else {
+        u[0] = bf_lo(raw.x); u[1] = bf_hi(raw.x); u[2] = bf_lo(raw.y); u[3] = bf_hi(raw.y);
+        u[4] = bf_lo(raw.z); u[5] = bf_hi(raw.z); u[6] = bf_lo(raw.w); u[7] = bf_hi(raw.w);
+      }
+#pragma unroll
+      for (int i = 0; i < V; ++i) v[i] = t0 < L ? u[i] : 0.0f;
+    } else {
+#pragma unroll
+      for (int i = 0; i < V; ++i) v[i] = t0 + i < L ? Io<IO>::ld1(p, base + t0 + i) : 0.0f;
+    }
+  }
+  // input before the run at position j of the halo (first lane of a wave)
+  __device__ float halo(int64_t t0, int j) const { return t0 - H + j >= 0 ? hx[j] : hs[j]; }
+};
+
 template <typename IO, int W, bool VEC>
 __global__ void __launch_bounds__(256) conv1d_fwd_kernel(const ConvArgs a) {
   constexpr int V = Io<IO>::V, H = W - 1;
@@ -1146,18 +1193,19 @@ __global__ void __launch_bounds__(256) conv1d_fwd_kernel(const ConvArgs a) {
   const int64_t t0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * V;
   for (int64_t r = blockIdx.y; r < a.rows; r += gridDim.y) {
     const int64_t d = r % a.dim, base = r * L;
-    float xe[H + V];  // the H inputs before this run, then the run
-    conv_load_run<IO, VEC>(a.x, base, t0, L, xe + H);
-#pragma unroll
-    for (int j = 0; j < H; ++j) xe[j] = wave_dpp<kWaveShr1>(xe[V + j]);
-    if (lane == 0) {
-#pragma unroll
-      for (int j = 0; j < H; ++j) xe[j] = conv_x_at<IO, W>(a, r, t0 - H + j);
-    }
     float wk[W];
 #pragma unroll
     for (int k = 0; k < W; ++k) wk[k] = a.w[d * W + k];
     const float b = a.bias ? a.bias[d] : 0.0f;
+    ConvRun<IO, W, VEC> run;
+    run.load(a, a.x, r, base, t0, lane == 0, true);
+    float xe[H + V];  // the H inputs before this run, then the run
+    run.values(a.x, base, t0, L, xe + H);
+#pragma unroll
+    for (int j = 0; j < H; ++j) {
+      xe[j] = wave_dpp<kWaveShr1>(xe[V + j]);
+      if (lane == 0) xe[j] = run.halo(t0, j);
+    }
     float o[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) {
@@ -1225,26 +1273,35 @@ __global__ void __launch_bounds__(256) conv1d_bwd_kernel(const ConvArgs a) {
 #pragma unroll
     for (int k = 0; k < W; ++k) wk[k] = a.w[d * W + k];
     const float b = a.bias ? a.bias[d] : 0.0f;
-    // inputs t0-H .. t0+V+H-1 and output gradients t0 .. t0+V+H-1
+    // inputs t0-H .. t0+V+H-1 and output gradients t0 .. t0+V+H-1; all loads
+    // are issued before the first wait (clamped addresses, values fixed up
+    // afterwards)
+    ConvRun<IO, W, VEC> rx, rg;
+    rx.load(a, a.x, r, base, t0, lane == 0, true);
+    rg.load(a, a.dout, r, base, t0, false, false);
+    float ax[H > 0 ? H : 1], ag[H > 0 ? H : 1];
+    if (lane == 63) {
+#pragma unroll
+      for (int j = 0; j < H; ++j) {
+        const int64_t t = t0 + V + j;
+        const int64_t tc = t < L ? t : L - 1;
+        ax[j] = Io<IO>::ld1(a.x, base + tc);
+        ag[j] = Io<IO>::ld1(a.dout, base + tc);
+      }
+    }
     float xe[H + V + H], ge[V + H];
-    conv_load_run<IO, VEC>(a.x, base, t0, L, xe + H);
-    conv_load_run<IO, VEC>(a.dout, base, t0, L, ge);
+    rx.values(a.x, base, t0, L, xe + H);
+    rg.values(a.dout, base, t0, L, ge);
 #pragma unroll
     for (int j = 0; j < H; ++j) {
       xe[j] = wave_dpp<kWaveShr1>(xe[V + j]);
       xe[H + V + j] = wave_dpp<kWaveShl1>(xe[H + j]);
       ge[V + j] = wave_dpp<kWaveShl1>(ge[j]);
-    }
-    if (lane == 0) {
-#pragma unroll
-      for (int j = 0; j < H; ++j) xe[j] = conv_x_at<IO, W>(a, r, t0 - H + j);
-    }
-    if (lane == 63) {
-#pragma unroll
-      for (int j = 0; j < H; ++j) {
-        const int64_t t = t0 + V + j;
-        xe[H + V + j] = t < L ? Io<IO>::ld1(a.x, base + t) : 0.0f;
-        ge[V + j] = t < L ? Io<IO>::ld1(a.dout, base + t) : 0.0f;
+      if (lane == 0) xe[j] = rx.halo(t0, j);
+      if (lane == 63) {
+        const bool in = t0 + V + j < L;
+        xe[H + V + j] = in ? ax[j] : 0.0f;
+        ge[V + j] = in ? ag[j] : 0.0f;
       }
     }
     // g for steps t0 .. t0+V+H-1 (zero past L, where dout is zero)
