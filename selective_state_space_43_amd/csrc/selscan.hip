@@ -1084,6 +1084,10 @@ __global__ void __launch_bounds__(256) store_io_kernel(const float* src, void* d
 // W-1 inputs before its vector come from the neighbouring lane by a DPP
 // wave shift, the first lane of each wave loads them itself.
 
+#ifndef SELSCAN_CONV_BWD_VPW
+#define SELSCAN_CONV_BWD_VPW 4  // spans of 256 runs per workgroup in the conv1d backward
+#endif
+
 struct ConvArgs {
   const void* x;
   const float* w;       // [dim, W]
@@ -1266,83 +1270,87 @@ __global__ void __launch_bounds__(256) conv1d_bwd_kernel(const ConvArgs a) {
   __shared__ float sRed[4][W + 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t L = a.seqlen;
-  const int64_t t0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * V;
   for (int64_t r = blockIdx.y; r < a.rows; r += gridDim.y) {
     const int64_t d = r % a.dim, base = r * L;
     float wk[W];
 #pragma unroll
     for (int k = 0; k < W; ++k) wk[k] = a.w[d * W + k];
     const float b = a.bias ? a.bias[d] : 0.0f;
-    // inputs t0-H .. t0+V+H-1 and output gradients t0 .. t0+V+H-1; all loads
-    // are issued before the first wait (clamped addresses, values fixed up
-    // afterwards)
-    ConvRun<IO, W, VEC> rx, rg;
-    rx.load(a, a.x, r, base, t0, lane == 0, true);
-    rg.load(a, a.dout, r, base, t0, false, false);
-    float ax[H > 0 ? H : 1], ag[H > 0 ? H : 1];
-    if (lane == 63) {
-#pragma unroll
-      for (int j = 0; j < H; ++j) {
-        const int64_t t = t0 + V + j;
-        const int64_t tc = t < L ? t : L - 1;
-        ax[j] = Io<IO>::ld1(a.x, base + tc);
-        ag[j] = Io<IO>::ld1(a.dout, base + tc);
-      }
-    }
-    float xe[H + V + H], ge[V + H];
-    rx.values(a.x, base, t0, L, xe + H);
-    rg.values(a.dout, base, t0, L, ge);
-#pragma unroll
-    for (int j = 0; j < H; ++j) {
-      xe[j] = wave_dpp<kWaveShr1>(xe[V + j]);
-      xe[H + V + j] = wave_dpp<kWaveShl1>(xe[H + j]);
-      ge[V + j] = wave_dpp<kWaveShl1>(ge[j]);
-      if (lane == 0) xe[j] = rx.halo(t0, j);
-      if (lane == 63) {
-        const bool in = t0 + V + j < L;
-        xe[H + V + j] = in ? ax[j] : 0.0f;
-        ge[V + j] = in ? ag[j] : 0.0f;
-      }
-    }
-    // g for steps t0 .. t0+V+H-1 (zero past L, where dout is zero)
-#pragma unroll
-    for (int i = 0; i < V + H; ++i) {
-      float pre = b;
-#pragma unroll
-      for (int k = 0; k < W; ++k) pre = fmaf(wk[k], xe[i + k], pre);
-      if (a.silu) {
-        const float s = rcp(1.0f + ex2(-pre * kLog2e));
-        ge[i] *= s * fmaf(pre, 1.0f - s, 1.0f);
-      }
-    }
     float dwp[W + 1];
 #pragma unroll
     for (int k = 0; k <= W; ++k) dwp[k] = 0.0f;
-    float dxo[V];
+    // the workgroup walks SELSCAN_CONV_BWD_VPW spans of 256 runs of the row
+    for (int it = 0; it < SELSCAN_CONV_BWD_VPW; ++it) {
+      const int64_t t0 = (((int64_t)blockIdx.x * SELSCAN_CONV_BWD_VPW + it) * 256 + threadIdx.x) * V;
+      if (t0 - threadIdx.x * V >= L) break;  // workgroup-uniform
+      // inputs t0-H .. t0+V+H-1 and output gradients t0 .. t0+V+H-1; all loads
+      // are issued before the first wait (clamped addresses, values fixed up
+      // afterwards)
+      ConvRun<IO, W, VEC> rx, rg;
+      rx.load(a, a.x, r, base, t0, lane == 0, true);
+      rg.load(a, a.dout, r, base, t0, false, false);
+      float ax[H > 0 ? H : 1], ag[H > 0 ? H : 1];
+      if (lane == 63) {
 #pragma unroll
-    for (int i = 0; i < V; ++i) {
-      // own outputs feed dw, dbias
+        for (int j = 0; j < H; ++j) {
+          const int64_t t = t0 + V + j;
+          const int64_t tc = t < L ? t : L - 1;
+          ax[j] = Io<IO>::ld1(a.x, base + tc);
+          ag[j] = Io<IO>::ld1(a.dout, base + tc);
+        }
+      }
+      float xe[H + V + H], ge[V + H];
+      rx.values(a.x, base, t0, L, xe + H);
+      rg.values(a.dout, base, t0, L, ge);
 #pragma unroll
-      for (int k = 0; k < W; ++k) dwp[k] = fmaf(ge[i], xe[i + k], dwp[k]);
-      dwp[W] += ge[i];
-      // input t0+i feeds outputs t0+i+H-k
-      float acc = 0.0f;
+      for (int j = 0; j < H; ++j) {
+        xe[j] = wave_dpp<kWaveShr1>(xe[V + j]);
+        xe[H + V + j] = wave_dpp<kWaveShl1>(xe[H + j]);
+        ge[V + j] = wave_dpp<kWaveShl1>(ge[j]);
+        if (lane == 0) xe[j] = rx.halo(t0, j);
+        if (lane == 63) {
+          const bool in = t0 + V + j < L;
+          xe[H + V + j] = in ? ax[j] : 0.0f;
+          ge[V + j] = in ? ag[j] : 0.0f;
+        }
+      }
+      // g for steps t0 .. t0+V+H-1 (zero past L, where dout is zero)
 #pragma unroll
-      for (int k = 0; k < W; ++k) acc = fmaf(wk[k], ge[i + H - k], acc);
-      dxo[i] = acc;
-    }
-    if (t0 < L) conv_store_run<IO, VEC>(a.dx, base, t0, L, dxo);
-    // the carried inputs before t = 0 feed outputs 0 .. H-1 (first thread of the row)
-    if (t0 == 0 && a.dstate_in) {
+      for (int i = 0; i < V + H; ++i) {
+        float pre = b;
 #pragma unroll
-      for (int j = 0; j < H; ++j) {  // input at time j - H
+        for (int k = 0; k < W; ++k) pre = fmaf(wk[k], xe[i + k], pre);
+        if (a.silu) {
+          const float s = rcp(1.0f + ex2(-pre * kLog2e));
+          ge[i] *= s * fmaf(pre, 1.0f - s, 1.0f);
+        }
+      }
+      float dxo[V];
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        // own outputs feed dw, dbias
+#pragma unroll
+        for (int k = 0; k < W; ++k) dwp[k] = fmaf(ge[i], xe[i + k], dwp[k]);
+        dwp[W] += ge[i];
+        // input t0+i feeds outputs t0+i+H-k
         float acc = 0.0f;
 #pragma unroll
-        for (int k = 0; k < W; ++k) {
-          const int t = j - k;  // output index j - H + H - k
-          if (t >= 0) acc = fmaf(wk[k], ge[t], acc);
+        for (int k = 0; k < W; ++k) acc = fmaf(wk[k], ge[i + H - k], acc);
+        dxo[i] = acc;
+      }
+      if (t0 < L) conv_store_run<IO, VEC>(a.dx, base, t0, L, dxo);
+      // the carried inputs before t = 0 feed outputs 0 .. H-1 (first thread of the row)
+      if (t0 == 0 && a.dstate_in) {
+#pragma unroll
+        for (int j = 0; j < H; ++j) {  // input at time j - H
+          float acc = 0.0f;
+#pragma unroll
+          for (int k = 0; k < W; ++k) {
+            const int t = j - k;  // output index j - H + H - k
+            if (t >= 0) acc = fmaf(wk[k], ge[t], acc);
+          }
+          a.dstate_in[r * H + j] = acc;
         }
-        a.dstate_in[r * H + j] = acc;
       }
     }
     // workgroup sums of dw and dbias
@@ -1666,9 +1674,9 @@ void launch_conv_fwd(const ConvArgs& a, bool vec, float* state_out, hipStream_t 
 
 template <typename IO, int W>
 void launch_conv_bwd(const ConvArgs& a, bool vec, hipStream_t s) {
-  constexpr int V = Io<IO>::V;
+  constexpr int V = Io<IO>::V, SPAN = 256 * SELSCAN_CONV_BWD_VPW;
   const int64_t nvec = (a.seqlen + V - 1) / V;
-  const dim3 grid((unsigned)((nvec + 255) / 256), (unsigned)(a.rows < 65535 ? a.rows : 65535));
+  const dim3 grid((unsigned)((nvec + SPAN - 1) / SPAN), (unsigned)(a.rows < 65535 ? a.rows : 65535));
   if (vec)
     hipLaunchKernelGGL((conv1d_bwd_kernel<IO, W, true>), grid, dim3(256), 0, s, a);
   else
