@@ -15,7 +15,8 @@ Each function cites the page passage it follows in ``ssm_oracle.c``.
 Parity status: every function here is pinned by ``tests/test_oracle_pins.py`` (forward,
 decode, LTI), ``tests/test_oracle_bwd_pins.py`` (backward, by finite differences) and
 ``tests/test_oracle_conv_pins.py`` (causal conv1d: torch's conv1d, closed forms, finite
-differences).
+differences) and ``tests/test_oracle_ssd_pins.py`` (Mamba-2 scan: the diagonal scan with a
+per-head A, the masked-attention form, brute force).
 """
 from __future__ import annotations
 
@@ -62,12 +63,14 @@ def _lib():
         lib.ssm_oracle_selective_scan_bwd.argtypes = [
             i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp,
             i64, i64, i64, i64, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32]
+        lib.ssm_oracle_ssd.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp,
+                                       i64, i64, i64, i64, i64, i64, vp, vp, i32]
         lib.ssm_oracle_conv1d.argtypes = [i32, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp, vp]
         lib.ssm_oracle_conv1d_bwd.argtypes = [i32, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32,
                                               vp, vp, vp, vp]
         for f in (lib.ssm_oracle_selective_scan, lib.ssm_oracle_state_update,
                   lib.ssm_oracle_lti_kernel, lib.ssm_oracle_causal_conv,
-                  lib.ssm_oracle_selective_scan_bwd, lib.ssm_oracle_conv1d,
+                  lib.ssm_oracle_selective_scan_bwd, lib.ssm_oracle_conv1d, lib.ssm_oracle_ssd,
                   lib.ssm_oracle_conv1d_bwd):
             f.restype = i32
         _LIB = lib
@@ -286,3 +289,31 @@ def conv1d_bwd(x, w, dout, bias=None, state_in=None, silu=True):
     if rc != 0:
         raise RuntimeError(f"ssm_oracle_conv1d_bwd failed ({rc})")
     return g
+
+
+def ssd(x, dt, A, B, C, nheads, ngroups, D=None, z=None, dt_bias=None, dt_softplus=True, h0=None,
+        n_threads=None):
+    """Mamba-2 scan (scalar A per head) in fp64.  x, z: [batch, nheads*headdim, L];
+    dt: [batch, nheads, L]; B, C: [batch, ngroups*dstate, L] (float32, bf16 bits
+    or float64, one dtype); A, D, dt_bias: [nheads]; h0: [batch, nheads, headdim,
+    dstate].  Returns (y float64 [batch, nheads*headdim, L], final_state float64
+    [batch, nheads, headdim, dstate])."""
+    x, dtc = _seq(x, "x")
+    dt, _ = _seq(dt, "dt")
+    B, _ = _seq(B, "B")
+    C, _ = _seq(C, "C")
+    if z is not None:
+        z, _ = _seq(z, "z")
+    batch, HP, L = x.shape
+    P = HP // nheads
+    N = B.shape[1] // ngroups
+    A64, D64, b64, h064 = _f64(A), _f64(D), _f64(dt_bias), _f64(h0)
+    y = np.empty((batch, HP, L), dtype=np.float64)
+    fs = np.empty((batch, nheads, P, N), dtype=np.float64)
+    rc = _lib().ssm_oracle_ssd(dtc, _ptr(x), _ptr(dt), _ptr(B), _ptr(C), _ptr(z), _ptr(A64),
+                               _ptr(D64), _ptr(b64), int(bool(dt_softplus)), _ptr(h064), batch, L,
+                               nheads, P, ngroups, N, _ptr(y), _ptr(fs),
+                               int(n_threads or default_threads()))
+    if rc != 0:
+        raise RuntimeError(f"ssm_oracle_ssd failed ({rc})")
+    return y, fs

@@ -609,3 +609,110 @@ int ssm_oracle_conv1d_bwd(int io_dtype, const void* x, const double* w, const do
   free(g);
   return 0;
 }
+
+/*
+ * Mamba-2 selective scan with a scalar A per head ("State-space models",
+ * section "The parallel scan", last sentences: A restricted to a scalar times
+ * the identity per head; "Structured State Space Models and Mamba ...",
+ * section "State Space Duality and Mamba-2").  Per sequence b, head h, head
+ * channel p and state n, with group g = h / (nheads / ngroups):
+ *
+ *   dt_t      = softplus(dt_raw_t + dt_bias_h)   (or dt_raw_t + dt_bias_h)
+ *   h_t[p,n]  = exp(dt_t A_h) h_{t-1}[p,n] + dt_t B_t[g,n] x_t[h,p]
+ *   y_t[h,p]  = sum_n C_t[g,n] h_t[p,n] + D_h x_t[h,p],   then * silu(z) if z
+ *
+ * Layouts (channel-major, as for the diagonal scan): x, z [batch, nheads *
+ * headdim, L]; dt [batch, nheads, L]; B, C [batch, ngroups * dstate, L];
+ * A, D, dt_bias [nheads]; h0 and final_state [batch, nheads, headdim,
+ * dstate].  y is double [batch, nheads * headdim, L].  Threads split
+ * (b, h) pairs.
+ */
+typedef struct {
+  int io_dtype;
+  const void *x, *dt, *Bm, *Cm, *z;
+  const double *A, *Dskip, *dt_bias, *h0;
+  int softplus;
+  int64_t batch, L, H, P, G, N;
+  double *y, *final_state;
+  int64_t next;
+  pthread_mutex_t lock;
+} or_ssd_job;
+
+static void or_ssd_one(const or_ssd_job* j, int64_t bh, double* st) {
+  const int64_t b = bh / j->H, h = bh % j->H, L = j->L, P = j->P, N = j->N;
+  const int64_t g = h / (j->H / j->G);
+  for (int64_t i = 0; i < P * N; ++i) st[i] = j->h0 ? j->h0[bh * P * N + i] : 0.0;
+  const double bias = j->dt_bias ? j->dt_bias[h] : 0.0;
+  const double Dh = j->Dskip ? j->Dskip[h] : 0.0;
+  for (int64_t t = 0; t < L; ++t) {
+    const double raw = or_widen(j->dt, j->io_dtype, (b * j->H + h) * L + t) + bias;
+    const double dt = j->softplus ? or_softplus(raw) : raw;
+    const double a = exp(dt * j->A[h]);
+    for (int64_t p = 0; p < P; ++p) {
+      const int64_t xrow = (b * j->H * P + h * P + p) * L;
+      const double xt = or_widen(j->x, j->io_dtype, xrow + t);
+      double yt = Dh * xt;
+      for (int64_t n = 0; n < N; ++n) {
+        const int64_t bcrow = (b * j->G * N + g * N + n) * L;
+        const double bt = or_widen(j->Bm, j->io_dtype, bcrow + t);
+        const double ct = or_widen(j->Cm, j->io_dtype, bcrow + t);
+        double* s = st + p * N + n;
+        *s = a * *s + dt * bt * xt;
+        yt += ct * *s;
+      }
+      if (j->z) yt *= or_silu(or_widen(j->z, j->io_dtype, xrow + t));
+      j->y[xrow + t] = yt;
+    }
+  }
+  if (j->final_state)
+    for (int64_t i = 0; i < P * N; ++i) j->final_state[bh * P * N + i] = st[i];
+}
+
+static void* or_ssd_worker(void* arg) {
+  or_ssd_job* j = (or_ssd_job*)arg;
+  double* st = (double*)malloc(sizeof(double) * (size_t)(j->P * j->N));
+  if (!st) return (void*)1;
+  for (;;) {
+    pthread_mutex_lock(&j->lock);
+    const int64_t bh = j->next++;
+    pthread_mutex_unlock(&j->lock);
+    if (bh >= j->batch * j->H) break;
+    or_ssd_one(j, bh, st);
+  }
+  free(st);
+  return NULL;
+}
+
+int ssm_oracle_ssd(int io_dtype, const void* x, const void* dt, const void* Bm, const void* Cm,
+                   const void* z, const double* A, const double* Dskip, const double* dt_bias,
+                   int dt_softplus, const double* h0, int64_t batch, int64_t L, int64_t nheads,
+                   int64_t headdim, int64_t ngroups, int64_t dstate, double* y,
+                   double* final_state, int n_threads) {
+  if (!x || !dt || !Bm || !Cm || !A || !y) return 1;
+  if (batch <= 0 || L <= 0 || nheads <= 0 || headdim <= 0 || ngroups <= 0 || dstate <= 0) return 1;
+  if (nheads % ngroups) return 1;
+  if (io_dtype != OR_F32 && io_dtype != OR_BF16 && io_dtype != OR_F64) return 1;
+  or_ssd_job j;
+  memset(&j, 0, sizeof j);
+  j.io_dtype = io_dtype;
+  j.x = x; j.dt = dt; j.Bm = Bm; j.Cm = Cm; j.z = z;
+  j.A = A; j.Dskip = Dskip; j.dt_bias = dt_bias; j.h0 = h0; j.softplus = dt_softplus;
+  j.batch = batch; j.L = L; j.H = nheads; j.P = headdim; j.G = ngroups; j.N = dstate;
+  j.y = y; j.final_state = final_state;
+  pthread_mutex_init(&j.lock, NULL);
+  if (n_threads < 1) n_threads = 1;
+  if (n_threads > 256) n_threads = 256;
+  if ((int64_t)n_threads > batch * nheads) n_threads = (int)(batch * nheads);
+  pthread_t tid[256];
+  int started = 0, rc = 0;
+  for (int i = 1; i < n_threads; ++i)
+    if (pthread_create(&tid[started], NULL, or_ssd_worker, &j) == 0) ++started;
+  if (or_ssd_worker(&j)) rc = 2;
+  for (int i = 0; i < started; ++i) {
+    void* r = NULL;
+    pthread_join(tid[i], &r);
+    if (r) rc = 2;
+  }
+  pthread_mutex_destroy(&j.lock);
+  return rc;
+}
