@@ -9,8 +9,8 @@ arithmetic and state).  Inputs are generated once, uploaded, and resident in
 HBM before timing starts.  The one-token decode step (ssm_state_update) is
 timed separately on the decode workload and reported under "decode", and the
 backward pass (ssm_selective_scan_bwd) on the same workload under "backward",
-and the causal conv1d in front of the scan (forward and backward) under
-"conv1d".
+the causal conv1d in front of the scan (forward and backward) under
+"conv1d", and the Mamba-2 scan (scalar A per head, on MFMA) under "ssd".
 
 Prints one JSON line: the metric (scan elements B*D*L*N per second), the
 roofline of the scan kernel (live HIP-event timing; HBM traffic from the
@@ -248,6 +248,58 @@ def bench_conv(ssm, torch, w, dev, steps, warmup):
     return res
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def bench_ssd(ssm, torch, dev, steps, warmup):
+    """The Mamba-2 scan (scalar A per head, chunks of 64 on MFMA) on the
+    Mamba-2 2.7B layer shape."""
+    w = wl.SSD_WORKLOADS["mamba2_2p7b"]
+    x = wl.ssd_inputs(w)
+    t = {k: to_dev(v, dev) for k, v in x.items() if v is not None}
+    y = torch.empty_like(t["x"])
+    fs = torch.empty((w.batch, w.nheads, w.headdim, w.dstate), dtype=torch.float32, device=dev)
+    ws = torch.empty(ssm.ssm_ssd_workspace_size(w.batch, w.seqlen, w.ngroups, w.dstate),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        ssm.ssm_ssd_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], w.nheads, w.ngroups, D=t["D"],
+                        z=t["z"], dt_bias=t["dt_bias"], dt_softplus=True, y=y, final_state=fs,
+                        workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        step()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    T = 64
+    chunks = -(-w.seqlen // T)
+    # algorithmic FLOPs of the chunked form: per (sequence, head, chunk) M X, C S^T and the
+    # state update; per (sequence, group, chunk) C B^T
+    flops = (w.batch * w.nheads * chunks * (2 * T * T * w.headdim + 4 * T * w.dstate * w.headdim)
+             + w.batch * w.ngroups * chunks * 2 * T * T * w.dstate)
+    gbps = w.io_bytes / (ms * 1e-3) / 1e9
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {
+        "workload": f"{w.name}: batch {w.batch}, L {w.seqlen}, {w.nheads} heads x {w.headdim}, "
+                    f"N {w.dstate}, {w.ngroups} group, bf16, gate",
+        "ms_per_call": round(ms, 4),
+        "elements_per_s": float("%.4g" % (w.elements / (ms * 1e-3))),
+        "algorithmic_bytes": w.io_bytes,
+        "hbm_gbps": round(gbps, 1),
+        "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "algorithmic_tflops": round(tflops, 2),
+        "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "steps": steps,
+    }
+
+
 def cpu_baseline(w, x, seconds_target=12.0):
     """The fp64 oracle on host cores over whole channels of the same inputs:
     as many channels (full length each) as fit the time target."""
@@ -286,6 +338,7 @@ def main(argv=None):
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-backward", action="store_true")
     p.add_argument("--no-conv", action="store_true")
+    p.add_argument("--no-ssd", action="store_true")
     p.add_argument("--backward-steps", type=int, default=5)
     p.add_argument("--copy-check", type=int, default=0, metavar="BYTES",
                    help="also run torch's plain copy of BYTES three times (counter calibration "
@@ -381,6 +434,9 @@ def main(argv=None):
         out["conv1d"] = bench_conv(ssm, torch, w, dev, 10, 2)
         print(f"[bench] conv1d: fwd {out['conv1d']['fwd']['ms']} ms, bwd "
               f"{out['conv1d']['bwd']['ms']} ms", file=sys.stderr, flush=True)
+    if not args.no_ssd:
+        out["ssd"] = bench_ssd(ssm, torch, dev, 10, 2)
+        print(f"[bench] ssd: {out['ssd']['ms_per_call']} ms/call", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, x)
         print(f"[bench] cpu baseline: {out['cpu_baseline']['seconds']}s", file=sys.stderr,

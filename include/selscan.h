@@ -235,6 +235,43 @@ int ssm_causal_conv1d_bwd(const void* x, const float* weight, const float* bias,
                           int64_t seqlen, int64_t width, int apply_silu, int io_dtype,
                           void* hip_stream);
 
+/*
+ * Mamba-2 scan: the selective scan with A restricted to a scalar per head
+ * ("State-space models", section "The parallel scan"; "Structured State
+ * Space Models and Mamba ...", section "State Space Duality and Mamba-2").
+ * Heads of headdim channels share a step dt and a decay A_h; groups of
+ * nheads / ngroups heads share B and C.  Per sequence b, head h, channel p,
+ * state n (g = h / (nheads / ngroups)):
+ *
+ *   dt_t     = softplus(dt_raw_t + dt_bias_h)   (or without the softplus)
+ *   h_t[p,n] = exp(dt_t A_h) h_{t-1}[p,n] + dt_t B_t[g,n] x_t[h,p]
+ *   y_t[h,p] = (sum_n C_t[g,n] h_t[p,n] + D_h x_t[h,p]) * silu(z_t[h,p])
+ *
+ * computed in chunks of 64 steps as block matrix products on MFMA (bf16
+ * operands, float32 accumulation and state).
+ *
+ *  x, z, y      [batch, nheads * headdim, seqlen] bf16 (z may be NULL)
+ *  dt           [batch, nheads, seqlen] bf16, raw step
+ *  Bm, Cm       [batch, ngroups * dstate, seqlen] bf16
+ *  A            [nheads] float32 (negative);  Dskip, dt_bias [nheads] or NULL
+ *  h0           [batch, nheads, headdim, dstate] float32 or NULL (zeros)
+ *  final_state  [batch, nheads, headdim, dstate] float32 or NULL
+ *  workspace    at least ssm_ssd_workspace_size(...) bytes of device memory,
+ *               16-byte aligned, owned by the caller; calls sharing it must
+ *               not run concurrently
+ * io_dtype must be SSM_DTYPE_BF16, headdim 64 and dstate one of 32, 64, 128,
+ * 256 (SSM_E_UNSUPPORTED otherwise); nheads a multiple of ngroups.  Outputs
+ * must not overlap inputs.
+ */
+int ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void* Bm, const void* Cm,
+                const float* Dskip, const void* z, const float* dt_bias, int dt_softplus,
+                const float* h0, void* y, float* final_state, void* workspace,
+                int64_t workspace_bytes, int64_t batch, int64_t seqlen, int64_t nheads,
+                int64_t headdim, int64_t ngroups, int64_t dstate, int io_dtype, void* hip_stream);
+
+/* Bytes of workspace ssm_ssd_fwd needs (-1 if an extent is out of range). */
+int64_t ssm_ssd_workspace_size(int64_t batch, int64_t seqlen, int64_t ngroups, int64_t dstate);
+
 /* Static description of a status code (never NULL). */
 const char* ssm_status_str(int status);
 

@@ -22,6 +22,8 @@ Entry points carry the C names:
   ssm_causal_conv1d_update(x, conv_state, weight, bias=None, silu=True) -> out
   ssm_causal_conv1d_bwd(x, weight, dout, bias=None, state_in=None, silu=True)
       -> dict of gradients
+  ssm_ssd_fwd(x, dt, A, B, C, nheads, ngroups, D=None, z=None, dt_bias=None,
+              dt_softplus=True, h0=None) -> (y, final_state)      (Mamba-2 scan)
 
 Layouts: u, delta, z, y [batch, dim, L]; B, C [batch, dstate, L]; A
 [dim, dstate]; D, delta_bias [dim]; h0 / final_state / state
@@ -34,14 +36,14 @@ from ._lib import (SSM_BBAR_DELTA_B, SSM_BBAR_ZOH_EXACT, SSM_DTYPE_BF16, SSM_DTY
                    SelscanError, library_path, lib, ssm_abi_version, ssm_last_error,
                    ssm_status_str)
 from .binding import (ssm_causal_conv1d_bwd, ssm_causal_conv1d_fwd, ssm_causal_conv1d_update,
-                      ssm_lti_kernel, ssm_selective_scan_bwd,
+                      ssm_lti_kernel, ssm_selective_scan_bwd, ssm_ssd_fwd, ssm_ssd_workspace_size,
                       ssm_selective_scan_bwd_workspace_size, ssm_selective_scan_fwd,
                       ssm_state_update)
 
 __all__ = [
     "ssm_selective_scan_fwd", "ssm_state_update", "ssm_lti_kernel", "ssm_selective_scan_bwd",
     "ssm_selective_scan_bwd_workspace_size", "ssm_causal_conv1d_fwd", "ssm_causal_conv1d_update",
-    "ssm_causal_conv1d_bwd", "ssm_status_str",
+    "ssm_causal_conv1d_bwd", "ssm_ssd_fwd", "ssm_ssd_workspace_size", "ssm_status_str",
     "ssm_last_error", "ssm_abi_version", "SelscanError", "library_path", "lib",
     "SSM_DTYPE_F32", "SSM_DTYPE_BF16", "SSM_BBAR_DELTA_B", "SSM_BBAR_ZOH_EXACT",
 ]

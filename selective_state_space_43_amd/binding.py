@@ -278,3 +278,55 @@ def ssm_causal_conv1d_bwd(x, weight, dout, bias=None, state_in=None, silu=True,
                                          W, int(bool(silu)), _IO[x.dtype], _stream(dev))
     check(st, "ssm_causal_conv1d_bwd")
     return g
+
+
+def ssm_ssd_workspace_size(batch, seqlen, ngroups, dstate):
+    n = lib().ssm_ssd_workspace_size(batch, seqlen, ngroups, dstate)
+    if n < 0:
+        raise ValueError("extents out of range")
+    return int(n)
+
+
+def ssm_ssd_fwd(x, dt, A, B, C, nheads, ngroups, D=None, z=None, dt_bias=None,
+                dt_softplus=True, h0=None, y=None, final_state=None, want_final_state=True,
+                workspace=None):
+    """Mamba-2 scan (scalar A per head); returns (y, final_state or None)."""
+    _dev(x, "x", None)
+    dev = x.device
+    if x.dim() != 3 or x.dtype != torch.bfloat16:
+        raise TypeError("x must be [batch, nheads * headdim, L] bfloat16")
+    batch, hp, L = x.shape
+    if hp % nheads:
+        raise ValueError("x's channel count is not a multiple of nheads")
+    P = hp // nheads
+    if B.dim() != 3 or B.shape[1] % ngroups:
+        raise ValueError("B must be [batch, ngroups * dstate, L]")
+    N = B.shape[1] // ngroups
+    _io(dt, "dt", torch.bfloat16, (batch, nheads, L), dev)
+    _io(B, "B", torch.bfloat16, (batch, ngroups * N, L), dev)
+    _io(C, "C", torch.bfloat16, (batch, ngroups * N, L), dev)
+    _io(A, "A", torch.float32, (nheads,), dev)
+    _f32(D, "D", (nheads,), dev)
+    _f32(dt_bias, "dt_bias", (nheads,), dev)
+    if z is not None:
+        _io(z, "z", torch.bfloat16, (batch, hp, L), dev)
+    _f32(h0, "h0", (batch, nheads, P, N), dev)
+    if y is None:
+        y = torch.empty_like(x)
+    else:
+        _io(y, "y", torch.bfloat16, (batch, hp, L), dev)
+    if final_state is None and want_final_state:
+        final_state = torch.empty((batch, nheads, P, N), dtype=torch.float32, device=dev)
+    elif final_state is not None:
+        _f32(final_state, "final_state", (batch, nheads, P, N), dev)
+    need = ssm_ssd_workspace_size(batch, L, ngroups, N)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        st = lib().ssm_ssd_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                               _ptr(dt_bias), int(bool(dt_softplus)), _ptr(h0), _ptr(y),
+                               _ptr(final_state), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), batch, L, nheads, P,
+                               ngroups, N, SSM_DTYPE_BF16, _stream(dev))
+    check(st, "ssm_ssd_fwd")
+    return y, final_state

@@ -1382,6 +1382,390 @@ __global__ void __launch_bounds__(256) conv1d_bwd_kernel(const ConvArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- Mamba-2 scan (scalar A per head)
+//
+// With A = a_h I per head the scan becomes block matrix products ("State-
+// space models", section "The parallel scan": the restriction of Mamba-2;
+// "Structured State Space Models and Mamba ...", section "State Space Duality
+// and Mamba-2": Y = (L o Q K^T) V with a 1-semiseparable decay L).  Per
+// sequence b, head h and chunk of T = 64 steps, with cs_t the running sum of
+// dt A over the chunk and S the state [headdim x N] entering it:
+//
+//   M[t][s]  = (C_t . B_s) exp(cs_t - cs_s) dt_s     (s <= t, else 0)
+//   Y        = M X + diag(exp(cs)) C S^T + D X       (then * silu(z))
+//   S'       = exp(cs_63) S + sum_s exp(cs_63 - cs_s) dt_s x_s B_s^T
+//
+// C . B^T does not depend on the head, so ssd_prep_kernel computes it once
+// per (sequence, group, chunk) on MFMA, together with a token-major copy of C.
+// ssd_fwd_kernel walks the chunks of one (sequence, head, half of the head
+// channels) in order; the three products per chunk run on
+// v_mfma_f32_16x16x32_bf16 / v_mfma_f32_32x32x16_bf16 with fp32 accumulation,
+// and the state lives in MFMA accumulators for the whole sequence.  Operands
+// that are not bf16 inputs (M, the state, the weighted x) are split into a
+// bf16 head and a bf16 remainder, v = hi + lo, and multiplied twice, which
+// keeps them to about 16 significant bits: a single bf16 rounding of these
+// operands alone costs a few percent of |y| on long sequences.
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4v_t __attribute__((ext_vector_type(4)));
+
+constexpr int kSsdT = 64;   // steps per chunk
+constexpr int kSsdP = 64;   // head channels (headdim)
+constexpr int kSsdPB = 32;  // head channels per workgroup
+
+struct SsdArgs {
+  const void* x;        // [batch, H * 64, L] bf16
+  const void* dt;       // [batch, H, L] bf16, raw
+  const float* A;       // [H]
+  const void* Bm;       // [batch, G * N, L] bf16
+  const void* Cm;
+  const float* Dskip;   // [H] or null
+  const void* z;        // [batch, H * 64, L] or null
+  const float* dt_bias; // [H] or null
+  const float* h0;      // [batch, H, 64, N] or null
+  void* y;
+  float* final_state;   // [batch, H, 64, N] or null
+  uint16_t* Ct;         // workspace: [batch, G, nchunks * 64, N] bf16, C token-major
+  float* Gf;            // workspace: [batch, G, nchunks, 3, 64, 16] C.B^T tiles, MFMA fragment order
+  int64_t batch, L, H, G, N, nchunks;
+  int softplus;
+};
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+__device__ __forceinline__ uint16_t f2bf(float v) { return __builtin_bit_cast(uint16_t, (__bf16)v); }
+
+// v rounded to bf16 and back
+__device__ __forceinline__ float bf16_round(float v) { return (float)(__bf16)v; }
+
+// inclusive prefix sum over the 64 lanes of a wave
+__device__ __forceinline__ float wave_prefix_sum(float v) {
+  v += dpp0<kRowShr1>(v);
+  v += dpp0<kRowShr2>(v);
+  v += dpp0<kRowShr4>(v);
+  v += dpp0<kRowShr8>(v);
+  v += dpp<kRowBcast15, 0xa>(0.0f, v);
+  v += dpp<kRowBcast31, 0xc>(0.0f, v);
+  return v;
+}
+
+// 8 bf16 of a row (length L) from step t on, zero past L; one 16-byte load
+// when the run is whole and aligned (rows of a length that is not a multiple
+// of 8 are read element by element)
+__device__ __forceinline__ uint4 load8_bf16(const uint16_t* rowp, int64_t t, int64_t L) {
+  if (t + 8 <= L && (reinterpret_cast<uintptr_t>(rowp + t) & 15) == 0)
+    return *reinterpret_cast<const uint4*>(rowp + t);
+  uint16_t e[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) e[j] = t + j < L ? rowp[t + j] : (uint16_t)0;
+  uint4 v;
+  __builtin_memcpy(&v, e, 16);
+  return v;
+}
+
+// Per (sequence, group, chunk): token-major C and the three non-zero 32x32
+// tiles of G^T[s][t] = B_s . C_t (s-block <= t-block), stored as each lane's
+// 16 accumulators.
+template <int N>
+__global__ void __launch_bounds__(256) ssd_prep_kernel(const SsdArgs a) {
+  constexpr int T = kSsdT, NP = N + 8;
+  __shared__ __align__(16) uint16_t sBt[T * NP];
+  __shared__ __align__(16) uint16_t sCt[T * NP];
+  const int64_t c = blockIdx.x, g = blockIdx.y, b = blockIdx.z, L = a.L, t0 = c * T;
+  const uint16_t* Bsrc = static_cast<const uint16_t*>(a.Bm) + (b * a.G + g) * N * L;
+  const uint16_t* Csrc = static_cast<const uint16_t*>(a.Cm) + (b * a.G + g) * N * L;
+  for (int item = threadIdx.x; item < 2 * N * (T / 8); item += 256) {
+    const int tensor = item / (N * (T / 8)), r = item % (N * (T / 8));
+    const int n = r / (T / 8), t8 = (r % (T / 8)) * 8;
+    const uint4 v = load8_bf16((tensor ? Csrc : Bsrc) + n * L, t0 + t8, L);
+    uint16_t e[8];
+    __builtin_memcpy(e, &v, 16);
+    uint16_t* dst = tensor ? sCt : sBt;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dst[(t8 + j) * NP + n] = e[j];
+  }
+  __syncthreads();
+  uint16_t* ct = a.Ct + ((b * a.G + g) * a.nchunks * T + t0) * N;
+  for (int item = threadIdx.x; item < T * (N / 8); item += 256) {
+    const int t = item / (N / 8), n8 = (item % (N / 8)) * 8;
+    *reinterpret_cast<uint4*>(ct + t * N + n8) = *reinterpret_cast<const uint4*>(sCt + t * NP + n8);
+  }
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (wave < 3) {
+    const int sb = wave == 2 ? 1 : 0, tb = wave == 0 ? 0 : 1;  // tiles (0,0), (0,1), (1,1)
+    f32x16_t acc = {};
+#pragma unroll
+    for (int k0 = 0; k0 < N; k0 += 16) {
+      const uint4 av = *reinterpret_cast<const uint4*>(sBt + (sb * 32 + lane % 32) * NP + k0 + (lane / 32) * 8);
+      const uint4 bv = *reinterpret_cast<const uint4*>(sCt + (tb * 32 + lane % 32) * NP + k0 + (lane / 32) * 8);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av), as_bf16x8(bv), acc, 0, 0, 0);
+    }
+    float* dst = a.Gf + ((((b * a.G + g) * a.nchunks + c) * 3 + wave) * 64 + lane) * 16;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<float4*>(dst + 4 * q) =
+          make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
+  }
+}
+
+// One workgroup per (sequence, head, half of the 64 head channels); four
+// waves.  Wave w owns output tile columns t in [16w, 16w + 16) (two 16x16
+// tiles of Y^T, one per 16 channels), state n-blocks w, w + 4, ... (32 x 32
+// tiles of S^T), and for w < 3 one 32x32 tile of M.
+template <int N, bool GATE>
+__global__ void __launch_bounds__(256) ssd_fwd_kernel(const SsdArgs a) {
+  constexpr int T = kSsdT, PB = kSsdPB, XP = T + 8, SP = N + 8, MP = T + 8;
+  constexpr int NB = N / 32, NBW = (NB + 3) / 4;  // state n-blocks, per wave
+  __shared__ __align__(16) uint16_t sX[PB * XP];   // x of the chunk, [p][t]
+  __shared__ __align__(16) uint16_t sZ[GATE ? PB * XP : 8];
+  __shared__ __align__(16) uint16_t sY[PB * XP];
+  __shared__ __align__(16) uint16_t sM[T * MP];    // M[t][s], bf16 head
+  __shared__ __align__(16) uint16_t sMl[T * MP];   // and remainder
+  __shared__ __align__(16) uint16_t sS[PB * SP];   // S[p][n] entering the chunk, bf16 head
+  __shared__ __align__(16) uint16_t sSl[PB * SP];  // and remainder
+  __shared__ float sCs[4][T], sDt[4][T];           // per wave: running decay, step
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t h = blockIdx.x >> 1, pb = blockIdx.x & 1, b = blockIdx.y;
+  const int64_t g = h / (a.H / a.G), L = a.L;
+  const float Ah = a.A[h];
+  const float Dh = a.Dskip ? a.Dskip[h] : 0.0f;
+  const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
+  const int64_t row0 = (b * a.H * kSsdP + h * kSsdP + pb * PB) * L;  // this workgroup's first channel row
+  const uint16_t* xg = static_cast<const uint16_t*>(a.x) + row0;
+  const uint16_t* zg = GATE ? static_cast<const uint16_t*>(a.z) + row0 : nullptr;
+  uint16_t* yg = static_cast<uint16_t*>(a.y) + row0;
+  const uint16_t* dtg = static_cast<const uint16_t*>(a.dt) + (b * a.H + h) * L;
+  const uint16_t* Bg = static_cast<const uint16_t*>(a.Bm) + (b * a.G + g) * N * L;
+  const uint16_t* Ctg = a.Ct + (b * a.G + g) * a.nchunks * T * N;
+  const float* Gg = a.Gf + (b * a.G + g) * a.nchunks * 3 * 64 * 16;
+  const int64_t st0 = ((b * a.H + h) * kSsdP + pb * PB) * N;  // state rows of this workgroup
+
+  // ---- state: S^T tiles in accumulators; lane: p = lane % 32, n = nb*32 + row(i)
+  f32x16_t S[NBW];
+#pragma unroll
+  for (int q = 0; q < NBW; ++q) {
+    const int nb = wave + 4 * q;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int n = nb * 32 + (i / 4) * 8 + (lane / 32) * 4 + i % 4;
+      S[q][i] = (a.h0 && nb < NB) ? a.h0[st0 + (lane % 32) * N + n] : 0.0f;
+    }
+  }
+  auto write_state_bf16 = [&]() {
+#pragma unroll
+    for (int q = 0; q < NBW; ++q) {
+      const int nb = wave + 4 * q;
+      if (nb < NB) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int n = nb * 32 + r * 8 + (lane / 32) * 4;
+          float hv[4], lv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            hv[e] = bf16_round(S[q][4 * r + e]);
+            lv[e] = S[q][4 * r + e] - hv[e];
+          }
+          uint2 v, w;
+          v.x = pack_bf16x2(hv[0], hv[1]);
+          v.y = pack_bf16x2(hv[2], hv[3]);
+          w.x = pack_bf16x2(lv[0], lv[1]);
+          w.y = pack_bf16x2(lv[2], lv[3]);
+          *reinterpret_cast<uint2*>(sS + (lane % 32) * SP + n) = v;
+          *reinterpret_cast<uint2*>(sSl + (lane % 32) * SP + n) = w;
+        }
+      }
+    }
+  };
+  write_state_bf16();
+
+  // ---- per-chunk operands, loaded one chunk ahead
+  const int xp = threadIdx.x / 8, xt8 = (threadIdx.x % 8) * 8;  // staging: channel row, 8 steps
+  struct Pre {
+    uint4 xv, zv;
+    uint16_t dtr;
+    f32x16_t gfr;
+    uint4 ct[N / 32];      // C^T fragments of this wave's t columns
+    uint4 bt[NBW][4];      // B^T fragments of this wave's state n-blocks
+  };
+  Pre nx;
+  auto fetch = [&](int64_t c) {
+    const int64_t t0 = c * T;
+    nx.xv = load8_bf16(xg + xp * L, t0 + xt8, L);
+    if constexpr (GATE) nx.zv = load8_bf16(zg + xp * L, t0 + xt8, L);
+    nx.dtr = t0 + lane < L ? dtg[t0 + lane] : (uint16_t)0;
+    if (wave < 3) {
+      const float* gp = Gg + ((c * 3 + wave) * 64 + lane) * 16;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 v = *reinterpret_cast<const float4*>(gp + 4 * q);
+        nx.gfr[4 * q] = v.x; nx.gfr[4 * q + 1] = v.y; nx.gfr[4 * q + 2] = v.z; nx.gfr[4 * q + 3] = v.w;
+      }
+    }
+    // 16x16x32 B operand: lane holds C^T[n = k0 + (lane/16)*8 + j][t = 16 wave + lane % 16]
+    const uint16_t* cp = Ctg + (t0 + 16 * wave + lane % 16) * N + (lane / 16) * 8;
+#pragma unroll
+    for (int k = 0; k < N / 32; ++k) nx.ct[k] = *reinterpret_cast<const uint4*>(cp + 32 * k);
+    // 32x32x16 A operand: lane holds B^T[n = nb*32 + lane % 32][s = 16 ks + (lane/32)*8 + j]
+#pragma unroll
+    for (int q = 0; q < NBW; ++q) {
+      const int nb = wave + 4 * q;
+      if (nb < NB) {
+        const uint16_t* bp = Bg + (nb * 32 + lane % 32) * L;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) nx.bt[q][ks] = load8_bf16(bp, t0 + 16 * ks + (lane / 32) * 8, L);
+      }
+    }
+  };
+  fetch(0);
+  __syncthreads();  // the initial state is in sS
+
+  for (int64_t c = 0; c < a.nchunks; ++c) {
+    const int64_t t0 = c * T;
+    const Pre cur = nx;
+    if (c + 1 < a.nchunks) fetch(c + 1);
+    // step sizes and running decay of the chunk, lane l <-> step t0 + l
+    float dtv = 0.0f;
+    if (t0 + lane < L) {
+      const float raw = __uint_as_float((uint32_t)cur.dtr << 16) + bias;
+      dtv = a.softplus ? softplus_f(raw) : raw;
+    }
+    const float cs = wave_prefix_sum(dtv * Ah);
+    sDt[wave][lane] = dtv;
+    sCs[wave][lane] = cs;
+    __syncthreads();  // the previous chunk is done with sX, sZ, sY, sM
+    *reinterpret_cast<uint4*>(sX + xp * XP + xt8) = cur.xv;
+    if constexpr (GATE) *reinterpret_cast<uint4*>(sZ + xp * XP + xt8) = cur.zv;
+    const float* csw = sCs[wave];
+    const float* dtw = sDt[wave];
+    if (wave < 3) {  // M tile (s-block, t-block) = (0,0), (0,1), (1,1)
+      const int sb = wave == 2 ? 1 : 0, tb = wave == 0 ? 0 : 1;
+      const int t = tb * 32 + lane % 32;
+      const float cst = csw[t];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int s = sb * 32 + r * 8 + (lane / 32) * 4;
+        float m[4], ml[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float v = s + i <= t ? cur.gfr[4 * r + i] * __expf(cst - csw[s + i]) * dtw[s + i] : 0.0f;
+          m[i] = bf16_round(v);
+          ml[i] = v - m[i];
+        }
+        uint2 v, vl;
+        v.x = pack_bf16x2(m[0], m[1]);
+        v.y = pack_bf16x2(m[2], m[3]);
+        vl.x = pack_bf16x2(ml[0], ml[1]);
+        vl.y = pack_bf16x2(ml[2], ml[3]);
+        *reinterpret_cast<uint2*>(sM + t * MP + s) = v;
+        *reinterpret_cast<uint2*>(sMl + t * MP + s) = vl;
+      }
+    }
+    __syncthreads();  // sX, sZ, sM ready
+    // ---- Y^T tiles [p][t], t in [16 wave, 16 wave + 16): C S^T scaled by exp(cs_t), plus X M^T
+    {
+      const int t = 16 * wave + lane % 16;
+      f32x4v_t yv[2] = {{}, {}};
+#pragma unroll
+      for (int pt = 0; pt < 2; ++pt) {
+#pragma unroll
+        for (int k = 0; k < N / 32; ++k) {
+          const int off = (pt * 16 + lane % 16) * SP + 32 * k + (lane / 16) * 8;
+          const uint4 av = *reinterpret_cast<const uint4*>(sS + off);
+          const uint4 al = *reinterpret_cast<const uint4*>(sSl + off);
+          yv[pt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(cur.ct[k]), yv[pt], 0, 0, 0);
+          yv[pt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(al), as_bf16x8(cur.ct[k]), yv[pt], 0, 0, 0);
+        }
+      }
+      const float f = __expf(csw[t]);
+      const int ks_end = wave >= 2 ? 2 : 1;  // M is zero for s > t
+#pragma unroll
+      for (int pt = 0; pt < 2; ++pt) {
+        yv[pt] *= f;
+        for (int k = 0; k < ks_end; ++k) {
+          const uint4 av = *reinterpret_cast<const uint4*>(sX + (pt * 16 + lane % 16) * XP + 32 * k + (lane / 16) * 8);
+          const uint4 bv = *reinterpret_cast<const uint4*>(sM + t * MP + 32 * k + (lane / 16) * 8);
+          const uint4 bl = *reinterpret_cast<const uint4*>(sMl + t * MP + 32 * k + (lane / 16) * 8);
+          yv[pt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(bv), yv[pt], 0, 0, 0);
+          yv[pt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(bl), yv[pt], 0, 0, 0);
+        }
+        // epilogue: rows p = pt*16 + (lane/16)*4 + i, column t
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int p = pt * 16 + (lane / 16) * 4 + i;
+          const float xv = __uint_as_float((uint32_t)sX[p * XP + t] << 16);
+          float v = fmaf(Dh, xv, yv[pt][i]);
+          if constexpr (GATE) v *= silu_f(__uint_as_float((uint32_t)sZ[p * XP + t] << 16));
+          sY[p * XP + t] = f2bf(v);
+        }
+      }
+    }
+    // ---- state: S^T = exp(cs_63) S^T + B^T (w o X), w_s = exp(cs_63 - cs_s) dt_s
+    {
+      const float cend = csw[T - 1];
+      const float decay = __expf(cend);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int s0 = 16 * ks + (lane / 32) * 8;
+        const uint4 xr = *reinterpret_cast<const uint4*>(sX + (lane % 32) * XP + s0);
+        uint16_t e[8];
+        __builtin_memcpy(e, &xr, 16);
+        float wv[8], wl[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float v = __uint_as_float((uint32_t)e[j] << 16) * (__expf(cend - csw[s0 + j]) * dtw[s0 + j]);
+          wv[j] = bf16_round(v);
+          wl[j] = v - wv[j];
+        }
+        uint4 xw, xl;
+        xw.x = pack_bf16x2(wv[0], wv[1]); xw.y = pack_bf16x2(wv[2], wv[3]);
+        xw.z = pack_bf16x2(wv[4], wv[5]); xw.w = pack_bf16x2(wv[6], wv[7]);
+        xl.x = pack_bf16x2(wl[0], wl[1]); xl.y = pack_bf16x2(wl[2], wl[3]);
+        xl.z = pack_bf16x2(wl[4], wl[5]); xl.w = pack_bf16x2(wl[6], wl[7]);
+#pragma unroll
+        for (int q = 0; q < NBW; ++q) {
+          if (wave + 4 * q < NB) {
+            if (ks == 0) S[q] *= decay;
+            S[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(cur.bt[q][ks]), as_bf16x8(xw), S[q], 0, 0, 0);
+            S[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(cur.bt[q][ks]), as_bf16x8(xl), S[q], 0, 0, 0);
+          }
+        }
+      }
+    }
+    __syncthreads();  // every wave is done with sS (old state) and has written sY
+    write_state_bf16();
+    {
+      const int64_t t = t0 + xt8;
+      if (t < L) {
+        uint16_t* dst = yg + xp * L + t;
+        const uint4 v = *reinterpret_cast<const uint4*>(sY + xp * XP + xt8);
+        if (t + 8 <= L && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+          *reinterpret_cast<uint4*>(dst) = v;
+        } else {
+          uint16_t e[8];
+          __builtin_memcpy(e, &v, 16);
+          for (int j = 0; j < 8; ++j)
+            if (t + j < L) dst[j] = e[j];
+        }
+      }
+    }
+  }
+  if (a.final_state) {
+#pragma unroll
+    for (int q = 0; q < NBW; ++q) {
+      const int nb = wave + 4 * q;
+      if (nb < NB) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int n = nb * 32 + r * 8 + (lane / 32) * 4;
+          *reinterpret_cast<float4*>(a.final_state + st0 + (lane % 32) * N + n) =
+              make_float4(S[q][4 * r], S[q][4 * r + 1], S[q][4 * r + 2], S[q][4 * r + 3]);
+        }
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- decode step
 
 struct StepArgs {
@@ -1704,6 +2088,34 @@ int conv_common_checks(int64_t batch, int64_t dim, int64_t seqlen, int64_t width
   if (io_dtype != SSM_DTYPE_F32 && io_dtype != SSM_DTYPE_BF16)
     return fail(SSM_E_DTYPE, "io_dtype = %d is not SSM_DTYPE_F32 or SSM_DTYPE_BF16", io_dtype);
   return SSM_OK;
+}
+
+
+// ---------------------------------------------------------------- Mamba-2 scan: launch
+
+struct SsdLayout {
+  int64_t nchunks, ct_off, g_off, bytes;
+};
+
+SsdLayout ssd_layout(int64_t batch, int64_t seqlen, int64_t ngroups, int64_t dstate) {
+  auto up = [](int64_t x) { return (x + 255) & ~(int64_t)255; };
+  SsdLayout l;
+  l.nchunks = (seqlen + kSsdT - 1) / kSsdT;
+  l.ct_off = 0;
+  l.g_off = up(batch * ngroups * l.nchunks * kSsdT * dstate * 2);
+  l.bytes = l.g_off + up(batch * ngroups * l.nchunks * 3 * 64 * 16 * 4);
+  return l;
+}
+
+template <int N>
+void launch_ssd(const SsdArgs& a, bool gate, hipStream_t s) {
+  hipLaunchKernelGGL((ssd_prep_kernel<N>), dim3((unsigned)a.nchunks, (unsigned)a.G, (unsigned)a.batch),
+                     dim3(256), 0, s, a);
+  const dim3 grid((unsigned)(2 * a.H), (unsigned)a.batch);
+  if (gate)
+    hipLaunchKernelGGL((ssd_fwd_kernel<N, true>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((ssd_fwd_kernel<N, false>), grid, dim3(256), 0, s, a);
 }
 
 }  // namespace
@@ -2126,6 +2538,85 @@ int ssm_causal_conv1d_bwd(const void* x, const float* weight, const float* bias,
       launch_conv_bwd<float, W>(a, vec, s);
   });
   return launch_status("ssm_causal_conv1d_bwd launch");
+}
+
+int64_t ssm_ssd_workspace_size(int64_t batch, int64_t seqlen, int64_t ngroups, int64_t dstate) {
+  if (batch <= 0 || seqlen <= 0 || ngroups <= 0 || dstate <= 0) return -1;
+  if (!product_ok(batch, ngroups, seqlen + kSsdT, dstate * 2)) return -1;
+  return ssd_layout(batch, seqlen, ngroups, dstate).bytes;
+}
+
+int ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void* Bm, const void* Cm,
+                const float* Dskip, const void* z, const float* dt_bias, int dt_softplus,
+                const float* h0, void* y, float* final_state, void* workspace,
+                int64_t workspace_bytes, int64_t batch, int64_t seqlen, int64_t nheads,
+                int64_t headdim, int64_t ngroups, int64_t dstate, int io_dtype,
+                void* hip_stream) {
+  g_last_error[0] = 0;
+  const struct { const void* p; const char* name; } req[] = {
+      {x, "x"}, {dt, "dt"}, {A, "A"}, {Bm, "B"}, {Cm, "C"}, {y, "y"}, {workspace, "workspace"}};
+  for (const auto& r : req)
+    if (!r.p) return fail(SSM_E_NULL, "%s is NULL", r.name);
+  int st;
+  if ((st = check_extent("batch", batch)) || (st = check_extent("seqlen", seqlen)) ||
+      (st = check_extent("nheads", nheads)) || (st = check_extent("headdim", headdim)) ||
+      (st = check_extent("ngroups", ngroups)) || (st = check_extent("dstate", dstate)))
+    return st;
+  if (nheads % ngroups)
+    return fail(SSM_E_SHAPE, "nheads = %lld is not a multiple of ngroups = %lld", (long long)nheads,
+                (long long)ngroups);
+  if (io_dtype != SSM_DTYPE_BF16)
+    return fail(io_dtype == SSM_DTYPE_F32 ? SSM_E_UNSUPPORTED : SSM_E_DTYPE,
+                "the Mamba-2 scan takes bf16 inputs (io_dtype = %d)", io_dtype);
+  if (headdim != kSsdP)
+    return fail(SSM_E_UNSUPPORTED, "headdim = %lld: supported headdim is 64", (long long)headdim);
+  if (dstate != 32 && dstate != 64 && dstate != 128 && dstate != 256)
+    return fail(SSM_E_UNSUPPORTED, "dstate = %lld: supported are 32, 64, 128, 256", (long long)dstate);
+  if (batch > 65535 || ngroups > 65535 || nheads > (1 << 30))
+    return fail(SSM_E_SHAPE, "batch, ngroups or nheads too large");
+  if (!product_ok(batch, nheads * headdim, seqlen, 2) || !product_ok(batch, nheads * headdim, dstate, 4))
+    return fail(SSM_E_SHAPE, "tensor sizes overflow");
+  const SsdLayout lay = ssd_layout(batch, seqlen, ngroups, dstate);
+  if (lay.nchunks > 65535) return fail(SSM_E_SHAPE, "seqlen = %lld is too long", (long long)seqlen);
+  if (workspace_bytes < lay.bytes)
+    return fail(SSM_E_SHAPE, "workspace holds %lld bytes, needs %lld", (long long)workspace_bytes,
+                (long long)lay.bytes);
+  if (!aligned16(workspace)) return fail(SSM_E_ALIGN, "workspace is not 16-byte aligned");
+  const int64_t seq = batch * nheads * headdim * seqlen * 2, bc = batch * ngroups * dstate * seqlen * 2;
+  const int64_t stb = batch * nheads * headdim * dstate * 4;
+  const Span ins[] = {{x, seq, "x"},        {dt, batch * nheads * seqlen * 2, "dt"},
+                      {A, nheads * 4, "A"}, {Bm, bc, "B"},
+                      {Cm, bc, "C"},        {Dskip, nheads * 4, "D"},
+                      {z, z ? seq : 0, "z"}, {dt_bias, nheads * 4, "dt_bias"},
+                      {h0, stb, "h0"}};
+  const Span outs[] = {{y, seq, "y"}, {final_state, stb, "final_state"},
+                       {workspace, lay.bytes, "workspace"}};
+  for (const Span& o : outs) {
+    for (const Span& i : ins)
+      if (overlaps(o, i)) return fail(SSM_E_ALIAS, "%s overlaps %s", o.name, i.name);
+    for (const Span& o2 : outs)
+      if (&o2 != &o && overlaps(o, o2)) return fail(SSM_E_ALIAS, "%s overlaps %s", o.name, o2.name);
+  }
+  if (final_state && !aligned16(final_state))
+    return fail(SSM_E_ALIGN, "final_state is not 16-byte aligned");
+  SsdArgs a;
+  memset(&a, 0, sizeof a);
+  a.x = x; a.dt = dt; a.A = A; a.Bm = Bm; a.Cm = Cm; a.Dskip = Dskip; a.z = z; a.dt_bias = dt_bias;
+  a.h0 = h0; a.y = y; a.final_state = final_state;
+  char* ws = static_cast<char*>(workspace);
+  a.Ct = reinterpret_cast<uint16_t*>(ws + lay.ct_off);
+  a.Gf = reinterpret_cast<float*>(ws + lay.g_off);
+  a.batch = batch; a.L = seqlen; a.H = nheads; a.G = ngroups; a.N = dstate; a.nchunks = lay.nchunks;
+  a.softplus = dt_softplus ? 1 : 0;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  const bool gate = z != nullptr;
+  switch (dstate) {
+    case 32: launch_ssd<32>(a, gate, s); break;
+    case 64: launch_ssd<64>(a, gate, s); break;
+    case 128: launch_ssd<128>(a, gate, s); break;
+    default: launch_ssd<256>(a, gate, s); break;
+  }
+  return launch_status("ssm_ssd_fwd launch");
 }
 
 }  // extern "C"

@@ -200,3 +200,37 @@ def test_conv1d_update_and_bwd_validation(lib):
     a = list(args)
     a[12] = 9
     assert bwd(*a) == 6
+
+
+SSD_KEYS = ("x", "dt", "A", "B", "C", "D", "z", "bias", "softplus", "h0", "y", "fs", "ws",
+            "ws_bytes", "batch", "L", "H", "P", "G", "N", "io", "stream")
+
+
+def ssd_args(**over):
+    a = dict(x=1 * P, dt=2 * P, A=3 * P, B=4 * P, C=5 * P, D=None, z=None, bias=None, softplus=1,
+             h0=None, y=6 * P, fs=None, ws=7 * P, ws_bytes=P, batch=2, L=64, H=4, P=64, G=1,
+             N=128, io=1, stream=None)
+    a.update(over)
+    return [a[k] for k in SSD_KEYS]
+
+
+def test_ssd_workspace_size(lib):
+    f = lib.ssm_ssd_workspace_size
+    assert f(0, 64, 1, 128) == -1
+    small, big = f(1, 64, 1, 128), f(1, 65, 1, 128)
+    assert 0 < small < big and small % 256 == 0
+    # token-major C (64 steps x 128 states bf16) and three 32x32 fp32 tiles per chunk
+    assert small >= 64 * 128 * 2 + 3 * 64 * 16 * 4
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(x=None), 1), (dict(dt=None), 1), (dict(B=None), 1), (dict(y=None), 1),
+    (dict(ws=None), 1),
+    (dict(L=0), 2), (dict(G=3), 2), (dict(ws_bytes=16), 2), (dict(batch=70000), 2),
+    (dict(io=5), 3),
+    (dict(ws=7 * P + 8), 4),
+    (dict(y=1 * P), 5), (dict(ws=4 * P), 5), (dict(fs=6 * P), 5),
+    (dict(io=0), 6), (dict(P=32), 6), (dict(N=16), 6), (dict(N=100), 6),
+])
+def test_ssd_validation(lib, over, status):
+    assert lib.ssm_ssd_fwd(*ssd_args(**over)) == status

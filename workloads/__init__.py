@@ -41,6 +41,7 @@ import numpy as np
 # tensor ids used in the per-row stream keys
 T_U, T_DELTA, T_Z, T_B, T_C, T_A, T_D, T_BIAS, T_STATE, T_DY, T_DFINAL = range(11)
 T_CX, T_CW, T_CB, T_CSTATE, T_CDOUT = range(11, 16)
+T_SX, T_SDT, T_SB, T_SC, T_SZ, T_SA, T_SD, T_SBIAS, T_SH0 = range(16, 25)
 
 
 @dataclass(frozen=True)
@@ -221,6 +222,64 @@ def conv_inputs(w: Workload, width=4, seed=None):
     return dict(x=x.reshape(w.batch, w.dim, w.seqlen), weight=weight, bias=bias,
                 state_in=state[:, :width - 1].reshape(w.batch, w.dim, width - 1).copy(),
                 dout=dout.reshape(w.batch, w.dim, w.seqlen))
+
+
+@dataclass(frozen=True)
+class SsdWorkload:
+    """A Mamba-2 layer's scan: x, z [batch, nheads * headdim, L], dt [batch,
+    nheads, L], B, C [batch, ngroups * dstate, L], all bf16."""
+    name: str
+    batch: int
+    seqlen: int
+    nheads: int
+    headdim: int
+    ngroups: int
+    dstate: int
+    gate: bool = True
+    seed: int = 4400
+
+    @property
+    def elements(self) -> int:
+        return self.batch * self.seqlen * self.nheads * self.headdim * self.dstate
+
+    @property
+    def io_bytes(self) -> int:
+        seq = self.batch * self.nheads * self.headdim * self.seqlen * 2
+        return ((3 if self.gate else 2) * seq + self.batch * self.nheads * self.seqlen * 2
+                + 2 * self.batch * self.ngroups * self.dstate * self.seqlen * 2)
+
+
+# Mamba-2 2.7B-shaped layer (d_inner 5120 = 80 heads x 64, N 128, one group)
+SSD_WORKLOADS = {
+    "mamba2_2p7b": SsdWorkload("mamba2_2p7b", 4, 8192, 80, 64, 1, 128),
+}
+
+
+def ssd_inputs(w: SsdWorkload, seed=None, with_h0=False):
+    """x, z, B, C ~ N(0,1) and raw dt ~ N(0,1) in bf16; A = -U[1, 16] per head
+    (A = -exp(log U[1, 16])), D ~ N(0,1), dt_bias = log(expm1(U[1e-3, 1e-1]))
+    (a step of 0.001..0.1 at zero raw input), all float32; h0 [batch, nheads,
+    headdim, dstate] ~ N(0, 0.1) float32 when asked for."""
+    seed = w.seed if seed is None else seed
+    hp = w.nheads * w.headdim
+
+    def seq(tid, rows):
+        out = np.empty((w.batch * rows, w.seqlen), dtype=np.uint16)
+        _normal_rows(seed, tid, 0, out, 0.0, 1.0, "bf16")
+        return out.reshape(w.batch, rows, w.seqlen)
+
+    A = -rng(seed, T_SA, 0).uniform(1.0, 16.0, w.nheads).astype(np.float32)
+    D = rng(seed, T_SD, 0).standard_normal(w.nheads).astype(np.float32)
+    step = rng(seed, T_SBIAS, 0).uniform(1e-3, 1e-1, w.nheads)
+    bias = np.log(np.expm1(step)).astype(np.float32)
+    x = dict(x=seq(T_SX, hp), dt=seq(T_SDT, w.nheads), B=seq(T_SB, w.ngroups * w.dstate),
+             C=seq(T_SC, w.ngroups * w.dstate), z=seq(T_SZ, hp) if w.gate else None,
+             A=A, D=D, dt_bias=bias, h0=None)
+    if with_h0:
+        h0 = np.empty((w.batch * w.nheads, w.headdim * w.dstate), dtype=np.float32)
+        _normal_rows(seed, T_SH0, 0, h0, 0.0, 0.1, "f32")
+        x["h0"] = h0.reshape(w.batch, w.nheads, w.headdim, w.dstate)
+    return x
 
 
 def decode_state(w: Workload, seed=None) -> np.ndarray:
