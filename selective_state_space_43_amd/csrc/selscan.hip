@@ -1450,24 +1450,31 @@ __device__ __forceinline__ float wave_prefix_sum(float v) {
   return v;
 }
 
-// 8 bf16 of a row (length L) from step t on, zero past L; one 16-byte load
-// when the run is whole and aligned (rows of a length that is not a multiple
-// of 8 are read element by element)
+// 8 bf16 of a row (length L) from step t on (t a multiple of 8), read from a
+// clamped address: past the end of the row the values are some of the row's
+// own (finite) inputs.  The scan never needs them to be zero: every product
+// with a step past L is multiplied by that step's dt, which is set to zero,
+// and outputs past L are not stored.  ALIGNED (L a multiple of 8, rows
+// 16-byte aligned): one 16-byte load; otherwise eight 2-byte loads.  Nothing
+// is selected on the loaded values here, so a prefetch is not waited for
+// where it is issued.
+template <bool ALIGNED>
 __device__ __forceinline__ uint4 load8_bf16(const uint16_t* rowp, int64_t t, int64_t L) {
-  if (t + 8 <= L && (reinterpret_cast<uintptr_t>(rowp + t) & 15) == 0)
-    return *reinterpret_cast<const uint4*>(rowp + t);
-  uint16_t e[8];
+  if constexpr (ALIGNED) {
+    return *reinterpret_cast<const uint4*>(rowp + (t < L ? t : L - 8));
+  } else {
+    uint32_t e[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) e[j] = t + j < L ? rowp[t + j] : (uint16_t)0;
-  uint4 v;
-  __builtin_memcpy(&v, e, 16);
-  return v;
+    for (int j = 0; j < 8; ++j) e[j] = rowp[t + j < L ? t + j : L - 1];
+    return make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16),
+                      e[6] | (e[7] << 16));
+  }
 }
 
 // Per (sequence, group, chunk): token-major C and the three non-zero 32x32
 // tiles of G^T[s][t] = B_s . C_t (s-block <= t-block), stored as each lane's
 // 16 accumulators.
-template <int N>
+template <int N, bool ALIGNED>
 __global__ void __launch_bounds__(256) ssd_prep_kernel(const SsdArgs a) {
   constexpr int T = kSsdT, NP = N + 8;
   __shared__ __align__(16) uint16_t sBt[T * NP];
@@ -1478,7 +1485,7 @@ __global__ void __launch_bounds__(256) ssd_prep_kernel(const SsdArgs a) {
   for (int item = threadIdx.x; item < 2 * N * (T / 8); item += 256) {
     const int tensor = item / (N * (T / 8)), r = item % (N * (T / 8));
     const int n = r / (T / 8), t8 = (r % (T / 8)) * 8;
-    const uint4 v = load8_bf16((tensor ? Csrc : Bsrc) + n * L, t0 + t8, L);
+    const uint4 v = load8_bf16<ALIGNED>((tensor ? Csrc : Bsrc) + n * L, t0 + t8, L);
     uint16_t e[8];
     __builtin_memcpy(e, &v, 16);
     uint16_t* dst = tensor ? sCt : sBt;
@@ -1513,7 +1520,7 @@ __global__ void __launch_bounds__(256) ssd_prep_kernel(const SsdArgs a) {
 // waves.  Wave w owns output tile columns t in [16w, 16w + 16) (two 16x16
 // tiles of Y^T, one per 16 channels), state n-blocks w, w + 4, ... (32 x 32
 // tiles of S^T), and for w < 3 one 32x32 tile of M.
-template <int N, bool GATE>
+template <int N, bool GATE, bool ALIGNED>
 __global__ void __launch_bounds__(256) ssd_fwd_kernel(const SsdArgs a) {
   constexpr int T = kSsdT, PB = kSsdPB, XP = T + 8, SP = N + 8, MP = T + 8;
   constexpr int NB = N / 32, NBW = (NB + 3) / 4;  // state n-blocks, per wave
@@ -1524,11 +1531,15 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(const SsdArgs a) {
   __shared__ __align__(16) uint16_t sMl[T * MP];   // and remainder
   __shared__ __align__(16) uint16_t sS[PB * SP];   // S[p][n] entering the chunk, bf16 head
   __shared__ __align__(16) uint16_t sSl[PB * SP];  // and remainder
-  __shared__ float sCs[4][T], sDt[4][T];           // per wave: running decay, step
+  // per wave: running decay (log2), step, and the weight exp(cs_63 - cs_s) dt_s
+  // of step s in the state update
+  __shared__ __align__(16) float sCs[4][T];
+  __shared__ __align__(16) float sDt[4][T];
+  __shared__ __align__(16) float sW[4][T];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t h = blockIdx.x >> 1, pb = blockIdx.x & 1, b = blockIdx.y;
   const int64_t g = h / (a.H / a.G), L = a.L;
-  const float Ah = a.A[h];
+  const float Ah2 = a.A[h] * kLog2e;  // decays are kept in log2 units
   const float Dh = a.Dskip ? a.Dskip[h] : 0.0f;
   const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
   const int64_t row0 = (b * a.H * kSsdP + h * kSsdP + pb * PB) * L;  // this workgroup's first channel row
@@ -1591,9 +1602,9 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(const SsdArgs a) {
   Pre nx;
   auto fetch = [&](int64_t c) {
     const int64_t t0 = c * T;
-    nx.xv = load8_bf16(xg + xp * L, t0 + xt8, L);
-    if constexpr (GATE) nx.zv = load8_bf16(zg + xp * L, t0 + xt8, L);
-    nx.dtr = t0 + lane < L ? dtg[t0 + lane] : (uint16_t)0;
+    nx.xv = load8_bf16<ALIGNED>(xg + xp * L, t0 + xt8, L);
+    if constexpr (GATE) nx.zv = load8_bf16<ALIGNED>(zg + xp * L, t0 + xt8, L);
+    nx.dtr = dtg[t0 + lane < L ? t0 + lane : L - 1];  // steps past L are zeroed where used
     if (wave < 3) {
       const float* gp = Gg + ((c * 3 + wave) * 64 + lane) * 16;
 #pragma unroll
@@ -1613,26 +1624,47 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(const SsdArgs a) {
       if (nb < NB) {
         const uint16_t* bp = Bg + (nb * 32 + lane % 32) * L;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) nx.bt[q][ks] = load8_bf16(bp, t0 + 16 * ks + (lane / 32) * 8, L);
+        for (int ks = 0; ks < 4; ++ks) nx.bt[q][ks] = load8_bf16<ALIGNED>(bp, t0 + 16 * ks + (lane / 32) * 8, L);
       }
     }
   };
   fetch(0);
   __syncthreads();  // the initial state is in sS
 
+  // y of a chunk leaves LDS at the start of the next chunk, after that
+  // chunk's prefetch is issued: a store still in flight where the prefetch
+  // is waited for would be waited for too
+  auto store_y = [&](int64_t c) {
+    const int64_t t = c * T + xt8;
+    if (t < L) {
+      uint16_t* dst = yg + xp * L + t;
+      const uint4 v = *reinterpret_cast<const uint4*>(sY + xp * XP + xt8);
+      if (ALIGNED) {
+        *reinterpret_cast<uint4*>(dst) = v;
+      } else {
+        uint16_t e[8];
+        __builtin_memcpy(e, &v, 16);
+        for (int j = 0; j < 8; ++j)
+          if (t + j < L) dst[j] = e[j];
+      }
+    }
+  };
   for (int64_t c = 0; c < a.nchunks; ++c) {
     const int64_t t0 = c * T;
     const Pre cur = nx;
     if (c + 1 < a.nchunks) fetch(c + 1);
+    if (c > 0) store_y(c - 1);
     // step sizes and running decay of the chunk, lane l <-> step t0 + l
     float dtv = 0.0f;
     if (t0 + lane < L) {
       const float raw = __uint_as_float((uint32_t)cur.dtr << 16) + bias;
       dtv = a.softplus ? softplus_f(raw) : raw;
     }
-    const float cs = wave_prefix_sum(dtv * Ah);
+    const float cs = wave_prefix_sum(dtv * Ah2);  // log2 units
+    const float cs_end = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs), T - 1));
     sDt[wave][lane] = dtv;
     sCs[wave][lane] = cs;
+    sW[wave][lane] = ex2(cs_end - cs) * dtv;
     __syncthreads();  // the previous chunk is done with sX, sZ, sY, sM
     *reinterpret_cast<uint4*>(sX + xp * XP + xt8) = cur.xv;
     if constexpr (GATE) *reinterpret_cast<uint4*>(sZ + xp * XP + xt8) = cur.zv;
@@ -1648,7 +1680,7 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(const SsdArgs a) {
         float m[4], ml[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float v = s + i <= t ? cur.gfr[4 * r + i] * __expf(cst - csw[s + i]) * dtw[s + i] : 0.0f;
+          const float v = s + i <= t ? cur.gfr[4 * r + i] * ex2(cst - csw[s + i]) * dtw[s + i] : 0.0f;
           m[i] = bf16_round(v);
           ml[i] = v - m[i];
         }
@@ -1677,7 +1709,7 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(const SsdArgs a) {
           yv[pt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(al), as_bf16x8(cur.ct[k]), yv[pt], 0, 0, 0);
         }
       }
-      const float f = __expf(csw[t]);
+      const float f = ex2(csw[t]);
       const int ks_end = wave >= 2 ? 2 : 1;  // M is zero for s > t
 #pragma unroll
       for (int pt = 0; pt < 2; ++pt) {
@@ -1702,18 +1734,21 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(const SsdArgs a) {
     }
     // ---- state: S^T = exp(cs_63) S^T + B^T (w o X), w_s = exp(cs_63 - cs_s) dt_s
     {
-      const float cend = csw[T - 1];
-      const float decay = __expf(cend);
+      const float decay = ex2(cs_end);
+      const float* ww = sW[wave];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const int s0 = 16 * ks + (lane / 32) * 8;
         const uint4 xr = *reinterpret_cast<const uint4*>(sX + (lane % 32) * XP + s0);
         uint16_t e[8];
         __builtin_memcpy(e, &xr, 16);
+        const float4 w0 = *reinterpret_cast<const float4*>(ww + s0);
+        const float4 w1 = *reinterpret_cast<const float4*>(ww + s0 + 4);
+        const float wj[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
         float wv[8], wl[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const float v = __uint_as_float((uint32_t)e[j] << 16) * (__expf(cend - csw[s0 + j]) * dtw[s0 + j]);
+          const float v = __uint_as_float((uint32_t)e[j] << 16) * wj[j];
           wv[j] = bf16_round(v);
           wl[j] = v - wv[j];
         }
@@ -1734,22 +1769,8 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(const SsdArgs a) {
     }
     __syncthreads();  // every wave is done with sS (old state) and has written sY
     write_state_bf16();
-    {
-      const int64_t t = t0 + xt8;
-      if (t < L) {
-        uint16_t* dst = yg + xp * L + t;
-        const uint4 v = *reinterpret_cast<const uint4*>(sY + xp * XP + xt8);
-        if (t + 8 <= L && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
-          *reinterpret_cast<uint4*>(dst) = v;
-        } else {
-          uint16_t e[8];
-          __builtin_memcpy(e, &v, 16);
-          for (int j = 0; j < 8; ++j)
-            if (t + j < L) dst[j] = e[j];
-        }
-      }
-    }
   }
+  store_y(a.nchunks - 1);
   if (a.final_state) {
 #pragma unroll
     for (int q = 0; q < NBW; ++q) {
@@ -2107,15 +2128,26 @@ SsdLayout ssd_layout(int64_t batch, int64_t seqlen, int64_t ngroups, int64_t dst
   return l;
 }
 
-template <int N>
-void launch_ssd(const SsdArgs& a, bool gate, hipStream_t s) {
-  hipLaunchKernelGGL((ssd_prep_kernel<N>), dim3((unsigned)a.nchunks, (unsigned)a.G, (unsigned)a.batch),
-                     dim3(256), 0, s, a);
+template <int N, bool ALIGNED>
+void launch_ssd_aligned(const SsdArgs& a, bool gate, hipStream_t s) {
+  hipLaunchKernelGGL((ssd_prep_kernel<N, ALIGNED>),
+                     dim3((unsigned)a.nchunks, (unsigned)a.G, (unsigned)a.batch), dim3(256), 0, s, a);
   const dim3 grid((unsigned)(2 * a.H), (unsigned)a.batch);
   if (gate)
-    hipLaunchKernelGGL((ssd_fwd_kernel<N, true>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((ssd_fwd_kernel<N, true, ALIGNED>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((ssd_fwd_kernel<N, false>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((ssd_fwd_kernel<N, false, ALIGNED>), grid, dim3(256), 0, s, a);
+}
+
+// ALIGNED when every sequence row starts on a 16-byte boundary
+template <int N>
+void launch_ssd(const SsdArgs& a, bool gate, hipStream_t s) {
+  const bool aligned = a.L % 8 == 0 && aligned16(a.x) && aligned16(a.dt) && aligned16(a.Bm) &&
+                       aligned16(a.Cm) && aligned16(a.y) && (!a.z || aligned16(a.z));
+  if (aligned)
+    launch_ssd_aligned<N, true>(a, gate, s);
+  else
+    launch_ssd_aligned<N, false>(a, gate, s);
 }
 
 }  // namespace
