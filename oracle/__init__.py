@@ -31,7 +31,7 @@ _SRC = os.path.join(_HERE, "ssm_oracle.c")
 _SO = os.path.join(_HERE, "libssm_oracle.so")
 _LIB = None
 
-BBAR_MODES = {"delta": 0, "delta_b": 0, "zoh": 1, "zoh_exact": 1}
+BBAR_MODES = {"delta": 0, "delta_b": 0, "zoh": 1, "zoh_exact": 1, "euler": 2, "bilinear": 3}
 
 
 def build(force: bool = False) -> str:

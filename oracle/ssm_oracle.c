@@ -43,7 +43,7 @@
 #include <string.h>
 
 enum { OR_F32 = 0, OR_BF16 = 1, OR_F64 = 2 };
-enum { OR_BBAR_DELTA_B = 0, OR_BBAR_ZOH_EXACT = 1 };
+enum { OR_BBAR_DELTA_B = 0, OR_BBAR_ZOH_EXACT = 1, OR_DISC_EULER = 2, OR_DISC_BILINEAR = 3 };
 
 /* bf16 is the upper half of an IEEE binary32; widening is exact. */
 static double or_widen(const void* p, int dtype, int64_t i) {
@@ -63,9 +63,26 @@ static double or_softplus(double x) {
 /* silu(z) = z * sigmoid(z). */
 static double or_silu(double z) { return z / (1.0 + exp(-z)); }
 
+/*
+ * The discretization rules of "State-space models", section
+ * "Discretization": zero-order hold (Abar = exp(delta a), with Bbar = delta b
+ * as the official package takes it, or the exact A^-1 (exp(delta a) - 1) b),
+ * Euler (Abar = 1 + delta a, Bbar = delta b) and bilinear / Tustin
+ * (Abar = (1 - delta a/2)^-1 (1 + delta a/2), Bbar = (1 - delta a/2)^-1 delta b);
+ * "Structured State Space Models and Mamba ...", section "Discretization
+ * Mechanics: Zero-Order Hold and Bilinear Transforms" prints the same
+ * bilinear pair.  For a diagonal A each is elementwise.
+ */
+static double or_abar(double dt, double a, int mode) {
+  if (mode == OR_DISC_EULER) return 1.0 + dt * a;
+  if (mode == OR_DISC_BILINEAR) return (1.0 + 0.5 * dt * a) / (1.0 - 0.5 * dt * a);
+  return exp(dt * a);
+}
+
 /* Input coefficient Bbar/B for one (delta, a) pair under the chosen rule. */
 static double or_bbar_factor(double dt, double a, int bbar_mode) {
-  if (bbar_mode == OR_BBAR_DELTA_B) return dt;
+  if (bbar_mode == OR_BBAR_DELTA_B || bbar_mode == OR_DISC_EULER) return dt;
+  if (bbar_mode == OR_DISC_BILINEAR) return dt / (1.0 - 0.5 * dt * a);
   /* exact ZOH: (exp(dt*a) - 1) / a, whose limit at a = 0 is dt */
   if (a == 0.0) return dt;
   return expm1(dt * a) / a;
@@ -105,7 +122,7 @@ static void or_scan_one(const or_scan_job* j, int64_t sel, double* h) {
     double acc = 0.0;
     for (int64_t n = 0; n < N; ++n) {
       const double a = j->A[d * N + n];
-      const double abar = exp(dt * a);
+      const double abar = or_abar(dt, a, j->bbar_mode);
       const double bt = or_widen(j->Bm, j->io_dtype, bc_base + n * L + t);
       const double ct = or_widen(j->Cm, j->io_dtype, bc_base + n * L + t);
       h[n] = abar * h[n] + or_bbar_factor(dt, a, j->bbar_mode) * bt * ut;
@@ -164,7 +181,7 @@ int ssm_oracle_selective_scan(int io_dtype, const void* u, const void* delta, co
   if (!u || !delta || !Bm || !Cm || !A) return 1;
   if (batch <= 0 || dim <= 0 || dstate <= 0 || seqlen <= 0) return 1;
   if (io_dtype != OR_F32 && io_dtype != OR_BF16 && io_dtype != OR_F64) return 1;
-  if (bbar_mode != OR_BBAR_DELTA_B && bbar_mode != OR_BBAR_ZOH_EXACT) return 1;
+  if (bbar_mode < OR_BBAR_DELTA_B || bbar_mode > OR_DISC_BILINEAR) return 1;
   if (!channels) n_channels = batch * dim;
   for (int64_t i = 0; channels && i < n_channels; ++i)
     if (channels[i] < 0 || channels[i] >= batch * dim) return 1;
@@ -237,7 +254,8 @@ int ssm_oracle_state_update(int io_dtype, double* state, const void* u, const vo
  *
  *   A : [dim, dstate];  Bv, Cv : rows of length dstate, row d at d*stride
  *   (stride 0 = one row shared by every channel);  delta : [dim]
- *   method 0 : Abar^k = exp(k * delta * A)      (direct)
+ *   method 0 : Abar^k directly: exp(k * delta * A) for the exp rules,
+ *              pow(Abar, k) for Euler and bilinear
  *   method 1 : Abar^k by repeated multiplication (k successive products)
  *   K : [dim, L] out
  */
@@ -246,18 +264,20 @@ int ssm_oracle_lti_kernel(const double* A, const double* Bv, const double* Cv,
                           int64_t b_row_stride, int64_t c_row_stride, int bbar_mode, int method,
                           double* K) {
   if (!A || !Bv || !Cv || !delta || !K || dim <= 0 || dstate <= 0 || L <= 0) return 1;
-  if (bbar_mode != OR_BBAR_DELTA_B && bbar_mode != OR_BBAR_ZOH_EXACT) return 1;
+  if (bbar_mode < OR_BBAR_DELTA_B || bbar_mode > OR_DISC_BILINEAR) return 1;
   for (int64_t d = 0; d < dim; ++d) {
     const double dt = delta[d];
     for (int64_t k = 0; k < L; ++k) K[d * L + k] = 0.0;
     for (int64_t n = 0; n < dstate; ++n) {
       const double a = A[d * dstate + n];
-      const double abar = exp(dt * a);
+      const double abar = or_abar(dt, a, bbar_mode);
       const double bbar = or_bbar_factor(dt, a, bbar_mode) * Bv[d * b_row_stride + n];
       const double cn = Cv[d * c_row_stride + n];
       double p = 1.0; /* Abar^k for method 1 */
       for (int64_t k = 0; k < L; ++k) {
-        const double pk = (method == 0) ? exp((double)k * dt * a) : p;
+        const double pk = method == 1 ? p
+                          : bbar_mode <= OR_BBAR_ZOH_EXACT ? exp((double)k * dt * a)
+                                                           : pow(abar, (double)k);
         K[d * L + k] += cn * pk * bbar;
         p *= abar;
       }
