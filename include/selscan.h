@@ -58,10 +58,22 @@ extern "C" {
 
 typedef enum { SSM_DTYPE_F32 = 0, SSM_DTYPE_BF16 = 1 } ssm_dtype;
 
-/* Bbar rule: delta*B (Mamba's simplified input matrix, the default; the
- * "Implementation" section of "State-space models" notes the official package
- * uses it) or the exact zero-order-hold input matrix. */
-typedef enum { SSM_BBAR_DELTA_B = 0, SSM_BBAR_ZOH_EXACT = 1 } ssm_bbar_mode;
+/* Discretization rule (the bbar_mode argument), per ("State-space models",
+ * section "Discretization"; "Implementation" for the default):
+ *  SSM_BBAR_DELTA_B    Abar = exp(delta A), Bbar = delta B  (Mamba's simplified
+ *                      input matrix, the default)
+ *  SSM_BBAR_ZOH_EXACT  Abar = exp(delta A), Bbar = A^-1 (exp(delta A) - 1) B
+ *  SSM_DISC_EULER      Abar = 1 + delta A,  Bbar = delta B
+ *  SSM_DISC_BILINEAR   Abar = (1 + delta A/2) / (1 - delta A/2),
+ *                      Bbar = delta B / (1 - delta A/2)
+ * The scan, the decode step and the LTI kernel take all four; the backward
+ * takes the first two (SSM_E_UNSUPPORTED otherwise). */
+typedef enum {
+  SSM_BBAR_DELTA_B = 0,
+  SSM_BBAR_ZOH_EXACT = 1,
+  SSM_DISC_EULER = 2,
+  SSM_DISC_BILINEAR = 3
+} ssm_bbar_mode;
 
 typedef enum {
   SSM_OK = 0,
@@ -70,7 +82,7 @@ typedef enum {
   SSM_E_DTYPE = 3,       /* io_dtype or bbar_mode is not a known value          */
   SSM_E_ALIGN = 4,       /* a sequence tensor is not 16-byte aligned            */
   SSM_E_ALIAS = 5,       /* an output overlaps an input it must not overlap     */
-  SSM_E_UNSUPPORTED = 6, /* dstate outside 1..64                                */
+  SSM_E_UNSUPPORTED = 6, /* a size or mode the entry point does not implement    */
   SSM_E_HIP = 7          /* the HIP runtime refused the launch                  */
 } ssm_status;
 

@@ -8,7 +8,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SO = os.path.join(_HERE, "libselscan.so")
 
 SSM_DTYPE_F32, SSM_DTYPE_BF16 = 0, 1
-SSM_BBAR_DELTA_B, SSM_BBAR_ZOH_EXACT = 0, 1
+SSM_BBAR_DELTA_B, SSM_BBAR_ZOH_EXACT, SSM_DISC_EULER, SSM_DISC_BILINEAR = 0, 1, 2, 3
 STATUS_NAMES = {0: "SSM_OK", 1: "SSM_E_NULL", 2: "SSM_E_SHAPE", 3: "SSM_E_DTYPE",
                 4: "SSM_E_ALIGN", 5: "SSM_E_ALIAS", 6: "SSM_E_UNSUPPORTED", 7: "SSM_E_HIP"}
 

@@ -8,7 +8,7 @@ import torch
 from ._lib import SSM_DTYPE_BF16, SSM_DTYPE_F32, check, lib
 
 _IO = {torch.bfloat16: SSM_DTYPE_BF16, torch.float32: SSM_DTYPE_F32}
-_BBAR = {"delta": 0, "delta_b": 0, "zoh": 1, "zoh_exact": 1}
+_BBAR = {"delta": 0, "delta_b": 0, "zoh": 1, "zoh_exact": 1, "euler": 2, "bilinear": 3}
 
 
 def _dev(t, name, device):

@@ -329,12 +329,19 @@ struct ScanArgs {
   float* ckpt;  // checkpoint mode: state every kCkptT steps, [batch, dim, ceil(L / kCkptT), dstate]
 };
 
+// Discretization rules (the bbar_mode of the C ABI): Abar = exp(delta A) with
+// Bbar = delta B or the exact ZOH input (A^-1 (exp(delta A) - 1) B); Euler,
+// Abar = 1 + delta A, Bbar = delta B; bilinear, Abar = (1 + delta A / 2) /
+// (1 - delta A / 2), Bbar = delta B / (1 - delta A / 2) ("State-space
+// models", section "Discretization").
+constexpr int kRuleDeltaB = 0, kRuleZoh = 1, kRuleEuler = 2, kRuleBilinear = 3;
+
 // Steps between the states that the checkpoint pass keeps for the backward.
 constexpr int kCkptT = 128;
 
 // CKPT: the pass that the backward recomputes from: it writes the state
 // entering every kCkptT-step block to a.ckpt and computes no output.
-template <typename IO, int LPC, int K, int W, int NT, bool VEC, bool ZOH, bool GATE,
+template <typename IO, int LPC, int K, int W, int NT, bool VEC, int RULE, bool GATE,
           bool CKPT = false>
 __global__ void __launch_bounds__(64 * W)
 #if SELSCAN_WAVES_PER_EU
@@ -456,13 +463,22 @@ __global__ void __launch_bounds__(64 * W)
         const float bq[4] = {bb.x, bb.y, bb.z, bb.w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          av[i + q] = ex2(dl[i + q] * An);
-          if constexpr (ZOH) {
+          if constexpr (RULE == kRuleDeltaB) {
+            av[i + q] = ex2(dl[i + q] * An);
+            xv[i + q] = w[i + q] * bq[q];
+          } else if constexpr (RULE == kRuleZoh) {
+            av[i + q] = ex2(dl[i + q] * An);
             const float r = dl[i + q] * An * kLn2;  // delta * A
             const float coef = An != 0.0f ? expm1_f(r, av[i + q]) * rcp(An) : dl[i + q] * kLn2;
             xv[i + q] = coef * bq[q] * (ul[i + q] * kLog2e);
-          } else {
+          } else if constexpr (RULE == kRuleEuler) {
+            av[i + q] = fmaf(dl[i + q] * kLn2, An, 1.0f);
             xv[i + q] = w[i + q] * bq[q];
+          } else {  // bilinear
+            const float x = 0.5f * kLn2 * dl[i + q] * An;  // delta A / 2
+            const float r = rcp(1.0f - x);
+            av[i + q] = (1.0f + x) * r;
+            xv[i + q] = w[i + q] * r * bq[q];
           }
         }
       }
@@ -472,7 +488,15 @@ __global__ void __launch_bounds__(64 * W)
       float H = fmaf(av[0], first ? c : 0.0f, xv[0]);
 #pragma unroll
       for (int i = 1; i < K; ++i) H = fmaf(av[i], H, xv[i]);
-      const float Al = ex2(An * S);  // product of the lane's K decays
+      // product of the lane's K decays
+      float Al;
+      if constexpr (RULE <= kRuleZoh) {
+        Al = ex2(An * S);
+      } else {
+        Al = av[0];
+#pragma unroll
+        for (int i = 1; i < K; ++i) Al *= av[i];
+      }
       group_scan<LPC>(Al, H);
       const float He = group_prev0<LPC>(H, first);
       float h = first ? c : He;
@@ -1808,7 +1832,7 @@ struct StepArgs {
 // (N floats, 16-byte vectors) in and out, so a wave keeps 64 rows in flight
 // and neighbouring lanes read neighbouring rows.  A is read as float4s; B and
 // C (one row per sequence, shared by the wave's channels) as 16-byte vectors.
-template <typename IO, bool ZOH, bool GATE>
+template <typename IO, int RULE, bool GATE>
 __global__ void __launch_bounds__(256) state_update_kernel(const StepArgs a) {
   const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (c >= a.batch * a.dim) return;
@@ -1852,13 +1876,22 @@ __global__ void __launch_bounds__(256) state_update_kernel(const StepArgs a) {
     }
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-      const float e = ex2(dl * An[k]);
-      float x;
-      if constexpr (ZOH) {
+      float e, x;
+      if constexpr (RULE == kRuleDeltaB) {
+        e = ex2(dl * An[k]);
+        x = w * Bv[k];
+      } else if constexpr (RULE == kRuleZoh) {
+        e = ex2(dl * An[k]);
         const float coef = An[k] != 0.0f ? expm1_f(dl * kLn2 * An[k], e) * rcp(An[k]) : dl * kLn2;
         x = coef * Bv[k] * uu;
-      } else {
+      } else if constexpr (RULE == kRuleEuler) {
+        e = fmaf(dl * kLn2, An[k], 1.0f);
         x = w * Bv[k];
+      } else {
+        const float hx = 0.5f * kLn2 * dl * An[k];
+        const float r = rcp(1.0f - hx);
+        e = (1.0f + hx) * r;
+        x = w * r * Bv[k];
       }
       h[k] = fmaf(e, h[k], x);
       acc = fmaf(Cv[k], h[k], acc);
@@ -1882,7 +1915,7 @@ __global__ void __launch_bounds__(256) state_update_kernel(const StepArgs a) {
 
 // ---------------------------------------------------------------- LTI kernel
 
-template <bool ZOH>
+template <int RULE>
 __global__ void __launch_bounds__(256)
     lti_kernel_kernel(const float* A, const float* Bv, const float* Cv, const float* delta,
                       float* K, int64_t dim, int64_t N, int64_t L, int64_t bs, int64_t cs) {
@@ -1893,15 +1926,26 @@ __global__ void __launch_bounds__(256)
   float acc = 0.0f;
   for (int64_t n = 0; n < N; ++n) {
     const float An = A[d * N + n];
-    float bbar;
-    if constexpr (ZOH) {
-      bbar = An != 0.0f ? expm1_f(dt * An, ex2(dt * An * kLog2e)) * rcp(An) : dt;
+    float bbar, pk;  // Bbar / B and Abar^k
+    if constexpr (RULE <= kRuleZoh) {
+      bbar = RULE == kRuleZoh && An != 0.0f ? expm1_f(dt * An, ex2(dt * An * kLog2e)) * rcp(An) : dt;
+      pk = ex2((float)k * (dt * An * kLog2e));  // exp(k dt A)
     } else {
-      bbar = dt;
+      float ab;
+      if constexpr (RULE == kRuleEuler) {
+        ab = fmaf(dt, An, 1.0f);
+        bbar = dt;
+      } else {
+        const float r = rcp(1.0f - 0.5f * dt * An);
+        ab = (1.0f + 0.5f * dt * An) * r;
+        bbar = dt * r;
+      }
+      // |Abar|^k with the sign of Abar^k (Euler's Abar can be zero or negative)
+      const float mag = k == 0 ? 1.0f : ex2((float)k * lg2(fabsf(ab)));
+      pk = (ab < 0.0f && (k & 1)) ? -mag : mag;
     }
     bbar *= Bv[d * bs + n];
-    // Abar^k = exp(k dt A)
-    acc = fmaf(Cv[d * cs + n] * ex2((float)k * (dt * An * kLog2e)), bbar, acc);
+    acc = fmaf(Cv[d * cs + n] * pk, bbar, acc);
   }
   K[d * L + k] = acc;
 }
@@ -1959,18 +2003,27 @@ int launch_status(const char* what) {
   return SSM_OK;
 }
 
+// calls f with the rule as a compile-time constant
+template <typename F>
+void with_rule(int rule, F&& f) {
+  switch (rule) {
+    case kRuleZoh: f(std::integral_constant<int, kRuleZoh>{}); break;
+    case kRuleEuler: f(std::integral_constant<int, kRuleEuler>{}); break;
+    case kRuleBilinear: f(std::integral_constant<int, kRuleBilinear>{}); break;
+    default: f(std::integral_constant<int, kRuleDeltaB>{}); break;
+  }
+}
+
 template <typename IO, int LPC, int K, int W, int NT, bool VEC>
-int launch_fwd_cfg(const ScanArgs& a, int64_t batch, bool zoh, bool gate, hipStream_t s) {
+int launch_fwd_cfg(const ScanArgs& a, int64_t batch, int rule, bool gate, hipStream_t s) {
   constexpr int CPB = (64 / LPC) * W;
   const dim3 grid((unsigned)((a.dim + CPB - 1) / CPB), (unsigned)batch);
   const size_t shmem = 2 * (size_t)CPB * (size_t)a.dstate * sizeof(float);
-  if (zoh) {
-    if (gate) hipLaunchKernelGGL((scan_fwd_kernel<IO, LPC, K, W, NT, VEC, true, true>), grid, dim3(64 * W), shmem, s, a);
-    else hipLaunchKernelGGL((scan_fwd_kernel<IO, LPC, K, W, NT, VEC, true, false>), grid, dim3(64 * W), shmem, s, a);
-  } else {
-    if (gate) hipLaunchKernelGGL((scan_fwd_kernel<IO, LPC, K, W, NT, VEC, false, true>), grid, dim3(64 * W), shmem, s, a);
-    else hipLaunchKernelGGL((scan_fwd_kernel<IO, LPC, K, W, NT, VEC, false, false>), grid, dim3(64 * W), shmem, s, a);
-  }
+  with_rule(rule, [&](auto rt) {
+    constexpr int R = decltype(rt)::value;
+    if (gate) hipLaunchKernelGGL((scan_fwd_kernel<IO, LPC, K, W, NT, VEC, R, true>), grid, dim3(64 * W), shmem, s, a);
+    else hipLaunchKernelGGL((scan_fwd_kernel<IO, LPC, K, W, NT, VEC, R, false>), grid, dim3(64 * W), shmem, s, a);
+  });
   return launch_status("ssm_selective_scan_fwd launch");
 }
 
@@ -1978,18 +2031,18 @@ int launch_fwd_cfg(const ScanArgs& a, int64_t batch, bool zoh, bool gate, hipStr
 // wider groups are used when there are too few channels to give every SIMD of
 // the 256 CUs several waves.
 template <typename IO, bool VEC>
-int launch_fwd_vec(const ScanArgs& a, int64_t batch, bool zoh, bool gate, hipStream_t s) {
+int launch_fwd_vec(const ScanArgs& a, int64_t batch, int rule, bool gate, hipStream_t s) {
   constexpr int K = SELSCAN_K, W = SELSCAN_W, NT = SELSCAN_NT;
   const int64_t channels = batch * a.dim;
-  if (channels >= 4 * 4096) return launch_fwd_cfg<IO, 16, K, W, NT, VEC>(a, batch, zoh, gate, s);
-  if (channels >= 2 * 4096) return launch_fwd_cfg<IO, 32, K, W, NT / 2, VEC>(a, batch, zoh, gate, s);
-  return launch_fwd_cfg<IO, 64, K, W, NT / 4, VEC>(a, batch, zoh, gate, s);
+  if (channels >= 4 * 4096) return launch_fwd_cfg<IO, 16, K, W, NT, VEC>(a, batch, rule, gate, s);
+  if (channels >= 2 * 4096) return launch_fwd_cfg<IO, 32, K, W, NT / 2, VEC>(a, batch, rule, gate, s);
+  return launch_fwd_cfg<IO, 64, K, W, NT / 4, VEC>(a, batch, rule, gate, s);
 }
 
 template <typename IO>
-int launch_fwd(const ScanArgs& a, int64_t batch, bool zoh, bool gate, bool vec, hipStream_t s) {
-  return vec ? launch_fwd_vec<IO, true>(a, batch, zoh, gate, s)
-             : launch_fwd_vec<IO, false>(a, batch, zoh, gate, s);
+int launch_fwd(const ScanArgs& a, int64_t batch, int rule, bool gate, bool vec, hipStream_t s) {
+  return vec ? launch_fwd_vec<IO, true>(a, batch, rule, gate, s)
+             : launch_fwd_vec<IO, false>(a, batch, rule, gate, s);
 }
 
 // Backward: the gradient pass works on chunks of T = 16 * kBwdK = kCkptT steps.
@@ -2022,7 +2075,7 @@ int launch_bwd_typed(const ScanArgs& fa, BwdArgs ba, int64_t batch, hipStream_t 
   const dim3 grid16((unsigned)((ba.dim + 15) / 16), (unsigned)batch);
   // 1. checkpoints: the state entering every kCkptT-step block (a forward
   // pass over 256-step chunks)
-  hipLaunchKernelGGL((scan_fwd_kernel<IO, 16, 16, 4, 16, VEC, ZOH, false, true>), grid16, dim3(256),
+  hipLaunchKernelGGL((scan_fwd_kernel<IO, 16, 16, 4, 16, VEC, ZOH ? kRuleZoh : kRuleDeltaB, false, true>), grid16, dim3(256),
                      2 * 16 * (size_t)ba.dstate * sizeof(float), s, fa);
   // 2. adjoint carries at every block end (a reverse pass over 256-step chunks)
   hipLaunchKernelGGL((scan_bwd_carry_kernel<IO, 16, VEC, GATE>), grid16, dim3(256), 0, s, ba);
@@ -2196,7 +2249,7 @@ int ssm_selective_scan_fwd(const void* u, const void* delta, const float* A, con
     return fail(SSM_E_SHAPE, "tensor sizes overflow");
   if (io_dtype != SSM_DTYPE_F32 && io_dtype != SSM_DTYPE_BF16)
     return fail(SSM_E_DTYPE, "io_dtype = %d is not SSM_DTYPE_F32 or SSM_DTYPE_BF16", io_dtype);
-  if (bbar_mode != SSM_BBAR_DELTA_B && bbar_mode != SSM_BBAR_ZOH_EXACT)
+  if (bbar_mode < SSM_BBAR_DELTA_B || bbar_mode > SSM_DISC_BILINEAR)
     return fail(SSM_E_DTYPE, "bbar_mode = %d is not a known rule", bbar_mode);
   if (dstate > kMaxDstate)
     return fail(SSM_E_UNSUPPORTED, "dstate = %lld is outside 1..%lld", (long long)dstate,
@@ -2237,9 +2290,9 @@ int ssm_selective_scan_fwd(const void* u, const void* delta, const float* A, con
   a.softplus = delta_softplus ? 1 : 0;
   const bool vec = (seqlen % (io_dtype == SSM_DTYPE_BF16 ? 8 : 4)) == 0;
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
-  const bool zoh = bbar_mode == SSM_BBAR_ZOH_EXACT, gate = z != nullptr;
-  return io_dtype == SSM_DTYPE_BF16 ? launch_fwd<uint16_t>(a, batch, zoh, gate, vec, s)
-                                    : launch_fwd<float>(a, batch, zoh, gate, vec, s);
+  const bool gate = z != nullptr;
+  return io_dtype == SSM_DTYPE_BF16 ? launch_fwd<uint16_t>(a, batch, bbar_mode, gate, vec, s)
+                                    : launch_fwd<float>(a, batch, bbar_mode, gate, vec, s);
 }
 
 int ssm_state_update(float* state, const void* u, const void* delta, const float* A,
@@ -2261,7 +2314,7 @@ int ssm_state_update(float* state, const void* u, const void* delta, const float
   if (!product_ok(batch, dim, dstate, 4)) return fail(SSM_E_SHAPE, "tensor sizes overflow");
   if (io_dtype != SSM_DTYPE_F32 && io_dtype != SSM_DTYPE_BF16)
     return fail(SSM_E_DTYPE, "io_dtype = %d is not SSM_DTYPE_F32 or SSM_DTYPE_BF16", io_dtype);
-  if (bbar_mode != SSM_BBAR_DELTA_B && bbar_mode != SSM_BBAR_ZOH_EXACT)
+  if (bbar_mode < SSM_BBAR_DELTA_B || bbar_mode > SSM_DISC_BILINEAR)
     return fail(SSM_E_DTYPE, "bbar_mode = %d is not a known rule", bbar_mode);
   if (dstate > kMaxDstate)
     return fail(SSM_E_UNSUPPORTED, "dstate = %lld is outside 1..%lld", (long long)dstate,
@@ -2287,20 +2340,17 @@ int ssm_state_update(float* state, const void* u, const void* delta, const float
   if (grid.x == 0 || (threads + 255) / 256 > 0x7fffffff)
     return fail(SSM_E_SHAPE, "batch * dim too large for one launch");
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
-  const bool zoh = bbar_mode == SSM_BBAR_ZOH_EXACT, gate = z != nullptr;
-#define SSM_STEP(IO)                                                                         \
-  do {                                                                                       \
-    if (zoh) {                                                                               \
-      if (gate) hipLaunchKernelGGL((state_update_kernel<IO, true, true>), grid, dim3(256), 0, s, a);   \
-      else hipLaunchKernelGGL((state_update_kernel<IO, true, false>), grid, dim3(256), 0, s, a);       \
-    } else {                                                                                 \
-      if (gate) hipLaunchKernelGGL((state_update_kernel<IO, false, true>), grid, dim3(256), 0, s, a);  \
-      else hipLaunchKernelGGL((state_update_kernel<IO, false, false>), grid, dim3(256), 0, s, a);      \
-    }                                                                                        \
-  } while (0)
-  if (io_dtype == SSM_DTYPE_BF16) SSM_STEP(uint16_t);
-  else SSM_STEP(float);
-#undef SSM_STEP
+  const bool gate = z != nullptr;
+  with_rule(bbar_mode, [&](auto rt) {
+    constexpr int R = decltype(rt)::value;
+    if (io_dtype == SSM_DTYPE_BF16) {
+      if (gate) hipLaunchKernelGGL((state_update_kernel<uint16_t, R, true>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((state_update_kernel<uint16_t, R, false>), grid, dim3(256), 0, s, a);
+    } else {
+      if (gate) hipLaunchKernelGGL((state_update_kernel<float, R, true>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((state_update_kernel<float, R, false>), grid, dim3(256), 0, s, a);
+    }
+  });
   return launch_status("ssm_state_update launch");
 }
 
@@ -2322,7 +2372,7 @@ int ssm_lti_kernel(const float* A, const float* Bv, const float* Cv, const float
     return fail(SSM_E_SHAPE, "tensor sizes overflow");
   if (b_row_stride < 0 || c_row_stride < 0)
     return fail(SSM_E_SHAPE, "row strides must be >= 0");
-  if (bbar_mode != SSM_BBAR_DELTA_B && bbar_mode != SSM_BBAR_ZOH_EXACT)
+  if (bbar_mode < SSM_BBAR_DELTA_B || bbar_mode > SSM_DISC_BILINEAR)
     return fail(SSM_E_DTYPE, "bbar_mode = %d is not a known rule", bbar_mode);
   const Span ks{K, dim * L * 4, "K"};
   const Span in[] = {{A, dim * dstate * 4, "A"},
@@ -2333,12 +2383,11 @@ int ssm_lti_kernel(const float* A, const float* Bv, const float* Cv, const float
     if (overlaps(ks, s)) return fail(SSM_E_ALIAS, "K overlaps %s", s.name);
   const dim3 grid((unsigned)((L + 255) / 256), (unsigned)dim);
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
-  if (bbar_mode == SSM_BBAR_ZOH_EXACT)
-    hipLaunchKernelGGL(lti_kernel_kernel<true>, grid, dim3(256), 0, s, A, Bv, Cv, delta, K, dim,
+  with_rule(bbar_mode, [&](auto rt) {
+    constexpr int R = decltype(rt)::value;
+    hipLaunchKernelGGL(lti_kernel_kernel<R>, grid, dim3(256), 0, s, A, Bv, Cv, delta, K, dim,
                        dstate, L, b_row_stride, c_row_stride);
-  else
-    hipLaunchKernelGGL(lti_kernel_kernel<false>, grid, dim3(256), 0, s, A, Bv, Cv, delta, K, dim,
-                       dstate, L, b_row_stride, c_row_stride);
+  });
   return launch_status("ssm_lti_kernel launch");
 }
 
@@ -2374,8 +2423,11 @@ int ssm_selective_scan_bwd(const void* u, const void* delta, const float* A, con
     return fail(SSM_E_SHAPE, "tensor sizes overflow");
   if (io_dtype != SSM_DTYPE_F32 && io_dtype != SSM_DTYPE_BF16)
     return fail(SSM_E_DTYPE, "io_dtype = %d is not SSM_DTYPE_F32 or SSM_DTYPE_BF16", io_dtype);
-  if (bbar_mode != SSM_BBAR_DELTA_B && bbar_mode != SSM_BBAR_ZOH_EXACT)
+  if (bbar_mode < SSM_BBAR_DELTA_B || bbar_mode > SSM_DISC_BILINEAR)
     return fail(SSM_E_DTYPE, "bbar_mode = %d is not a known rule", bbar_mode);
+  if (bbar_mode != SSM_BBAR_DELTA_B && bbar_mode != SSM_BBAR_ZOH_EXACT)
+    return fail(SSM_E_UNSUPPORTED, "the backward takes the exp rules (bbar_mode 0 or 1), got %d",
+                bbar_mode);
   if (dstate > kBwdMaxDstate)
     return fail(SSM_E_UNSUPPORTED, "backward supports dstate 1..%lld, got %lld",
                 (long long)kBwdMaxDstate, (long long)dstate);

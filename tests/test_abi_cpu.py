@@ -80,7 +80,7 @@ def step_args(**over):
 
 @pytest.mark.parametrize("over,status", [
     (dict(state=None), 1), (dict(y=None), 1), (dict(B=None), 1),
-    (dict(dim=0), 2), (dict(io=5), 3), (dict(bbar=2), 3), (dict(N=100), 6),
+    (dict(dim=0), 2), (dict(io=5), 3), (dict(bbar=4), 3), (dict(N=100), 6),
     (dict(state=1 * P + 4), 4),
     (dict(y=1 * P), 5), (dict(state=2 * P), 5),
 ])
@@ -93,7 +93,7 @@ def test_lti_kernel_validation(lib):
     assert f(None, 2 * P, 3 * P, 4 * P, 5 * P, 4, 4, 16, 0, 0, 0, None) == 1
     assert f(1 * P, 2 * P, 3 * P, 4 * P, 5 * P, 4, 4, 0, 0, 0, 0, None) == 2
     assert f(1 * P, 2 * P, 3 * P, 4 * P, 5 * P, 4, 4, 16, -1, 0, 0, None) == 2
-    assert f(1 * P, 2 * P, 3 * P, 4 * P, 5 * P, 4, 4, 16, 0, 0, 3, None) == 3
+    assert f(1 * P, 2 * P, 3 * P, 4 * P, 5 * P, 4, 4, 16, 0, 0, 4, None) == 3
     assert f(1 * P, 2 * P, 3 * P, 4 * P, 1 * P, 4, 4, 16, 0, 0, 0, None) == 5
 
 
@@ -146,7 +146,7 @@ def test_bwd_workspace_size(lib):
     (dict(du=7 * P + 2), 4), (dict(ws=12 * P + 8), 4),
     (dict(du=1 * P), 5), (dict(dA=3 * P), 5), (dict(dB=10 * P + 64, dC=10 * P + 64), 5),
     (dict(ws=6 * P), 5), (dict(dh0=9 * P), 5),
-    (dict(N=17), 6), (dict(N=64), 6),
+    (dict(N=17), 6), (dict(N=64), 6), (dict(bbar=2), 6), (dict(bbar=3), 6),
 ])
 def test_bwd_validation(lib, over, status):
     assert lib.ssm_selective_scan_bwd(*bwd_args(**over)) == status

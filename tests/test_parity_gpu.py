@@ -155,6 +155,27 @@ def test_exact_zoh_rule(ssm, dev, dt):
     _check(ssm, dev, w, x, bbar="zoh", label=f"zoh {dt}")
 
 
+# Euler and bilinear rules: the three lane layouts (64, 32 and 16 lanes per
+# channel, chosen by the channel count), ragged lengths, both dtypes.  Euler
+# is run with small steps (raw delta ~ N(-4, 0.5) through softplus) so that
+# |1 + delta A| stays below 1 and the recurrence stays bounded.
+RULE_CASES = [  # batch, dim, N, L
+    (2, 24, 16, 600),
+    (1, 8200, 4, 72),
+    (2, 8200, 4, 41),
+]
+
+
+@pytest.mark.parametrize("rule", ["euler", "bilinear"])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("case", RULE_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_discretization_rules(ssm, dev, rule, dt, case):
+    b, d, n, L = case
+    kw = dict(delta_mean=-4.0, delta_std=0.5, bias=False) if rule == "euler" else {}
+    w, x = wl.custom(b, d, n, L, dtype=dt, gate=True, seed=120 + L, **kw)
+    _check(ssm, dev, w, x, bbar=rule, label=f"{rule} {dt} {case}")
+
+
 def test_no_softplus_positive_raw_step(ssm, dev):
     w, x = wl.custom(1, 20, 8, 300, dtype="f32", gate=False, bias=False, seed=41)
     x["delta"] = np.abs(x["delta"]) * np.float32(0.1)
@@ -220,8 +241,9 @@ def test_decode_steps_replay_the_scan(ssm, dev):
     assert norm_err(to_np(state), to_np(fs)) <= TOL["f32"]
 
 
+@pytest.mark.parametrize("rule", ["delta", "zoh", "euler", "bilinear"])
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-def test_state_update_small_shapes(ssm, dev, dt):
+def test_state_update_small_shapes(ssm, dev, dt, rule):
     for (b, d, n) in [(1, 1, 1), (3, 7, 5), (2, 33, 16), (5, 19, 64)]:
         w, x = wl.custom(b, d, n, 1, dtype=dt, gate=True, seed=90 + n)
         col = {k: np.ascontiguousarray(v[..., 0]) for k, v in x.items()
@@ -231,19 +253,20 @@ def test_state_update_small_shapes(ssm, dev, dt):
         y = ssm.ssm_state_update(state, to_dev(col["u"], dev), to_dev(col["delta"], dev),
                                  to_dev(x["A"], dev), to_dev(col["B"], dev), to_dev(col["C"], dev),
                                  D=to_dev(x["D"], dev), z=to_dev(col["z"], dev),
-                                 delta_bias=to_dev(x["delta_bias"], dev), delta_softplus=True)
+                                 delta_bias=to_dev(x["delta_bias"], dev), delta_softplus=True,
+                                 bbar=rule)
         torch.cuda.synchronize()
         ref = s0.reshape(-1, n).astype(np.float64)
         yr = oracle.state_update(ref, col["u"], col["delta"], x["A"], col["B"], col["C"],
                                  D=x["D"], z=col["z"], delta_bias=x["delta_bias"],
-                                 delta_softplus=True)
+                                 delta_softplus=True, bbar=rule)
         assert norm_err(to_np(y).reshape(-1), yr) <= TOL[dt]
         assert norm_err(to_np(state).reshape(ref.shape), ref) <= TOL[dt]
 
 
 # ---------------------------------------------------------------- LTI check path
 
-@pytest.mark.parametrize("bbar", ["delta", "zoh"])
+@pytest.mark.parametrize("bbar", ["delta", "zoh", "euler", "bilinear"])
 def test_lti_kernel_matches_oracle(ssm, dev, bbar):
     r = np.random.default_rng(5)
     dim, N, L = 12, 16, 700
