@@ -284,6 +284,18 @@ int ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void* Bm, c
 /* Bytes of workspace ssm_ssd_fwd needs (-1 if an extent is out of range). */
 int64_t ssm_ssd_workspace_size(int64_t batch, int64_t seqlen, int64_t ngroups, int64_t dstate);
 
+/*
+ * Time-invariant path: y = K * u + D u, the causal convolution of every
+ * channel with its kernel K_k = C Abar^k Bbar (from ssm_lti_kernel), which is
+ * what the recurrence computes when delta, B and C do not depend on the
+ * input ("State-space models", section "Recurrence and convolution").
+ *  K      [dim, seqlen] float32
+ *  u, y   [batch, dim, seqlen] io_dtype;  Dskip [dim] float32 or NULL
+ * Direct sum in float32: O(seqlen^2) work per channel.
+ */
+int ssm_lti_conv(const float* K, const void* u, const float* Dskip, void* y, int64_t batch,
+                 int64_t dim, int64_t seqlen, int io_dtype, void* hip_stream);
+
 /* Static description of a status code (never NULL). */
 const char* ssm_status_str(int status);
 

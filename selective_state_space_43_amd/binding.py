@@ -143,6 +143,26 @@ def ssm_lti_kernel(A, Bv, Cv, delta, L, bbar="delta", K=None):
     return K
 
 
+def ssm_lti_conv(K, u, D=None, y=None):
+    """y = K * u + D u per channel (causal): K [dim, L] float32, u [batch, dim, L]."""
+    _dev(u, "u", None)
+    dev = u.device
+    if u.dim() != 3 or u.dtype not in _IO:
+        raise TypeError("u must be [batch, dim, L] bfloat16 or float32")
+    batch, dim, L = u.shape
+    _io(K, "K", torch.float32, (dim, L), dev)
+    _f32(D, "D", (dim,), dev)
+    if y is None:
+        y = torch.empty_like(u)
+    else:
+        _io(y, "y", u.dtype, (batch, dim, L), dev)
+    with torch.cuda.device(dev):
+        st = lib().ssm_lti_conv(_ptr(K), _ptr(u), _ptr(D), _ptr(y), batch, dim, L, _IO[u.dtype],
+                                _stream(dev))
+    check(st, "ssm_lti_conv")
+    return y
+
+
 def ssm_selective_scan_bwd_workspace_size(batch, dim, dstate, seqlen):
     n = lib().ssm_selective_scan_bwd_workspace_size(batch, dim, dstate, seqlen)
     if n < 0:

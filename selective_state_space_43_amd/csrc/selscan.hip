@@ -1950,6 +1950,52 @@ __global__ void __launch_bounds__(256)
   K[d * L + k] = acc;
 }
 
+// ---------------------------------------------------------------- LTI convolution
+//
+// y[t] = sum_{k<=t} K[k] u[t-k] + D u[t] per (sequence, channel): the
+// time-invariant path, where the recurrence collapses into one causal
+// convolution with the kernel K_k = C Abar^k Bbar ("State-space models",
+// section "Recurrence and convolution").  Direct sum: a workgroup owns 256
+// consecutive outputs of one row and walks the inputs before them in
+// 256-step tiles, with the tile of u and the 511 kernel lags it needs staged
+// in LDS; each thread accumulates its output in float32.
+template <typename IO>
+__global__ void __launch_bounds__(256) lti_conv_kernel(const float* K, const void* u,
+                                                       const float* Dskip, void* y, int64_t dim,
+                                                       int64_t L) {
+  __shared__ float sU[256];
+  __shared__ float sK[512];
+  const int64_t t0 = (int64_t)blockIdx.x * 256, d = blockIdx.y, b = blockIdx.z;
+  const int64_t row = (b * dim + d) * L;
+  const int64_t t = t0 + threadIdx.x;
+  const float* Kd = K + d * L;
+  float acc = 0.0f;
+  // input tiles s0 = t0 - 256 j, j = 0 .. t0 / 256
+  for (int64_t s0 = t0; s0 >= 0; s0 -= 256) {
+    __syncthreads();  // the previous tile is no longer read
+    const int64_t s = s0 + threadIdx.x;
+    sU[threadIdx.x] = s < L ? Io<IO>::ld1(u, row + s) : 0.0f;
+    // lags k = t - s for t in [t0, t0 + 256), s in [s0, s0 + 256): k in
+    // [t0 - s0 - 255, t0 - s0 + 255]; sK[i] = K[t0 - s0 - 255 + i]
+    for (int i = threadIdx.x; i < 511; i += 256) {
+      const int64_t k = t0 - s0 - 255 + i;
+      sK[i] = (k >= 0 && k < L) ? Kd[k] : 0.0f;
+    }
+    __syncthreads();
+    // t - s = (t0 - s0) + threadIdx.x - j  ->  sK index threadIdx.x - j + 255
+    if (s0 == t0) {  // the diagonal tile: only s <= t
+      for (int j = 0; j <= (int)threadIdx.x; ++j) acc = fmaf(sK[threadIdx.x - j + 255], sU[j], acc);
+    } else {
+#pragma unroll 8
+      for (int j = 0; j < 256; ++j) acc = fmaf(sK[threadIdx.x - j + 255], sU[j], acc);
+    }
+  }
+  if (t < L) {
+    const float ut = Io<IO>::ld1(u, row + t);
+    Io<IO>::st1(y, row + t, fmaf(Dskip ? Dskip[d] : 0.0f, ut, acc));
+  }
+}
+
 // ---------------------------------------------------------------- host side
 
 thread_local char g_last_error[512] = "";
@@ -2701,6 +2747,36 @@ int ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void* Bm, c
     default: launch_ssd<256>(a, gate, s); break;
   }
   return launch_status("ssm_ssd_fwd launch");
+}
+
+int ssm_lti_conv(const float* K, const void* u, const float* Dskip, void* y, int64_t batch,
+                 int64_t dim, int64_t seqlen, int io_dtype, void* hip_stream) {
+  g_last_error[0] = 0;
+  if (!K) return fail(SSM_E_NULL, "K is NULL");
+  if (!u) return fail(SSM_E_NULL, "u is NULL");
+  if (!y) return fail(SSM_E_NULL, "y is NULL");
+  int st;
+  if ((st = check_extent("batch", batch)) || (st = check_extent("dim", dim)) ||
+      (st = check_extent("seqlen", seqlen)))
+    return st;
+  if (batch > 65535 || dim > 65535) return fail(SSM_E_SHAPE, "batch and dim must be <= 65535");
+  if (seqlen > ((int64_t)1 << 24)) return fail(SSM_E_SHAPE, "seqlen = %lld is too long", (long long)seqlen);
+  if (!product_ok(batch, dim, seqlen, 4)) return fail(SSM_E_SHAPE, "tensor sizes overflow");
+  if (io_dtype != SSM_DTYPE_F32 && io_dtype != SSM_DTYPE_BF16)
+    return fail(SSM_E_DTYPE, "io_dtype = %d is not SSM_DTYPE_F32 or SSM_DTYPE_BF16", io_dtype);
+  const int64_t es = io_dtype == SSM_DTYPE_BF16 ? 2 : 4;
+  const Span ys{y, batch * dim * seqlen * es, "y"};
+  const Span in[] = {{K, dim * seqlen * 4, "K"}, {u, batch * dim * seqlen * es, "u"},
+                     {Dskip, dim * 4, "D"}};
+  for (const Span& s : in)
+    if (overlaps(ys, s)) return fail(SSM_E_ALIAS, "y overlaps %s", s.name);
+  const dim3 grid((unsigned)((seqlen + 255) / 256), (unsigned)dim, (unsigned)batch);
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  if (io_dtype == SSM_DTYPE_BF16)
+    hipLaunchKernelGGL(lti_conv_kernel<uint16_t>, grid, dim3(256), 0, s, K, u, Dskip, y, dim, seqlen);
+  else
+    hipLaunchKernelGGL(lti_conv_kernel<float>, grid, dim3(256), 0, s, K, u, Dskip, y, dim, seqlen);
+  return launch_status("ssm_lti_conv launch");
 }
 
 }  // extern "C"

@@ -234,3 +234,13 @@ def test_ssd_workspace_size(lib):
 ])
 def test_ssd_validation(lib, over, status):
     assert lib.ssm_ssd_fwd(*ssd_args(**over)) == status
+
+
+def test_lti_conv_validation(lib):
+    f = lib.ssm_lti_conv
+    assert f(None, 2 * P, None, 3 * P, 2, 4, 64, 1, None) == 1
+    assert f(1 * P, None, None, 3 * P, 2, 4, 64, 1, None) == 1
+    assert f(1 * P, 2 * P, None, 3 * P, 2, 4, 0, 1, None) == 2
+    assert f(1 * P, 2 * P, None, 3 * P, 2, 4, 64, 9, None) == 3
+    assert f(1 * P, 2 * P, None, 2 * P, 2, 4, 64, 1, None) == 5
+    assert f(1 * P, 2 * P, None, 1 * P, 2, 4, 64, 1, None) == 5
