@@ -45,9 +45,17 @@ KERNEL_SRC = os.path.join(ROOT, "selective_state_space_43_amd", "csrc", "selscan
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "scan_fwd_mamba2p8b_pmc.md")
 
 
+SCAN_SOURCE_END = b"// ---------------------------------------------------------------- backward"
+
+
 def kernel_source_hash() -> str:
+    """Hash of the forward scan's source: selscan.hip up to the backward
+    section (the helpers and scan_fwd_kernel); later kernels do not change
+    the scan's traffic."""
     with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+        src = f.read()
+    end = src.find(SCAN_SOURCE_END)
+    return hashlib.sha256(src[:end] if end >= 0 else src).hexdigest()[:16]
 
 
 def committed_traffic():
