@@ -272,8 +272,8 @@ int ssm_causal_conv1d_bwd(const void* x, const float* weight, const float* bias,
  *               16-byte aligned, owned by the caller; calls sharing it must
  *               not run concurrently
  * io_dtype must be SSM_DTYPE_BF16, headdim 64 and dstate one of 32, 64, 128,
- * 256 (SSM_E_UNSUPPORTED otherwise); nheads a multiple of ngroups.  Outputs
- * must not overlap inputs.
+ * 256 (SSM_E_UNSUPPORTED otherwise); nheads a multiple of ngroups; seqlen at
+ * most 65535 x 64 (SSM_E_SHAPE otherwise).  Outputs must not overlap inputs.
  */
 int ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void* Bm, const void* Cm,
                 const float* Dskip, const void* z, const float* dt_bias, int dt_softplus,

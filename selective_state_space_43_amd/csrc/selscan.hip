@@ -1540,40 +1540,113 @@ __global__ void __launch_bounds__(256) ssd_prep_kernel(const SsdArgs a) {
   }
 }
 
+typedef float f32x2v_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+
+// two floats rounded to bf16 (nearest even), packed low then high
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  const f32x2v_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v_t));
+}
+
+// v = hi + lo for two floats: hi their bf16 rounding, lo the bf16 rounding of
+// the remainder (about 16 significant bits together)
+__device__ __forceinline__ void split_bf16(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = pk_bf16(a, b);
+  lo = pk_bf16(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
+}
+
+// Raw buffer accesses: a 32-bit byte offset from a base whose extent is
+// given, and reads past the extent return zero, so addresses need no clamps.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_ld128(Rsrc r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ uint2 buf_ld64(Rsrc r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+__device__ __forceinline__ uint32_t buf_ld16(Rsrc r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
+__device__ __forceinline__ void buf_st64(uint2 v, Rsrc r, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int, v), r, voff, soff, 0);
+}
+__device__ __forceinline__ void buf_st16(uint32_t v, Rsrc r, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v, r, voff, soff, 0);
+}
+
+// 8 (4) bf16 of a row at byte offset voff + soff: one 16-byte (8-byte) load
+// when rows are 16-byte aligned, else 2-byte loads
+template <bool ALIGNED>
+__device__ __forceinline__ uint4 buf_ld8_bf16(Rsrc r, uint32_t voff, uint32_t soff) {
+  if constexpr (ALIGNED) {
+    return buf_ld128(r, voff, soff);
+  } else {
+    uint32_t e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = buf_ld16(r, voff + 2 * j, soff);
+    return make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16));
+  }
+}
+template <bool ALIGNED>
+__device__ __forceinline__ uint2 buf_ld4_bf16(Rsrc r, uint32_t voff, uint32_t soff) {
+  if constexpr (ALIGNED) {
+    return buf_ld64(r, voff, soff);
+  } else {
+    uint32_t e[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) e[j] = buf_ld16(r, voff + 2 * j, soff);
+    return make_uint2(e[0] | (e[1] << 16), e[2] | (e[3] << 16));
+  }
+}
+
 // One workgroup per (sequence, head, half of the 64 head channels); four
-// waves.  Wave w owns output tile columns t in [16w, 16w + 16) (two 16x16
-// tiles of Y^T, one per 16 channels), state n-blocks w, w + 4, ... (32 x 32
-// tiles of S^T), and for w < 3 one 32x32 tile of M.
+// waves.  Wave w owns the output rows t in [16w, 16w + 16) (two 16x16 tiles
+// of Y, one per 16 channels), the state n-blocks w, w + 4, ... (32 x 32
+// tiles of S^T) and 12 of the 48 (tile, accumulator) slots of the three
+// non-zero 32 x 32 tiles of M.  Per chunk:
+//   1. step sizes and running decay (lane = step);
+//   2. x and the weighted x (hi, lo) to LDS, M (hi, lo) to LDS;
+//   3. Y = C S^T scaled by exp(cs_t), + M X, then D x and the gate; the
+//      state update S^T = exp(cs_63) S^T + B^T (w o X);
+//   4. the new state (hi, lo) to LDS.
+// The operands of chunk c + 1 are loaded into the other register set while
+// chunk c is computed; every load of chunk c is waited for at the top of its
+// iteration, before anything else is issued, so no store is pending at a
+// wait that should only cover loads.
 template <int N, bool GATE, bool ALIGNED>
 __global__ void __launch_bounds__(256) ssd_fwd_kernel(const SsdArgs a) {
   constexpr int T = kSsdT, PB = kSsdPB, XP = T + 8, SP = N + 8, MP = T + 8;
   constexpr int NB = N / 32, NBW = (NB + 3) / 4;  // state n-blocks, per wave
-  __shared__ __align__(16) uint16_t sX[PB * XP];   // x of the chunk, [p][t]
-  __shared__ __align__(16) uint16_t sZ[GATE ? PB * XP : 8];
-  __shared__ __align__(16) uint16_t sY[PB * XP];
-  __shared__ __align__(16) uint16_t sM[T * MP];    // M[t][s], bf16 head
-  __shared__ __align__(16) uint16_t sMl[T * MP];   // and remainder
-  __shared__ __align__(16) uint16_t sS[PB * SP];   // S[p][n] entering the chunk, bf16 head
-  __shared__ __align__(16) uint16_t sSl[PB * SP];  // and remainder
-  // per wave: running decay (log2), step, and the weight exp(cs_63 - cs_s) dt_s
-  // of step s in the state update
-  __shared__ __align__(16) float sCs[4][T];
-  __shared__ __align__(16) float sDt[4][T];
-  __shared__ __align__(16) float sW[4][T];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ __align__(16) uint16_t sX[PB * XP];    // x of the chunk, [p][t]
+  __shared__ __align__(16) uint16_t sXw[PB * XP];   // w o x, [p][s], bf16 head
+  __shared__ __align__(16) uint16_t sXwl[PB * XP];  // and remainder
+  __shared__ __align__(16) uint16_t sM[T * MP];     // M[t][s], bf16 head
+  __shared__ __align__(16) uint16_t sMl[T * MP];    // and remainder
+  __shared__ __align__(16) uint16_t sS[PB * SP];    // S[p][n] entering the chunk, bf16 head
+  __shared__ __align__(16) uint16_t sSl[PB * SP];   // and remainder
+  // per step: running decay cs (log2 units), step dt, exp(cs), and the
+  // weight exp(cs_63 - cs_s) dt_s of step s in the state update
+  __shared__ __align__(16) float sCs[T], sDt[T], sE[T], sW[T];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t h = blockIdx.x >> 1, pb = blockIdx.x & 1, b = blockIdx.y;
   const int64_t g = h / (a.H / a.G), L = a.L;
   const float Ah2 = a.A[h] * kLog2e;  // decays are kept in log2 units
   const float Dh = a.Dskip ? a.Dskip[h] : 0.0f;
   const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
   const int64_t row0 = (b * a.H * kSsdP + h * kSsdP + pb * PB) * L;  // this workgroup's first channel row
-  const uint16_t* xg = static_cast<const uint16_t*>(a.x) + row0;
-  const uint16_t* zg = GATE ? static_cast<const uint16_t*>(a.z) + row0 : nullptr;
-  uint16_t* yg = static_cast<uint16_t*>(a.y) + row0;
-  const uint16_t* dtg = static_cast<const uint16_t*>(a.dt) + (b * a.H + h) * L;
-  const uint16_t* Bg = static_cast<const uint16_t*>(a.Bm) + (b * a.G + g) * N * L;
-  const uint16_t* Ctg = a.Ct + (b * a.G + g) * a.nchunks * T * N;
-  const float* Gg = a.Gf + (b * a.G + g) * a.nchunks * 3 * 64 * 16;
+  // buffers: this workgroup's channel rows of x, z, y; its head's steps; its
+  // group's B rows, token-major C and C.B^T tiles
+  const Rsrc rX = make_rsrc(static_cast<const uint16_t*>(a.x) + row0, PB * L * 2);
+  const Rsrc rZ = make_rsrc(GATE ? static_cast<const uint16_t*>(a.z) + row0 : a.x, PB * L * 2);
+  const Rsrc rY = make_rsrc(static_cast<uint16_t*>(a.y) + row0, PB * L * 2);
+  const Rsrc rDt = make_rsrc(static_cast<const uint16_t*>(a.dt) + (b * a.H + h) * L, L * 2);
+  const Rsrc rB = make_rsrc(static_cast<const uint16_t*>(a.Bm) + (b * a.G + g) * N * L, N * L * 2);
+  const Rsrc rC = make_rsrc(a.Ct + (b * a.G + g) * a.nchunks * T * N, a.nchunks * T * N * 2);
+  const Rsrc rG = make_rsrc(a.Gf + (b * a.G + g) * a.nchunks * 3 * 64 * 16, a.nchunks * 3 * 64 * 16 * 4);
   const int64_t st0 = ((b * a.H + h) * kSsdP + pb * PB) * N;  // state rows of this workgroup
 
   // ---- state: S^T tiles in accumulators; lane: p = lane % 32, n = nb*32 + row(i)
@@ -1595,17 +1668,9 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(const SsdArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int n = nb * 32 + r * 8 + (lane / 32) * 4;
-          float hv[4], lv[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            hv[e] = bf16_round(S[q][4 * r + e]);
-            lv[e] = S[q][4 * r + e] - hv[e];
-          }
           uint2 v, w;
-          v.x = pack_bf16x2(hv[0], hv[1]);
-          v.y = pack_bf16x2(hv[2], hv[3]);
-          w.x = pack_bf16x2(lv[0], lv[1]);
-          w.y = pack_bf16x2(lv[2], lv[3]);
+          split_bf16(S[q][4 * r], S[q][4 * r + 1], v.x, w.x);
+          split_bf16(S[q][4 * r + 2], S[q][4 * r + 3], v.y, w.y);
           *reinterpret_cast<uint2*>(sS + (lane % 32) * SP + n) = v;
           *reinterpret_cast<uint2*>(sSl + (lane % 32) * SP + n) = w;
         }
@@ -1614,186 +1679,208 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(const SsdArgs a) {
   };
   write_state_bf16();
 
-  // ---- per-chunk operands, loaded one chunk ahead
+  // ---- per-chunk operands, loaded one chunk ahead into the other set
   const int xp = threadIdx.x / 8, xt8 = (threadIdx.x % 8) * 8;  // staging: channel row, 8 steps
+  const int ty = 16 * wave + (lane / 16) * 4;                      // first Y row of this lane
   struct Pre {
-    uint4 xv, zv;
-    uint16_t dtr;
-    f32x16_t gfr;
-    uint4 ct[N / 32];      // C^T fragments of this wave's t columns
-    uint4 bt[NBW][4];      // B^T fragments of this wave's state n-blocks
+    uint4 xv;
+    uint2 zv[2];           // z at the lane's Y rows, for its two channels
+    uint32_t dtr;
+    float4 gf[3];          // this wave's 12 slots of C.B^T
+    uint4 ct[N / 32];      // C[t = 16 wave + lane % 16][32 k + (lane/16)*8 + j]
+    uint4 bt[NBW][4];      // B^T[n = nb*32 + lane % 32][16 ks + (lane/32)*8 + j]
   };
-  Pre nx;
-  auto fetch = [&](int64_t c) {
-    const int64_t t0 = c * T;
-    nx.xv = load8_bf16<ALIGNED>(xg + xp * L, t0 + xt8, L);
-    if constexpr (GATE) nx.zv = load8_bf16<ALIGNED>(zg + xp * L, t0 + xt8, L);
-    nx.dtr = dtg[t0 + lane < L ? t0 + lane : L - 1];  // steps past L are zeroed where used
-    if (wave < 3) {
-      const float* gp = Gg + ((c * 3 + wave) * 64 + lane) * 16;
+  // per-lane byte offsets; the chunk's offset is added as a scalar.  Reads
+  // past the end of a row return another row's (finite) inputs or zero: every
+  // product with a step past L is multiplied by that step's dt, which is set
+  // to zero, and outputs past L are not stored.
+  const uint32_t oX = (uint32_t)((xp * L + xt8) * 2);
+  const uint32_t oZ = (uint32_t)(((lane % 16) * L + ty) * 2), oZ16 = (uint32_t)(16 * L * 2);
+  const uint32_t oC = (uint32_t)(((16 * wave + lane % 16) * N + (lane / 16) * 8) * 2);
+  const uint32_t oB = (uint32_t)(((wave * 32 + lane % 32) * L + (lane / 32) * 8) * 2), oB4 = (uint32_t)(128 * L * 2);
+  // the operands of a chunk are loaded piece by piece, each into the
+  // registers the previous chunk's copy has just left
+  auto fetch_dt = [&](int64_t c, Pre& p) {
+    p.dtr = buf_ld16(rDt, lane * 2, (uint32_t)(c * T * 2));  // steps past L are zeroed where used
+  };
+  auto fetch_x = [&](int64_t c, Pre& p) { p.xv = buf_ld8_bf16<ALIGNED>(rX, oX, (uint32_t)(c * T * 2)); };
+  auto fetch_g = [&](int64_t c, Pre& p) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 v = *reinterpret_cast<const float4*>(gp + 4 * q);
-        nx.gfr[4 * q] = v.x; nx.gfr[4 * q + 1] = v.y; nx.gfr[4 * q + 2] = v.z; nx.gfr[4 * q + 3] = v.w;
-      }
+    for (int q = 0; q < 3; ++q) {
+      const int k = 12 * wave + 4 * q;  // slot: tile k / 16, accumulators k % 16 ..
+      p.gf[q] = __builtin_bit_cast(float4, buf_ld128(rG, lane * 64, (uint32_t)((c * 3 + (k >> 4)) * 4096 + (k & 15) * 4)));
     }
-    // 16x16x32 B operand: lane holds C^T[n = k0 + (lane/16)*8 + j][t = 16 wave + lane % 16]
-    const uint16_t* cp = Ctg + (t0 + 16 * wave + lane % 16) * N + (lane / 16) * 8;
+  };
+  auto fetch_c = [&](int64_t c, Pre& p) {
 #pragma unroll
-    for (int k = 0; k < N / 32; ++k) nx.ct[k] = *reinterpret_cast<const uint4*>(cp + 32 * k);
-    // 32x32x16 A operand: lane holds B^T[n = nb*32 + lane % 32][s = 16 ks + (lane/32)*8 + j]
+    for (int k = 0; k < N / 32; ++k) p.ct[k] = buf_ld128(rC, oC + 64 * k, (uint32_t)(c * T * N * 2));
+  };
+  auto fetch_z = [&](int64_t c, Pre& p) {
+    if constexpr (GATE) {
+#pragma unroll
+      for (int pt = 0; pt < 2; ++pt) p.zv[pt] = buf_ld4_bf16<ALIGNED>(rZ, oZ + pt * oZ16, (uint32_t)(c * T * 2));
+    }
+  };
+  auto fetch_b = [&](int64_t c, Pre& p) {
 #pragma unroll
     for (int q = 0; q < NBW; ++q) {
-      const int nb = wave + 4 * q;
-      if (nb < NB) {
-        const uint16_t* bp = Bg + (nb * 32 + lane % 32) * L;
+      if (wave + 4 * q < NB) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) nx.bt[q][ks] = load8_bf16<ALIGNED>(bp, t0 + 16 * ks + (lane / 32) * 8, L);
+        for (int ks = 0; ks < 4; ++ks) p.bt[q][ks] = buf_ld8_bf16<ALIGNED>(rB, oB + q * oB4 + 32 * ks, (uint32_t)(c * T * 2));
       }
     }
   };
-  fetch(0);
-  __syncthreads();  // the initial state is in sS
+  auto fetch = [&](int64_t c, Pre& p) {
+    fetch_dt(c, p); fetch_x(c, p); fetch_g(c, p); fetch_c(c, p); fetch_z(c, p); fetch_b(c, p);
+  };
 
-  // y of a chunk leaves LDS at the start of the next chunk, after that
-  // chunk's prefetch is issued: a store still in flight where the prefetch
-  // is waited for would be waited for too
+  uint2 ypend[2];  // y of the previous chunk, stored after the next prefetch is issued
   auto store_y = [&](int64_t c) {
-    const int64_t t = c * T + xt8;
-    if (t < L) {
-      uint16_t* dst = yg + xp * L + t;
-      const uint4 v = *reinterpret_cast<const uint4*>(sY + xp * XP + xt8);
+    const int64_t t = c * T + ty;
+    const uint32_t t2 = (uint32_t)(c * T * 2);
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt) {
       if (ALIGNED) {
-        *reinterpret_cast<uint4*>(dst) = v;
+        if (t < L) buf_st64(ypend[pt], rY, oZ + pt * oZ16, t2);
       } else {
-        uint16_t e[8];
-        __builtin_memcpy(e, &v, 16);
-        for (int j = 0; j < 8; ++j)
-          if (t + j < L) dst[j] = e[j];
+        const uint32_t e[2] = {ypend[pt].x, ypend[pt].y};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (t + j < L) buf_st16(e[j / 2] >> (16 * (j % 2)), rY, oZ + pt * oZ16 + 2 * j, t2);
       }
     }
   };
-  for (int64_t c = 0; c < a.nchunks; ++c) {
+
+  Pre cur;
+  auto chunk = [&](int64_t c) {
     const int64_t t0 = c * T;
-    const Pre cur = nx;
-    if (c + 1 < a.nchunks) fetch(c + 1);
+    const bool more = c + 1 < a.nchunks;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the operands of chunk c have arrived
     if (c > 0) store_y(c - 1);
-    // step sizes and running decay of the chunk, lane l <-> step t0 + l
+    // ---- 1. step sizes and running decay, lane l <-> step t0 + l
     float dtv = 0.0f;
     if (t0 + lane < L) {
-      const float raw = __uint_as_float((uint32_t)cur.dtr << 16) + bias;
+      const float raw = __uint_as_float(cur.dtr << 16) + bias;
       dtv = a.softplus ? softplus_f(raw) : raw;
     }
-    const float cs = wave_prefix_sum(dtv * Ah2);  // log2 units
+    if (more) fetch_dt(c + 1, cur);
+    const float cs = wave_prefix_sum(dtv * Ah2);
     const float cs_end = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs), T - 1));
-    sDt[wave][lane] = dtv;
-    sCs[wave][lane] = cs;
-    sW[wave][lane] = ex2(cs_end - cs) * dtv;
-    __syncthreads();  // the previous chunk is done with sX, sZ, sY, sM
-    *reinterpret_cast<uint4*>(sX + xp * XP + xt8) = cur.xv;
-    if constexpr (GATE) *reinterpret_cast<uint4*>(sZ + xp * XP + xt8) = cur.zv;
-    const float* csw = sCs[wave];
-    const float* dtw = sDt[wave];
-    if (wave < 3) {  // M tile (s-block, t-block) = (0,0), (0,1), (1,1)
-      const int sb = wave == 2 ? 1 : 0, tb = wave == 0 ? 0 : 1;
-      const int t = tb * 32 + lane % 32;
-      const float cst = csw[t];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int s = sb * 32 + r * 8 + (lane / 32) * 4;
-        float m[4], ml[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float v = s + i <= t ? cur.gfr[4 * r + i] * ex2(cst - csw[s + i]) * dtw[s + i] : 0.0f;
-          m[i] = bf16_round(v);
-          ml[i] = v - m[i];
-        }
-        uint2 v, vl;
-        v.x = pack_bf16x2(m[0], m[1]);
-        v.y = pack_bf16x2(m[2], m[3]);
-        vl.x = pack_bf16x2(ml[0], ml[1]);
-        vl.y = pack_bf16x2(ml[2], ml[3]);
-        *reinterpret_cast<uint2*>(sM + t * MP + s) = v;
-        *reinterpret_cast<uint2*>(sMl + t * MP + s) = vl;
-      }
+    if (wave == 0) {
+      sCs[lane] = cs;
+      sDt[lane] = dtv;
+      sE[lane] = ex2(cs);
+      sW[lane] = ex2(cs_end - cs) * dtv;
     }
-    __syncthreads();  // sX, sZ, sM ready
-    // ---- Y^T tiles [p][t], t in [16 wave, 16 wave + 16): C S^T scaled by exp(cs_t), plus X M^T
+    __syncthreads();  // A: step data visible; the previous chunk is done with sX, sXw, sM
+    // ---- 2. x, w o x and M to LDS
     {
-      const int t = 16 * wave + lane % 16;
+      *reinterpret_cast<uint4*>(sX + xp * XP + xt8) = cur.xv;
+      const float4 w0 = *reinterpret_cast<const float4*>(sW + xt8);
+      const float4 w1 = *reinterpret_cast<const float4*>(sW + xt8 + 4);
+      const uint32_t e[4] = {cur.xv.x, cur.xv.y, cur.xv.z, cur.xv.w};
+      const float wj[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        split_bf16(bf_lo(e[j]) * wj[2 * j], bf_hi(e[j]) * wj[2 * j + 1], hi[j], lo[j]);
+      *reinterpret_cast<uint4*>(sXw + xp * XP + xt8) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      *reinterpret_cast<uint4*>(sXwl + xp * XP + xt8) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+      if (more) fetch_x(c + 1, cur);
+    }
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      const int k = 12 * wave + 4 * q, tile = k >> 4, r = (k & 15) >> 2;
+      const int sb = tile == 2 ? 1 : 0, tb = tile == 0 ? 0 : 1;  // tiles (0,0), (0,1), (1,1)
+      const int t = tb * 32 + lane % 32, s = sb * 32 + r * 8 + (lane / 32) * 4;
+      const float cst = sCs[t];
+      const float4 css = *reinterpret_cast<const float4*>(sCs + s);
+      const float4 dts = *reinterpret_cast<const float4*>(sDt + s);
+      const float csv[4] = {css.x, css.y, css.z, css.w}, dtj[4] = {dts.x, dts.y, dts.z, dts.w};
+      const float gv[4] = {cur.gf[q].x, cur.gf[q].y, cur.gf[q].z, cur.gf[q].w};
+      float m[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) m[e] = s + e <= t ? gv[e] * ex2(cst - csv[e]) * dtj[e] : 0.0f;
+      uint2 v, vl;
+      split_bf16(m[0], m[1], v.x, vl.x);
+      split_bf16(m[2], m[3], v.y, vl.y);
+      *reinterpret_cast<uint2*>(sM + t * MP + s) = v;
+      *reinterpret_cast<uint2*>(sMl + t * MP + s) = vl;
+    }
+    if (more) fetch_g(c + 1, cur);
+    __syncthreads();  // B: sX, sXw, sM ready
+    // ---- 3a. Y rows t in [16 wave, 16 wave + 16), channels p = pt*16 + lane % 16
+    {
       f32x4v_t yv[2] = {{}, {}};
 #pragma unroll
       for (int pt = 0; pt < 2; ++pt) {
 #pragma unroll
         for (int k = 0; k < N / 32; ++k) {
           const int off = (pt * 16 + lane % 16) * SP + 32 * k + (lane / 16) * 8;
-          const uint4 av = *reinterpret_cast<const uint4*>(sS + off);
-          const uint4 al = *reinterpret_cast<const uint4*>(sSl + off);
-          yv[pt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(cur.ct[k]), yv[pt], 0, 0, 0);
-          yv[pt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(al), as_bf16x8(cur.ct[k]), yv[pt], 0, 0, 0);
+          const uint4 sv = *reinterpret_cast<const uint4*>(sS + off);
+          const uint4 sl = *reinterpret_cast<const uint4*>(sSl + off);
+          yv[pt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.ct[k]), as_bf16x8(sv), yv[pt], 0, 0, 0);
+          yv[pt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.ct[k]), as_bf16x8(sl), yv[pt], 0, 0, 0);
         }
       }
-      const float f = ex2(csw[t]);
-      const int ks_end = wave >= 2 ? 2 : 1;  // M is zero for s > t
+      if (more) fetch_c(c + 1, cur);
+      const float4 ev = *reinterpret_cast<const float4*>(sE + ty);
 #pragma unroll
       for (int pt = 0; pt < 2; ++pt) {
-        yv[pt] *= f;
-        for (int k = 0; k < ks_end; ++k) {
-          const uint4 av = *reinterpret_cast<const uint4*>(sX + (pt * 16 + lane % 16) * XP + 32 * k + (lane / 16) * 8);
-          const uint4 bv = *reinterpret_cast<const uint4*>(sM + t * MP + 32 * k + (lane / 16) * 8);
-          const uint4 bl = *reinterpret_cast<const uint4*>(sMl + t * MP + 32 * k + (lane / 16) * 8);
-          yv[pt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(bv), yv[pt], 0, 0, 0);
-          yv[pt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av), as_bf16x8(bl), yv[pt], 0, 0, 0);
-        }
-        // epilogue: rows p = pt*16 + (lane/16)*4 + i, column t
+        yv[pt][0] *= ev.x; yv[pt][1] *= ev.y; yv[pt][2] *= ev.z; yv[pt][3] *= ev.w;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int p = pt * 16 + (lane / 16) * 4 + i;
-          const float xv = __uint_as_float((uint32_t)sX[p * XP + t] << 16);
-          float v = fmaf(Dh, xv, yv[pt][i]);
-          if constexpr (GATE) v *= silu_f(__uint_as_float((uint32_t)sZ[p * XP + t] << 16));
-          sY[p * XP + t] = f2bf(v);
+        for (int k = 0; k < 2; ++k) {
+          if (k == 0 || wave >= 2) {  // M is zero for s > t
+            const int mo = (16 * wave + lane % 16) * MP + 32 * k + (lane / 16) * 8;
+            const uint4 mv = *reinterpret_cast<const uint4*>(sM + mo);
+            const uint4 ml = *reinterpret_cast<const uint4*>(sMl + mo);
+            const uint4 xv = *reinterpret_cast<const uint4*>(sX + (pt * 16 + lane % 16) * XP + 32 * k + (lane / 16) * 8);
+            yv[pt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(mv), as_bf16x8(xv), yv[pt], 0, 0, 0);
+            yv[pt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ml), as_bf16x8(xv), yv[pt], 0, 0, 0);
+          }
         }
+        // epilogue: channel p, steps ty .. ty + 3
+        const uint2 xr = *reinterpret_cast<const uint2*>(sX + (pt * 16 + lane % 16) * XP + ty);
+        float v[4] = {fmaf(Dh, bf_lo(xr.x), yv[pt][0]), fmaf(Dh, bf_hi(xr.x), yv[pt][1]),
+                      fmaf(Dh, bf_lo(xr.y), yv[pt][2]), fmaf(Dh, bf_hi(xr.y), yv[pt][3])};
+        if constexpr (GATE) {
+          v[0] *= silu_f(bf_lo(cur.zv[pt].x));
+          v[1] *= silu_f(bf_hi(cur.zv[pt].x));
+          v[2] *= silu_f(bf_lo(cur.zv[pt].y));
+          v[3] *= silu_f(bf_hi(cur.zv[pt].y));
+        }
+        ypend[pt] = make_uint2(pk_bf16(v[0], v[1]), pk_bf16(v[2], v[3]));
       }
+      if (more) fetch_z(c + 1, cur);
     }
-    // ---- state: S^T = exp(cs_63) S^T + B^T (w o X), w_s = exp(cs_63 - cs_s) dt_s
+    // ---- 3b. state: S^T = exp(cs_63) S^T + B^T (w o X)
     {
       const float decay = ex2(cs_end);
-      const float* ww = sW[wave];
+#pragma unroll
+      for (int q = 0; q < NBW; ++q)
+        if (wave + 4 * q < NB) S[q] *= decay;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const int s0 = 16 * ks + (lane / 32) * 8;
-        const uint4 xr = *reinterpret_cast<const uint4*>(sX + (lane % 32) * XP + s0);
-        uint16_t e[8];
-        __builtin_memcpy(e, &xr, 16);
-        const float4 w0 = *reinterpret_cast<const float4*>(ww + s0);
-        const float4 w1 = *reinterpret_cast<const float4*>(ww + s0 + 4);
-        const float wj[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-        float wv[8], wl[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float v = __uint_as_float((uint32_t)e[j] << 16) * wj[j];
-          wv[j] = bf16_round(v);
-          wl[j] = v - wv[j];
-        }
-        uint4 xw, xl;
-        xw.x = pack_bf16x2(wv[0], wv[1]); xw.y = pack_bf16x2(wv[2], wv[3]);
-        xw.z = pack_bf16x2(wv[4], wv[5]); xw.w = pack_bf16x2(wv[6], wv[7]);
-        xl.x = pack_bf16x2(wl[0], wl[1]); xl.y = pack_bf16x2(wl[2], wl[3]);
-        xl.z = pack_bf16x2(wl[4], wl[5]); xl.w = pack_bf16x2(wl[6], wl[7]);
+        const int xo = (lane % 32) * XP + 16 * ks + (lane / 32) * 8;
+        const uint4 xw = *reinterpret_cast<const uint4*>(sXw + xo);
+        const uint4 xl = *reinterpret_cast<const uint4*>(sXwl + xo);
 #pragma unroll
         for (int q = 0; q < NBW; ++q) {
           if (wave + 4 * q < NB) {
-            if (ks == 0) S[q] *= decay;
             S[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(cur.bt[q][ks]), as_bf16x8(xw), S[q], 0, 0, 0);
             S[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(cur.bt[q][ks]), as_bf16x8(xl), S[q], 0, 0, 0);
           }
         }
       }
+      if (more) fetch_b(c + 1, cur);
     }
-    __syncthreads();  // every wave is done with sS (old state) and has written sY
+    __syncthreads();  // C: every wave is done with sS (old state) and the step data
     write_state_bf16();
-  }
+  };
+
+  fetch(0, cur);
+  __syncthreads();  // the initial state is in sS
+  for (int64_t c = 0; c < a.nchunks; ++c) chunk(c);
   store_y(a.nchunks - 1);
   if (a.final_state) {
 #pragma unroll
@@ -2707,6 +2794,8 @@ int ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void* Bm, c
   if (!product_ok(batch, nheads * headdim, seqlen, 2) || !product_ok(batch, nheads * headdim, dstate, 4))
     return fail(SSM_E_SHAPE, "tensor sizes overflow");
   const SsdLayout lay = ssd_layout(batch, seqlen, ngroups, dstate);
+  // this bound also keeps every buffer the scan kernel addresses (one group's B
+  // rows, its C.B^T tiles, 32 channel rows) below 2^31 bytes
   if (lay.nchunks > 65535) return fail(SSM_E_SHAPE, "seqlen = %lld is too long", (long long)seqlen);
   if (workspace_bytes < lay.bytes)
     return fail(SSM_E_SHAPE, "workspace holds %lld bytes, needs %lld", (long long)workspace_bytes,
