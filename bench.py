@@ -89,6 +89,20 @@ def host_threads() -> int:
     return max(1, min(16, n))  # one GPU's share of the host
 
 
+def settle(fn, torch, warmup, min_ms=250.0):
+    """Untimed calls before a timed region: `warmup` of them, and more until
+    the GPU has run this work for `min_ms` (clocks ramp up under sustained
+    load; a short burst after an idle gap is timed at lower clocks)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < min_ms:
+        for _ in range(4):
+            fn()
+        torch.cuda.synchronize()
+
+
 def bench_scan(ssm, torch, w, x, dev, steps, warmup):
     u, dl, A, B, C = (to_dev(x[k], dev) for k in ("u", "delta", "A", "B", "C"))
     D, z, bias = to_dev(x["D"], dev), to_dev(x["z"], dev), to_dev(x["delta_bias"], dev)
@@ -139,17 +153,15 @@ def bench_decode(ssm, torch, dev, steps, warmup):
         ssm.ssm_state_update(state, p["u"], p["delta"], Ad, p["B"], p["C"], D=Dd, z=p["z"],
                              delta_bias=bd, delta_softplus=True, y=y)
 
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
+    ctr = iter(range(1 << 30))
+    settle(lambda: step(next(ctr)), torch, warmup)
     per_graph = 50
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for i in range(per_graph):
             step(i)
     torch.cuda.synchronize()
-    g.replay()  # warm replay
-    torch.cuda.synchronize()
+    settle(g.replay, torch, 1)
     reps = max(1, steps // per_graph)
     stream = torch.cuda.current_stream(dev)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -181,7 +193,9 @@ def bench_bwd(ssm, torch, w, x, dev, steps, warmup):
     """The backward pass (ssm_selective_scan_bwd: checkpointed forward, adjoint
     carries, gradients) on the same inputs with a seeded upstream gradient.
     Every gradient is produced; the workspace is allocated once outside the
-    timed region."""
+    timed region.  Timed standalone (the backward recomputes its checkpoints)
+    and as a training step: a forward that writes checkpoints followed by a
+    backward that takes them."""
     g = wl.grad_inputs(w)
     u, dl, A, B, C = (to_dev(x[k], dev) for k in ("u", "delta", "A", "B", "C"))
     D, z, bias = to_dev(x["D"], dev), to_dev(x["z"], dev), to_dev(x["delta_bias"], dev)
@@ -190,21 +204,35 @@ def bench_bwd(ssm, torch, w, x, dev, steps, warmup):
                                                                w.seqlen),
                      dtype=torch.uint8, device=dev)
 
+    ck = torch.empty(ssm.ssm_checkpoint_shape(w.batch, w.dim, w.dstate, w.seqlen),
+                     dtype=torch.float32, device=dev)
+    y = torch.empty_like(u)
+
     def step():
         return ssm.ssm_selective_scan_bwd(u, dl, A, B, C, dy, D=D, z=z, delta_bias=bias,
                                           delta_softplus=True, workspace=ws, want_dh0=True)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    def train_step():
+        ssm.ssm_selective_scan_fwd(u, dl, A, B, C, D=D, z=z, delta_bias=bias, delta_softplus=True,
+                                   y=y, want_final_state=False, checkpoints=ck)
+        return ssm.ssm_selective_scan_bwd(u, dl, A, B, C, dy, D=D, z=z, delta_bias=bias,
+                                          delta_softplus=True, workspace=ws, want_dh0=True,
+                                          checkpoints=ck)
+
     stream = torch.cuda.current_stream(dev)
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(steps):
-        step()
-    b.record(stream)
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / steps
+
+    def timed(fn):
+        settle(fn, torch, warmup)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(steps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    ms = timed(step)
+    ms_train = timed(train_step)
     es = 2 if w.dtype == "bf16" else 4
     seq = w.batch * w.dim * w.seqlen * es
     bc = w.batch * w.dstate * w.seqlen * es
@@ -220,6 +248,8 @@ def bench_bwd(ssm, torch, w, x, dev, steps, warmup):
         "algorithmic_bytes": algo,
         "hbm_gbps": round(gbps, 1),
         "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "train_step_ms": round(ms_train, 4),
+        "train_step": "forward writing checkpoints, then the backward taking them",
         "steps": steps,
     }
 
@@ -233,9 +263,7 @@ def bench_conv(ssm, torch, w, dev, steps, warmup):
     stream = torch.cuda.current_stream(dev)
 
     def timed(fn):
-        for _ in range(warmup):
-            fn()
-        torch.cuda.synchronize()
+        settle(fn, torch, warmup)
         a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
         for _ in range(steps):
@@ -275,9 +303,7 @@ def bench_ssd(ssm, torch, dev, steps, warmup):
                         z=t["z"], dt_bias=t["dt_bias"], dt_softplus=True, y=y, final_state=fs,
                         workspace=ws)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    settle(step, torch, warmup)
     stream = torch.cuda.current_stream(dev)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record(stream)
@@ -337,8 +363,8 @@ def cpu_baseline(w, x, seconds_target=12.0):
 def main(argv=None):
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=300)
     p.add_argument("--workload", default="mamba2p8b",
                    choices=[k for k in wl.WORKLOADS if k != "decode"])
     p.add_argument("--decode-steps", type=int, default=200)
@@ -439,11 +465,11 @@ def main(argv=None):
         print(f"[bench] backward: {out['backward']['ms_per_call']} ms/call", file=sys.stderr,
               flush=True)
     if not args.no_conv:
-        out["conv1d"] = bench_conv(ssm, torch, w, dev, 10, 2)
+        out["conv1d"] = bench_conv(ssm, torch, w, dev, 50, 2)
         print(f"[bench] conv1d: fwd {out['conv1d']['fwd']['ms']} ms, bwd "
               f"{out['conv1d']['bwd']['ms']} ms", file=sys.stderr, flush=True)
     if not args.no_ssd:
-        out["ssd"] = bench_ssd(ssm, torch, dev, 10, 2)
+        out["ssd"] = bench_ssd(ssm, torch, dev, 30, 2)
         print(f"[bench] ssd: {out['ssd']['ms_per_call']} ms/call", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, x)

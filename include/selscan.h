@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 1
+#define SSM_ABI_VERSION 2
 
 typedef enum { SSM_DTYPE_F32 = 0, SSM_DTYPE_BF16 = 1 } ssm_dtype;
 
@@ -106,14 +106,19 @@ typedef enum {
  *  y           [batch, dim, seqlen] io_dtype, out.  Must not overlap any input.
  *  final_state [batch, dim, dstate] float32 out, or NULL.  May be exactly h0
  *              (in-place resume) but must not otherwise overlap it.
+ *  checkpoints [batch, dim, ceil(seqlen / 128), dstate] float32 out, or NULL:
+ *              the state entering every 128-step block (block 0: h0), which
+ *              ssm_selective_scan_bwd can take instead of recomputing them.
+ *              Must not overlap any input or output.
  *
  * The expanded state [batch, seqlen, dim, dstate] is never written to memory.
  */
 int ssm_selective_scan_fwd(const void* u, const void* delta, const float* A, const void* Bm,
                            const void* Cm, const float* Dskip, const void* z,
                            const float* delta_bias, int delta_softplus, const float* h0, void* y,
-                           float* final_state, int64_t batch, int64_t dim, int64_t dstate,
-                           int64_t seqlen, int io_dtype, int bbar_mode, void* hip_stream);
+                           float* final_state, float* checkpoints, int64_t batch, int64_t dim,
+                           int64_t dstate, int64_t seqlen, int io_dtype, int bbar_mode,
+                           void* hip_stream);
 
 /*
  * One decode step: every sequence advances by one token at constant cost,
@@ -164,6 +169,8 @@ int ssm_lti_kernel(const float* A, const float* Bv, const float* Cv, const float
  * final state are not needed), and
  *  dy           [batch, dim, seqlen] io_dtype: gradient of y
  *  dfinal_state [batch, dim, dstate] float32 or NULL (= 0)
+ *  checkpoints  the forward's checkpoints for these same inputs, or NULL:
+ *               then the backward recomputes them (one more forward pass)
  * Outputs (overwritten; none may overlap an input or another output):
  *  du, ddelta   [batch, dim, seqlen] io_dtype; ddelta is the gradient of the
  *               raw step (before bias and softplus)
@@ -185,8 +192,8 @@ int ssm_lti_kernel(const float* A, const float* Bv, const float* Cv, const float
 int ssm_selective_scan_bwd(const void* u, const void* delta, const float* A, const void* Bm,
                            const void* Cm, const float* Dskip, const void* z,
                            const float* delta_bias, int delta_softplus, const float* h0,
-                           const void* dy, const float* dfinal_state, void* du, void* ddelta,
-                           float* dA, void* dB, void* dC, float* dD, void* dz,
+                           const void* dy, const float* dfinal_state, const float* checkpoints,
+                           void* du, void* ddelta, float* dA, void* dB, void* dC, float* dD, void* dz,
                            float* ddelta_bias, float* dh0, void* workspace,
                            int64_t workspace_bytes, int64_t batch, int64_t dim, int64_t dstate,
                            int64_t seqlen, int io_dtype, int bbar_mode, void* hip_stream);

@@ -8,15 +8,18 @@ Entry points carry the C names:
 
   ssm_selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
                          delta_softplus=False, h0=None, bbar="delta",
-                         y=None, final_state=None, want_final_state=True)
+                         y=None, final_state=None, want_final_state=True,
+                         checkpoints=None)
       -> (y, final_state)
+  ssm_checkpoint_shape(batch, dim, dstate, seqlen) -> shape of `checkpoints`
   ssm_state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None,
                    delta_softplus=False, bbar="delta", y=None) -> y
   ssm_lti_kernel(A, Bv, Cv, delta, L, bbar="delta", K=None) -> K
   ssm_lti_conv(K, u, D=None, y=None) -> y                   (y = K * u + D u, causal)
   ssm_selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None,
                          delta_softplus=False, h0=None, dfinal_state=None,
-                         bbar="delta", workspace=None) -> dict of gradients
+                         bbar="delta", workspace=None, checkpoints=None)
+      -> dict of gradients
   ssm_causal_conv1d_fwd(x, weight, bias=None, state_in=None, silu=True,
                         out=None, state_out=None, want_state_out=False)
       -> (out, state_out)
@@ -37,14 +40,15 @@ from ._lib import (SSM_BBAR_DELTA_B, SSM_BBAR_ZOH_EXACT, SSM_DTYPE_BF16, SSM_DTY
                    SelscanError, library_path, lib, ssm_abi_version, ssm_last_error,
                    ssm_status_str)
 from .binding import (ssm_causal_conv1d_bwd, ssm_causal_conv1d_fwd, ssm_causal_conv1d_update,
-                      ssm_lti_conv, ssm_lti_kernel, ssm_selective_scan_bwd, ssm_ssd_fwd,
+                      ssm_checkpoint_shape, ssm_lti_conv, ssm_lti_kernel,
+                      ssm_selective_scan_bwd, ssm_ssd_fwd,
                       ssm_ssd_workspace_size,
                       ssm_selective_scan_bwd_workspace_size, ssm_selective_scan_fwd,
                       ssm_state_update)
 
 __all__ = [
     "ssm_selective_scan_fwd", "ssm_state_update", "ssm_lti_kernel", "ssm_lti_conv",
-    "ssm_selective_scan_bwd",
+    "ssm_selective_scan_bwd", "ssm_checkpoint_shape",
     "ssm_selective_scan_bwd_workspace_size", "ssm_causal_conv1d_fwd", "ssm_causal_conv1d_update",
     "ssm_causal_conv1d_bwd", "ssm_ssd_fwd", "ssm_ssd_workspace_size", "ssm_status_str",
     "ssm_last_error", "ssm_abi_version", "SelscanError", "library_path", "lib",

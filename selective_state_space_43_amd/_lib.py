@@ -7,6 +7,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SO = os.path.join(_HERE, "libselscan.so")
 
+ABI_VERSION = 2  # the SSM_ABI_VERSION these signatures follow
 SSM_DTYPE_F32, SSM_DTYPE_BF16 = 0, 1
 SSM_BBAR_DELTA_B, SSM_BBAR_ZOH_EXACT, SSM_DISC_EULER, SSM_DISC_BILINEAR = 0, 1, 2, 3
 STATUS_NAMES = {0: "SSM_OK", 1: "SSM_E_NULL", 2: "SSM_E_SHAPE", 3: "SSM_E_DTYPE",
@@ -37,12 +38,12 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(_SO)
         vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
         L.ssm_selective_scan_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp,
-                                             i64, i64, i64, i64, i32, i32, vp]
+                                             vp, i64, i64, i64, i64, i32, i32, vp]
         L.ssm_state_update.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp,
                                        i64, i64, i64, i32, i32, vp]
         L.ssm_lti_kernel.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, vp]
         L.ssm_selective_scan_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp,
-                                             vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64,
+                                             vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64,
                                              i64, i64, i64, i64, i32, i32, vp]
         L.ssm_selective_scan_bwd_workspace_size.argtypes = [i64, i64, i64, i64]
         L.ssm_selective_scan_bwd_workspace_size.restype = i64
@@ -66,6 +67,9 @@ def lib() -> ctypes.CDLL:
         L.ssm_last_error.restype = ctypes.c_char_p
         L.ssm_abi_version.argtypes = []
         L.ssm_abi_version.restype = i32
+        if L.ssm_abi_version() != ABI_VERSION:
+            raise ImportError(f"{_SO} has ABI version {L.ssm_abi_version()}, this binding "
+                              f"expects {ABI_VERSION}: rebuild it")
         _LIB = L
     return _LIB
 

@@ -46,10 +46,21 @@ def _stream(device):
     return torch.cuda.current_stream(device).cuda_stream
 
 
+CKPT_STEPS = 128  # steps between the forward's checkpoints
+
+
+def ssm_checkpoint_shape(batch, dim, dstate, seqlen):
+    """Shape of the forward's checkpoints: the state entering every 128-step
+    block."""
+    return (batch, dim, (seqlen + CKPT_STEPS - 1) // CKPT_STEPS, dstate)
+
+
 def ssm_selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
                            delta_softplus=False, h0=None, bbar="delta", y=None,
-                           final_state=None, want_final_state=True):
-    """Forward selective scan; returns (y, final_state or None)."""
+                           final_state=None, want_final_state=True, checkpoints=None):
+    """Forward selective scan; returns (y, final_state or None).  With
+    `checkpoints` (a float32 tensor of ssm_checkpoint_shape) it also writes the
+    states the backward can take instead of recomputing them."""
     _dev(u, "u", None)
     dev = u.device
     if u.dim() != 3:
@@ -78,11 +89,12 @@ def ssm_selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
         final_state = torch.empty((batch, dim, N), dtype=torch.float32, device=dev)
     elif final_state is not None:
         _f32(final_state, "final_state", (batch, dim, N), dev)
+    _f32(checkpoints, "checkpoints", ssm_checkpoint_shape(batch, dim, N, L), dev)
     with torch.cuda.device(dev):
         st = lib().ssm_selective_scan_fwd(
             _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
-            int(bool(delta_softplus)), _ptr(h0), _ptr(y), _ptr(final_state), batch, dim, N, L,
-            _IO[io], _BBAR[bbar], _stream(dev))
+            int(bool(delta_softplus)), _ptr(h0), _ptr(y), _ptr(final_state), _ptr(checkpoints),
+            batch, dim, N, L, _IO[io], _BBAR[bbar], _stream(dev))
     check(st, "ssm_selective_scan_fwd")
     return y, final_state
 
@@ -172,10 +184,11 @@ def ssm_selective_scan_bwd_workspace_size(batch, dim, dstate, seqlen):
 
 def ssm_selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None,
                            delta_softplus=False, h0=None, dfinal_state=None, bbar="delta",
-                           workspace=None, want_dh0=None):
+                           workspace=None, want_dh0=None, checkpoints=None):
     """Gradients of sum(dy * y) + sum(dfinal_state * final_state).  Returns a
     dict with du, ddelta (raw step), dA, dB, dC, and dD / dz / ddelta_bias /
-    dh0 when D / z / delta_bias / h0 (or want_dh0) are given."""
+    dh0 when D / z / delta_bias / h0 (or want_dh0) are given.  `checkpoints`
+    from the forward on the same inputs saves recomputing them."""
     _dev(u, "u", None)
     dev = u.device
     if u.dim() != 3 or u.dtype not in _IO:
@@ -193,6 +206,7 @@ def ssm_selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=Non
     _f32(delta_bias, "delta_bias", (dim,), dev)
     _f32(h0, "h0", (batch, dim, N), dev)
     _f32(dfinal_state, "dfinal_state", (batch, dim, N), dev)
+    _f32(checkpoints, "checkpoints", ssm_checkpoint_shape(batch, dim, N, L), dev)
     need = ssm_selective_scan_bwd_workspace_size(batch, dim, N, L)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -210,7 +224,8 @@ def ssm_selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=Non
     with torch.cuda.device(dev):
         st = lib().ssm_selective_scan_bwd(
             _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
-            int(bool(delta_softplus)), _ptr(h0), _ptr(dy), _ptr(dfinal_state), _ptr(g["du"]),
+            int(bool(delta_softplus)), _ptr(h0), _ptr(dy), _ptr(dfinal_state),
+            _ptr(checkpoints), _ptr(g["du"]),
             _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]),
             _ptr(g["dz"]), _ptr(g["ddelta_bias"]), _ptr(g["dh0"]), _ptr(workspace),
             workspace.numel() * workspace.element_size(), batch, dim, N, L, _IO[io],

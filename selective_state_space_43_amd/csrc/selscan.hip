@@ -326,7 +326,7 @@ struct ScanArgs {
   float* final_state;
   int64_t dim, dstate, seqlen;
   int softplus;
-  float* ckpt;  // checkpoint mode: state every kCkptT steps, [batch, dim, ceil(L / kCkptT), dstate]
+  float* ckpt;  // or null: state entering every kCkptT-step block, [batch, dim, ceil(L / kCkptT), dstate]
 };
 
 // Discretization rules (the bbar_mode of the C ABI): Abar = exp(delta A) with
@@ -501,9 +501,9 @@ __global__ void __launch_bounds__(64 * W)
       const float He = group_prev0<LPC>(H, first);
       float h = first ? c : He;
       if (seg == LPC - 1) carry_row[n] = H;
-      if constexpr (CKPT) {
-        static_assert(kCkptT % K == 0 && T % kCkptT == 0, "checkpoints fall on lane starts");
-        if (dvalid && (seg * K) % kCkptT == 0 && tl < L)
+      static_assert(!CKPT || (kCkptT % K == 0 && T % kCkptT == 0), "checkpoints fall on lane starts");
+      if constexpr (kCkptT % K == 0 && T % kCkptT == 0) {
+        if (a.ckpt && dvalid && (seg * K) % kCkptT == 0 && tl < L)
           a.ckpt[((b * a.dim + d) * ((L + kCkptT - 1) / kCkptT) + tl / kCkptT) * N + n] = h;
       }
 #pragma unroll
@@ -2207,9 +2207,10 @@ int launch_bwd_typed(const ScanArgs& fa, BwdArgs ba, int64_t batch, hipStream_t 
   constexpr int K = kBwdK;
   const dim3 grid16((unsigned)((ba.dim + 15) / 16), (unsigned)batch);
   // 1. checkpoints: the state entering every kCkptT-step block (a forward
-  // pass over 256-step chunks)
-  hipLaunchKernelGGL((scan_fwd_kernel<IO, 16, 16, 4, 16, VEC, ZOH ? kRuleZoh : kRuleDeltaB, false, true>), grid16, dim3(256),
-                     2 * 16 * (size_t)ba.dstate * sizeof(float), s, fa);
+  // pass over 256-step chunks), unless the caller brings the forward's
+  if (fa.ckpt)
+    hipLaunchKernelGGL((scan_fwd_kernel<IO, 16, 16, 4, 16, VEC, ZOH ? kRuleZoh : kRuleDeltaB, false, true>), grid16, dim3(256),
+                       2 * 16 * (size_t)ba.dstate * sizeof(float), s, fa);
   // 2. adjoint carries at every block end (a reverse pass over 256-step chunks)
   hipLaunchKernelGGL((scan_bwd_carry_kernel<IO, 16, VEC, GATE>), grid16, dim3(256), 0, s, ba);
   // 3. gradients, every (sequence, chunk) independently; groups of 4 channels
@@ -2363,8 +2364,9 @@ const char* ssm_status_str(int status) {
 int ssm_selective_scan_fwd(const void* u, const void* delta, const float* A, const void* Bm,
                            const void* Cm, const float* Dskip, const void* z,
                            const float* delta_bias, int delta_softplus, const float* h0, void* y,
-                           float* final_state, int64_t batch, int64_t dim, int64_t dstate,
-                           int64_t seqlen, int io_dtype, int bbar_mode, void* hip_stream) {
+                           float* final_state, float* checkpoints, int64_t batch, int64_t dim,
+                           int64_t dstate, int64_t seqlen, int io_dtype, int bbar_mode,
+                           void* hip_stream) {
   g_last_error[0] = 0;
   if (!u) return fail(SSM_E_NULL, "u is NULL");
   if (!delta) return fail(SSM_E_NULL, "delta is NULL");
@@ -2416,7 +2418,19 @@ int ssm_selective_scan_fwd(const void* u, const void* delta, const float* A, con
       if (overlaps(fs, s)) return fail(SSM_E_ALIAS, "final_state overlaps %s", s.name);
     }
   }
+  if (checkpoints) {
+    if (kCkptT % SELSCAN_K != 0)
+      return fail(SSM_E_UNSUPPORTED, "checkpoints need steps per lane dividing %d", kCkptT);
+    const Span cs{checkpoints, batch * dim * ((seqlen + kCkptT - 1) / kCkptT) * dstate * 4,
+                  "checkpoints"};
+    if (overlaps(cs, ys)) return fail(SSM_E_ALIAS, "checkpoints overlap y");
+    if (final_state && overlaps(cs, Span{final_state, st_bytes, "final_state"}))
+      return fail(SSM_E_ALIAS, "checkpoints overlap final_state");
+    for (const Span& s : in)
+      if (overlaps(cs, s)) return fail(SSM_E_ALIAS, "checkpoints overlap %s", s.name);
+  }
   ScanArgs a;
+  a.ckpt = checkpoints;
   a.u = u; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm; a.Dskip = Dskip; a.z = z;
   a.delta_bias = delta_bias; a.h0 = h0; a.y = y; a.final_state = final_state;
   a.dim = dim; a.dstate = dstate; a.seqlen = seqlen;
@@ -2534,7 +2548,8 @@ int64_t ssm_selective_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_
 int ssm_selective_scan_bwd(const void* u, const void* delta, const float* A, const void* Bm,
                            const void* Cm, const float* Dskip, const void* z,
                            const float* delta_bias, int delta_softplus, const float* h0,
-                           const void* dy, const float* dfinal_state, void* du, void* ddelta,
+                           const void* dy, const float* dfinal_state, const float* checkpoints,
+                           void* du, void* ddelta,
                            float* dA, void* dB, void* dC, float* dD, void* dz,
                            float* ddelta_bias, float* dh0, void* workspace,
                            int64_t workspace_bytes, int64_t batch, int64_t dim, int64_t dstate,
@@ -2581,7 +2596,8 @@ int ssm_selective_scan_bwd(const void* u, const void* delta, const float* A, con
   const Span ins[] = {{u, seq, "u"},           {delta, seq, "delta"},     {A, dim * dstate * 4, "A"},
                       {Bm, bc, "B"},           {Cm, bc, "C"},             {Dskip, dim * 4, "D"},
                       {z, z ? seq : 0, "z"},   {delta_bias, dim * 4, "delta_bias"},
-                      {h0, stb, "h0"},         {dy, seq, "dy"},           {dfinal_state, stb, "dfinal_state"}};
+                      {h0, stb, "h0"},         {dy, seq, "dy"},           {dfinal_state, stb, "dfinal_state"},
+                      {checkpoints, batch * dim * lay.chunks * dstate * 4, "checkpoints"}};
   const Span outs[] = {{du, seq, "du"},          {ddelta, seq, "ddelta"},  {dA, dim * dstate * 4, "dA"},
                        {dB, bc, "dB"},           {dC, bc, "dC"},           {dD, dim * 4, "dD"},
                        {dz, z ? seq : 0, "dz"},  {ddelta_bias, dim * 4, "ddelta_bias"},
@@ -2599,13 +2615,14 @@ int ssm_selective_scan_bwd(const void* u, const void* delta, const float* A, con
   fa.u = u; fa.delta = delta; fa.A = A; fa.Bm = Bm; fa.Cm = Cm; fa.Dskip = Dskip; fa.z = nullptr;
   fa.delta_bias = delta_bias; fa.h0 = h0; fa.y = nullptr; fa.final_state = nullptr;
   fa.dim = dim; fa.dstate = dstate; fa.seqlen = seqlen; fa.softplus = delta_softplus ? 1 : 0;
-  fa.ckpt = reinterpret_cast<float*>(ws + lay.ckpt_off);
+  // the forward's checkpoints when the caller has them, else recomputed
+  fa.ckpt = checkpoints ? nullptr : reinterpret_cast<float*>(ws + lay.ckpt_off);
   BwdArgs ba;
   memset(&ba, 0, sizeof ba);
   ba.u = u; ba.delta = delta; ba.A = A; ba.Bm = Bm; ba.Cm = Cm; ba.Dskip = Dskip; ba.z = z;
   ba.delta_bias = delta_bias; ba.dy = dy; ba.dfinal = dfinal_state; ba.du = du; ba.ddelta = ddelta;
   ba.dA = dA; ba.dD = dD; ba.dz = dz; ba.ddelta_bias = ddelta_bias; ba.dh0 = dh0;
-  ba.ckpt = fa.ckpt;
+  ba.ckpt = checkpoints ? checkpoints : fa.ckpt;
   ba.carry = reinterpret_cast<float*>(ws + lay.carry_off);
   ba.accB = reinterpret_cast<float*>(ws + lay.accB_off);
   ba.accC = reinterpret_cast<float*>(ws + lay.accC_off);

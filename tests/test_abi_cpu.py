@@ -34,7 +34,7 @@ def test_library_exports_every_declared_function(lib):
 
 def test_abi_version_and_status_strings(lib):
     import selective_state_space_43_amd as ssm
-    assert ssm.ssm_abi_version() == 1
+    assert ssm.ssm_abi_version() == 2
     assert ssm.ssm_status_str(0) == "ok"
     for s in range(1, 8):
         assert ssm.ssm_status_str(s) not in ("", "unknown status")
@@ -46,11 +46,11 @@ P = 1 << 20  # fake, 16-byte-aligned, non-overlapping addresses
 
 def fwd_args(**over):
     a = dict(u=1 * P, delta=2 * P, A=3 * P, B=4 * P, C=5 * P, D=None, z=None, bias=None,
-             softplus=1, h0=None, y=6 * P, fs=None, batch=2, dim=8, N=4, L=16, io=1, bbar=0,
-             stream=None)
+             softplus=1, h0=None, y=6 * P, fs=None, ck=None, batch=2, dim=8, N=4, L=16, io=1,
+             bbar=0, stream=None)
     a.update(over)
     return [a[k] for k in ("u", "delta", "A", "B", "C", "D", "z", "bias", "softplus", "h0", "y",
-                           "fs", "batch", "dim", "N", "L", "io", "bbar", "stream")]
+                           "fs", "ck", "batch", "dim", "N", "L", "io", "bbar", "stream")]
 
 
 @pytest.mark.parametrize("over,status", [
@@ -62,6 +62,7 @@ def fwd_args(**over):
     (dict(u=1 * P + 2), 4), (dict(y=6 * P + 8), 4), (dict(z=7 * P + 4), 4),
     (dict(y=1 * P), 5), (dict(y=2 * P + 32), 5), (dict(fs=6 * P), 5), (dict(fs=3 * P), 5),
     (dict(h0=7 * P, fs=7 * P + 16), 5),
+    (dict(ck=6 * P + 64), 5), (dict(ck=4 * P), 5), (dict(fs=8 * P, ck=8 * P + 32), 5),
     (dict(N=65), 6),
 ])
 def test_scan_fwd_validation(lib, over, status):
@@ -116,13 +117,13 @@ def test_no_cpu_fallback_in_product_path():
 
 
 BWD_KEYS = ("u", "delta", "A", "B", "C", "D", "z", "bias", "softplus", "h0", "dy", "dfinal",
-            "du", "ddelta", "dA", "dB", "dC", "dD", "dz", "dbias", "dh0", "ws", "ws_bytes",
+            "ck", "du", "ddelta", "dA", "dB", "dC", "dD", "dz", "dbias", "dh0", "ws", "ws_bytes",
             "batch", "dim", "N", "L", "io", "bbar", "stream")
 
 
 def bwd_args(**over):
     a = dict(u=1 * P, delta=2 * P, A=3 * P, B=4 * P, C=5 * P, D=None, z=None, bias=None,
-             softplus=1, h0=None, dy=6 * P, dfinal=None, du=7 * P, ddelta=8 * P, dA=9 * P,
+             softplus=1, h0=None, dy=6 * P, dfinal=None, ck=None, du=7 * P, ddelta=8 * P, dA=9 * P,
              dB=10 * P, dC=11 * P, dD=None, dz=None, dbias=None, dh0=None, ws=12 * P,
              ws_bytes=P, batch=2, dim=8, N=4, L=16, io=1, bbar=0, stream=None)
     a.update(over)
@@ -145,7 +146,7 @@ def test_bwd_workspace_size(lib):
     (dict(io=2), 3), (dict(bbar=5), 3),
     (dict(du=7 * P + 2), 4), (dict(ws=12 * P + 8), 4),
     (dict(du=1 * P), 5), (dict(dA=3 * P), 5), (dict(dB=10 * P + 64, dC=10 * P + 64), 5),
-    (dict(ws=6 * P), 5), (dict(dh0=9 * P), 5),
+    (dict(ws=6 * P), 5), (dict(dh0=9 * P), 5), (dict(ck=7 * P), 5), (dict(ck=12 * P + 256), 5),
     (dict(N=17), 6), (dict(N=64), 6), (dict(bbar=2), 6), (dict(bbar=3), 6),
 ])
 def test_bwd_validation(lib, over, status):

@@ -214,3 +214,56 @@ def test_bwd_mamba2p8b_sampled(ssm, dev):
         ref_sub[k] = ref[k][d_sel]
     compare(w, sub, ref_sub, w.name + " sampled", channels=channels,
             reduced=("dA", "dD", "ddelta_bias"))
+
+
+# (batch, dim, dstate, L, dtype, gate, bias, bbar): the three lane layouts of
+# the forward (16384 channels and more: 16 lanes per channel; fewer: 32 or 64)
+CKPT_CASES = [
+    (2, 40, 16, 300, "bf16", True, True, "delta"),
+    (1, 24, 16, 333, "f32", True, False, "zoh"),
+    (2, 8192, 16, 256, "bf16", True, True, "delta"),
+    (1, 8192, 8, 640, "f32", False, True, "zoh"),
+]
+
+
+@pytest.mark.parametrize("case", CKPT_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_bwd_with_forward_checkpoints(ssm, dev, case):
+    """A forward that writes checkpoints leaves y and the final state bit for
+    bit as they are without; its checkpoints are the oracle's states at every
+    128-step block start; the backward that takes them meets the bounds."""
+    batch, dim, N, L, dt, gate, bias, bbar = case
+    w, x = wl.custom(batch, dim, N, L, dtype=dt, gate=gate, bias=bias, seed=5800 + L)
+    g = wl.grad_inputs(w)
+    h0 = wl.decode_state(w)
+    t = {k: to_dev(x.get(k), dev) for k in ("u", "delta", "A", "B", "C", "D", "z", "delta_bias")}
+    h0d = to_dev(h0, dev)
+    kw = dict(D=t["D"], z=t["z"], delta_bias=t["delta_bias"], delta_softplus=True, h0=h0d,
+              bbar=bbar)
+    ck = torch.full(ssm.ssm_checkpoint_shape(batch, dim, N, L), float("nan"),
+                    dtype=torch.float32, device=dev)
+    y0, f0 = ssm.ssm_selective_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], **kw)
+    y1, f1 = ssm.ssm_selective_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], **kw,
+                                        checkpoints=ck)
+    got = ssm.ssm_selective_scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"],
+                                     to_dev(g["dy"], dev), D=t["D"], z=t["z"],
+                                     delta_bias=t["delta_bias"], delta_softplus=True, h0=h0d,
+                                     dfinal_state=to_dev(g["dfinal"], dev), bbar=bbar,
+                                     want_dh0=True, checkpoints=ck)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1) and torch.equal(f0, f1)
+    # the checkpoints: h0, then the oracle's state after every whole block
+    cks = to_np(ck)
+    assert np.array_equal(cks[:, :, 0, :], h0)
+    rows = np.random.default_rng(L).choice(batch * dim, min(batch * dim, 48), replace=False)
+    for blk in range(1, cks.shape[2]):
+        cut = 128 * blk
+        part = {k: np.ascontiguousarray(x[k][..., :cut]) for k in ("u", "delta", "B", "C")}
+        _, fr = oracle.selective_scan(part["u"], part["delta"], x["A"], part["B"], part["C"],
+                                      D=x["D"], delta_bias=x.get("delta_bias"),
+                                      delta_softplus=True, bbar=bbar,
+                                      h0=h0.reshape(batch * dim, N)[rows], want_y=False,
+                                      channels=rows)
+        err = norm_err(cks[:, :, blk, :].reshape(batch * dim, N)[rows], fr)
+        assert err <= TOL[dt], (blk, err)
+    ref = run_oracle(x, g, bbar, h0, g["dfinal"])
+    compare(w, got, ref, f"{case} with forward checkpoints")

@@ -363,7 +363,7 @@ def test_abi_rejects_misaligned_and_aliased_buffers(ssm, dev):
     y = torch.empty_like(keep["u"])
     args = [big[1:].data_ptr(), keep["delta"].data_ptr(), keep["A"].data_ptr(),
             keep["B"].data_ptr(), keep["C"].data_ptr(), None, None, None, 0,
-            None, y.data_ptr(), None, 1, 8, 4, 64, 0, 0, None]
+            None, y.data_ptr(), None, None, 1, 8, 4, 64, 0, 0, None]
     assert lib.ssm_selective_scan_fwd(*args) == 4  # SSM_E_ALIGN
     args[0] = keep["u"].data_ptr()
     args[10] = keep["u"].data_ptr()  # y aliases u
