@@ -284,6 +284,41 @@ def bench_conv(ssm, torch, w, dev, steps, warmup):
     return res
 
 
+def bench_lti(ssm, torch, dev, steps, warmup):
+    """The time-invariant path on the mamba130m shape (batch 8, dim 1536,
+    N 16, L 2048, bf16 u and y): the kernel K from ssm_lti_kernel, then
+    y = K * u + D u by the direct causal sum and by FFT."""
+    w = wl.WORKLOADS["mamba130m"]
+    A, D, _ = wl.params(w)
+    r = np.random.default_rng(w.seed)
+    Bv, Cv = r.standard_normal(w.dstate).astype(np.float32), r.standard_normal(w.dstate).astype(np.float32)
+    step = r.uniform(0.01, 0.2, w.dim).astype(np.float32)
+    u = torch.randn((w.batch, w.dim, w.seqlen), generator=torch.Generator().manual_seed(w.seed)
+                    ).to(torch.bfloat16).to(dev)
+    Ad, Bd, Cd, sd, Dd = (to_dev(v, dev) for v in (A, Bv, Cv, step, D))
+    K = ssm.ssm_lti_kernel(Ad, Bd, Cd, sd, w.seqlen)
+    y = torch.empty_like(u)
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn):
+        settle(fn, torch, warmup)
+        a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(steps):
+            fn()
+        e.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(e) / steps
+
+    ms_k = timed(lambda: ssm.ssm_lti_kernel(Ad, Bd, Cd, sd, w.seqlen, K=K))
+    ms_d = timed(lambda: ssm.ssm_lti_conv(K, u, D=Dd, y=y))
+    ms_f = timed(lambda: ssm.ssm_lti_conv(K, u, D=Dd, y=y, method="fft"))
+    return {"workload": f"LTI path: batch {w.batch}, dim {w.dim}, N {w.dstate}, L {w.seqlen}, "
+                        "bf16 u and y",
+            "kernel_ms": round(ms_k, 4), "conv_direct_ms": round(ms_d, 4),
+            "conv_fft_ms": round(ms_f, 4), "steps": steps}
+
+
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -373,6 +408,7 @@ def main(argv=None):
     p.add_argument("--no-backward", action="store_true")
     p.add_argument("--no-conv", action="store_true")
     p.add_argument("--no-ssd", action="store_true")
+    p.add_argument("--no-lti", action="store_true")
     p.add_argument("--backward-steps", type=int, default=5)
     p.add_argument("--copy-check", type=int, default=0, metavar="BYTES",
                    help="also run torch's plain copy of BYTES three times (counter calibration "
@@ -471,6 +507,11 @@ def main(argv=None):
     if not args.no_ssd:
         out["ssd"] = bench_ssd(ssm, torch, dev, 30, 2)
         print(f"[bench] ssd: {out['ssd']['ms_per_call']} ms/call", file=sys.stderr, flush=True)
+    if not args.no_lti:
+        out["lti"] = bench_lti(ssm, torch, dev, 5, 1)
+        print(f"[bench] lti: kernel {out['lti']['kernel_ms']} ms, conv direct "
+              f"{out['lti']['conv_direct_ms']} ms, fft {out['lti']['conv_fft_ms']} ms",
+              file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, x)
         print(f"[bench] cpu baseline: {out['cpu_baseline']['seconds']}s", file=sys.stderr,

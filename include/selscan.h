@@ -303,6 +303,17 @@ int64_t ssm_ssd_workspace_size(int64_t batch, int64_t seqlen, int64_t ngroups, i
 int ssm_lti_conv(const float* K, const void* u, const float* Dskip, void* y, int64_t batch,
                  int64_t dim, int64_t seqlen, int io_dtype, void* hip_stream);
 
+/*
+ * The same y = K * u + D u by FFT ("State-space models", section
+ * "Recurrence and convolution": the precomputed kernel applied with an FFT in
+ * O(L log L)): per channel, K and each sequence are zero-padded to a power of
+ * two M >= 2 seqlen - 1, transformed, multiplied and transformed back, in
+ * float32.  Arguments as for ssm_lti_conv; seqlen at most 4096
+ * (SSM_E_UNSUPPORTED beyond: the direct sum takes any length).
+ */
+int ssm_lti_conv_fft(const float* K, const void* u, const float* Dskip, void* y, int64_t batch,
+                     int64_t dim, int64_t seqlen, int io_dtype, void* hip_stream);
+
 /* Static description of a status code (never NULL). */
 const char* ssm_status_str(int status);
 

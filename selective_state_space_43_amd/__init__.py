@@ -15,7 +15,8 @@ Entry points carry the C names:
   ssm_state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None,
                    delta_softplus=False, bbar="delta", y=None) -> y
   ssm_lti_kernel(A, Bv, Cv, delta, L, bbar="delta", K=None) -> K
-  ssm_lti_conv(K, u, D=None, y=None) -> y                   (y = K * u + D u, causal)
+  ssm_lti_conv(K, u, D=None, y=None, method="direct") -> y  (y = K * u + D u, causal;
+                                                              method "direct" or "fft")
   ssm_selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None,
                          delta_softplus=False, h0=None, dfinal_state=None,
                          bbar="delta", workspace=None, checkpoints=None)

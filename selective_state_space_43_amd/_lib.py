@@ -55,11 +55,13 @@ def lib() -> ctypes.CDLL:
         L.ssm_ssd_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, i64,
                                   i64, i64, i64, i64, i64, i64, i32, vp]
         L.ssm_lti_conv.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, vp]
+        L.ssm_lti_conv_fft.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, vp]
         L.ssm_ssd_workspace_size.argtypes = [i64, i64, i64, i64]
         L.ssm_ssd_workspace_size.restype = i64
         for f in (L.ssm_selective_scan_fwd, L.ssm_state_update, L.ssm_lti_kernel,
                   L.ssm_selective_scan_bwd, L.ssm_causal_conv1d_fwd, L.ssm_causal_conv1d_update,
-                  L.ssm_causal_conv1d_bwd, L.ssm_ssd_fwd, L.ssm_lti_conv):
+                  L.ssm_causal_conv1d_bwd, L.ssm_ssd_fwd, L.ssm_lti_conv,
+                  L.ssm_lti_conv_fft):
             f.restype = i32
         L.ssm_status_str.argtypes = [i32]
         L.ssm_status_str.restype = ctypes.c_char_p

@@ -155,8 +155,11 @@ def ssm_lti_kernel(A, Bv, Cv, delta, L, bbar="delta", K=None):
     return K
 
 
-def ssm_lti_conv(K, u, D=None, y=None):
-    """y = K * u + D u per channel (causal): K [dim, L] float32, u [batch, dim, L]."""
+def ssm_lti_conv(K, u, D=None, y=None, method="direct"):
+    """y = K * u + D u per channel (causal): K [dim, L] float32, u [batch, dim, L].
+    method "direct" (the causal sum, any L) or "fft" (L up to 4096)."""
+    if method not in ("direct", "fft"):
+        raise ValueError(f"method {method!r}: expected 'direct' or 'fft'")
     _dev(u, "u", None)
     dev = u.device
     if u.dim() != 3 or u.dtype not in _IO:
@@ -168,10 +171,10 @@ def ssm_lti_conv(K, u, D=None, y=None):
         y = torch.empty_like(u)
     else:
         _io(y, "y", u.dtype, (batch, dim, L), dev)
+    fn = lib().ssm_lti_conv_fft if method == "fft" else lib().ssm_lti_conv
     with torch.cuda.device(dev):
-        st = lib().ssm_lti_conv(_ptr(K), _ptr(u), _ptr(D), _ptr(y), batch, dim, L, _IO[u.dtype],
-                                _stream(dev))
-    check(st, "ssm_lti_conv")
+        st = fn(_ptr(K), _ptr(u), _ptr(D), _ptr(y), batch, dim, L, _IO[u.dtype], _stream(dev))
+    check(st, "ssm_lti_conv_fft" if method == "fft" else "ssm_lti_conv")
     return y
 
 

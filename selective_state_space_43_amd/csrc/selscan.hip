@@ -2083,6 +2083,81 @@ __global__ void __launch_bounds__(256) lti_conv_kernel(const float* K, const voi
   }
 }
 
+// ---------------------------------------------------------------- LTI convolution by FFT
+//
+// The same y = K * u + D u through the frequency domain ("State-space
+// models", section "Recurrence and convolution": the kernel computed once and
+// applied with an FFT in O(L log L)).  One workgroup per channel: K is
+// zero-padded to M >= 2L - 1 points (a power of two, so that the circular
+// convolution of length M equals the causal one for t < L) and transformed
+// once; every sequence of the channel is then transformed, multiplied by it
+// and transformed back.  Radix-2 decimation in time in LDS with the input in
+// bit-reversed order; twiddles exp(-2 pi i j / M) from sincospif; the
+// inverse is the forward transform of the conjugate.
+constexpr int kFftMinLog2 = 8, kFftMaxLog2 = 13;  // M from 256 to 8192 points
+
+template <typename IO, int LOG2M>
+__global__ void __launch_bounds__(256) lti_conv_fft_kernel(const float* K, const void* u,
+                                                           const float* Dskip, void* y,
+                                                           int64_t batch, int64_t dim, int64_t L) {
+  constexpr int M = 1 << LOG2M, R = M / 256;
+  __shared__ float2 sK[M], sX[M], sTw[M / 2];
+  const int64_t d = blockIdx.x;
+  const int tid = threadIdx.x;
+  for (int j = tid; j < M / 2; j += 256) {
+    float sn, cs;
+    sincospif(-2.0f * (float)j / (float)M, &sn, &cs);
+    sTw[j] = make_float2(cs, sn);
+  }
+  auto rev = [](int i) { return (int)(__brev((unsigned)i) >> (32 - LOG2M)); };
+  // in-place transform of X (bit-reversed in, natural order out); the
+  // barriers also order the caller's writes before and its reads after
+  auto fft = [&](float2* X) {
+#pragma unroll 1
+    for (int st = 0; st < LOG2M; ++st) {
+      __syncthreads();
+      const int half = 1 << st;
+#pragma unroll
+      for (int r = 0; r < (R + 1) / 2; ++r) {
+        const int j = tid + 256 * r;  // butterfly
+        if (j >= M / 2) break;
+        const int pos = j & (half - 1), i0 = ((j >> st) << (st + 1)) + pos, i1 = i0 + half;
+        const float2 w = sTw[pos << (LOG2M - 1 - st)];
+        const float2 a = X[i0], bb = X[i1];
+        const float2 t = make_float2(w.x * bb.x - w.y * bb.y, w.x * bb.y + w.y * bb.x);
+        X[i0] = make_float2(a.x + t.x, a.y + t.y);
+        X[i1] = make_float2(a.x - t.x, a.y - t.y);
+      }
+    }
+    __syncthreads();
+  };
+  const float* Kd = K + d * L;
+  for (int i = tid; i < M; i += 256) sK[rev(i)] = make_float2(i < L ? Kd[i] : 0.0f, 0.0f);
+  fft(sK);
+  const float Dd = Dskip ? Dskip[d] : 0.0f;
+  const float scale = 1.0f / (float)M;
+#pragma unroll 1
+  for (int64_t b = 0; b < batch; ++b) {
+    const int64_t row = (b * dim + d) * L;
+    for (int i = tid; i < M; i += 256) sX[rev(i)] = make_float2(i < L ? Io<IO>::ld1(u, row + i) : 0.0f, 0.0f);
+    fft(sX);
+    // conj(K^ X^), written back in bit-reversed order for the inverse
+    float2 pr[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float2 kk = sK[tid + 256 * r], xx = sX[tid + 256 * r];
+      pr[r] = make_float2(kk.x * xx.x - kk.y * xx.y, -(kk.x * xx.y + kk.y * xx.x));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < R; ++r) sX[rev(tid + 256 * r)] = pr[r];
+    fft(sX);
+    for (int64_t t = tid; t < L; t += 256)
+      Io<IO>::st1(y, row + t, fmaf(Dd, Io<IO>::ld1(u, row + t), sX[t].x * scale));
+    __syncthreads();  // the next sequence overwrites sX
+  }
+}
+
 // ---------------------------------------------------------------- host side
 
 thread_local char g_last_error[512] = "";
@@ -2883,6 +2958,53 @@ int ssm_lti_conv(const float* K, const void* u, const float* Dskip, void* y, int
   else
     hipLaunchKernelGGL(lti_conv_kernel<float>, grid, dim3(256), 0, s, K, u, Dskip, y, dim, seqlen);
   return launch_status("ssm_lti_conv launch");
+}
+
+int ssm_lti_conv_fft(const float* K, const void* u, const float* Dskip, void* y, int64_t batch,
+                     int64_t dim, int64_t seqlen, int io_dtype, void* hip_stream) {
+  g_last_error[0] = 0;
+  if (!K) return fail(SSM_E_NULL, "K is NULL");
+  if (!u) return fail(SSM_E_NULL, "u is NULL");
+  if (!y) return fail(SSM_E_NULL, "y is NULL");
+  int st;
+  if ((st = check_extent("batch", batch)) || (st = check_extent("dim", dim)) ||
+      (st = check_extent("seqlen", seqlen)))
+    return st;
+  if (dim > ((int64_t)1 << 30)) return fail(SSM_E_SHAPE, "dim = %lld exceeds 2^30", (long long)dim);
+  if (!product_ok(batch, dim, seqlen, 4)) return fail(SSM_E_SHAPE, "tensor sizes overflow");
+  if (io_dtype != SSM_DTYPE_F32 && io_dtype != SSM_DTYPE_BF16)
+    return fail(SSM_E_DTYPE, "io_dtype = %d is not SSM_DTYPE_F32 or SSM_DTYPE_BF16", io_dtype);
+  int lg = kFftMinLog2;
+  while ((int64_t(1) << lg) < 2 * seqlen - 1) ++lg;
+  if (lg > kFftMaxLog2)
+    return fail(SSM_E_UNSUPPORTED, "seqlen = %lld: the FFT path takes seqlen up to %d",
+                (long long)seqlen, 1 << (kFftMaxLog2 - 1));
+  const int64_t es = io_dtype == SSM_DTYPE_BF16 ? 2 : 4;
+  const Span ys{y, batch * dim * seqlen * es, "y"};
+  const Span in[] = {{K, dim * seqlen * 4, "K"}, {u, batch * dim * seqlen * es, "u"},
+                     {Dskip, dim * 4, "D"}};
+  for (const Span& s : in)
+    if (overlaps(ys, s)) return fail(SSM_E_ALIAS, "y overlaps %s", s.name);
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  const bool bf = io_dtype == SSM_DTYPE_BF16;
+  auto go = [&](auto lg_tag) {
+    constexpr int LG = decltype(lg_tag)::value;
+    if (bf)
+      hipLaunchKernelGGL((lti_conv_fft_kernel<uint16_t, LG>), dim3((unsigned)dim), dim3(256), 0, s,
+                         K, u, Dskip, y, batch, dim, seqlen);
+    else
+      hipLaunchKernelGGL((lti_conv_fft_kernel<float, LG>), dim3((unsigned)dim), dim3(256), 0, s,
+                         K, u, Dskip, y, batch, dim, seqlen);
+  };
+  switch (lg) {
+    case 8: go(std::integral_constant<int, 8>{}); break;
+    case 9: go(std::integral_constant<int, 9>{}); break;
+    case 10: go(std::integral_constant<int, 10>{}); break;
+    case 11: go(std::integral_constant<int, 11>{}); break;
+    case 12: go(std::integral_constant<int, 12>{}); break;
+    default: go(std::integral_constant<int, 13>{}); break;
+  }
+  return launch_status("ssm_lti_conv_fft launch");
 }
 
 }  // extern "C"

@@ -245,3 +245,14 @@ def test_lti_conv_validation(lib):
     assert f(1 * P, 2 * P, None, 3 * P, 2, 4, 64, 9, None) == 3
     assert f(1 * P, 2 * P, None, 2 * P, 2, 4, 64, 1, None) == 5
     assert f(1 * P, 2 * P, None, 1 * P, 2, 4, 64, 1, None) == 5
+
+
+def test_lti_conv_fft_validation(lib):
+    f = lib.ssm_lti_conv_fft
+    assert f(None, 2 * P, None, 3 * P, 2, 4, 64, 1, None) == 1
+    assert f(1 * P, 2 * P, None, None, 2, 4, 64, 1, None) == 1
+    assert f(1 * P, 2 * P, None, 3 * P, 2, 4, 0, 1, None) == 2
+    assert f(1 * P, 2 * P, None, 3 * P, 2, 4, 64, 9, None) == 3
+    assert f(1 * P, 2 * P, None, 2 * P, 2, 4, 64, 1, None) == 5
+    assert f(1 * P, 2 * P, None, 1 * P, 2, 4, 64, 1, None) == 5
+    assert f(1 * P, 2 * P, None, 3 * P, 1, 1, 4097, 1, None) == 6  # beyond the FFT length

@@ -330,6 +330,41 @@ def test_lti_conv_matches_oracle(ssm, dev, dt, L):
             assert norm_err(to_np(y[b, d]), yc) <= TOL[dt], (b, d)
 
 
+@pytest.mark.parametrize("dt,L", [("f32", 1), ("f32", 7), ("f32", 129), ("bf16", 300),
+                                  ("f32", 2048), ("bf16", 2048), ("f32", 3000), ("f32", 4096)])
+def test_lti_conv_fft_matches_oracle(ssm, dev, dt, L):
+    """ssm_lti_conv_fft against the oracle's direct causal sum: transform
+    sizes 256 to 8192 (L = 1 .. 4096, powers of two and not)."""
+    r = np.random.default_rng(100 + L)
+    batch, dim, N = 3, 4, 16
+    A = -np.exp(r.uniform(np.log(0.5), np.log(16), (dim, N)))
+    Bv, Cv = r.standard_normal((dim, N)), r.standard_normal((dim, N))
+    step = r.uniform(0.01, 0.2, dim)
+    K = oracle.lti_kernel(A, Bv, Cv, step, L, bbar="zoh").astype(np.float32)
+    Dv = r.standard_normal(dim).astype(np.float32)
+    u = r.standard_normal((batch, dim, L)).astype(np.float32)
+    if dt == "bf16":
+        u = wl.to_bf16_bits(u)
+    y = ssm.ssm_lti_conv(to_dev(K, dev), to_dev(u, dev), D=to_dev(Dv, dev), method="fft")
+    torch.cuda.synchronize()
+    uf = wl.bf16_bits_to_f32(u) if dt == "bf16" else u
+    worst = 0.0
+    for b in range(batch):
+        for d in range(dim):
+            yc = oracle.causal_conv(K[d].astype(np.float64), uf[b, d].astype(np.float64),
+                                    float(Dv[d]))
+            worst = max(worst, norm_err(to_np(y[b, d]), yc))
+    print(f"fft L={L} {dt}: {worst:.2e}", flush=True)
+    assert worst <= TOL[dt]
+
+
+def test_lti_conv_fft_rejects_long_sequences(ssm, dev):
+    K = torch.zeros((1, 4097), dtype=torch.float32, device=dev)
+    u = torch.zeros((1, 1, 4097), dtype=torch.float32, device=dev)
+    with pytest.raises(ssm.SelscanError, match="SSM_E_UNSUPPORTED"):
+        ssm.ssm_lti_conv(K, u, method="fft")
+
+
 def test_lti_path_equals_time_invariant_scan(ssm, dev):
     """The whole LTI path on the GPU (ssm_lti_kernel then ssm_lti_conv) equals
     the GPU scan with delta, B, C fixed in time."""
@@ -349,8 +384,10 @@ def test_lti_path_equals_time_invariant_scan(ssm, dev):
     K = ssm.ssm_lti_kernel(to_dev(A, dev), to_dev(Bv, dev), to_dev(Cv, dev), to_dev(dt, dev), L,
                            bbar="bilinear")
     yk = ssm.ssm_lti_conv(K, to_dev(u, dev), D=to_dev(Dv, dev))
+    yf = ssm.ssm_lti_conv(K, to_dev(u, dev), D=to_dev(Dv, dev), method="fft")
     torch.cuda.synchronize()
     assert norm_err(to_np(yk), to_np(y)) <= 1e-4
+    assert norm_err(to_np(yf), to_np(y)) <= 1e-4
 
 
 # ---------------------------------------------------------------- ABI errors with real buffers
