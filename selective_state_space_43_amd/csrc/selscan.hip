@@ -881,7 +881,9 @@ __global__ void __launch_bounds__(256) scan_bwd_main_kernel(const BwdArgs a) {
       *reinterpret_cast<float2*>(sPrep + (2 * 64 + lane) * SP + s0) = dyp;
     }
     __syncthreads();  // every wave's steps are in; the previous group's sums are read
-    float dt[K], uu[K], w[K], dyc[K], yc[K], ddt[K], du[K];
+    // lb[i] (delta*B rule): sum over this wave's states of lambda_t B_t, from
+    // which du and the input's part of ddelta follow once per step
+    float dt[K], uu[K], w[K], dyc[K], yc[K], ddt[K], du[K], lb[K];
     float S = 0.0f;  // sum of the lane's steps, in log2 units
 #pragma unroll
     for (int i = 0; i < K; i += 4) {
@@ -899,6 +901,7 @@ __global__ void __launch_bounds__(256) scan_bwd_main_kernel(const BwdArgs a) {
       yc[i] = 0.0f;
       ddt[i] = 0.0f;
       du[i] = 0.0f;
+      lb[i] = 0.0f;
     }
     S *= kLog2e;
     const float* pA = par + row * N;
@@ -959,20 +962,19 @@ __global__ void __launch_bounds__(256) scan_bwd_main_kernel(const BwdArgs a) {
           const float lam = fmaf(dyc[i], cq[i], mu);  // lambda_t
           const float mun = av[i] * lam;               // Abar_t lambda_t
           const float daa = mun * hh[i];               // lambda_t Abar_t h_{t-1}
-          const float lb = lam * bq[i];
           ddt[i] = fmaf(daa, An, ddt[i]);
           dAacc = fmaf(daa, dt[i], dAacc);
           if constexpr (ZOH) {
-            const float dbeta = lb * uu[i];  // lambda B u
+            const float lbn = lam * bq[i];
+            const float dbeta = lbn * uu[i];  // lambda B u
             ddt[i] = fmaf(dbeta, av[i], ddt[i]);
             const float dcf = An != 0.0f ? (dt[i] * av[i] - cf[i]) * rcp(An) : 0.5f * dt[i] * dt[i];
             dAacc = fmaf(dbeta, dcf, dAacc);
             gB[i] = lam * cf[i] * uu[i];
-            du[i] = fmaf(lb, cf[i], du[i]);
+            du[i] = fmaf(lbn, cf[i], du[i]);
           } else {
-            ddt[i] = fmaf(lb, uu[i], ddt[i]);
+            lb[i] = fmaf(lam, bq[i], lb[i]);
             gB[i] = lam * w[i];
-            du[i] = fmaf(lb, dt[i], du[i]);
           }
           gC[i] = dyc[i] * hh[i + 1];
           mu = mun;
@@ -987,6 +989,13 @@ __global__ void __launch_bounds__(256) scan_bwd_main_kernel(const BwdArgs a) {
         dAacc = row_sum16(dAacc);
         if (last && dvalid) unsafeAtomicAdd(&a.dA[d * N + n], dAacc);
         if (ci == 0 && first && dvalid && a.dh0) a.dh0[ch * N + n] = mu;
+      }
+    }
+    if constexpr (!ZOH) {
+#pragma unroll
+      for (int i = 0; i < K; ++i) {
+        ddt[i] = fmaf(lb[i], uu[i], ddt[i]);
+        du[i] = lb[i] * dt[i];
       }
     }
     // ---- per-step gradients: sum the four waves' partials for this wave's
