@@ -46,7 +46,11 @@
 #define SELSCAN_NT 16  // states staged per LDS tile (16 lanes per channel)
 #endif
 #ifndef SELSCAN_WAVES_PER_EU
-#define SELSCAN_WAVES_PER_EU 0  // occupancy hint for the register allocator (0: none)
+// occupancy the register allocator must keep for bf16 io and the delta*B
+// rule (0: no constraint): 3 waves per SIMD fit in 168 VGPRs with a few
+// spills and run about 1 % faster than 2; float32 io and the other rules
+// need more registers and get no constraint
+#define SELSCAN_WAVES_PER_EU 3
 #endif
 
 
@@ -279,13 +283,14 @@ struct Run<float, K> {
 };
 
 // r <- p[base + t .. base + t + K), zero past L or when !valid.  VEC: rows
-// are 16-byte aligned, so whole runs load as 16-byte vectors.
-template <typename IO, int K, bool VEC>
+// are 16-byte aligned, so whole runs load as 16-byte vectors.  INB: the
+// caller knows that t + K <= L.
+template <typename IO, int K, bool VEC, bool INB = false>
 __device__ __forceinline__ void run_load(Run<IO, K>& r, const void* p, int64_t base, int64_t t,
                                          int64_t L, bool valid) {
   using VT = typename std::remove_reference<decltype(r.v[0])>::type;
   constexpr int V = Io<IO>::V;
-  if (VEC && valid && t + K <= L) {
+  if (VEC && valid && (INB || t + K <= L)) {
     const VT* q = reinterpret_cast<const VT*>(static_cast<const IO*>(p) + base + t);
 #pragma unroll
     for (int i = 0; i < K / V; ++i) r.v[i] = q[i];
@@ -298,11 +303,11 @@ __device__ __forceinline__ void run_load(Run<IO, K>& r, const void* p, int64_t b
   }
 }
 
-template <typename IO, int K, bool VEC>
+template <typename IO, int K, bool VEC, bool INB = false>
 __device__ __forceinline__ void run_store(void* p, int64_t base, int64_t t, int64_t L,
                                           bool valid, const float* v) {
   if (!valid) return;
-  if (VEC && t + K <= L) {
+  if (VEC && (INB || t + K <= L)) {
 #pragma unroll
     for (int i = 0; i < K; i += Io<IO>::V) Io<IO>::stv(p, base + t + i, v + i);
   } else {
@@ -344,9 +349,7 @@ constexpr int kCkptT = 128;
 template <typename IO, int LPC, int K, int W, int NT, bool VEC, int RULE, bool GATE,
           bool CKPT = false>
 __global__ void __launch_bounds__(64 * W)
-#if SELSCAN_WAVES_PER_EU
-    __attribute__((amdgpu_waves_per_eu(SELSCAN_WAVES_PER_EU, SELSCAN_WAVES_PER_EU)))
-#endif
+    __attribute__((amdgpu_waves_per_eu(RULE == 0 && sizeof(IO) == 2 && SELSCAN_WAVES_PER_EU ? SELSCAN_WAVES_PER_EU : 1)))
     scan_fwd_kernel(const ScanArgs a) {
   constexpr int CPW = 64 / LPC;  // channels per wave
   constexpr int CPB = CPW * W;   // channels per workgroup
@@ -393,8 +396,12 @@ __global__ void __launch_bounds__(64 * W)
   const float* a_row = sA + chb * N;
 
   // B, C rows [n0, n0 + nt) x [t0, t0 + T) -> LDS as float32, laid out so
-  // that each lane reads its K steps as contiguous float4s.
-  auto stage_bc = [&](int64_t t0, int64_t n0, int nt) {
+  // that each lane reads its K steps as contiguous float4s.  FULL: nt = NT
+  // and the chunk lies inside [0, L) (the index arithmetic is then by
+  // constants).
+  auto stage_bc = [&](int64_t t0, int64_t n0, int nt_arg, auto full_tag) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    const int nt = FULL ? NT : nt_arg;
 #pragma unroll
     for (int k = 0; k < ITEMS; ++k) {
       const int item = threadIdx.x + k * NTH;
@@ -403,7 +410,7 @@ __global__ void __launch_bounds__(64 * W)
         const int r = item % (nt * TV);
         const int nl = r / TV, tloc = (r % TV) * V;
         Run<IO, V> rv;
-        run_load<IO, V, VEC>(rv, tensor ? a.Cm : a.Bm, bcrow + (n0 + nl) * L, t0 + tloc, L, true);
+        run_load<IO, V, VEC, FULL>(rv, tensor ? a.Cm : a.Bm, bcrow + (n0 + nl) * L, t0 + tloc, L, true);
         float v[V];
         rv.unpack(v);
         float* dst = (tensor ? sC : sB) + (nl * LPC + tloc / K) * KP + tloc % K;
@@ -427,11 +434,11 @@ __global__ void __launch_bounds__(64 * W)
     // issue this chunk's sequence loads first: they complete while the first
     // B/C tile is staged
     Run<IO, K> ru, rd, rz;
-    run_load<IO, K, VEC>(ru, a.u, row, tl, L, dvalid);
-    run_load<IO, K, VEC>(rd, a.delta, row, tl, L, dvalid);
-    if constexpr (GATE) run_load<IO, K, VEC>(rz, a.z, row, tl, L, dvalid);
+    run_load<IO, K, VEC, FULL>(ru, a.u, row, tl, L, dvalid);
+    run_load<IO, K, VEC, FULL>(rd, a.delta, row, tl, L, dvalid);
+    if constexpr (GATE) run_load<IO, K, VEC, FULL>(rz, a.z, row, tl, L, dvalid);
     __syncthreads();  // every wave is done with the previous chunk's last tile
-    stage_bc(t0, 0, (int)(N < NT ? N : NT));
+    stage_bc(t0, 0, (int)(N < NT ? N : NT), full_tag);
     __syncthreads();
     {
       float raw[K];
@@ -521,7 +528,7 @@ __global__ void __launch_bounds__(64 * W)
     for (int64_t n0 = 0; n0 < N; n0 += NT) {
       if (n0 > 0) {
         __syncthreads();  // every wave is done with the previous tile
-        stage_bc(t0, n0, (int)((N - n0) < NT ? (N - n0) : NT));
+        stage_bc(t0, n0, (int)((N - n0) < NT ? (N - n0) : NT), full_tag);
         __syncthreads();
       }
       const int nt = FULL ? NT : (int)((N - n0) < NT ? (N - n0) : NT);
@@ -535,7 +542,7 @@ __global__ void __launch_bounds__(64 * W)
 #pragma unroll
       for (int i = 0; i < K; ++i) y[i] *= silu_f(zz[i]);
     }
-    run_store<IO, K, VEC>(a.y, row, tl, L, dvalid, y);
+    run_store<IO, K, VEC, FULL>(a.y, row, tl, L, dvalid, y);
   };
 
   int64_t t0 = 0;
