@@ -43,6 +43,7 @@ VALU_PEAK_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
 SLOTS_PER_ELEMENT = 6
 KERNEL_SRC = os.path.join(ROOT, "selective_state_space_43_amd", "csrc", "selscan.hip")
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "scan_fwd_mamba2p8b_pmc.md")
+VALU_SUMMARY = os.path.join(ROOT, "profiles", "scan_fwd_mamba2p8b_valu.md")
 
 
 SCAN_SOURCE_END = b"// ---------------------------------------------------------------- backward"
@@ -70,6 +71,20 @@ def committed_traffic():
     if not (m_src and m_tr) or m_src.group(1) != kernel_source_hash():
         return None
     return float(m_tr.group(1))
+
+
+def committed_valu_busy():
+    """VALU busy fraction of the scan kernel from the committed counter
+    summary, or None if it is missing or was taken on a different source."""
+    try:
+        text = open(VALU_SUMMARY).read()
+    except OSError:
+        return None
+    m_src = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    m_b = re.search(r"VALU busy:.*=\s*([0-9.]+)", text)
+    if not (m_src and m_b) or m_src.group(1) != kernel_source_hash():
+        return None
+    return float(m_b.group(1))
 
 
 def to_dev(a, dev):
@@ -473,6 +488,7 @@ def main(argv=None):
             "unit": "T VALU lane-slots/s (6 slots per element)",
             "frac": round(achieved_tslots / VALU_PEAK_TSLOTS, 4),
             "traffic": traffic,
+            "valu_busy": committed_valu_busy(),
             "algorithmic_bytes_per_launch": w.io_bytes,
             "kernel_ms": round(ms_kernel, 4),
         },
