@@ -1474,11 +1474,6 @@ struct SsdArgs {
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
-__device__ __forceinline__ uint16_t f2bf(float v) { return __builtin_bit_cast(uint16_t, (__bf16)v); }
-
-// v rounded to bf16 and back
-__device__ __forceinline__ float bf16_round(float v) { return (float)(__bf16)v; }
-
 // inclusive prefix sum over the 64 lanes of a wave
 __device__ __forceinline__ float wave_prefix_sum(float v) {
   v += dpp0<kRowShr1>(v);
