@@ -10,7 +10,9 @@ HBM before timing starts.  The one-token decode step (ssm_state_update) is
 timed separately on the decode workload and reported under "decode", and the
 backward pass (ssm_selective_scan_bwd) on the same workload under "backward",
 the causal conv1d in front of the scan (forward and backward) under
-"conv1d", and the Mamba-2 scan (scalar A per head, on MFMA) under "ssd".
+"conv1d", the Mamba-2 scan (scalar A per head, on MFMA) under "ssd", the
+forward scan on the long-context workload under "long_context" and the
+time-invariant path under "lti".
 
 Prints one JSON line: the metric (scan elements B*D*L*N per second), the
 roofline of the scan kernel (live HIP-event timing; HBM traffic from the
@@ -299,6 +301,40 @@ def bench_conv(ssm, torch, w, dev, steps, warmup):
     return res
 
 
+def bench_long(ssm, torch, dev, steps, warmup):
+    """The forward scan on the long-context workload (batch 1, dim 2048, N 16,
+    L 524288, bf16, no gate): 64 lanes per channel, 1024-step chunks."""
+    w = wl.WORKLOADS["long_context"]
+    x = wl.scan_inputs(w)
+    u, dl, A, B, C = (to_dev(x[k], dev) for k in ("u", "delta", "A", "B", "C"))
+    D = to_dev(x["D"], dev)
+    del x
+    y = torch.empty_like(u)
+    fs = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device=dev)
+
+    def step():
+        ssm.ssm_selective_scan_fwd(u, dl, A, B, C, D=D, delta_softplus=True, y=y, final_state=fs)
+
+    settle(step, torch, warmup)
+    stream = torch.cuda.current_stream(dev)
+    a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        step()
+    e.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(e) / steps
+    gbps = w.io_bytes / (ms * 1e-3) / 1e9
+    slots = SLOTS_PER_ELEMENT * w.elements / (ms * 1e-3) / 1e12
+    return {"workload": f"{w.name}: batch {w.batch}, dim {w.dim}, N {w.dstate}, L {w.seqlen}, "
+                        "bf16, no gate",
+            "ms_per_call": round(ms, 4),
+            "elements_per_s": float("%.4g" % (w.elements / (ms * 1e-3))),
+            "algorithmic_bytes": w.io_bytes, "hbm_gbps": round(gbps, 1),
+            "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+            "alu_frac": round(slots / VALU_PEAK_TSLOTS, 4), "steps": steps}
+
+
 def bench_lti(ssm, torch, dev, steps, warmup):
     """The time-invariant path on the mamba130m shape (batch 8, dim 1536,
     N 16, L 2048, bf16 u and y): the kernel K from ssm_lti_kernel, then
@@ -424,6 +460,7 @@ def main(argv=None):
     p.add_argument("--no-conv", action="store_true")
     p.add_argument("--no-ssd", action="store_true")
     p.add_argument("--no-lti", action="store_true")
+    p.add_argument("--no-long", action="store_true")
     p.add_argument("--backward-steps", type=int, default=5)
     p.add_argument("--copy-check", type=int, default=0, metavar="BYTES",
                    help="also run torch's plain copy of BYTES three times (counter calibration "
@@ -523,6 +560,10 @@ def main(argv=None):
     if not args.no_ssd:
         out["ssd"] = bench_ssd(ssm, torch, dev, 30, 2)
         print(f"[bench] ssd: {out['ssd']['ms_per_call']} ms/call", file=sys.stderr, flush=True)
+    if not args.no_long:
+        out["long_context"] = bench_long(ssm, torch, dev, 10, 1)
+        print(f"[bench] long_context: {out['long_context']['ms_per_call']} ms/call",
+              file=sys.stderr, flush=True)
     if not args.no_lti:
         out["lti"] = bench_lti(ssm, torch, dev, 5, 1)
         print(f"[bench] lti: kernel {out['lti']['kernel_ms']} ms, conv direct "
