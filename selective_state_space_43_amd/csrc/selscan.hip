@@ -1661,15 +1661,22 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(const SsdArgs a) {
   const int64_t st0 = ((b * a.H + h) * kSsdP + pb * PB) * N;  // state rows of this workgroup
 
   // ---- state: S^T tiles in accumulators; lane: p = lane % 32, n = nb*32 + row(i)
-  f32x16_t S[NBW];
+  // state n-block nb (32 states) of the 32 channels as four 16 x 16 tiles of
+  // S^T, tile (ns, pb): lane holds n = nb*32 + ns*16 + (lane/16)*4 + i,
+  // p = pb*16 + lane % 16 (four short MFMA chains instead of one long one)
+  f32x4v_t S[NBW][2][2];
 #pragma unroll
   for (int q = 0; q < NBW; ++q) {
     const int nb = wave + 4 * q;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int n = nb * 32 + (i / 4) * 8 + (lane / 32) * 4 + i % 4;
-      S[q][i] = (a.h0 && nb < NB) ? a.h0[st0 + (lane % 32) * N + n] : 0.0f;
-    }
+    for (int ns = 0; ns < 2; ++ns)
+#pragma unroll
+      for (int pb2 = 0; pb2 < 2; ++pb2)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int n = nb * 32 + ns * 16 + (lane / 16) * 4 + i;
+          S[q][ns][pb2][i] = (a.h0 && nb < NB) ? a.h0[st0 + (pb2 * 16 + lane % 16) * N + n] : 0.0f;
+        }
   }
   auto write_state_bf16 = [&]() {
 #pragma unroll
@@ -1677,14 +1684,17 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(const SsdArgs a) {
       const int nb = wave + 4 * q;
       if (nb < NB) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int n = nb * 32 + r * 8 + (lane / 32) * 4;
-          uint2 v, w;
-          split_bf16(S[q][4 * r], S[q][4 * r + 1], v.x, w.x);
-          split_bf16(S[q][4 * r + 2], S[q][4 * r + 3], v.y, w.y);
-          *reinterpret_cast<uint2*>(sS + (lane % 32) * SP + n) = v;
-          *reinterpret_cast<uint2*>(sSl + (lane % 32) * SP + n) = w;
-        }
+        for (int ns = 0; ns < 2; ++ns)
+#pragma unroll
+          for (int pb2 = 0; pb2 < 2; ++pb2) {
+            const int n = nb * 32 + ns * 16 + (lane / 16) * 4, p = pb2 * 16 + lane % 16;
+            const f32x4v_t& v4 = S[q][ns][pb2];
+            uint2 v, w;
+            split_bf16(v4[0], v4[1], v.x, w.x);
+            split_bf16(v4[2], v4[3], v.y, w.y);
+            *reinterpret_cast<uint2*>(sS + p * SP + n) = v;
+            *reinterpret_cast<uint2*>(sSl + p * SP + n) = w;
+          }
       }
     }
   };
@@ -1699,7 +1709,7 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(const SsdArgs a) {
     uint32_t dtr;
     float4 gf[3];          // this wave's 12 slots of C.B^T
     uint4 ct[N / 32];      // C[t = 16 wave + lane % 16][32 k + (lane/16)*8 + j]
-    uint4 bt[NBW][4];      // B^T[n = nb*32 + lane % 32][16 ks + (lane/32)*8 + j]
+    uint4 bt[NBW][4];      // B^T[n = nb*32 + (f/2)*16 + lane % 16][32 (f%2) + (lane/16)*8 + j]
   };
   // per-lane byte offsets; the chunk's offset is added as a scalar.  Reads
   // past the end of a row return another row's (finite) inputs or zero: every
@@ -1708,7 +1718,8 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(const SsdArgs a) {
   const uint32_t oX = (uint32_t)((xp * L + xt8) * 2);
   const uint32_t oZ = (uint32_t)(((lane % 16) * L + ty) * 2), oZ16 = (uint32_t)(16 * L * 2);
   const uint32_t oC = (uint32_t)(((16 * wave + lane % 16) * N + (lane / 16) * 8) * 2);
-  const uint32_t oB = (uint32_t)(((wave * 32 + lane % 32) * L + (lane / 32) * 8) * 2), oB4 = (uint32_t)(128 * L * 2);
+  const uint32_t oB = (uint32_t)(((wave * 32 + lane % 16) * L + (lane / 16) * 8) * 2), oB4 = (uint32_t)(128 * L * 2),
+                 oB16 = (uint32_t)(16 * L * 2);
   // the operands of a chunk are loaded piece by piece, each into the
   // registers the previous chunk's copy has just left
   auto fetch_dt = [&](int64_t c, Pre& p) {
@@ -1737,7 +1748,8 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(const SsdArgs a) {
     for (int q = 0; q < NBW; ++q) {
       if (wave + 4 * q < NB) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) p.bt[q][ks] = buf_ld8_bf16<ALIGNED>(rB, oB + q * oB4 + 32 * ks, (uint32_t)(c * T * 2));
+        for (int f = 0; f < 4; ++f)  // (n half, 32-step half)
+          p.bt[q][f] = buf_ld8_bf16<ALIGNED>(rB, oB + q * oB4 + (f >> 1) * oB16 + 64 * (f & 1), (uint32_t)(c * T * 2));
       }
     }
   };
@@ -1869,17 +1881,29 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(const SsdArgs a) {
       const float decay = ex2(cs_end);
 #pragma unroll
       for (int q = 0; q < NBW; ++q)
-        if (wave + 4 * q < NB) S[q] *= decay;
+        if (wave + 4 * q < NB)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int xo = (lane % 32) * XP + 16 * ks + (lane / 32) * 8;
-        const uint4 xw = *reinterpret_cast<const uint4*>(sXw + xo);
-        const uint4 xl = *reinterpret_cast<const uint4*>(sXwl + xo);
+          for (int ns = 0; ns < 2; ++ns)
 #pragma unroll
-        for (int q = 0; q < NBW; ++q) {
-          if (wave + 4 * q < NB) {
-            S[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(cur.bt[q][ks]), as_bf16x8(xw), S[q], 0, 0, 0);
-            S[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(cur.bt[q][ks]), as_bf16x8(xl), S[q], 0, 0, 0);
+            for (int pb2 = 0; pb2 < 2; ++pb2) S[q][ns][pb2] *= decay;
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2) {
+#pragma unroll
+        for (int pb2 = 0; pb2 < 2; ++pb2) {
+          // w o X as the B operand: lane holds xw[s = 32 ks2 + (lane/16)*8 + j][p = pb2*16 + lane % 16]
+          const int xo = (pb2 * 16 + lane % 16) * XP + 32 * ks2 + (lane / 16) * 8;
+          const uint4 xw = *reinterpret_cast<const uint4*>(sXw + xo);
+          const uint4 xl = *reinterpret_cast<const uint4*>(sXwl + xo);
+#pragma unroll
+          for (int q = 0; q < NBW; ++q) {
+            if (wave + 4 * q < NB) {
+#pragma unroll
+              for (int ns = 0; ns < 2; ++ns) {
+                f32x4v_t& acc = S[q][ns][pb2];
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.bt[q][2 * ns + ks2]), as_bf16x8(xw), acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.bt[q][2 * ns + ks2]), as_bf16x8(xl), acc, 0, 0, 0);
+              }
+            }
           }
         }
       }
@@ -1899,11 +1923,13 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(const SsdArgs a) {
       const int nb = wave + 4 * q;
       if (nb < NB) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int n = nb * 32 + r * 8 + (lane / 32) * 4;
-          *reinterpret_cast<float4*>(a.final_state + st0 + (lane % 32) * N + n) =
-              make_float4(S[q][4 * r], S[q][4 * r + 1], S[q][4 * r + 2], S[q][4 * r + 3]);
-        }
+        for (int ns = 0; ns < 2; ++ns)
+#pragma unroll
+          for (int pb2 = 0; pb2 < 2; ++pb2) {
+            const int n = nb * 32 + ns * 16 + (lane / 16) * 4, p = pb2 * 16 + lane % 16;
+            const f32x4v_t& v4 = S[q][ns][pb2];
+            *reinterpret_cast<float4*>(a.final_state + st0 + p * N + n) = make_float4(v4[0], v4[1], v4[2], v4[3]);
+          }
       }
     }
   }
