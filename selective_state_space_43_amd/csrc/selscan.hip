@@ -46,10 +46,11 @@
 #define SELSCAN_NT 16  // states staged per LDS tile (16 lanes per channel)
 #endif
 #ifndef SELSCAN_WAVES_PER_EU
-// occupancy the register allocator must keep for bf16 io and the delta*B
-// rule (0: no constraint): 3 waves per SIMD fit in 168 VGPRs with a few
-// spills and run about 1 % faster than 2; float32 io and the other rules
-// need more registers and get no constraint
+// occupancy the register allocator must keep for bf16 io, the delta*B rule
+// and 16 lanes per channel (0: no constraint): 3 waves per SIMD fit in 168
+// VGPRs with a few spills and run about 1 % faster than 2; float32 io and the
+// other rules need more registers, and the wider lane layouts are held to two
+// waves per SIMD by their grid and LDS, so they get no constraint
 #define SELSCAN_WAVES_PER_EU 3
 #endif
 
@@ -349,7 +350,7 @@ constexpr int kCkptT = 128;
 template <typename IO, int LPC, int K, int W, int NT, bool VEC, int RULE, bool GATE,
           bool CKPT = false>
 __global__ void __launch_bounds__(64 * W)
-    __attribute__((amdgpu_waves_per_eu(RULE == 0 && sizeof(IO) == 2 && SELSCAN_WAVES_PER_EU ? SELSCAN_WAVES_PER_EU : 1)))
+    __attribute__((amdgpu_waves_per_eu(RULE == 0 && sizeof(IO) == 2 && LPC == 16 && SELSCAN_WAVES_PER_EU ? SELSCAN_WAVES_PER_EU : 1)))
     scan_fwd_kernel(const ScanArgs a) {
   constexpr int CPW = 64 / LPC;  // channels per wave
   constexpr int CPB = CPW * W;   // channels per workgroup
@@ -2281,7 +2282,10 @@ int launch_fwd_vec(const ScanArgs& a, int64_t batch, int rule, bool gate, hipStr
   const int64_t channels = batch * a.dim;
   if (channels >= 4 * 4096) return launch_fwd_cfg<IO, 16, K, W, NT, VEC>(a, batch, rule, gate, s);
   if (channels >= 2 * 4096) return launch_fwd_cfg<IO, 32, K, W, NT / 2, VEC>(a, batch, rule, gate, s);
-  return launch_fwd_cfg<IO, 64, K, W, NT / 4, VEC>(a, batch, rule, gate, s);
+  // 64 lanes per channel: eight waves per workgroup and 8-state tiles, so each
+  // staged B/C tile serves 8 channels (at most 2048 waves in such a launch:
+  // the grid, not the workgroup size, sets the occupancy)
+  return launch_fwd_cfg<IO, 64, K, 2 * W, NT / 2, VEC>(a, batch, rule, gate, s);
 }
 
 template <typename IO>
