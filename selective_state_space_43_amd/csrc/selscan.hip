@@ -342,6 +342,9 @@ struct ScanArgs {
 // models", section "Discretization").
 constexpr int kRuleDeltaB = 0, kRuleZoh = 1, kRuleEuler = 2, kRuleBilinear = 3;
 
+// LDS of one CU on gfx950 (the most one workgroup can hold).
+constexpr size_t kLdsBytes = 160 * 1024;
+
 // Steps between the states that the checkpoint pass keeps for the backward.
 constexpr int kCkptT = 128;
 
@@ -2265,6 +2268,11 @@ int launch_fwd_cfg(const ScanArgs& a, int64_t batch, int rule, bool gate, hipStr
   constexpr int CPB = (64 / LPC) * W;
   const dim3 grid((unsigned)((a.dim + CPB - 1) / CPB), (unsigned)batch);
   const size_t shmem = 2 * (size_t)CPB * (size_t)a.dstate * sizeof(float);
+  // the B/C tiles (static) and the carry and A rows (dynamic) must fit one CU's LDS
+  constexpr size_t kTiles = 2 * (size_t)NT * LPC * (K + 4) * sizeof(float);
+  if (kTiles + shmem > kLdsBytes)
+    return fail(SSM_E_UNSUPPORTED, "dstate = %lld needs %zu bytes of LDS", (long long)a.dstate,
+                kTiles + shmem);
   with_rule(rule, [&](auto rt) {
     constexpr int R = decltype(rt)::value;
     if (gate) hipLaunchKernelGGL((scan_fwd_kernel<IO, LPC, K, W, NT, VEC, R, true>), grid, dim3(64 * W), shmem, s, a);
