@@ -49,6 +49,8 @@ CASES = [  # batch, L, nheads, ngroups, dstate, gate, softplus, h0
     (2, 517, 8, 4, 128, True, False, False),
     (1, 7, 2, 1, 128, True, True, True),
     (3, 4096, 2, 1, 128, True, True, False),
+    (1, 2048, 2, 1, 256, True, True, True),    # N 256 over 32 chunks
+    (2, 3001, 4, 2, 64, False, True, True),    # ragged, unaligned rows, two groups
 ]
 
 
