@@ -587,7 +587,8 @@ __global__ void __launch_bounds__(64 * W)
 //     for a run of channel groups: it recomputes the chunk's states from the
 //     checkpoint, runs the adjoint from the stored carry and accumulates the
 //     gradients; dB and dC, which sum over the channels of a sequence, are
-//     reduced in LDS before one global atomic add per value.
+//     summed in registers over the channels a workgroup visits before one
+//     global atomic add per value.
 
 struct BwdArgs {
   const void* u;
@@ -763,7 +764,10 @@ struct Pair<uint16_t> {
 };
 
 template <typename IO, int K, bool VEC, bool ZOH, bool GATE>
-__global__ void __launch_bounds__(256) scan_bwd_main_kernel(const BwdArgs a) {
+// two waves per SIMD: the register file holds two of these waves only if
+// every instantiation stays within 256 registers (AGPRs included)
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+scan_bwd_main_kernel(const BwdArgs a) {
   static_assert(K == 8, "the channel reduction of dB and dC handles eight steps per lane");
   constexpr int LPC = 16, T = LPC * K, KP = K + 4, V = Io<IO>::V, TV = T / V;
   constexpr int NT = 16, NTH = 256, ITEMS = (2 * NT * TV + NTH - 1) / NTH;
@@ -808,13 +812,14 @@ __global__ void __launch_bounds__(256) scan_bwd_main_kernel(const BwdArgs a) {
     }
   }
 
-  // dB and dC of this chunk for states wave + 4j and steps seg K + red_row
-  // (lo) and seg K + 4 + red_row (hi), summed over every channel visited
-  float acc[4][4];
+  // dB and dC of this chunk for states wave + 4j and the lane's K steps,
+  // summed over every channel of the lane's row the workgroup visits; the sum
+  // over the wave's four rows is taken once, at the end
+  float accB[4][K], accC[4][K];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) acc[j][q] = 0.0f;
+    for (int q = 0; q < K; ++q) accB[j][q] = accC[j][q] = 0.0f;
 
   const int64_t ngroups = (a.dim + CPG - 1) / CPG;
   const int64_t g_begin = (int64_t)blockIdx.x * a.groups_per_block;
@@ -822,7 +827,7 @@ __global__ void __launch_bounds__(256) scan_bwd_main_kernel(const BwdArgs a) {
   float* par = sPar + wave * 3 * CPG * NT;
   // loads of group g + 1 are issued while group g computes
   Pair<IO> nu, nd, ndy, nz;
-  float npar[3];
+  float npar[3], nbias = 0.0f, nDd = 0.0f;
   auto fetch = [&](int64_t g) {
     const int64_t d = g * CPG + row;
     const bool okd = d < a.dim;
@@ -858,6 +863,50 @@ __global__ void __launch_bounds__(256) scan_bwd_main_kernel(const BwdArgs a) {
     npar[0] = own ? a.A[(okd ? d : 0) * N + seg] : 0.0f;
     npar[1] = own ? a.ckpt[cb] : 0.0f;
     npar[2] = own ? a.carry[cb] : 0.0f;
+    nbias = (a.delta_bias && okd) ? a.delta_bias[d] : 0.0f;
+    nDd = (a.Dskip && okd) ? a.Dskip[d] : 0.0f;
+  };
+  // Outputs of group g are written at the top of group g + 1, next to the
+  // loads of group g + 2: a wait for those loads then finds the writes long
+  // done instead of stalling on writes just issued.
+  float p_du[2] = {0.0f, 0.0f}, p_dr[2] = {0.0f, 0.0f}, p_dz[2] = {0.0f, 0.0f};
+  float p_dA[4] = {0.0f, 0.0f, 0.0f, 0.0f}, p_db = 0.0f, p_dD = 0.0f;
+  int64_t p_d = -1;  // channel of the pending outputs (-1: none)
+  auto flush = [&]() {
+    if (p_d < 0 || p_d >= a.dim) return;
+    const int64_t pch = b * a.dim + p_d;
+    const int64_t base = pch * L + ts;
+    if (VEC && ok1) {
+      if constexpr (std::is_same<IO, float>::value) {
+        *reinterpret_cast<float2*>(static_cast<float*>(a.du) + base) = make_float2(p_du[0], p_du[1]);
+        *reinterpret_cast<float2*>(static_cast<float*>(a.ddelta) + base) = make_float2(p_dr[0], p_dr[1]);
+        if constexpr (GATE)
+          *reinterpret_cast<float2*>(static_cast<float*>(a.dz) + base) = make_float2(p_dz[0], p_dz[1]);
+      } else {
+        *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.du) + base) = pack_bf16x2(p_du[0], p_du[1]);
+        *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.ddelta) + base) = pack_bf16x2(p_dr[0], p_dr[1]);
+        if constexpr (GATE)
+          *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.dz) + base) = pack_bf16x2(p_dz[0], p_dz[1]);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        if (k ? ok1 : ok0) {
+          Io<IO>::st1(a.du, base + k, p_du[k]);
+          Io<IO>::st1(a.ddelta, base + k, p_dr[k]);
+          if constexpr (GATE) Io<IO>::st1(a.dz, base + k, p_dz[k]);
+        }
+      }
+    }
+    if (last) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int n = wave + NW * j;
+        if (n < N) unsafeAtomicAdd(&a.dA[p_d * N + n], p_dA[j]);
+      }
+      if (a.ddelta_bias) unsafeAtomicAdd(&a.ddelta_bias[p_d], p_db);
+      if (a.dD) unsafeAtomicAdd(&a.dD[p_d], p_dD);
+    }
   };
   if (g_begin < g_end) fetch(g_begin);
   for (int64_t g = g_begin; g < g_end; ++g) {
@@ -865,13 +914,14 @@ __global__ void __launch_bounds__(256) scan_bwd_main_kernel(const BwdArgs a) {
     const bool dvalid = d < a.dim;
     const int64_t ch = b * a.dim + (dvalid ? d : 0);
     const Pair<IO> pu = nu, pd = nd, pdy = ndy, pz = nz;
+    const float bias = nbias, Dd = nDd;
     if (seg < N) {
       par[row * N + seg] = npar[0];
       par[(CPG + row) * N + seg] = npar[1];
       par[(2 * CPG + row) * N + seg] = npar[2];
     }
     if (g + 1 < g_end) fetch(g + 1);
-    const float bias = (a.delta_bias && dvalid) ? a.delta_bias[d] : 0.0f;
+    flush();
     // ---- per-step inputs of this wave's two steps, shared through LDS
     float xs[2], us[2], gs[2], zs[2], dycs[2];
     {
@@ -967,7 +1017,7 @@ __global__ void __launch_bounds__(256) scan_bwd_main_kernel(const BwdArgs a) {
         row_scan16_rev(Al, H2);
         const float Hn = dpp0<kRowShl1>(H2);
         float mu = last ? mu_end : Hn;
-        float dAacc = 0.0f, gB[K], gC[K];
+        float dAacc = 0.0f;
 #pragma unroll
         for (int i = K - 1; i >= 0; --i) {
           const float lam = fmaf(dyc[i], cq[i], mu);  // lambda_t
@@ -981,24 +1031,17 @@ __global__ void __launch_bounds__(256) scan_bwd_main_kernel(const BwdArgs a) {
             ddt[i] = fmaf(dbeta, av[i], ddt[i]);
             const float dcf = An != 0.0f ? (dt[i] * av[i] - cf[i]) * rcp(An) : 0.5f * dt[i] * dt[i];
             dAacc = fmaf(dbeta, dcf, dAacc);
-            gB[i] = lam * cf[i] * uu[i];
+            accB[j][i] = fmaf(lam, cf[i] * uu[i], accB[j][i]);
             du[i] = fmaf(lbn, cf[i], du[i]);
           } else {
             lb[i] = fmaf(lam, bq[i], lb[i]);
-            gB[i] = lam * w[i];
+            accB[j][i] = fmaf(lam, w[i], accB[j][i]);
           }
-          gC[i] = dyc[i] * hh[i + 1];
+          accC[j][i] = fmaf(dyc[i], hh[i + 1], accC[j][i]);
           mu = mun;
         }
-        float lo, hi;
-        rows_sum8(gB, lo, hi);
-        acc[j][0] += lo;
-        acc[j][1] += hi;
-        rows_sum8(gC, lo, hi);
-        acc[j][2] += lo;
-        acc[j][3] += hi;
         dAacc = row_sum16(dAacc);
-        if (last && dvalid) unsafeAtomicAdd(&a.dA[d * N + n], dAacc);
+        p_dA[j] = dAacc;
         if (ci == 0 && first && dvalid && a.dh0) a.dh0[ch * N + n] = mu;
       }
     }
@@ -1036,56 +1079,27 @@ __global__ void __launch_bounds__(256) scan_bwd_main_kernel(const BwdArgs a) {
           syc.x += p2.x; syc.y += p2.y;
         }
       }
-      const float Dd = (a.Dskip && dvalid) ? a.Dskip[d] : 0.0f;
-      float o_du[2], o_dr[2], o_dz[2];
       float dbacc = 0.0f, dDacc = 0.0f;
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         const bool okk = k ? ok1 : ok0;
         const float s_ddt = k ? sddt.y : sddt.x, s_du = k ? sdu.y : sdu.x, s_yc = k ? syc.y : syc.x;
         const float sig = a.softplus ? rcp(1.0f + ex2(-xs[k] * kLog2e)) : 1.0f;
-        o_dr[k] = okk ? s_ddt * sig : 0.0f;
-        dbacc += o_dr[k];
+        p_dr[k] = okk ? s_ddt * sig : 0.0f;
+        dbacc += p_dr[k];
         dDacc += okk ? dycs[k] * us[k] : 0.0f;
-        o_du[k] = fmaf(dycs[k], Dd, s_du);
+        p_du[k] = fmaf(dycs[k], Dd, s_du);
         if constexpr (GATE) {
           const float sz = rcp(1.0f + ex2(-zs[k] * kLog2e));
-          o_dz[k] = gs[k] * fmaf(Dd, us[k], s_yc) * sz * fmaf(zs[k], 1.0f - sz, 1.0f);
+          p_dz[k] = gs[k] * fmaf(Dd, us[k], s_yc) * sz * fmaf(zs[k], 1.0f - sz, 1.0f);
         }
       }
-      if (dvalid) {
-        const int64_t base = ch * L + ts;
-        if (VEC && ok1) {
-          if constexpr (std::is_same<IO, float>::value) {
-            *reinterpret_cast<float2*>(static_cast<float*>(a.du) + base) = make_float2(o_du[0], o_du[1]);
-            *reinterpret_cast<float2*>(static_cast<float*>(a.ddelta) + base) = make_float2(o_dr[0], o_dr[1]);
-            if constexpr (GATE)
-              *reinterpret_cast<float2*>(static_cast<float*>(a.dz) + base) = make_float2(o_dz[0], o_dz[1]);
-          } else {
-            *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.du) + base) = pack_bf16x2(o_du[0], o_du[1]);
-            *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.ddelta) + base) = pack_bf16x2(o_dr[0], o_dr[1]);
-            if constexpr (GATE)
-              *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.dz) + base) = pack_bf16x2(o_dz[0], o_dz[1]);
-          }
-        } else {
-#pragma unroll
-          for (int k = 0; k < 2; ++k) {
-            if (k ? ok1 : ok0) {
-              Io<IO>::st1(a.du, base + k, o_du[k]);
-              Io<IO>::st1(a.ddelta, base + k, o_dr[k]);
-              if constexpr (GATE) Io<IO>::st1(a.dz, base + k, o_dz[k]);
-            }
-          }
-        }
-      }
-      dbacc = row_sum16(dbacc);
-      dDacc = row_sum16(dDacc);
-      if (last && dvalid) {
-        if (a.ddelta_bias) unsafeAtomicAdd(&a.ddelta_bias[d], dbacc);
-        if (a.dD) unsafeAtomicAdd(&a.dD[d], dDacc);
-      }
+      p_db = row_sum16(dbacc);
+      p_dD = row_sum16(dDacc);
+      p_d = d;
     }
   }
+  flush();
   // ---- this chunk's dB and dC from every channel the block visited
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -1094,13 +1108,16 @@ __global__ void __launch_bounds__(256) scan_bwd_main_kernel(const BwdArgs a) {
     if (n < N) {
       float* pBn = a.accB + (b * N + n) * L;
       float* pCn = a.accC + (b * N + n) * L;
+      float bl, bh, cl, chh;
+      rows_sum8(accB[j], bl, bh);
+      rows_sum8(accC[j], cl, chh);
       if (t < L) {
-        unsafeAtomicAdd(pBn + t, acc[j][0]);
-        unsafeAtomicAdd(pCn + t, acc[j][2]);
+        unsafeAtomicAdd(pBn + t, bl);
+        unsafeAtomicAdd(pCn + t, cl);
       }
       if (t + 4 < L) {
-        unsafeAtomicAdd(pBn + t + 4, acc[j][1]);
-        unsafeAtomicAdd(pCn + t + 4, acc[j][3]);
+        unsafeAtomicAdd(pBn + t + 4, bh);
+        unsafeAtomicAdd(pCn + t + 4, chh);
       }
     }
   }
