@@ -1609,6 +1609,12 @@ __device__ __forceinline__ void buf_st64(uint2 v, Rsrc r, uint32_t voff, uint32_
 __device__ __forceinline__ void buf_st16(uint32_t v, Rsrc r, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v, r, voff, soff, 0);
 }
+__device__ __forceinline__ uint32_t buf_ld32(Rsrc r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+__device__ __forceinline__ void buf_st32(uint32_t v, Rsrc r, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, voff, soff, 0);
+}
 
 // 8 (4) bf16 of a row at byte offset voff + soff: one 16-byte (8-byte) load
 // when rows are 16-byte aligned, else 2-byte loads
@@ -2148,71 +2154,203 @@ __global__ void __launch_bounds__(256) lti_conv_kernel(const float* K, const voi
 // applied with an FFT in O(L log L)).  One workgroup per channel: K is
 // zero-padded to M >= 2L - 1 points (a power of two, so that the circular
 // convolution of length M equals the causal one for t < L) and transformed
-// once; every sequence of the channel is then transformed, multiplied by it
-// and transformed back.  Radix-2 decimation in time in LDS with the input in
-// bit-reversed order; twiddles exp(-2 pi i j / M) from sincospif; the
-// inverse is the forward transform of the conjugate.
+// once; the channel's sequences are then taken two at a time as the real and
+// imaginary parts of one complex signal (the product with the transform of a
+// real kernel is linear, so the inverse returns the two convolutions as the
+// real and imaginary parts), transformed, multiplied and transformed back.
+//
+// Each transform is Stockham's self-sorting formulation: passes of radix 16
+// (and one of radix 2, 4 or 8 when log2 M is not a multiple of 4), natural
+// order in and out.  A pass over sub-transforms of length Ns reads, for
+// butterfly j, the R points j + q M/R, turns them by exp(-2 pi i q k / (Ns R))
+// with k = j mod Ns, takes their R-point DFT in registers and writes point q
+// to (j - k) R + k + q Ns.  Passes ping-pong between two LDS buffers (one
+// barrier each), padded by one point per 16 so that the strided writes of the
+// first passes spread over the banks.  The first pass of a forward transform
+// reads HBM directly, the last pass of the kernel's transform keeps its
+// points in registers (every later transform's last pass produces the same
+// points in the same lanes), and the inverse (the forward transform of the
+// conjugate, conjugated) writes y from its last pass.
 constexpr int kFftMinLog2 = 8, kFftMaxLog2 = 13;  // M from 256 to 8192 points
 
-template <typename IO, int LOG2M>
-__global__ void __launch_bounds__(256) lti_conv_fft_kernel(const float* K, const void* u,
-                                                           const float* Dskip, void* y,
-                                                           int64_t batch, int64_t dim, int64_t L) {
-  constexpr int M = 1 << LOG2M, R = M / 256;
-  __shared__ float2 sK[M], sX[M], sTw[M / 2];
-  const int64_t d = blockIdx.x;
-  const int tid = threadIdx.x;
-  for (int j = tid; j < M / 2; j += 256) {
-    float sn, cs;
-    sincospif(-2.0f * (float)j / (float)M, &sn, &cs);
-    sTw[j] = make_float2(cs, sn);
-  }
-  auto rev = [](int i) { return (int)(__brev((unsigned)i) >> (32 - LOG2M)); };
-  // in-place transform of X (bit-reversed in, natural order out); the
-  // barriers also order the caller's writes before and its reads after
-  auto fft = [&](float2* X) {
-#pragma unroll 1
-    for (int st = 0; st < LOG2M; ++st) {
-      __syncthreads();
-      const int half = 1 << st;
+__device__ __forceinline__ float2 cmul(float2 a, float2 b) {
+  return make_float2(fmaf(a.x, b.x, -a.y * b.y), fmaf(a.x, b.y, a.y * b.x));
+}
+
+// cos(pi m / 8) and sin(pi m / 8), m = 0 .. 7
+__device__ __forceinline__ constexpr float cos_pi8(int m) {
+  return m == 0 ? 1.0f : m == 1 ? 0.92387953f : m == 2 ? 0.70710678f : m == 3 ? 0.38268343f
+       : m == 4 ? 0.0f : m == 5 ? -0.38268343f : m == 6 ? -0.70710678f : -0.92387953f;
+}
+__device__ __forceinline__ constexpr float sin_pi8(int m) {
+  return m == 0 ? 0.0f : m == 1 ? 0.38268343f : m == 2 ? 0.70710678f : m == 3 ? 0.92387953f
+       : m == 4 ? 1.0f : m == 5 ? 0.92387953f : m == 6 ? 0.70710678f : 0.38268343f;
+}
+
+// R-point DFT (R = 2, 4, 8, 16) of values in registers, natural order in and
+// out: radix-2 decimation in time over the bit-reversed input; the twiddle of
+// a butterfly of span 2s at offset j is exp(-i pi j / s) = exp(-i pi m / 8)
+// with m = 8 j / s, a compile-time constant (m = 0 and m = 4, i.e. 1 and -i,
+// need no multiply).
+template <int R>
+__device__ __forceinline__ void dft_reg(float2 (&v)[R]) {
+  constexpr int LG = R == 2 ? 1 : R == 4 ? 2 : R == 8 ? 3 : 4;
+  static_assert((1 << LG) == R, "radix 2, 4, 8 or 16");
+  float2 a[R];
 #pragma unroll
-      for (int r = 0; r < (R + 1) / 2; ++r) {
-        const int j = tid + 256 * r;  // butterfly
-        if (j >= M / 2) break;
-        const int pos = j & (half - 1), i0 = ((j >> st) << (st + 1)) + pos, i1 = i0 + half;
-        const float2 w = sTw[pos << (LOG2M - 1 - st)];
-        const float2 a = X[i0], bb = X[i1];
-        const float2 t = make_float2(w.x * bb.x - w.y * bb.y, w.x * bb.y + w.y * bb.x);
-        X[i0] = make_float2(a.x + t.x, a.y + t.y);
-        X[i1] = make_float2(a.x - t.x, a.y - t.y);
+  for (int i = 0; i < R; ++i) {
+    int r = 0;
+#pragma unroll
+    for (int bit = 0; bit < LG; ++bit) r |= ((i >> bit) & 1) << (LG - 1 - bit);
+    a[r] = v[i];
+  }
+#pragma unroll
+  for (int s = 1; s < R; s <<= 1) {
+#pragma unroll
+    for (int k = 0; k < R; k += 2 * s) {
+#pragma unroll
+      for (int j = 0; j < s; ++j) {
+        const int m = j * (8 / s);
+        const float2 b = a[k + j + s];
+        float2 t;
+        if (m == 0) {
+          t = b;
+        } else if (m == 4) {
+          t = make_float2(b.y, -b.x);
+        } else {
+          const float c = cos_pi8(m), sn = sin_pi8(m);  // (c - i sn) b
+          t = make_float2(fmaf(c, b.x, sn * b.y), fmaf(c, b.y, -sn * b.x));
+        }
+        const float2 x = a[k + j];
+        a[k + j] = make_float2(x.x + t.x, x.y + t.y);
+        a[k + j + s] = make_float2(x.x - t.x, x.y - t.y);
       }
     }
+  }
+#pragma unroll
+  for (int i = 0; i < R; ++i) v[i] = a[i];
+}
+
+// One Stockham pass of radix R over M points: ld(i) gives point i of the
+// input, st(i, value, it, q) takes point i of the output, where it and q name
+// the register slot (the thread's it-th butterfly, its q-th point).
+template <int R, int M, typename Ld, typename St>
+__device__ __forceinline__ void fft_pass(int Ns, Ld ld, St st) {
+  constexpr int NBF = M / R, IT = (NBF + 255) / 256;
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int j = (int)threadIdx.x + 256 * it;
+    if (NBF % 256 == 0 || j < NBF) {
+      const int k = j & (Ns - 1);
+      float2 v[R];
+#pragma unroll
+      for (int q = 0; q < R; ++q) v[q] = ld(j + q * NBF);
+      if (Ns > 1) {
+        float sn, cs;
+        sincospif(-2.0f * (float)k / (float)(Ns * R), &sn, &cs);
+        const float2 w = make_float2(cs, sn);
+        float2 wq = w;
+#pragma unroll
+        for (int q = 1; q < R; ++q) {
+          v[q] = cmul(v[q], wq);
+          if (q + 1 < R) wq = cmul(wq, w);
+        }
+      }
+      dft_reg<R>(v);
+      const int base = (j - k) * R + k;
+#pragma unroll
+      for (int q = 0; q < R; ++q) st(base + q * Ns, v[q], it, q);
+    }
+  }
+}
+
+// LDS (2 x 1.0625 M points of 8 bytes) lets two workgroups share a CU up to
+// M = 4096; the register budget is held to match
+template <typename IO, int LOG2M>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LOG2M <= 12 ? 2 : 1)))
+lti_conv_fft_kernel(const float* K, const void* u,
+                                                           const float* Dskip, void* y,
+                                                           int64_t batch, int64_t dim, int64_t L) {
+  constexpr int M = 1 << LOG2M, P16 = LOG2M / 4, REM = LOG2M % 4;
+  constexpr int NP = P16 + (REM ? 1 : 0);   // passes: radix 16, then radix RL
+  constexpr int RL = REM ? (1 << REM) : 16;  // radix of the last pass
+  constexpr int MP = M + M / 16;             // one pad point per 16
+  constexpr int ITL = (M / RL + 255) / 256;  // butterflies per thread in the last pass
+  static_assert(NP >= 2, "the first pass is never the last");
+  __shared__ float2 sbuf[2][MP];
+  const int64_t d = blockIdx.x;
+  auto P = [](int i) { return i + (i >> 4); };
+  // whole transform: first(i) gives the input, last(i, v, it, q, buf) takes
+  // the output (buf: the LDS buffer the last pass does not read); passes
+  // write w0 first, then alternate
+  auto transform = [&](auto first, auto last, float2* w0, float2* w1) {
+    int Ns = 1;
+    fft_pass<16, M>(Ns, first, [&](int i, float2 v, int, int) { w0[P(i)] = v; });
+    Ns *= 16;
     __syncthreads();
+    float2* src = w0;
+    float2* dst = w1;
+#pragma unroll 1
+    for (int p = 1; p < NP - 1; ++p) {
+      fft_pass<16, M>(Ns, [&](int i) { return src[P(i)]; },
+                      [&](int i, float2 v, int, int) { dst[P(i)] = v; });
+      Ns *= 16;
+      __syncthreads();
+      float2* t = src;
+      src = dst;
+      dst = t;
+    }
+    fft_pass<RL, M>(Ns, [&](int i) { return src[P(i)]; },
+                    [&](int i, float2 v, int it, int q) { last(i, v, it, q, dst); });
+    return dst;
   };
-  const float* Kd = K + d * L;
-  for (int i = tid; i < M; i += 256) sK[rev(i)] = make_float2(i < L ? Kd[i] : 0.0f, 0.0f);
-  fft(sK);
+
+  // HBM rows through buffer resources of extent L: points past L read as
+  // zero (the padding) and are not written
+  constexpr uint32_t ES = sizeof(IO);
+  auto ldv = [](Rsrc r, int i) -> float {
+    if constexpr (ES == 2) return __uint_as_float(buf_ld16(r, (uint32_t)i * 2u, 0) << 16);
+    else return __uint_as_float(buf_ld32(r, (uint32_t)i * 4u, 0));
+  };
+  auto stv = [](Rsrc r, int i, float v) {
+    if constexpr (ES == 2) buf_st16(__builtin_bit_cast(uint16_t, (__bf16)v), r, (uint32_t)i * 2u, 0);
+    else buf_st32(__float_as_uint(v), r, (uint32_t)i * 4u, 0);
+  };
+  // the kernel's transform, kept where each lane's last pass puts it
+  float2 kh[ITL][RL];
+  const Rsrc rK = make_rsrc(K + d * L, L * 4);
+  transform([&](int i) { return make_float2(__uint_as_float(buf_ld32(rK, (uint32_t)i * 4u, 0)), 0.0f); },
+            [&](int, float2 v, int it, int q, float2*) { kh[it][q] = v; }, sbuf[0], sbuf[1]);
   const float Dd = Dskip ? Dskip[d] : 0.0f;
   const float scale = 1.0f / (float)M;
 #pragma unroll 1
-  for (int64_t b = 0; b < batch; ++b) {
-    const int64_t row = (b * dim + d) * L;
-    for (int i = tid; i < M; i += 256) sX[rev(i)] = make_float2(i < L ? Io<IO>::ld1(u, row + i) : 0.0f, 0.0f);
-    fft(sX);
-    // conj(K^ X^), written back in bit-reversed order for the inverse
-    float2 pr[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const float2 kk = sK[tid + 256 * r], xx = sX[tid + 256 * r];
-      pr[r] = make_float2(kk.x * xx.x - kk.y * xx.y, -(kk.x * xx.y + kk.y * xx.x));
-    }
+  for (int64_t b = 0; b < batch; b += 2) {
+    const bool two = b + 1 < batch;
+    // sequence b + 1 absent: an empty extent reads zeros and drops the writes
+    const int64_t row0 = (b * dim + d) * L, row1 = two ? ((b + 1) * dim + d) * L : row0;
+    const Rsrc rU0 = make_rsrc(static_cast<const char*>(u) + row0 * ES, L * ES);
+    const Rsrc rU1 = make_rsrc(static_cast<const char*>(u) + row1 * ES, two ? L * ES : 0);
+    const Rsrc rY0 = make_rsrc(static_cast<char*>(y) + row0 * ES, L * ES);
+    const Rsrc rY1 = make_rsrc(static_cast<char*>(y) + row1 * ES, two ? L * ES : 0);
+    __syncthreads();  // the previous pair's last pass has read its buffer
+    // forward transform of u_b + i u_{b+1}; its last pass multiplies by the
+    // kernel's transform and conjugates, into the buffer it does not read
+    float2* X = transform(
+        [&](int i) { return make_float2(ldv(rU0, i), ldv(rU1, i)); },
+        [&](int i, float2 v, int it, int q, float2* buf) {
+          const float2 z = cmul(v, kh[it][q]);
+          buf[P(i)] = make_float2(z.x, -z.y);
+        },
+        sbuf[0], sbuf[1]);
     __syncthreads();
-#pragma unroll
-    for (int r = 0; r < R; ++r) sX[rev(tid + 256 * r)] = pr[r];
-    fft(sX);
-    for (int64_t t = tid; t < L; t += 256)
-      Io<IO>::st1(y, row + t, fmaf(Dd, Io<IO>::ld1(u, row + t), sX[t].x * scale));
-    __syncthreads();  // the next sequence overwrites sX
+    float2* other = X == sbuf[0] ? sbuf[1] : sbuf[0];
+    // inverse: conj of the forward transform of the conjugate, over M
+    transform([&](int i) { return X[P(i)]; },
+              [&](int i, float2 v, int, int, float2*) {
+                stv(rY0, i, fmaf(Dd, ldv(rU0, i), v.x * scale));
+                stv(rY1, i, fmaf(Dd, ldv(rU1, i), -v.y * scale));
+              },
+              other, X);
   }
 }
 
