@@ -590,6 +590,20 @@ __global__ void __launch_bounds__(64 * W)
 //     summed in registers over the channels a workgroup visits before one
 //     global atomic add per value.
 
+// K step sizes in log2 units, in place: softplus(raw + bias) / ln 2, or
+// (raw + bias) / ln 2.  One branch around the whole run, so that the K
+// softplus chains (two transcendentals each) interleave.
+template <int K>
+__device__ __forceinline__ void step_log2(float (&v)[K], float bias, int softplus) {
+  if (softplus) {
+#pragma unroll
+    for (int i = 0; i < K; ++i) v[i] = softplus_log2(v[i] + bias);
+  } else {
+#pragma unroll
+    for (int i = 0; i < K; ++i) v[i] = (v[i] + bias) * kLog2e;
+  }
+}
+
 struct BwdArgs {
   const void* u;
   const void* delta;
@@ -707,11 +721,10 @@ __global__ void __launch_bounds__(256) scan_bwd_carry_kernel(const BwdArgs a) {
       rdy.unpack(g);
       if constexpr (GATE) rz.unpack(zz);
       const float bias = (a.delta_bias && dvalid) ? a.delta_bias[d] : 0.0f;
+      step_log2<K>(raw, bias, a.softplus);
 #pragma unroll
       for (int i = 0; i < K; ++i) {
-        const float x = raw[i] + bias;
-        const float v = a.softplus ? softplus_log2(x) : x * kLog2e;
-        dl[i] = (tl + i < L) ? v : 0.0f;
+        dl[i] = (tl + i < L) ? raw[i] : 0.0f;
         dyc[i] = GATE ? g[i] * silu_f(zz[i]) : g[i];
         S += dl[i];
       }
