@@ -1683,7 +1683,16 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(const SsdArgs a) {
   // weight exp(cs_63 - cs_s) dt_s of step s in the state update
   __shared__ __align__(16) float sCs[T], sDt[T], sE[T], sW[T];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t h = blockIdx.x >> 1, pb = blockIdx.x & 1, b = blockIdx.y;
+  // Workgroups are handed to the eight XCDs round-robin in dispatch order;
+  // when they divide evenly, XCD x takes one contiguous run of (sequence,
+  // half-head) cells, so the operands a sequence's heads share (B, C, C.B^T)
+  // are fetched into as few of the per-XCD L2 caches as possible.
+  int64_t cell = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+  {
+    const int64_t total = (int64_t)gridDim.x * gridDim.y;
+    if (total % 8 == 0) cell = (cell % 8) * (total / 8) + cell / 8;
+  }
+  const int64_t h = (cell % gridDim.x) >> 1, pb = (cell % gridDim.x) & 1, b = cell / gridDim.x;
   const int64_t g = h / (a.H / a.G), L = a.L;
   const float Ah2 = a.A[h] * kLog2e;  // decays are kept in log2 units
   const float Dh = a.Dskip ? a.Dskip[h] : 0.0f;
