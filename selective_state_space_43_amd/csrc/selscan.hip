@@ -2466,7 +2466,9 @@ int launch_fwd_vec(const ScanArgs& a, int64_t batch, int rule, bool gate, hipStr
   constexpr int K = SELSCAN_K, W = SELSCAN_W, NT = SELSCAN_NT;
   const int64_t channels = batch * a.dim;
   if (channels >= 4 * 4096) return launch_fwd_cfg<IO, 16, K, W, NT, VEC>(a, batch, rule, gate, s);
-  if (channels >= 2 * 4096) return launch_fwd_cfg<IO, 32, K, W, NT / 2, VEC>(a, batch, rule, gate, s);
+  // 32 lanes per channel: eight waves (16 channels) share each staged
+  // 16-state B/C tile
+  if (channels >= 2 * 4096) return launch_fwd_cfg<IO, 32, K, 2 * W, NT, VEC>(a, batch, rule, gate, s);
   // 64 lanes per channel: eight waves per workgroup and 8-state tiles, so each
   // staged B/C tile serves 8 channels (at most 2048 waves in such a launch:
   // the grid, not the workgroup size, sets the occupancy)
