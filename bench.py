@@ -443,7 +443,7 @@ def cpu_baseline(w, x, seconds_target=12.0):
     return {"value": float("%.4g" % (el / dt)), "unit": "elements/s", "cores": n_thr,
             "kind": "oracle", "seconds": round(dt, 2),
             "sample": f"{n_ch} of {total} channels (b, d), full length {w.seqlen}, all "
-                      f"{w.dstate} states, same bf16 inputs; fp64 sequential recurrence"}
+                      f"{w.dstate} states, same {w.dtype} inputs; fp64 sequential recurrence"}
 
 
 def main(argv=None):
