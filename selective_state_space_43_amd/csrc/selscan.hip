@@ -993,13 +993,25 @@ scan_bwd_main_kernel(const BwdArgs a) {
     const float* pA = par + row * N;
     const float* pH = par + (CPG + row) * N;
     const float* pM = par + (2 * CPG + row) * N;
+    // the four states' parameters, read once ahead of the state loop (rows
+    // past N read another row's values, which no state then uses); the ZOH
+    // instantiation has no registers to spare for them and reads each in turn
+    float Av[4], Hv[4], Mv[4];
+    if constexpr (!ZOH) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        Av[j] = pA[wave + NW * j];
+        Hv[j] = pH[wave + NW * j];
+        Mv[j] = pM[wave + NW * j];
+      }
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int n = wave + NW * j;
       if (n < N) {
-        const float An = pA[n];
-        const float hs = pH[n];      // state before the chunk
-        const float mu_end = pM[n];  // Abar lambda entering from the chunk's end
+        const float An = ZOH ? pA[n] : Av[j];
+        const float hs = ZOH ? pH[n] : Hv[j];      // state before the chunk
+        const float mu_end = ZOH ? pM[n] : Mv[j];  // Abar lambda entering from the chunk's end
         const float Anl = An * kLog2e;
         const float* pb = reinterpret_cast<const float*>(sB4) + (n * LPC + seg) * KP;
         const float* pc = reinterpret_cast<const float*>(sC4) + (n * LPC + seg) * KP;
