@@ -185,9 +185,11 @@ int ssm_lti_kernel(const float* A, const float* Bv, const float* Cv, const float
  *               bytes, 16-byte aligned, owned by the caller; its contents on
  *               entry do not matter.  Calls that share a workspace must not
  *               run concurrently.
- * dstate must be 1..16 (SSM_E_UNSUPPORTED otherwise).  dA, dD, ddelta_bias,
- * dB and dC are sums accumulated in float32 with atomic adds, so they can
- * differ in the last bits from run to run.
+ * dstate must be 1..64 (SSM_E_UNSUPPORTED otherwise); above 16 the states
+ * are taken in tiles of 16, one kernel launch each, and the workspace also
+ * holds three float32 [batch, dim, seqlen] sums carried between them.  dA,
+ * dD, ddelta_bias, dB and dC are sums accumulated in float32 with atomic
+ * adds, so they can differ in the last bits from run to run.
  */
 int ssm_selective_scan_bwd(const void* u, const void* delta, const float* A, const void* Bm,
                            const void* Cm, const float* Dskip, const void* z,

@@ -616,6 +616,9 @@ __device__ __forceinline__ float expm1_f(float r, float e) {
   return fabsf(r) < 0.03125f ? p : e - 1.0f;
 }
 
+// largest state size the backward takes: states are processed in tiles of 16
+constexpr int kBwdMaxN = 64;
+
 struct BwdArgs {
   const void* u;
   const void* delta;
@@ -641,6 +644,12 @@ struct BwdArgs {
   int64_t dim, dstate, seqlen, chunks;
   int softplus;
   int groups_per_block;  // channel groups of 16 per workgroup in the main pass
+  // states n0 .. n0 + 15 in this launch of the main pass; with more than 16
+  // states the launches run in order and carry the per-step sums over states
+  // (ddelta before the softplus factor, du before D u, C . h) in psum
+  int n0;
+  int tile_mode;  // 0: the only tile, 1: first of several, 2: middle, 3: last
+  float* psum;    // [3][batch * dim * seqlen] float32 partial sums (tile_mode 1..3)
 };
 
 // sum over the 16 lanes of a row; the row's last lane holds the total
@@ -676,12 +685,12 @@ __device__ __forceinline__ void rows_sum8(const float* v, float& lo, float& hi) 
   hi = __uint_as_float(y1[0]) + __uint_as_float(y1[1]);
 }
 
-template <typename IO, int K, bool VEC, bool GATE>
+template <typename IO, int K, bool VEC, bool GATE, bool TILED>
 __global__ void __launch_bounds__(256) scan_bwd_carry_kernel(const BwdArgs a) {
   constexpr int LPC = 16, CPB = 16, T = LPC * K, KP = K + 4, V = Io<IO>::V, TV = T / V;
   constexpr int NT = 16, NTH = 256, ITEMS = (NT * TV + NTH - 1) / NTH;
-  __shared__ float4 sC4[NT * LPC * KP / 4];
-  __shared__ float sMu[CPB * NT], sA[CPB * NT];
+  __shared__ float4 sC4[NT * LPC * KP / 4];  // C rows of one 16-state tile
+  __shared__ float sMu[CPB * kBwdMaxN], sA[CPB * kBwdMaxN];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int seg = lane % LPC;
   const int chb = wave * 4 + lane / LPC;
@@ -708,24 +717,35 @@ __global__ void __launch_bounds__(256) scan_bwd_carry_kernel(const BwdArgs a) {
     __syncthreads();  // previous chunk's tile is no longer read; sMu/sA visible
     {
       const int64_t cend = ((t0 + T < L ? t0 + T : L) - 1) / kCkptT;  // last block of the chunk
-      if (dvalid && seg < N) carry_ch[cend * N + seg] = sMu[chb * N + seg];
-    }
-#pragma unroll
-    for (int k = 0; k < ITEMS; ++k) {
-      const int item = threadIdx.x + k * NTH;
-      if (item < N * TV) {
-        const int nl = item / TV, tloc = (item % TV) * V;
-        Run<IO, V> rv;
-        run_load<IO, V, VEC>(rv, a.Cm, bcrow + nl * L, t0 + tloc, L, true);
-        float v[V];
-        rv.unpack(v);
-        float* dst = reinterpret_cast<float*>(sC4) + (nl * LPC + tloc / K) * KP + tloc % K;
-#pragma unroll
-        for (int q = 0; q < V; q += 4)
-          *reinterpret_cast<float4*>(dst + q) = make_float4(v[q], v[q + 1], v[q + 2], v[q + 3]);
+      if constexpr (TILED) {
+        if (dvalid)
+          for (int64_t n = seg; n < N; n += LPC) carry_ch[cend * N + n] = sMu[chb * N + n];
+      } else {
+        if (dvalid && seg < N) carry_ch[cend * N + seg] = sMu[chb * N + seg];
       }
     }
-    __syncthreads();
+    // C rows of states n0 .. n0 + nt - 1 -> LDS
+    auto stage = [&](int64_t n0, int nt) {
+#pragma unroll
+      for (int k = 0; k < ITEMS; ++k) {
+        const int item = threadIdx.x + k * NTH;
+        if (item < nt * TV) {
+          const int nl = item / TV, tloc = (item % TV) * V;
+          Run<IO, V> rv;
+          run_load<IO, V, VEC>(rv, a.Cm, bcrow + (n0 + nl) * L, t0 + tloc, L, true);
+          float v[V];
+          rv.unpack(v);
+          float* dst = reinterpret_cast<float*>(sC4) + (nl * LPC + tloc / K) * KP + tloc % K;
+#pragma unroll
+          for (int q = 0; q < V; q += 4)
+            *reinterpret_cast<float4*>(dst + q) = make_float4(v[q], v[q + 1], v[q + 2], v[q + 3]);
+        }
+      }
+    };
+    if constexpr (!TILED) {  // one tile: staged before the per-step values are formed
+      stage(0, (int)N);
+      __syncthreads();
+    }
     float dl[K], dyc[K], S = 0.0f;
     {
       float raw[K], g[K], zz[K];
@@ -741,33 +761,42 @@ __global__ void __launch_bounds__(256) scan_bwd_carry_kernel(const BwdArgs a) {
         S += dl[i];
       }
     }
-#pragma unroll 1
-    for (int64_t n = 0; n < N; ++n) {
-      const float An = sA[chb * N + n];
-      const float mu = sMu[chb * N + n];
-      const float* pc = reinterpret_cast<const float*>(sC4) + (n * LPC + seg) * KP;
-      float av[K], gv[K];
-#pragma unroll
-      for (int i = 0; i < K; i += 4) {
-        const float4 cc = *reinterpret_cast<const float4*>(pc + i);
-        const float cq[4] = {cc.x, cc.y, cc.z, cc.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          av[i + q] = ex2(dl[i + q] * An);
-          gv[i + q] = dyc[i + q] * cq[q];
-        }
+    for (int64_t n0 = 0; n0 < N; n0 += NT) {
+      const int nt = TILED ? (int)(N - n0 < NT ? N - n0 : NT) : (int)N;
+      if constexpr (TILED) {
+        if (n0 > 0) __syncthreads();  // every wave is done with the previous tile
+        stage(n0, nt);
+        __syncthreads();
       }
-      // fold the lane's steps backwards; the row's last lane starts from the
-      // adjoint entering the chunk
-      float Lam = gv[K - 1] + (seg == LPC - 1 ? mu : 0.0f);
+#pragma unroll 1
+      for (int64_t n = n0; n < n0 + nt; ++n) {
+        const float An = sA[chb * N + n];
+        const float mu = sMu[chb * N + n];
+        const float* pc = reinterpret_cast<const float*>(sC4) + ((n - n0) * LPC + seg) * KP;
+        float av[K], gv[K];
 #pragma unroll
-      for (int i = K - 2; i >= 0; --i) Lam = fmaf(av[i + 1], Lam, gv[i]);
-      float H = av[0] * Lam;
-      row_scan16_rev(ex2(An * S), H);
-      if (seg == 0) sMu[chb * N + n] = H;  // Abar lambda at the chunk's first step
-      // lanes that start a block inside the chunk hand the block before it its carry
-      if (seg > 0 && (seg * K) % kCkptT == 0 && tl < L && dvalid)
-        carry_ch[(tl / kCkptT - 1) * N + n] = H;
+        for (int i = 0; i < K; i += 4) {
+          const float4 cc = *reinterpret_cast<const float4*>(pc + i);
+          const float cq[4] = {cc.x, cc.y, cc.z, cc.w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            av[i + q] = ex2(dl[i + q] * An);
+            gv[i + q] = dyc[i + q] * cq[q];
+          }
+        }
+        // fold the lane's steps backwards; the row's last lane starts from the
+        // adjoint entering the chunk
+        float Lam = gv[K - 1] + (seg == LPC - 1 ? mu : 0.0f);
+#pragma unroll
+        for (int i = K - 2; i >= 0; --i) Lam = fmaf(av[i + 1], Lam, gv[i]);
+        float H = av[0] * Lam;
+        row_scan16_rev(ex2(An * S), H);
+        if (seg == 0) sMu[chb * N + n] = H;  // Abar lambda at the chunk's first step
+        // lanes that start a block inside the chunk hand the block before it its carry
+        if (seg > 0 && (seg * K) % kCkptT == 0 && tl < L && dvalid)
+          carry_ch[(tl / kCkptT - 1) * N + n] = H;
+      }
+      if constexpr (!TILED) break;  // a single tile holds every state
     }
   }
 }
@@ -788,7 +817,7 @@ struct Pair<uint16_t> {
   __device__ float get(int k) const { return k ? bf_hi(v) : bf_lo(v); }
 };
 
-template <typename IO, int K, bool VEC, bool ZOH, bool GATE>
+template <typename IO, int K, bool VEC, bool ZOH, bool GATE, bool TILED>
 // two waves per SIMD: the register file holds two of these waves only if
 // every instantiation stays within 256 registers (AGPRs included)
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
@@ -815,6 +844,8 @@ scan_bwd_main_kernel(const BwdArgs a) {
   const int red_row = red_step(row);
   const int64_t b = blockIdx.z, ci = blockIdx.y;
   const int64_t N = a.dstate, L = a.seqlen;
+  const int n0 = TILED ? a.n0 : 0;  // this launch's states: n0 .. n0 + nt - 1
+  const int nt = TILED ? (int)(N - n0 < NT ? N - n0 : NT) : (int)N;
   const int64_t t0 = ci * T, tl = t0 + seg * K, bcrow = b * N * L;
   const int s0 = 2 * wave;               // this wave's two steps
   const int64_t ts = tl + s0;            // their time index
@@ -822,12 +853,12 @@ scan_bwd_main_kernel(const BwdArgs a) {
 #pragma unroll
   for (int k = 0; k < ITEMS; ++k) {
     const int item = threadIdx.x + k * NTH;
-    if (item < 2 * N * TV) {
-      const int tensor = item / (N * TV);
-      const int r = item % (N * TV);
+    if (item < 2 * nt * TV) {
+      const int tensor = item / (nt * TV);
+      const int r = item % (nt * TV);
       const int nl = r / TV, tloc = (r % TV) * V;
       Run<IO, V> rv;
-      run_load<IO, V, VEC>(rv, tensor ? a.Cm : a.Bm, bcrow + nl * L, t0 + tloc, L, true);
+      run_load<IO, V, VEC>(rv, tensor ? a.Cm : a.Bm, bcrow + (n0 + nl) * L, t0 + tloc, L, true);
       float v[V];
       rv.unpack(v);
       float* dst = reinterpret_cast<float*>(tensor ? sC4 : sB4) + (nl * LPC + tloc / K) * KP + tloc % K;
@@ -853,6 +884,7 @@ scan_bwd_main_kernel(const BwdArgs a) {
   // loads of group g + 1 are issued while group g computes
   Pair<IO> nu, nd, ndy, nz;
   float npar[3], nbias = 0.0f, nDd = 0.0f;
+  float2 nps[3] = {};  // partial sums of earlier tiles at this wave's two steps
   auto fetch = [&](int64_t g) {
     const int64_t d = g * CPG + row;
     const bool okd = d < a.dim;
@@ -883,13 +915,23 @@ scan_bwd_main_kernel(const BwdArgs a) {
         ndy.v = pack_bf16x2(e[2][0], e[2][1]); nz.v = pack_bf16x2(e[3][0], e[3][1]);
       }
     }
-    const int64_t cb = (ch * a.chunks + ci) * N + seg;
-    const bool own = okd && seg < N;
-    npar[0] = own ? a.A[(okd ? d : 0) * N + seg] : 0.0f;
+    const int64_t cb = (ch * a.chunks + ci) * N + n0 + seg;
+    const bool own = okd && seg < nt;
+    npar[0] = own ? a.A[(okd ? d : 0) * N + n0 + seg] : 0.0f;
     npar[1] = own ? a.ckpt[cb] : 0.0f;
     npar[2] = own ? a.carry[cb] : 0.0f;
     nbias = (a.delta_bias && okd) ? a.delta_bias[d] : 0.0f;
     nDd = (a.Dskip && okd) ? a.Dskip[d] : 0.0f;
+    if constexpr (TILED) {
+      if (a.tile_mode >= 2) {
+        const int64_t bdl = a.dim * L * (int64_t)gridDim.z;  // batch * dim * seqlen
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+          nps[q].x = (okd && ok0) ? a.psum[q * bdl + base] : 0.0f;
+          nps[q].y = (okd && ok1) ? a.psum[q * bdl + base + 1] : 0.0f;
+        }
+      }
+    }
   };
   // Outputs of group g are written at the top of group g + 1, next to the
   // loads of group g + 2: a wait for those loads then finds the writes long
@@ -897,11 +939,23 @@ scan_bwd_main_kernel(const BwdArgs a) {
   float p_du[2] = {0.0f, 0.0f}, p_dr[2] = {0.0f, 0.0f}, p_dz[2] = {0.0f, 0.0f};
   float p_dA[4] = {0.0f, 0.0f, 0.0f, 0.0f}, p_db = 0.0f, p_dD = 0.0f;
   int64_t p_d = -1;  // channel of the pending outputs (-1: none)
+  // partial tiles (tile_mode 1, 2) leave their per-step sums in psum instead
+  const bool partial = TILED && (a.tile_mode == 1 || a.tile_mode == 2);
   auto flush = [&]() {
     if (p_d < 0 || p_d >= a.dim) return;
     const int64_t pch = b * a.dim + p_d;
     const int64_t base = pch * L + ts;
-    if (VEC && ok1) {
+    if (partial) {
+      const int64_t bdl = a.dim * L * (int64_t)gridDim.z;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        if (k ? ok1 : ok0) {
+          a.psum[base + k] = p_dr[k];
+          a.psum[bdl + base + k] = p_du[k];
+          a.psum[2 * bdl + base + k] = p_dz[k];
+        }
+      }
+    } else if (VEC && ok1) {
       if constexpr (std::is_same<IO, float>::value) {
         *reinterpret_cast<float2*>(static_cast<float*>(a.du) + base) = make_float2(p_du[0], p_du[1]);
         *reinterpret_cast<float2*>(static_cast<float*>(a.ddelta) + base) = make_float2(p_dr[0], p_dr[1]);
@@ -927,10 +981,12 @@ scan_bwd_main_kernel(const BwdArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int n = wave + NW * j;
-        if (n < N) unsafeAtomicAdd(&a.dA[p_d * N + n], p_dA[j]);
+        if (n < nt) unsafeAtomicAdd(&a.dA[p_d * N + n0 + n], p_dA[j]);
       }
-      if (a.ddelta_bias) unsafeAtomicAdd(&a.ddelta_bias[p_d], p_db);
-      if (a.dD) unsafeAtomicAdd(&a.dD[p_d], p_dD);
+      if (!partial) {
+        if (a.ddelta_bias) unsafeAtomicAdd(&a.ddelta_bias[p_d], p_db);
+        if (a.dD) unsafeAtomicAdd(&a.dD[p_d], p_dD);
+      }
     }
   };
   if (g_begin < g_end) fetch(g_begin);
@@ -940,11 +996,13 @@ scan_bwd_main_kernel(const BwdArgs a) {
     const int64_t ch = b * a.dim + (dvalid ? d : 0);
     const Pair<IO> pu = nu, pd = nd, pdy = ndy, pz = nz;
     const float bias = nbias, Dd = nDd;
-    if (seg < N) {
-      par[row * N + seg] = npar[0];
-      par[(CPG + row) * N + seg] = npar[1];
-      par[(2 * CPG + row) * N + seg] = npar[2];
+    float2 ps[3];
+    if constexpr (TILED) {
+      ps[0] = nps[0]; ps[1] = nps[1]; ps[2] = nps[2];
     }
+    par[row * NT + seg] = npar[0];
+    par[(CPG + row) * NT + seg] = npar[1];
+    par[(2 * CPG + row) * NT + seg] = npar[2];
     if (g + 1 < g_end) fetch(g + 1);
     flush();
     // ---- per-step inputs of this wave's two steps, shared through LDS
@@ -990,9 +1048,9 @@ scan_bwd_main_kernel(const BwdArgs a) {
       lb[i] = 0.0f;
     }
     S *= kLog2e;
-    const float* pA = par + row * N;
-    const float* pH = par + (CPG + row) * N;
-    const float* pM = par + (2 * CPG + row) * N;
+    const float* pA = par + row * NT;
+    const float* pH = par + (CPG + row) * NT;
+    const float* pM = par + (2 * CPG + row) * NT;
     // the four states' parameters, read once ahead of the state loop (rows
     // past N read another row's values, which no state then uses); the ZOH
     // instantiation has no registers to spare for them and reads each in turn
@@ -1008,7 +1066,7 @@ scan_bwd_main_kernel(const BwdArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int n = wave + NW * j;
-      if (n < N) {
+      if (n < nt) {
         const float An = ZOH ? pA[n] : Av[j];
         const float hs = ZOH ? pH[n] : Hv[j];      // state before the chunk
         const float mu_end = ZOH ? pM[n] : Mv[j];  // Abar lambda entering from the chunk's end
@@ -1079,7 +1137,7 @@ scan_bwd_main_kernel(const BwdArgs a) {
         }
         dAacc = row_sum16(dAacc);
         p_dA[j] = dAacc;
-        if (ci == 0 && first && dvalid && a.dh0) a.dh0[ch * N + n] = mu;
+        if (ci == 0 && first && dvalid && a.dh0) a.dh0[ch * N + n0 + n] = mu;
       }
     }
     if constexpr (!ZOH) {
@@ -1116,19 +1174,32 @@ scan_bwd_main_kernel(const BwdArgs a) {
           syc.x += p2.x; syc.y += p2.y;
         }
       }
+      if constexpr (TILED) {
+        if (a.tile_mode >= 2) {
+          sddt.x += ps[0].x; sddt.y += ps[0].y;
+          sdu.x += ps[1].x; sdu.y += ps[1].y;
+          syc.x += ps[2].x; syc.y += ps[2].y;
+        }
+      }
       float dbacc = 0.0f, dDacc = 0.0f;
+      if (partial) {
+        p_dr[0] = sddt.x; p_dr[1] = sddt.y;
+        p_du[0] = sdu.x; p_du[1] = sdu.y;
+        p_dz[0] = syc.x; p_dz[1] = syc.y;
+      } else {
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const bool okk = k ? ok1 : ok0;
-        const float s_ddt = k ? sddt.y : sddt.x, s_du = k ? sdu.y : sdu.x, s_yc = k ? syc.y : syc.x;
-        const float sig = a.softplus ? rcp(1.0f + ex2(-xs[k] * kLog2e)) : 1.0f;
-        p_dr[k] = okk ? s_ddt * sig : 0.0f;
-        dbacc += p_dr[k];
-        dDacc += okk ? dycs[k] * us[k] : 0.0f;
-        p_du[k] = fmaf(dycs[k], Dd, s_du);
-        if constexpr (GATE) {
-          const float sz = rcp(1.0f + ex2(-zs[k] * kLog2e));
-          p_dz[k] = gs[k] * fmaf(Dd, us[k], s_yc) * sz * fmaf(zs[k], 1.0f - sz, 1.0f);
+        for (int k = 0; k < 2; ++k) {
+          const bool okk = k ? ok1 : ok0;
+          const float s_ddt = k ? sddt.y : sddt.x, s_du = k ? sdu.y : sdu.x, s_yc = k ? syc.y : syc.x;
+          const float sig = a.softplus ? rcp(1.0f + ex2(-xs[k] * kLog2e)) : 1.0f;
+          p_dr[k] = okk ? s_ddt * sig : 0.0f;
+          dbacc += p_dr[k];
+          dDacc += okk ? dycs[k] * us[k] : 0.0f;
+          p_du[k] = fmaf(dycs[k], Dd, s_du);
+          if constexpr (GATE) {
+            const float sz = rcp(1.0f + ex2(-zs[k] * kLog2e));
+            p_dz[k] = gs[k] * fmaf(Dd, us[k], s_yc) * sz * fmaf(zs[k], 1.0f - sz, 1.0f);
+          }
         }
       }
       p_db = row_sum16(dbacc);
@@ -1142,9 +1213,9 @@ scan_bwd_main_kernel(const BwdArgs a) {
   for (int j = 0; j < 4; ++j) {
     const int n = wave + NW * j;
     const int64_t t = t0 + seg * K + red_row;
-    if (n < N) {
-      float* pBn = a.accB + (b * N + n) * L;
-      float* pCn = a.accC + (b * N + n) * L;
+    if (n < nt) {
+      float* pBn = a.accB + (b * N + n0 + n) * L;
+      float* pCn = a.accC + (b * N + n0 + n) * L;
       float bl, bh, cl, chh;
       rows_sum8(accB[j], bl, bh);
       rows_sum8(accC[j], cl, chh);
@@ -2508,10 +2579,10 @@ int launch_fwd(const ScanArgs& a, int64_t batch, int rule, bool gate, bool vec, 
 // Backward: the gradient pass works on chunks of T = 16 * kBwdK = kCkptT steps.
 constexpr int kBwdK = 8;
 static_assert(16 * kBwdK == kCkptT, "gradient chunks are the checkpoint blocks");
-constexpr int64_t kBwdMaxDstate = 16;
+constexpr int64_t kBwdMaxDstate = kBwdMaxN;
 
 struct BwdLayout {
-  int64_t chunks, ckpt_off, carry_off, accB_off, accC_off, bytes;
+  int64_t chunks, ckpt_off, carry_off, accB_off, accC_off, psum_off, bytes;
 };
 
 BwdLayout bwd_layout(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen) {
@@ -2525,7 +2596,10 @@ BwdLayout bwd_layout(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen)
   l.carry_off = up(states);
   l.accB_off = l.carry_off + up(states);
   l.accC_off = l.accB_off + up(acc);
-  l.bytes = l.accC_off + up(acc);
+  l.psum_off = l.accC_off + up(acc);
+  // per-step sums carried between the 16-state launches (more than 16 states)
+  const int64_t psum = dstate > 16 ? 3 * batch * dim * seqlen * 4 : 0;
+  l.bytes = l.psum_off + up(psum);
   return l;
 }
 
@@ -2539,7 +2613,10 @@ int launch_bwd_typed(const ScanArgs& fa, BwdArgs ba, int64_t batch, hipStream_t 
     hipLaunchKernelGGL((scan_fwd_kernel<IO, 16, 16, 4, 16, VEC, ZOH ? kRuleZoh : kRuleDeltaB, false, true>), grid16, dim3(256),
                        2 * 16 * (size_t)ba.dstate * sizeof(float), s, fa);
   // 2. adjoint carries at every block end (a reverse pass over 256-step chunks)
-  hipLaunchKernelGGL((scan_bwd_carry_kernel<IO, 16, VEC, GATE>), grid16, dim3(256), 0, s, ba);
+  if (ba.dstate <= 16)
+    hipLaunchKernelGGL((scan_bwd_carry_kernel<IO, 16, VEC, GATE, false>), grid16, dim3(256), 0, s, ba);
+  else
+    hipLaunchKernelGGL((scan_bwd_carry_kernel<IO, 16, VEC, GATE, true>), grid16, dim3(256), 0, s, ba);
   // 3. gradients, every (sequence, chunk) independently; groups of 4 channels
   const int64_t ngroups = (ba.dim + 3) / 4;
   const int64_t cells = ngroups * ba.chunks * batch;
@@ -2548,7 +2625,19 @@ int launch_bwd_typed(const ScanArgs& fa, BwdArgs ba, int64_t batch, hipStream_t 
   if (gpb > ngroups) gpb = ngroups;
   ba.groups_per_block = (int)gpb;
   const dim3 gridm((unsigned)((ngroups + gpb - 1) / gpb), (unsigned)ba.chunks, (unsigned)batch);
-  hipLaunchKernelGGL((scan_bwd_main_kernel<IO, K, VEC, ZOH, GATE>), gridm, dim3(256), 0, s, ba);
+  if (ba.dstate <= 16) {
+    ba.n0 = 0;
+    ba.tile_mode = 0;
+    hipLaunchKernelGGL((scan_bwd_main_kernel<IO, K, VEC, ZOH, GATE, false>), gridm, dim3(256), 0, s, ba);
+    return SSM_OK;
+  }
+  // more than 16 states: one launch per 16-state tile, in order on the
+  // stream, the per-step sums over states carried from one to the next
+  for (int64_t n0 = 0; n0 < ba.dstate; n0 += 16) {
+    ba.n0 = (int)n0;
+    ba.tile_mode = n0 == 0 ? 1 : (n0 + 16 >= ba.dstate ? 3 : 2);
+    hipLaunchKernelGGL((scan_bwd_main_kernel<IO, K, VEC, ZOH, GATE, true>), gridm, dim3(256), 0, s, ba);
+  }
   return SSM_OK;
 }
 
@@ -2953,6 +3042,7 @@ int ssm_selective_scan_bwd(const void* u, const void* delta, const float* A, con
   ba.carry = reinterpret_cast<float*>(ws + lay.carry_off);
   ba.accB = reinterpret_cast<float*>(ws + lay.accB_off);
   ba.accC = reinterpret_cast<float*>(ws + lay.accC_off);
+  ba.psum = dstate > 16 ? reinterpret_cast<float*>(ws + lay.psum_off) : nullptr;
   ba.dim = dim; ba.dstate = dstate; ba.seqlen = seqlen; ba.chunks = lay.chunks;
   ba.softplus = delta_softplus ? 1 : 0;
   const int64_t nacc = batch * dstate * seqlen;

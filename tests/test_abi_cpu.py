@@ -137,6 +137,10 @@ def test_bwd_workspace_size(lib):
     assert 0 < small < big and small % 256 == 0
     # two state checkpoints per 128-step chunk plus two float32 [batch, N, L] sums
     assert big >= 2 * (2 * 8 * 8 * 4 * 4) + 2 * (2 * 4 * 1000 * 4)
+    # more than 16 states: also three float32 [batch, dim, L] per-step sums
+    n16, n32 = f(2, 8, 16, 1000), f(2, 8, 32, 1000)
+    assert n32 >= 2 * (2 * 8 * 8 * 32 * 4) + 2 * (2 * 32 * 1000 * 4) + 3 * (2 * 8 * 1000 * 4)
+    assert n16 < 2 * (2 * 8 * 8 * 16 * 4) + 2 * (2 * 16 * 1000 * 4) + 3 * (2 * 8 * 1000 * 4)
 
 
 @pytest.mark.parametrize("over,status", [
@@ -147,7 +151,7 @@ def test_bwd_workspace_size(lib):
     (dict(du=7 * P + 2), 4), (dict(ws=12 * P + 8), 4),
     (dict(du=1 * P), 5), (dict(dA=3 * P), 5), (dict(dB=10 * P + 64, dC=10 * P + 64), 5),
     (dict(ws=6 * P), 5), (dict(dh0=9 * P), 5), (dict(ck=7 * P), 5), (dict(ck=12 * P + 256), 5),
-    (dict(N=17), 6), (dict(N=64), 6), (dict(bbar=2), 6), (dict(bbar=3), 6),
+    (dict(N=65), 6), (dict(N=100), 6), (dict(bbar=2), 6), (dict(bbar=3), 6),
 ])
 def test_bwd_validation(lib, over, status):
     assert lib.ssm_selective_scan_bwd(*bwd_args(**over)) == status

@@ -114,6 +114,12 @@ BWD_CASES = [
     (2, 48, 16, 1000, "bf16", True, True, "delta"),
     (1, 33, 16, 517, "bf16", True, True, "zoh"),
     (3, 16, 8, 260, "bf16", False, False, "delta"),
+    # more than 16 states: tiles of 16, one launch each, the last ragged
+    (2, 40, 32, 300, "f32", True, True, "delta"),
+    (1, 24, 40, 333, "f32", True, False, "zoh"),
+    (2, 20, 64, 260, "bf16", True, True, "delta"),
+    (1, 17, 48, 129, "bf16", False, True, "zoh"),
+    (1, 8, 17, 77, "f32", True, True, "delta"),
 ]
 
 
@@ -175,7 +181,7 @@ def test_bwd_workspace_reuse(ssm, dev):
 
 
 def test_bwd_rejects_large_dstate(ssm, dev):
-    w, x = wl.custom(1, 16, 32, 64, dtype="f32", seed=5600)
+    w, x = wl.custom(1, 16, 65, 64, dtype="f32", seed=5600)
     g = wl.grad_inputs(w)
     with pytest.raises(ssm.SelscanError, match="SSM_E_UNSUPPORTED"):
         run_gpu(ssm, dev, x, g, "delta", None, None)
@@ -223,6 +229,7 @@ CKPT_CASES = [
     (1, 24, 16, 333, "f32", True, False, "zoh"),
     (2, 8192, 16, 256, "bf16", True, True, "delta"),
     (1, 8192, 8, 640, "f32", False, True, "zoh"),
+    (1, 24, 48, 300, "f32", True, True, "delta"),
 ]
 
 
