@@ -549,7 +549,7 @@ def main(argv=None):
         out["decode"] = bench_decode(ssm, torch, dev, args.decode_steps, 10)
         print(f"[bench] decode: {out['decode']['us_per_step']} us/step", file=sys.stderr,
               flush=True)
-    if not args.no_backward and w.dstate <= 16:
+    if not args.no_backward and w.dstate <= 64:
         out["backward"] = bench_bwd(ssm, torch, w, x, dev, args.backward_steps, 1)
         print(f"[bench] backward: {out['backward']['ms_per_call']} ms/call", file=sys.stderr,
               flush=True)
