@@ -11,8 +11,9 @@ timed separately on the decode workload and reported under "decode", and the
 backward pass (ssm_selective_scan_bwd) on the same workload under "backward",
 the causal conv1d in front of the scan (forward and backward) under
 "conv1d", the Mamba-2 scan (scalar A per head, on MFMA) under "ssd", the
-forward scan on the long-context workload under "long_context" and the
-time-invariant path under "lti".
+forward scan on the long-context workload under "long_context", the
+forward under each discretization rule under "rules" and the time-invariant
+path under "lti".
 
 Prints one JSON line: the metric (scan elements B*D*L*N per second), the
 roofline of the scan kernel (live HIP-event timing; HBM traffic from the
@@ -150,6 +151,31 @@ def bench_scan(ssm, torch, w, x, dev, steps, warmup):
     per_launch_ms = [a.elapsed_time(b) for a, b in ev]
     total_ms = t_start.elapsed_time(t_end)
     return total_ms / steps, float(np.mean(per_launch_ms)), float(np.min(per_launch_ms)), wall
+
+
+def bench_rules(ssm, torch, w, x, dev, steps):
+    """The forward scan on the same inputs under each discretization rule
+    (delta*B, exact ZOH, Euler, bilinear): milliseconds per call."""
+    u, dl, A, B, C = (to_dev(x[k], dev) for k in ("u", "delta", "A", "B", "C"))
+    D, z, bias = to_dev(x["D"], dev), to_dev(x["z"], dev), to_dev(x["delta_bias"], dev)
+    y = torch.empty_like(u)
+    fs = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    res = {"workload": f"{w.name} forward, same inputs, per discretization rule"}
+    for rule in ("delta", "zoh", "euler", "bilinear"):
+        def step():
+            ssm.ssm_selective_scan_fwd(u, dl, A, B, C, D=D, z=z, delta_bias=bias,
+                                       delta_softplus=True, bbar=rule, y=y, final_state=fs)
+        settle(step, torch, 2)
+        a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(steps):
+            step()
+        e.record(stream)
+        torch.cuda.synchronize()
+        res[rule + "_ms"] = round(a.elapsed_time(e) / steps, 4)
+    res["steps"] = steps
+    return res
 
 
 def bench_decode(ssm, torch, dev, steps, warmup):
@@ -461,6 +487,7 @@ def main(argv=None):
     p.add_argument("--no-ssd", action="store_true")
     p.add_argument("--no-lti", action="store_true")
     p.add_argument("--no-long", action="store_true")
+    p.add_argument("--no-rules", action="store_true")
     p.add_argument("--backward-steps", type=int, default=5)
     p.add_argument("--copy-check", type=int, default=0, metavar="BYTES",
                    help="also run torch's plain copy of BYTES three times (counter calibration "
@@ -560,6 +587,10 @@ def main(argv=None):
     if not args.no_ssd:
         out["ssd"] = bench_ssd(ssm, torch, dev, 30, 2)
         print(f"[bench] ssd: {out['ssd']['ms_per_call']} ms/call", file=sys.stderr, flush=True)
+    if not args.no_rules:
+        out["rules"] = bench_rules(ssm, torch, w, x, dev, 20)
+        print(f"[bench] rules: " + ", ".join(f"{k} {v}" for k, v in out["rules"].items()
+                                              if k.endswith("_ms")), file=sys.stderr, flush=True)
     if not args.no_long:
         out["long_context"] = bench_long(ssm, torch, dev, 10, 1)
         print(f"[bench] long_context: {out['long_context']['ms_per_call']} ms/call",
