@@ -46,12 +46,12 @@
 #define SELSCAN_NT 16  // states staged per LDS tile (16 lanes per channel)
 #endif
 #ifndef SELSCAN_WAVES_PER_EU
-// occupancy the register allocator must keep for bf16 io and 16 lanes per
-// channel, every rule (0: no constraint): 3 waves per SIMD fit in 168 VGPRs
-// with a few spills; against 2 waves, delta*B runs about 1 % faster, exact
-// ZOH 11 %, bilinear 15 % and Euler 29 %.  float32 io needs more registers,
-// and the wider lane layouts are held to two waves per SIMD by their grid
-// and LDS, so they get no constraint
+// occupancy the register allocator must keep with 16 lanes per channel, for
+// every rule and io type (0: no constraint): 3 waves per SIMD fit in 168
+// VGPRs with some spills, and against 2 waves the bf16 forward runs about
+// 1 % faster for delta*B, 11 % for exact ZOH, 15 % bilinear, 29 % Euler, and
+// the float32 one 7-21 % faster (it spills more).  The wider lane layouts
+// are held to two waves per SIMD by their grid and LDS: no constraint
 #define SELSCAN_WAVES_PER_EU 3
 #endif
 
@@ -357,7 +357,7 @@ constexpr int kCkptT = 128;
 template <typename IO, int LPC, int K, int W, int NT, bool VEC, int RULE, bool GATE,
           bool CKPT = false>
 __global__ void __launch_bounds__(64 * W)
-    __attribute__((amdgpu_waves_per_eu(sizeof(IO) == 2 && LPC == 16 && SELSCAN_WAVES_PER_EU ? SELSCAN_WAVES_PER_EU : 1)))
+    __attribute__((amdgpu_waves_per_eu(LPC == 16 && SELSCAN_WAVES_PER_EU ? SELSCAN_WAVES_PER_EU : 1)))
     scan_fwd_kernel(const ScanArgs a) {
   constexpr int CPW = 64 / LPC;  // channels per wave
   constexpr int CPB = CPW * W;   // channels per workgroup
