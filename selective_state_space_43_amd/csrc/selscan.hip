@@ -1125,7 +1125,12 @@ scan_bwd_main_kernel(const BwdArgs a) {
             const float lbn = lam * bq[i];
             const float dbeta = lbn * uu[i];  // lambda B u
             ddt[i] = fmaf(dbeta, av[i], ddt[i]);
-            const float dcf = An != 0.0f ? (dt[i] * av[i] - cf[i]) * rcp(An) : 0.5f * dt[i] * dt[i];
+            // d cf / dA = (dt Abar - cf) / A, or where |dt A| < 1/32 (and that
+            // difference would cancel) its series dt^2 (1/2 + r/3 + r^2/8 + r^3/30)
+            const float r = dt[i] * An;
+            const float dcf = fabsf(r) < 0.03125f
+                                  ? dt[i] * dt[i] * fmaf(r, fmaf(r, fmaf(r, 1.0f / 30, 0.125f), 1.0f / 3), 0.5f)
+                                  : (dt[i] * av[i] - cf[i]) * rcp(An);
             dAacc = fmaf(dbeta, dcf, dAacc);
             accB[j][i] = fmaf(lam, cf[i] * uu[i], accB[j][i]);
             du[i] = fmaf(lbn, cf[i], du[i]);

@@ -130,6 +130,17 @@ def test_bwd_shapes(ssm, dev, case):
     _case(ssm, dev, w, x, bbar=bbar, label=f"{case}")
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_bwd_exact_zoh_degenerate_a(ssm, dev, dt):
+    """The exact-ZOH gradients where the coefficient and its derivative in A
+    are delicate: A = 0, |delta A| far below 1/32 and around it."""
+    w, x = wl.custom(1, 24, 16, 333, dtype=dt, seed=5900)
+    A = x["A"].copy()
+    A[:, 0], A[:, 1], A[:, 2], A[:, 3], A[:, 4] = 0.0, -1e-4, -0.3, -0.6, -1e-6
+    x["A"] = A
+    _case(ssm, dev, w, x, bbar="zoh", label=f"zoh, degenerate A, {dt}")
+
+
 def test_bwd_no_h0_no_dfinal(ssm, dev):
     w, x = wl.custom(2, 32, 16, 400, dtype="f32", seed=5200)
     _case(ssm, dev, w, x, with_h0=False, with_dfinal=False, label="no h0 / dfinal")

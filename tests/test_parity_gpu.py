@@ -155,6 +155,18 @@ def test_exact_zoh_rule(ssm, dev, dt):
     _check(ssm, dev, w, x, bbar="zoh", label=f"zoh {dt}")
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_exact_zoh_degenerate_a(ssm, dev, dt):
+    """Exact ZOH where its coefficient (exp(delta A) - 1) / A is delicate:
+    A = 0 (no decay; the coefficient is delta), |delta A| far below 1/32 (the
+    series branch) and around it (the switch to (Abar - 1) / A)."""
+    w, x = wl.custom(2, 24, 16, 600, dtype=dt, gate=True, seed=33)
+    A = x["A"].copy()
+    A[:, 0], A[:, 1], A[:, 2], A[:, 3] = 0.0, -1e-4, -0.3, -0.6
+    x["A"] = A
+    _check(ssm, dev, w, x, bbar="zoh", label=f"zoh, degenerate A, {dt}")
+
+
 # Euler and bilinear rules: the three lane layouts (64, 32 and 16 lanes per
 # channel, chosen by the channel count), ragged lengths, both dtypes.  Euler
 # is run with small steps (raw delta ~ N(-4, 0.5) through softplus) so that
