@@ -162,7 +162,7 @@ def test_exact_zoh_degenerate_a(ssm, dev, dt):
     series branch) and around it (the switch to (Abar - 1) / A)."""
     w, x = wl.custom(2, 24, 16, 600, dtype=dt, gate=True, seed=33)
     A = x["A"].copy()
-    A[:, 0], A[:, 1], A[:, 2], A[:, 3] = 0.0, -1e-4, -0.3, -0.6
+    A[:, 0], A[:, 1], A[:, 2], A[:, 3], A[:, 4] = 0.0, -1e-4, -0.3, -0.6, -1e-6
     x["A"] = A
     _check(ssm, dev, w, x, bbar="zoh", label=f"zoh, degenerate A, {dt}")
 
