@@ -29,6 +29,10 @@ Entry points carry the C names:
       -> dict of gradients
   ssm_ssd_fwd(x, dt, A, B, C, nheads, ngroups, D=None, z=None, dt_bias=None,
               dt_softplus=True, h0=None) -> (y, final_state)      (Mamba-2 scan)
+  selective_scan_fn(u, delta, A, B, C, D=None, z=None, delta_bias=None,
+                    delta_softplus=False, h0=None, bbar="delta")
+      -> (y, final_state), differentiable (torch.autograd): the forward's
+         checkpoints feed ssm_selective_scan_bwd
 
 Layouts: u, delta, z, y [batch, dim, L]; B, C [batch, dstate, L]; A
 [dim, dstate]; D, delta_bias [dim]; h0 / final_state / state
@@ -45,11 +49,11 @@ from .binding import (ssm_causal_conv1d_bwd, ssm_causal_conv1d_fwd, ssm_causal_c
                       ssm_selective_scan_bwd, ssm_ssd_fwd,
                       ssm_ssd_workspace_size,
                       ssm_selective_scan_bwd_workspace_size, ssm_selective_scan_fwd,
-                      ssm_state_update)
+                      ssm_state_update, selective_scan_fn)
 
 __all__ = [
     "ssm_selective_scan_fwd", "ssm_state_update", "ssm_lti_kernel", "ssm_lti_conv",
-    "ssm_selective_scan_bwd", "ssm_checkpoint_shape",
+    "ssm_selective_scan_bwd", "ssm_checkpoint_shape", "selective_scan_fn",
     "ssm_selective_scan_bwd_workspace_size", "ssm_causal_conv1d_fwd", "ssm_causal_conv1d_update",
     "ssm_causal_conv1d_bwd", "ssm_ssd_fwd", "ssm_ssd_workspace_size", "ssm_status_str",
     "ssm_last_error", "ssm_abi_version", "SelscanError", "library_path", "lib",

@@ -237,6 +237,42 @@ def ssm_selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=Non
     return g
 
 
+
+class _SelectiveScanFn(torch.autograd.Function):
+    """The scan as an autograd function: the forward writes the checkpoints
+    that the backward then takes instead of recomputing them."""
+
+    @staticmethod
+    def forward(ctx, u, delta, A, B, C, D, z, delta_bias, h0, delta_softplus, bbar):
+        batch, dim, L = u.shape
+        ck = torch.empty(ssm_checkpoint_shape(batch, dim, A.shape[1], L), dtype=torch.float32,
+                         device=u.device)
+        y, final_state = ssm_selective_scan_fwd(u, delta, A, B, C, D=D, z=z, delta_bias=delta_bias,
+                                                delta_softplus=delta_softplus, h0=h0, bbar=bbar,
+                                                checkpoints=ck)
+        ctx.save_for_backward(u, delta, A, B, C, D, z, delta_bias, h0, ck)
+        ctx.delta_softplus, ctx.bbar = delta_softplus, bbar
+        return y, final_state
+
+    @staticmethod
+    def backward(ctx, dy, dfinal):
+        u, delta, A, B, C, D, z, delta_bias, h0, ck = ctx.saved_tensors
+        dy = torch.zeros_like(u) if dy is None else dy.contiguous()
+        g = ssm_selective_scan_bwd(u, delta, A, B, C, dy, D=D, z=z, delta_bias=delta_bias,
+                                   delta_softplus=ctx.delta_softplus, h0=h0,
+                                   dfinal_state=None if dfinal is None else dfinal.contiguous(),
+                                   bbar=ctx.bbar, checkpoints=ck)
+        return (g["du"], g["ddelta"], g["dA"], g["dB"], g["dC"], g["dD"], g["dz"],
+                g["ddelta_bias"], g["dh0"], None, None)
+
+
+def selective_scan_fn(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=False,
+                      h0=None, bbar="delta"):
+    """(y, final_state) of ssm_selective_scan_fwd, differentiable in every
+    tensor argument through ssm_selective_scan_bwd (rules "delta" and "zoh";
+    the backward raises for the others)."""
+    return _SelectiveScanFn.apply(u, delta, A, B, C, D, z, delta_bias, h0, delta_softplus, bbar)
+
 def _conv_params(x, weight, bias, dev):
     if x.dim() != 3 or x.dtype not in _IO:
         raise TypeError("x must be [batch, dim, L] bfloat16 or float32")
