@@ -33,6 +33,8 @@ Entry points carry the C names:
                     delta_softplus=False, h0=None, bbar="delta")
       -> (y, final_state), differentiable (torch.autograd): the forward's
          checkpoints feed ssm_selective_scan_bwd
+  causal_conv1d_fn(x, weight, bias=None, state_in=None, silu=True) -> out,
+      differentiable through ssm_causal_conv1d_bwd
 
 Layouts: u, delta, z, y [batch, dim, L]; B, C [batch, dstate, L]; A
 [dim, dstate]; D, delta_bias [dim]; h0 / final_state / state
@@ -49,11 +51,11 @@ from .binding import (ssm_causal_conv1d_bwd, ssm_causal_conv1d_fwd, ssm_causal_c
                       ssm_selective_scan_bwd, ssm_ssd_fwd,
                       ssm_ssd_workspace_size,
                       ssm_selective_scan_bwd_workspace_size, ssm_selective_scan_fwd,
-                      ssm_state_update, selective_scan_fn)
+                      ssm_state_update, selective_scan_fn, causal_conv1d_fn)
 
 __all__ = [
     "ssm_selective_scan_fwd", "ssm_state_update", "ssm_lti_kernel", "ssm_lti_conv",
-    "ssm_selective_scan_bwd", "ssm_checkpoint_shape", "selective_scan_fn",
+    "ssm_selective_scan_bwd", "ssm_checkpoint_shape", "selective_scan_fn", "causal_conv1d_fn",
     "ssm_selective_scan_bwd_workspace_size", "ssm_causal_conv1d_fwd", "ssm_causal_conv1d_update",
     "ssm_causal_conv1d_bwd", "ssm_ssd_fwd", "ssm_ssd_workspace_size", "ssm_status_str",
     "ssm_last_error", "ssm_abi_version", "SelscanError", "library_path", "lib",

@@ -354,6 +354,30 @@ def ssm_causal_conv1d_bwd(x, weight, dout, bias=None, state_in=None, silu=True,
     return g
 
 
+
+class _CausalConv1dFn(torch.autograd.Function):
+    """The depthwise causal conv1d (+ silu) as an autograd function."""
+
+    @staticmethod
+    def forward(ctx, x, weight, bias, state_in, silu):
+        out, _ = ssm_causal_conv1d_fwd(x, weight, bias=bias, state_in=state_in, silu=silu)
+        ctx.save_for_backward(x, weight, bias, state_in)
+        ctx.silu = silu
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        x, weight, bias, state_in = ctx.saved_tensors
+        g = ssm_causal_conv1d_bwd(x, weight, dout.contiguous(), bias=bias, state_in=state_in,
+                                  silu=ctx.silu)
+        return g["dx"], g["dweight"], g["dbias"], g["dstate_in"], None
+
+
+def causal_conv1d_fn(x, weight, bias=None, state_in=None, silu=True):
+    """ssm_causal_conv1d_fwd's output, differentiable in x, weight, bias and
+    state_in through ssm_causal_conv1d_bwd."""
+    return _CausalConv1dFn.apply(x, weight, bias, state_in, silu)
+
 def ssm_ssd_workspace_size(batch, seqlen, ngroups, dstate):
     n = lib().ssm_ssd_workspace_size(batch, seqlen, ngroups, dstate)
     if n < 0:

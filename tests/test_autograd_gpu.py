@@ -1,10 +1,12 @@
-"""selective_scan_fn: the scan as a torch.autograd function (forward with
-checkpoints, backward through ssm_selective_scan_bwd), checked against the
-fp64 oracle's gradients for the loss sum(dy y) + sum(dfinal final_state),
-with the bounds of the backward's parity tests."""
+"""The autograd functions of the binding against the fp64 oracle's
+gradients: selective_scan_fn (forward with checkpoints, backward through
+ssm_selective_scan_bwd) for the loss sum(dy y) + sum(dfinal final_state),
+and causal_conv1d_fn (backward through ssm_causal_conv1d_bwd) for
+sum(dout out), with the bounds of the backward parity tests."""
 import numpy as np
 import pytest
 
+import oracle
 import workloads as wl
 from helpers import TOL, norm_err, to_dev, to_np
 from test_bwd_parity_gpu import compare, run_oracle
@@ -65,3 +67,27 @@ def test_selective_scan_fn_unsupported_rule_raises_in_backward(ssm, dev):
                                  bbar="bilinear")
     with pytest.raises(ssm.SelscanError, match="SSM_E_UNSUPPORTED"):
         y.sum().backward()
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_causal_conv1d_fn_gradients(ssm, dev, dt):
+    w = wl.Workload("conv", 0, 2, 24, 16, 300, dt, False, 0.0, 1.0, False, "s4d_real")
+    c = wl.conv_inputs(w, width=4, seed=6300)
+    x = to_dev(c["x"], dev).requires_grad_()
+    wt = to_dev(c["weight"], dev).requires_grad_()
+    b = to_dev(c["bias"], dev).requires_grad_()
+    st = to_dev(c["state_in"], dev).requires_grad_()
+    out = ssm.causal_conv1d_fn(x, wt, b, st, silu=True)
+    dout = to_dev(c["dout"], dev)
+    (out.float() * dout.float()).sum().backward()
+    torch.cuda.synchronize()
+    f64 = (lambda a: wl.bf16_bits_to_f32(a).astype(np.float64) if a.dtype == np.uint16
+           else a.astype(np.float64))
+    ref = oracle.conv1d_bwd(c["x"], c["weight"], f64(c["dout"]), bias=c["bias"],
+                            state_in=c["state_in"], silu=True)
+    tol = TOL[dt]
+    assert norm_err(to_np(x.grad), ref["dx"]) <= tol
+    assert norm_err(to_np(st.grad), ref["dstate_in"]) <= tol
+    for got, r in ((wt.grad, ref["dw"]), (b.grad, ref["dbias"])):
+        g = to_np(got)
+        assert np.max(np.abs(g - r)) / (1.0 + np.max(np.abs(r))) <= tol
