@@ -12,6 +12,9 @@ widens them itself.  Per-channel parameters (A, D,
 delta_bias, h0) are widened to float64 here with ``astype`` (exact for float32).
 
 Each function cites the page passage it follows in ``ssm_oracle.c``.
+The backward functions can also return, for every gradient that is a sum
+(dA, dB, dC, dD, ddelta_bias; conv dw, dbias), the sum of the absolute values
+of its terms: the parity tests bound each such element by tol * (1 + that sum).
 Parity status: every function here is pinned by ``tests/test_oracle_pins.py`` (forward,
 decode, LTI), ``tests/test_oracle_bwd_pins.py`` (backward, by finite differences) and
 ``tests/test_oracle_conv_pins.py`` (causal conv1d: torch's conv1d, closed forms, finite
@@ -62,12 +65,13 @@ def _lib():
         lib.ssm_oracle_causal_conv.argtypes = [vp, vp, ctypes.c_double, i64, vp]
         lib.ssm_oracle_selective_scan_bwd.argtypes = [
             i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp,
-            i64, i64, i64, i64, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32]
+            i64, i64, i64, i64, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+            vp, vp, vp, vp, vp, i32]
         lib.ssm_oracle_ssd.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp,
                                        i64, i64, i64, i64, i64, i64, vp, vp, i32]
         lib.ssm_oracle_conv1d.argtypes = [i32, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp, vp]
         lib.ssm_oracle_conv1d_bwd.argtypes = [i32, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32,
-                                              vp, vp, vp, vp]
+                                              vp, vp, vp, vp, vp, vp]
         for f in (lib.ssm_oracle_selective_scan, lib.ssm_oracle_state_update,
                   lib.ssm_oracle_lti_kernel, lib.ssm_oracle_causal_conv,
                   lib.ssm_oracle_selective_scan_bwd, lib.ssm_oracle_conv1d, lib.ssm_oracle_ssd,
@@ -212,12 +216,14 @@ def causal_conv(K, u, D=0.0):
 
 def selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None,
                        delta_softplus=False, bbar="delta", h0=None, dfinal=None, channels=None,
-                       n_threads=None):
+                       want_abs=False, n_threads=None):
     """Gradients of the fp64 selective scan for the loss sum(dy * y) +
     sum(dfinal * final_state).  Returns a dict of float64 arrays: per selected
     channel du, ddelta (raw step), dz (if z), dh0 ([n_sel, dstate]); summed over
     the selected channels dA [dim, dstate], dB, dC [batch, dstate, L], dD,
-    ddelta_bias [dim]."""
+    ddelta_bias [dim].  With ``want_abs`` also dA_abs, dB_abs, dC_abs, dD_abs,
+    ddelta_bias_abs: per element the sum of the absolute values of the terms
+    that the corresponding sum adds (the scale of its rounding error)."""
     u, dt = _seq(u, "u")
     delta, _ = _seq(delta, "delta")
     B, _ = _seq(B, "B")
@@ -239,15 +245,21 @@ def selective_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None,
                dh0=np.empty((n_sel, N)),
                dA=np.empty((dim, N)), dB=np.empty((batch, N, L)), dC=np.empty((batch, N, L)),
                dD=np.empty(dim), ddelta_bias=np.empty(dim))
+    ab = dict(dA_abs=np.empty((dim, N)), dB_abs=np.empty((batch, N, L)),
+              dC_abs=np.empty((batch, N, L)), dD_abs=np.empty(dim),
+              ddelta_bias_abs=np.empty(dim)) if want_abs else {}
     rc = _lib().ssm_oracle_selective_scan_bwd(
         dt, _ptr(u), _ptr(delta), _ptr(B), _ptr(C), _ptr(z), _ptr(A64), _ptr(D64),
         _ptr(bias64), int(bool(delta_softplus)), BBAR_MODES[bbar], _ptr(h064),
         _ptr(dy64), _ptr(df64), batch, dim, N, L, _ptr(sel), n_sel,
         _ptr(out["du"]), _ptr(out["ddelta"]), _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]),
         _ptr(out["dD"]), _ptr(out["dz"]), _ptr(out["ddelta_bias"]), _ptr(out["dh0"]),
+        _ptr(ab.get("dA_abs")), _ptr(ab.get("dB_abs")), _ptr(ab.get("dC_abs")),
+        _ptr(ab.get("dD_abs")), _ptr(ab.get("ddelta_bias_abs")),
         int(n_threads or default_threads()))
     if rc != 0:
         raise RuntimeError(f"ssm_oracle_selective_scan_bwd failed ({rc})")
+    out.update(ab)
     return out
 
 
@@ -270,9 +282,11 @@ def conv1d(x, w, bias=None, state_in=None, silu=True):
     return out, st
 
 
-def conv1d_bwd(x, w, dout, bias=None, state_in=None, silu=True):
+def conv1d_bwd(x, w, dout, bias=None, state_in=None, silu=True, want_abs=False):
     """Gradients of conv1d for the loss sum(dout * out): dict of float64 dx
-    [batch, dim, L], dw [dim, W], dbias [dim], dstate_in [batch, dim, W-1]."""
+    [batch, dim, L], dw [dim, W], dbias [dim], dstate_in [batch, dim, W-1];
+    with ``want_abs`` also dw_abs and dbias_abs, the sums of the absolute
+    values of the terms of dw and dbias."""
     x, dt = _seq(x, "x")
     batch, dim, L = x.shape
     w64 = _f64(w)
@@ -282,10 +296,13 @@ def conv1d_bwd(x, w, dout, bias=None, state_in=None, silu=True):
     assert d64.shape == (batch, dim, L)
     g = dict(dx=np.empty((batch, dim, L)), dw=np.empty((dim, W)), dbias=np.empty(dim),
              dstate_in=np.empty((batch, dim, W - 1)))
+    if want_abs:
+        g["dw_abs"], g["dbias_abs"] = np.empty((dim, W)), np.empty(dim)
     rc = _lib().ssm_oracle_conv1d_bwd(dt, _ptr(x), _ptr(w64), _ptr(b64), _ptr(s64), _ptr(d64),
                                       batch, dim, L, W, int(bool(silu)), _ptr(g["dx"]),
                                       _ptr(g["dw"]), _ptr(g["dbias"]),
-                                      _ptr(g["dstate_in"]) if W > 1 else None)
+                                      _ptr(g["dstate_in"]) if W > 1 else None,
+                                      _ptr(g.get("dw_abs")), _ptr(g.get("dbias_abs")))
     if rc != 0:
         raise RuntimeError(f"ssm_oracle_conv1d_bwd failed ({rc})")
     return g

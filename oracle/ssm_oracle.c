@@ -88,6 +88,16 @@ static double or_bbar_factor(double dt, double a, int bbar_mode) {
   return expm1(dt * a) / a;
 }
 
+/* Channels a worker claims at a time: enough steps per claim that the lock
+ * is rare (decode steps are one step each), few enough that the threads
+ * stay balanced.  Which thread runs a channel changes no arithmetic. */
+static int64_t or_claim_block(int64_t n_channels, int64_t seqlen, int n_threads) {
+  int64_t blk = 16384 / (seqlen > 0 ? seqlen : 1);
+  const int64_t fair = n_channels / (8 * (int64_t)(n_threads > 0 ? n_threads : 1));
+  if (blk > fair) blk = fair;
+  return blk < 1 ? 1 : blk;
+}
+
 typedef struct {
   int io_dtype;
   const void *u, *delta, *Bm, *Cm, *z;
@@ -99,6 +109,7 @@ typedef struct {
   int64_t n_channels;
   double *y, *final_state;
   /* work distribution */
+  int n_threads;
   int64_t next;
   pthread_mutex_t lock;
   int status;
@@ -145,12 +156,15 @@ static void* or_scan_worker(void* arg) {
     pthread_mutex_unlock(&j->lock);
     return NULL;
   }
+  const int64_t blk = or_claim_block(j->n_channels, j->seqlen, j->n_threads);
   for (;;) {
     pthread_mutex_lock(&j->lock);
-    const int64_t sel = j->next++;
+    const int64_t first = j->next;
+    j->next += blk;
     pthread_mutex_unlock(&j->lock);
-    if (sel >= j->n_channels) break;
-    or_scan_one(j, sel, h);
+    if (first >= j->n_channels) break;
+    const int64_t last = first + blk < j->n_channels ? first + blk : j->n_channels;
+    for (int64_t sel = first; sel < last; ++sel) or_scan_one(j, sel, h);
   }
   free(h);
   return NULL;
@@ -213,6 +227,7 @@ int ssm_oracle_selective_scan(int io_dtype, const void* u, const void* delta, co
   if (n_threads < 1) n_threads = 1;
   if (n_threads > 256) n_threads = 256;
   if ((int64_t)n_threads > n_channels) n_threads = (int)n_channels;
+  j.n_threads = n_threads;
   pthread_t tid[256];
   int started = 0;
   for (int i = 1; i < n_threads; ++i)
@@ -320,6 +335,12 @@ int ssm_oracle_causal_conv(const double* K, const double* u, double Dskip, int64
  *   draw_t = ddt_t softplus'(raw_t + bias) = ddt_t sigmoid(raw_t + bias)
  *   dh0 = Abar_0 lambda_0
  *
+ * For the gradients that are sums over steps or channels (dA, dB, dC, dD,
+ * dbias) the oracle can also return, element by element, the sum of the
+ * absolute values of the terms written above (ddt expanded into its
+ * per-state terms for dbias): the scale against which the rounding of a
+ * float32 accumulation of the same terms, in any order, is measured.
+ *
  * with bbar = dt (delta*B rule: dbbar/ddt = 1, dbbar/dA = 0) or
  * bbar = (exp(dt A) - 1)/A (exact ZOH: dbbar/ddt = Abar,
  * dbbar/dA = (dt Abar - bbar)/A, limit dt^2/2 at A = 0).
@@ -337,6 +358,8 @@ typedef struct {
   int64_t n_channels;
   double *du, *ddelta, *dz, *dh0;            /* per selected channel */
   double *dA, *dB, *dC, *dD, *dbias;         /* shared sums (per-thread copies) */
+  double *aA, *aB, *aC, *aD, *abias;         /* sums of |term| (optional, all or none) */
+  int n_threads;
   int64_t next;
   pthread_mutex_t lock;
   int status;
@@ -344,6 +367,7 @@ typedef struct {
 
 typedef struct {
   double *dA, *dB, *dC, *dD, *dbias;
+  double *aA, *aB, *aC, *aD, *abias;  /* NULL unless the job asks for them */
 } or_bwd_acc;
 
 static void or_bwd_one(const or_bwd_job* j, int64_t sel, double* hs, double* lam, or_bwd_acc* acc) {
@@ -384,7 +408,8 @@ static void or_bwd_one(const or_bwd_job* j, int64_t sel, double* hs, double* lam
       if (j->dz) j->dz[sel * L + t] = g * yc * sg * (1.0 + zz * (1.0 - sg));
     }
     acc->dD[d] += dyc * ut;
-    double du = dyc * Dd, ddt = 0.0;
+    if (acc->aD) acc->aD[d] += fabs(dyc * ut);
+    double du = dyc * Dd, ddt = 0.0, addt = 0.0;
     for (int64_t n = 0; n < N; ++n) {
       const double a = j->A[d * N + n];
       const double abar = exp(dt * a);
@@ -396,6 +421,10 @@ static void or_bwd_one(const or_bwd_job* j, int64_t sel, double* hs, double* lam
       const double dbbar = l * bt * ut;
       acc->dC[bc_base + n * L + t] += dyc * hs[(t + 1) * N + n];
       acc->dB[bc_base + n * L + t] += l * bbar * ut;
+      if (acc->aC) {
+        acc->aC[bc_base + n * L + t] += fabs(dyc * hs[(t + 1) * N + n]);
+        acc->aB[bc_base + n * L + t] += fabs(l * bbar * ut);
+      }
       du += l * bbar * bt;
       double dbbar_ddt, dbbar_dA;
       if (j->bbar_mode == OR_BBAR_DELTA_B) {
@@ -407,12 +436,17 @@ static void or_bwd_one(const or_bwd_job* j, int64_t sel, double* hs, double* lam
       }
       ddt += dabar * abar * a + dbbar * dbbar_ddt;
       acc->dA[d * N + n] += dabar * abar * dt + dbbar * dbbar_dA;
+      if (acc->aA) {
+        addt += fabs(dabar * abar * a) + fabs(dbbar * dbbar_ddt);
+        acc->aA[d * N + n] += fabs(dabar * abar * dt) + fabs(dbbar * dbbar_dA);
+      }
       lam[n] = abar * l;
     }
     const double dr = j->delta_softplus ? ddt * or_sigmoid(raw) : ddt;
     j->du[sel * L + t] = du;
     j->ddelta[sel * L + t] = dr;
     acc->dbias[d] += dr;
+    if (acc->abias) acc->abias[d] += j->delta_softplus ? addt * or_sigmoid(raw) : addt;
   }
   if (j->dh0)
     for (int64_t n = 0; n < N; ++n) j->dh0[sel * N + n] = lam[n];
@@ -429,13 +463,25 @@ static void* or_bwd_worker(void* arg) {
   acc.dbias = (double*)calloc((size_t)D, sizeof(double));
   acc.dB = (double*)calloc((size_t)(Bt * N * L), sizeof(double));
   acc.dC = (double*)calloc((size_t)(Bt * N * L), sizeof(double));
+  acc.aA = acc.aB = acc.aC = acc.aD = acc.abias = NULL;
   int ok = hs && lam && acc.dA && acc.dD && acc.dbias && acc.dB && acc.dC;
+  if (j->aA) {
+    acc.aA = (double*)calloc((size_t)(D * N), sizeof(double));
+    acc.aD = (double*)calloc((size_t)D, sizeof(double));
+    acc.abias = (double*)calloc((size_t)D, sizeof(double));
+    acc.aB = (double*)calloc((size_t)(Bt * N * L), sizeof(double));
+    acc.aC = (double*)calloc((size_t)(Bt * N * L), sizeof(double));
+    ok = ok && acc.aA && acc.aD && acc.abias && acc.aB && acc.aC;
+  }
+  const int64_t blk = or_claim_block(j->n_channels, L, j->n_threads);
   for (; ok;) {
     pthread_mutex_lock(&j->lock);
-    const int64_t sel = j->next++;
+    const int64_t first = j->next;
+    j->next += blk;
     pthread_mutex_unlock(&j->lock);
-    if (sel >= j->n_channels) break;
-    or_bwd_one(j, sel, hs, lam, &acc);
+    if (first >= j->n_channels) break;
+    const int64_t last = first + blk < j->n_channels ? first + blk : j->n_channels;
+    for (int64_t sel = first; sel < last; ++sel) or_bwd_one(j, sel, hs, lam, &acc);
   }
   pthread_mutex_lock(&j->lock);
   if (!ok) {
@@ -446,6 +492,13 @@ static void* or_bwd_worker(void* arg) {
     for (int64_t i = 0; i < D; ++i) j->dbias[i] += acc.dbias[i];
     for (int64_t i = 0; i < Bt * N * L; ++i) j->dB[i] += acc.dB[i];
     for (int64_t i = 0; i < Bt * N * L; ++i) j->dC[i] += acc.dC[i];
+    if (j->aA) {
+      for (int64_t i = 0; i < D * N; ++i) j->aA[i] += acc.aA[i];
+      for (int64_t i = 0; i < D; ++i) j->aD[i] += acc.aD[i];
+      for (int64_t i = 0; i < D; ++i) j->abias[i] += acc.abias[i];
+      for (int64_t i = 0; i < Bt * N * L; ++i) j->aB[i] += acc.aB[i];
+      for (int64_t i = 0; i < Bt * N * L; ++i) j->aC[i] += acc.aC[i];
+    }
   }
   pthread_mutex_unlock(&j->lock);
   free(hs);
@@ -455,6 +508,11 @@ static void* or_bwd_worker(void* arg) {
   free(acc.dbias);
   free(acc.dB);
   free(acc.dC);
+  free(acc.aA);
+  free(acc.aD);
+  free(acc.abias);
+  free(acc.aB);
+  free(acc.aC);
   return NULL;
 }
 
@@ -468,6 +526,8 @@ static void* or_bwd_worker(void* arg) {
  *   dz          : [n_channels, seqlen] or NULL
  *   dh0         : [n_channels, dstate] or NULL
  *   dA          : [dim, dstate];  dB, dC : [batch, dstate, seqlen];  dD, dbias : [dim]
+ *   aA, aB, aC, aD, abias : NULL, or all five: the sums of |term| of dA, dB,
+ *                 dC, dD, dbias, same shapes
  * The sums are overwritten (zeroed first).  Returns 0, 1 on bad arguments,
  * 2 on allocation failure.
  */
@@ -479,10 +539,14 @@ int ssm_oracle_selective_scan_bwd(int io_dtype, const void* u, const void* delta
                                   int64_t dim, int64_t dstate, int64_t seqlen,
                                   const int64_t* channels, int64_t n_channels, double* du,
                                   double* ddelta, double* dA, double* dB, double* dC, double* dD,
-                                  double* dz, double* dbias, double* dh0, int n_threads) {
+                                  double* dz, double* dbias, double* dh0, double* aA,
+                                  double* aB, double* aC, double* aD, double* abias,
+                                  int n_threads) {
   if (!u || !delta || !Bm || !Cm || !A || !dy || !du || !ddelta || !dA || !dB || !dC || !dD ||
       !dbias)
     return 1;
+  const int any_abs = aA || aB || aC || aD || abias;
+  if (any_abs && !(aA && aB && aC && aD && abias)) return 1;
   if (batch <= 0 || dim <= 0 || dstate <= 0 || seqlen <= 0) return 1;
   if (io_dtype != OR_F32 && io_dtype != OR_BF16 && io_dtype != OR_F64) return 1;
   if (bbar_mode != OR_BBAR_DELTA_B && bbar_mode != OR_BBAR_ZOH_EXACT) return 1;
@@ -494,6 +558,13 @@ int ssm_oracle_selective_scan_bwd(int io_dtype, const void* u, const void* delta
   memset(dbias, 0, sizeof(double) * (size_t)dim);
   memset(dB, 0, sizeof(double) * (size_t)(batch * dstate * seqlen));
   memset(dC, 0, sizeof(double) * (size_t)(batch * dstate * seqlen));
+  if (any_abs) {
+    memset(aA, 0, sizeof(double) * (size_t)(dim * dstate));
+    memset(aD, 0, sizeof(double) * (size_t)dim);
+    memset(abias, 0, sizeof(double) * (size_t)dim);
+    memset(aB, 0, sizeof(double) * (size_t)(batch * dstate * seqlen));
+    memset(aC, 0, sizeof(double) * (size_t)(batch * dstate * seqlen));
+  }
   or_bwd_job j;
   memset(&j, 0, sizeof j);
   j.io_dtype = io_dtype;
@@ -525,10 +596,16 @@ int ssm_oracle_selective_scan_bwd(int io_dtype, const void* u, const void* delta
   j.dC = dC;
   j.dD = dD;
   j.dbias = dbias;
+  j.aA = aA;
+  j.aB = aB;
+  j.aC = aC;
+  j.aD = aD;
+  j.abias = abias;
   pthread_mutex_init(&j.lock, NULL);
   if (n_threads < 1) n_threads = 1;
   if (n_threads > 256) n_threads = 256;
   if ((int64_t)n_threads > n_channels) n_threads = (int)n_channels;
+  j.n_threads = n_threads;
   pthread_t tid[256];
   int started = 0;
   for (int i = 1; i < n_threads; ++i)
@@ -589,16 +666,22 @@ int ssm_oracle_conv1d(int io_dtype, const void* x, const double* w, const double
  *   dw_{d,k} = sum_{b,t} g_t x_{t-(W-1)+k}      dbias_d = sum_{b,t} g_t
  *   dstate_j = the dx of the pre-start input at time j-(W-1).
  * dx and dout are double [batch, dim, L]; dw [dim, W], dbias [dim] are
- * overwritten; dstate_in [batch, dim, W-1] may be NULL.
+ * overwritten; dstate_in [batch, dim, W-1] may be NULL.  aw [dim, W] and
+ * abias [dim] (both or neither) receive the sums of |term| of dw and dbias.
  */
 int ssm_oracle_conv1d_bwd(int io_dtype, const void* x, const double* w, const double* bias,
                           const double* state_in, const double* dout, int64_t batch, int64_t dim,
                           int64_t L, int64_t W, int silu, double* dx, double* dw, double* dbias,
-                          double* dstate_in) {
+                          double* dstate_in, double* aw, double* abias) {
   if (!x || !w || !dout || !dx || !dw || !dbias || batch <= 0 || dim <= 0 || L <= 0 || W <= 0)
     return 1;
+  if (!aw != !abias) return 1;
   memset(dw, 0, sizeof(double) * (size_t)(dim * W));
   memset(dbias, 0, sizeof(double) * (size_t)dim);
+  if (aw) {
+    memset(aw, 0, sizeof(double) * (size_t)(dim * W));
+    memset(abias, 0, sizeof(double) * (size_t)dim);
+  }
   double* g = (double*)malloc(sizeof(double) * (size_t)L);
   if (!g) return 2;
   for (int64_t c = 0; c < batch * dim; ++c) {
@@ -610,8 +693,12 @@ int ssm_oracle_conv1d_bwd(int io_dtype, const void* x, const double* w, const do
       const double s = or_sigmoid(pre);
       g[t] = silu ? dout[row + t] * s * (1.0 + pre * (1.0 - s)) : dout[row + t];
       dbias[d] += g[t];
-      for (int64_t k = 0; k < W; ++k)
-        dw[d * W + k] += g[t] * or_conv_x(x, io_dtype, state_in, row, sb, W, t - (W - 1) + k);
+      if (abias) abias[d] += fabs(g[t]);
+      for (int64_t k = 0; k < W; ++k) {
+        const double term = g[t] * or_conv_x(x, io_dtype, state_in, row, sb, W, t - (W - 1) + k);
+        dw[d * W + k] += term;
+        if (aw) aw[d * W + k] += fabs(term);
+      }
     }
     /* input at time s (s >= -(W-1)) feeds outputs t = s + (W-1) - k */
     for (int64_t s = -(W - 1); s < L; ++s) {

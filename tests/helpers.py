@@ -1,8 +1,14 @@
-"""Shared test helpers: numpy <-> torch transfer and the parity measure."""
+"""Shared test helpers: numpy <-> torch transfer and the parity measures."""
 import numpy as np
 
-# Parity bounds, elementwise: |got - ref| <= tol * (1 + |ref|).
+# Parity bounds, elementwise: |got - ref| <= tol * (1 + |ref|), tol by the
+# io dtype (2e-2 covers the bf16 rounding of outputs stored in bf16).
 TOL = {"f32": 1e-4, "bf16": 2e-2}
+# Gradients that are sums of terms (dA, dB, dC, dD, ddelta_bias; conv dweight,
+# dbias) are float32 outputs whose terms are formed in float32 from the same
+# input bits as the oracle's, with no bf16 rounding anywhere: for every io
+# dtype, |got - ref| <= TOL_SUM * (1 + sum |term|).
+TOL_SUM = 1e-4
 
 
 def to_dev(a, dev):
@@ -28,6 +34,23 @@ def norm_err(got, ref):
     if not np.all(np.isfinite(got)):
         return float("inf")
     return float(np.max(np.abs(got - ref) / (1.0 + np.abs(ref))))
+
+
+def sum_err(got, ref, ref_abs):
+    """Largest error of a summed gradient, element by element, against the
+    sum of the absolute values of the element's terms (the oracle's
+    ``*_abs`` outputs): max |got - ref| / (1 + abs_sum).  The rounding of a
+    float32 accumulation of those terms, in any order, scales with that sum,
+    not with |ref|, which can be small by cancellation."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    ref_abs = np.asarray(ref_abs, dtype=np.float64)
+    assert got.shape == ref.shape == ref_abs.shape, (got.shape, ref.shape, ref_abs.shape)
+    if got.size == 0:
+        return 0.0
+    if not np.all(np.isfinite(got)):
+        return float("inf")
+    return float(np.max(np.abs(got - ref) / (1.0 + ref_abs)))
 
 
 def scan_gpu(ssm, x, dev, bbar="delta", h0=None, final_state=None, want_final_state=True):

@@ -4,15 +4,17 @@ adjoint recurrence on the same seeded inputs and upstream gradients.
 Bounds: per-step gradients (du, ddelta, dz) and dh0 elementwise,
 |gpu - oracle| <= tol * (1 + |oracle|), as for y.  Gradients that are sums
 over many steps or channels (dA, dB, dC, dD, ddelta_bias) are accumulated in
-float32 in an order that depends on scheduling, so they are bounded against
-the scale of the tensor: max |gpu - oracle| <= tol * (1 + max |oracle|).
+float32 in an order that depends on scheduling; each element is bounded by
+the sum of the absolute values of its own terms, which the oracle returns:
+|gpu - oracle| <= 1e-4 * (1 + sum |term|) for both io dtypes (they are float32
+outputs formed without any bf16 rounding).
 tol = 1e-4 for float32 inputs, 2e-2 for bf16 inputs."""
 import numpy as np
 import pytest
 
 import oracle
 import workloads as wl
-from helpers import TOL, norm_err, to_dev, to_np
+from helpers import TOL, TOL_SUM, norm_err, sum_err, to_dev, to_np
 
 torch = pytest.importorskip("torch")
 
@@ -36,15 +38,6 @@ def dev(ssm):
     return torch.device("cuda:0")
 
 
-def red_err(got, ref):
-    got = np.asarray(got, dtype=np.float64)
-    ref = np.asarray(ref, dtype=np.float64)
-    assert got.shape == ref.shape, (got.shape, ref.shape)
-    if not np.all(np.isfinite(got)):
-        return float("inf")
-    return float(np.max(np.abs(got - ref)) / (1.0 + np.max(np.abs(ref))))
-
-
 def _as_f64(a):
     return wl.bf16_bits_to_f32(a).astype(np.float64) if a.dtype == np.uint16 else a.astype(np.float64)
 
@@ -62,7 +55,7 @@ def run_oracle(x, g, bbar, h0, dfinal, channels=None):
     return oracle.selective_scan_bwd(
         x["u"], x["delta"], x["A"], x["B"], x["C"], _as_f64(g["dy"]), D=x["D"], z=x.get("z"),
         delta_bias=x.get("delta_bias"), delta_softplus=x.get("delta_softplus", True), bbar=bbar,
-        h0=h0, dfinal=dfinal, channels=channels)
+        h0=h0, dfinal=dfinal, channels=channels, want_abs=True)
 
 
 def compare(w, got, ref, label, channels=None, reduced=REDUCED):
@@ -76,13 +69,16 @@ def compare(w, got, ref, label, channels=None, reduced=REDUCED):
         gk = got[k].reshape(w.batch * w.dim, -1)
         if rows is not None:
             gk = gk[rows]
-        errs[k] = norm_err(to_np(gk), ref[k].reshape(gk.shape[0], -1))
+        r = ref[k].reshape(gk.shape[0], -1)
+        # row blocks: the full-size tensors are large
+        errs[k] = max(norm_err(to_np(gk[i:i + 2048]), r[i:i + 2048])
+                      for i in range(0, gk.shape[0], 2048))
     for k in reduced:
         if ref.get(k) is None or got.get(k) is None:
             continue
-        errs[k] = red_err(to_np(got[k]).reshape(ref[k].shape), ref[k])
+        errs[k] = sum_err(to_np(got[k]).reshape(ref[k].shape), ref[k], ref[k + "_abs"])
     print(f"{label}: " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
-    bad = {k: v for k, v in errs.items() if not v <= tol}
+    bad = {k: v for k, v in errs.items() if not v <= (TOL_SUM if k in reduced else tol)}
     assert not bad, bad
     return errs
 
@@ -209,28 +205,17 @@ def test_bwd_mamba130m_full(ssm, dev):
     compare(w, got, ref, w.name)
 
 
-def test_bwd_mamba2p8b_sampled(ssm, dev):
-    """The mamba2p8b shape at full size; per-channel gradients and the
-    per-channel sums (dA, dD, ddelta_bias) on every sequence of 48 sampled
-    channels.  dB and dC sum over all 5120 channels and are covered at the
-    smaller shapes."""
+def test_bwd_mamba2p8b_full(ssm, dev):
+    """The mamba2p8b shape at full size: every gradient of every channel,
+    including dB and dC, the sums over all 5120 channels of a sequence."""
     w = wl.WORKLOADS["mamba2p8b"]
     x = wl.scan_inputs(w)
     g = wl.grad_inputs(w)
-    got = run_gpu(ssm, dev, x, g, "delta", None, None)
+    got = run_gpu(ssm, dev, x, g, "delta", None, g["dfinal"])
     torch.cuda.synchronize()
-    d_sel = np.random.default_rng(7).choice(w.dim, 48, replace=False)
-    d_sel[:2] = (0, w.dim - 1)
-    channels = (np.arange(w.batch)[:, None] * w.dim + d_sel[None, :]).reshape(-1)
-    ref = run_oracle(x, g, "delta", None, None, channels=channels)
-    idx = torch.as_tensor(d_sel, device=dev)
-    sub = {k: (got[k][idx] if k in ("dA", "dD", "ddelta_bias") else got[k])
-           for k in PER_STEP + ("dA", "dD", "ddelta_bias") if got.get(k) is not None}
-    ref_sub = dict(ref)
-    for k in ("dA", "dD", "ddelta_bias"):
-        ref_sub[k] = ref[k][d_sel]
-    compare(w, sub, ref_sub, w.name + " sampled", channels=channels,
-            reduced=("dA", "dD", "ddelta_bias"))
+    print("mamba2p8b backward: GPU done, running the oracle", flush=True)
+    ref = run_oracle(x, g, "delta", None, g["dfinal"])
+    compare(w, got, ref, w.name + " full")
 
 
 # (batch, dim, dstate, L, dtype, gate, bias, bbar): the three lane layouts of

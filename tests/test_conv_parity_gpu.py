@@ -1,15 +1,16 @@
 """Parity of the causal conv1d entry points (through the C ABI) against the
 fp64 oracle on the same seeded inputs.  Bounds as for the scan: outputs and
 per-step gradients elementwise |gpu - oracle| <= tol (1 + |oracle|); the
-weight and bias gradients (sums over sequences and steps) against the
-tensor's scale, max |gpu - oracle| <= tol (1 + max |oracle|); tol 1e-4 for
-float32 inputs, 2e-2 for bf16."""
+weight and bias gradients (sums over sequences and steps, float32 outputs)
+element by element against the sum of the absolute values of their terms,
+|gpu - oracle| <= 1e-4 (1 + sum |term|); tol 1e-4 for float32 inputs, 2e-2
+for bf16."""
 import numpy as np
 import pytest
 
 import oracle
 import workloads as wl
-from helpers import TOL, norm_err, to_dev, to_np
+from helpers import TOL, TOL_SUM, norm_err, sum_err, to_dev, to_np
 
 torch = pytest.importorskip("torch")
 
@@ -36,14 +37,6 @@ def _wl(batch, dim, L, dtype, name="conv"):
 
 def _f64(a):
     return wl.bf16_bits_to_f32(a).astype(np.float64) if a.dtype == np.uint16 else a.astype(np.float64)
-
-
-def red_err(got, ref):
-    got = np.asarray(got, dtype=np.float64)
-    ref = np.asarray(ref, dtype=np.float64)
-    if not np.all(np.isfinite(got)):
-        return float("inf")
-    return float(np.max(np.abs(got - ref)) / (1.0 + np.max(np.abs(ref))))
 
 
 CASES = [  # batch, dim, L, W, dtype, silu, bias, state_in
@@ -75,17 +68,17 @@ def test_conv1d_fwd_bwd(ssm, dev, case):
     torch.cuda.synchronize()
     ro, rst = oracle.conv1d(c["x"], c["weight"], bias=bias, state_in=st, silu=silu)
     rg = oracle.conv1d_bwd(c["x"], c["weight"], _f64(c["dout"]), bias=bias, state_in=st,
-                           silu=silu)
+                           silu=silu, want_abs=True)
     tol = TOL[dt]
     errs = dict(out=norm_err(to_np(out), ro), dx=norm_err(to_np(g["dx"]), rg["dx"]),
-                dweight=red_err(to_np(g["dweight"]), rg["dw"]))
+                dweight=sum_err(to_np(g["dweight"]), rg["dw"], rg["dw_abs"]))
     if W > 1:
         errs["state_out"] = norm_err(to_np(st_out), rst)
         errs["dstate_in"] = norm_err(to_np(g["dstate_in"]), rg["dstate_in"])
     if with_bias:
-        errs["dbias"] = red_err(to_np(g["dbias"]), rg["dbias"])
+        errs["dbias"] = sum_err(to_np(g["dbias"]), rg["dbias"], rg["dbias_abs"])
     print(case, " ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
-    assert all(v <= tol for v in errs.values()), errs
+    assert all(v <= (TOL_SUM if k in ("dweight", "dbias") else tol) for k, v in errs.items()), errs
     if W > 1:  # the state is a copy of inputs: exact
         assert np.array_equal(to_np(st_out), rst)
 
@@ -124,9 +117,9 @@ def test_conv1d_chunked_prefill_in_place_state(ssm, dev):
     assert torch.equal(torch.cat([a, d], dim=-1), full)
 
 
-def test_conv1d_mamba2p8b_sampled(ssm, dev):
+def test_conv1d_mamba2p8b_full(ssm, dev):
     """The conv at the mamba2p8b layer shape ([4, 5120, 8192] bf16, width 4,
-    silu, bias), checked on 64 sampled channels of every sequence."""
+    silu, bias): every output and gradient of every channel."""
     w = wl.WORKLOADS["mamba2p8b"]
     c = wl.conv_inputs(w, width=4)
     out, _ = ssm.ssm_causal_conv1d_fwd(to_dev(c["x"], dev), to_dev(c["weight"], dev),
@@ -134,17 +127,15 @@ def test_conv1d_mamba2p8b_sampled(ssm, dev):
     g = ssm.ssm_causal_conv1d_bwd(to_dev(c["x"], dev), to_dev(c["weight"], dev),
                                   to_dev(c["dout"], dev), to_dev(c["bias"], dev))
     torch.cuda.synchronize()
-    d_sel = np.random.default_rng(11).choice(w.dim, 64, replace=False)
-    d_sel[:2] = (0, w.dim - 1)
-    xs = np.ascontiguousarray(c["x"][:, d_sel, :])
-    ro, _ = oracle.conv1d(xs, c["weight"][d_sel], bias=c["bias"][d_sel])
-    rg = oracle.conv1d_bwd(xs, c["weight"][d_sel], _f64(np.ascontiguousarray(c["dout"][:, d_sel, :])),
-                           bias=c["bias"][d_sel])
-    idx = torch.as_tensor(d_sel, device=dev)
-    e_out = norm_err(to_np(out[:, idx, :]), ro)
-    e_dx = norm_err(to_np(g["dx"][:, idx, :]), rg["dx"])
-    e_dw = red_err(to_np(g["dweight"][idx]), rg["dw"])
-    e_db = red_err(to_np(g["dbias"][idx]), rg["dbias"])
+    ro, _ = oracle.conv1d(c["x"], c["weight"], bias=c["bias"])
+    rg = oracle.conv1d_bwd(c["x"], c["weight"], _f64(c["dout"]), bias=c["bias"], want_abs=True)
+    rows = w.batch * w.dim
+    out_g, dx_g = out.view(rows, -1), g["dx"].view(rows, -1)
+    ro, rdx = ro.reshape(rows, -1), rg["dx"].reshape(rows, -1)
+    e_out = max(norm_err(to_np(out_g[i:i + 2048]), ro[i:i + 2048]) for i in range(0, rows, 2048))
+    e_dx = max(norm_err(to_np(dx_g[i:i + 2048]), rdx[i:i + 2048]) for i in range(0, rows, 2048))
+    e_dw = sum_err(to_np(g["dweight"]), rg["dw"], rg["dw_abs"])
+    e_db = sum_err(to_np(g["dbias"]), rg["dbias"], rg["dbias_abs"])
     print(f"mamba2p8b conv: out {e_out:.2e} dx {e_dx:.2e} dweight {e_dw:.2e} dbias {e_db:.2e}",
           flush=True)
-    assert max(e_out, e_dx, e_dw, e_db) <= TOL["bf16"]
+    assert max(e_out, e_dx) <= TOL["bf16"] and max(e_dw, e_db) <= TOL_SUM

@@ -118,3 +118,59 @@ def test_backward_float32_parameters_marshalled_like_float64():
         for k, v in g64.items():
             if v is not None:
                 assert np.array_equal(g32[k], v), (bbar, k)
+
+
+SUMS = ("dA", "dB", "dC", "dD", "ddelta_bias")
+
+
+def _nonneg_case(seed, sign=1.0):
+    """Inputs for which every term of every summed gradient has the sign of
+    `sign`: u, B, C >= 0, a positive A (so exp(delta A) > 0, the exact-ZOH
+    coefficient and both of its derivatives are positive), no gate, zero
+    initial state (so every state is >= 0) and upstream gradients of one
+    sign (so every adjoint has that sign)."""
+    r = np.random.default_rng(seed)
+    Bt, Dm, N, L = 2, 3, 4, 7
+    x = dict(u=r.uniform(0.1, 1.0, (Bt, Dm, L)), delta=r.normal(-0.5, 0.5, (Bt, Dm, L)),
+             A=r.uniform(0.1, 0.6, (Dm, N)), B=r.uniform(0.1, 1.0, (Bt, N, L)),
+             C=r.uniform(0.1, 1.0, (Bt, N, L)), D=r.uniform(0.1, 1.0, Dm),
+             delta_bias=r.normal(0, 0.3, Dm))
+    dy = sign * r.uniform(0.1, 1.0, (Bt, Dm, L))
+    dfinal = sign * r.uniform(0.1, 1.0, (Bt * Dm, N))
+    return x, dy, dfinal
+
+
+@pytest.mark.parametrize("bbar", ["delta", "zoh"])
+@pytest.mark.parametrize("sign", [1.0, -1.0])
+def test_abs_sums_equal_the_sums_when_terms_share_a_sign(bbar, sign):
+    """The sums of |term| that bound the rounding of the summed gradients:
+    where every term has one sign they equal the (finite-difference pinned)
+    gradient itself, or its negation, so each holds exactly the terms of its
+    sum, each once."""
+    x, dy, dfinal = _nonneg_case(31, sign)
+    g = oracle.selective_scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], dy, D=x["D"],
+                                  delta_bias=x["delta_bias"], delta_softplus=True, bbar=bbar,
+                                  dfinal=dfinal, want_abs=True, n_threads=2)
+    for k in SUMS:
+        assert np.all(g[k] * sign > 0), k
+        assert np.allclose(g[k + "_abs"], sign * g[k], rtol=1e-14, atol=0), k
+
+
+@pytest.mark.parametrize("bbar", ["delta", "zoh"])
+def test_abs_sums_bound_the_sums(bbar):
+    """With terms of both signs (the usual case) each sum of |term| is at
+    least |gradient| and, somewhere, strictly more."""
+    x, dy, dfinal, sp = _case(5)
+    g = oracle.selective_scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], dy, D=x["D"],
+                                  z=x["z"], delta_bias=x["delta_bias"], delta_softplus=sp,
+                                  bbar=bbar, h0=x["h0"], dfinal=dfinal, want_abs=True,
+                                  n_threads=1)
+    # one thread each: the per-thread partial sums merge in a fixed order
+    plain = oracle.selective_scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], dy, D=x["D"],
+                                      z=x["z"], delta_bias=x["delta_bias"], delta_softplus=sp,
+                                      bbar=bbar, h0=x["h0"], dfinal=dfinal, n_threads=1)
+    for k in SUMS:
+        assert np.array_equal(g[k], plain[k]), k  # asking for them changes nothing else
+        assert np.all(g[k + "_abs"] >= np.abs(g[k]) * (1 - 1e-14)), k
+        assert np.any(g[k + "_abs"] > np.abs(g[k]) * (1 + 1e-6)), k
+    assert "dA_abs" not in plain

@@ -124,3 +124,23 @@ def test_conv1d_backward_matches_finite_differences(silu, W):
                        - _loss(am["x"], am["w"], am["b"], am["s"], dout, silu)) / (2 * h)
         err = np.max(np.abs(g[gk].reshape(fd.shape) - fd) / (1 + np.abs(fd)))
         assert err < 1e-7, (key, err)
+
+
+@pytest.mark.parametrize("silu", [True, False])
+def test_conv1d_abs_sums(silu):
+    """The sums of |term| of dweight and dbias: equal to the gradients where
+    every term is positive (x, w, bias > 0 keep silu' > 0; dout > 0), at least
+    |gradient| and somewhere more with mixed signs."""
+    r = np.random.default_rng(17)
+    x, w = r.uniform(0.1, 1, (2, 3, 9)), r.uniform(0.1, 1, (3, 4))
+    b, dout = r.uniform(0.1, 1, 3), r.uniform(0.1, 1, (2, 3, 9))
+    g = oracle.conv1d_bwd(x, w, dout, bias=b, silu=silu, want_abs=True)
+    assert np.all(g["dw"] > 0) and np.all(g["dbias"] > 0)
+    assert np.allclose(g["dw_abs"], g["dw"], rtol=1e-14, atol=0)
+    assert np.allclose(g["dbias_abs"], g["dbias"], rtol=1e-14, atol=0)
+    xm, wm, bm, s = _case(23)
+    dm = r.standard_normal(xm.shape)
+    g = oracle.conv1d_bwd(xm, wm, dm, bias=bm, state_in=s, silu=silu, want_abs=True)
+    for k in ("dw", "dbias"):
+        assert np.all(g[k + "_abs"] >= np.abs(g[k]) * (1 - 1e-14))
+        assert np.any(g[k + "_abs"] > np.abs(g[k]) * (1 + 1e-6))

@@ -3,8 +3,8 @@ scan under every discretization rule and the backward under both exponential
 rules, over random (batch, dim, N, L) with and without gate, bias, softplus
 and an initial state.  Bounds as in the other parity tests: elementwise
 |gpu - oracle| <= tol (1 + |oracle|), tol 1e-4 for float32 inputs and 2e-2
-for bf16 (sums over steps or channels in the backward against the tensor's
-scale)."""
+for bf16 (sums over steps or channels in the backward element by element
+against the sum of the absolute values of their terms, 1e-4 (1 + sum |term|))."""
 import numpy as np
 import pytest
 
