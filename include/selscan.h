@@ -131,6 +131,9 @@ int ssm_selective_scan_fwd(const void* u, const void* delta, const float* A, con
  *  Bm, Cm      [batch, dstate] io_dtype
  *  A, Dskip, delta_bias, delta_softplus, bbar_mode: as for the forward scan
  *  y           [batch, dim] io_dtype out; must not overlap any input or state
+ * state, Bm and Cm must be 16-byte aligned (SSM_E_ALIGN otherwise); A is read
+ * with 16-byte accesses when it is aligned and dstate is a multiple of 16,
+ * element by element otherwise.
  */
 int ssm_state_update(float* state, const void* u, const void* delta, const float* A,
                      const void* Bm, const void* Cm, const float* Dskip, const void* z,

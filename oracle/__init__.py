@@ -32,6 +32,10 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ssm_oracle.c")
 _SO = os.path.join(_HERE, "libssm_oracle.so")
+_SO_SANITIZED = os.path.join(_HERE, "libssm_oracle_san.so")
+# A prebuilt oracle library to load instead (the sanitizer test points this at
+# the AddressSanitizer / UndefinedBehaviorSanitizer build); not built here.
+_SO_OVERRIDE = os.environ.get("SSM_ORACLE_LIB")
 _LIB = None
 
 BBAR_MODES = {"delta": 0, "delta_b": 0, "zoh": 1, "zoh_exact": 1, "euler": 2, "bilinear": 3}
@@ -48,11 +52,27 @@ def build(force: bool = False) -> str:
     return _SO
 
 
+def build_sanitized() -> str:
+    """The same source built with AddressSanitizer and UndefinedBehaviorSanitizer
+    (host code only; run the pins against it with the sanitizer runtimes
+    preloaded and SSM_ORACLE_LIB pointing at the returned path)."""
+    tmp = _SO_SANITIZED + ".tmp%d" % os.getpid()
+    subprocess.check_call(
+        ["gcc", "-O1", "-g", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared",
+         "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+         "-fno-omit-frame-pointer", "-o", tmp, _SRC, "-lm", "-lpthread"])
+    os.replace(tmp, _SO_SANITIZED)
+    return _SO_SANITIZED
+
+
 def _lib():
     global _LIB
     if _LIB is None:
-        build()
-        lib = ctypes.CDLL(_SO)
+        if _SO_OVERRIDE:
+            lib = ctypes.CDLL(_SO_OVERRIDE)
+        else:
+            build()
+            lib = ctypes.CDLL(_SO)
         i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
         lib.ssm_oracle_selective_scan.argtypes = [
             i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp,

@@ -2100,6 +2100,7 @@ struct StepArgs {
   void* y;
   int64_t batch, dim, dstate;
   int softplus;
+  int vec;  // dstate % 16 == 0 and A 16-byte aligned: 16-byte accesses
 };
 
 // One lane per channel: the lane streams its channel's whole state row
@@ -2120,8 +2121,10 @@ __global__ void __launch_bounds__(256) state_update_kernel(const StepArgs a) {
   const float* Ar = a.A + d * N;
   const int64_t bc = b * N;
   float acc = 0.0f;
-  // 16 states at a time with vector accesses when rows allow it
-  const bool vec = (N % 16) == 0;
+  // 16 states at a time with vector accesses when rows allow it (the host
+  // checks the extent and the alignment of A; state, B and C bases are
+  // 16-byte aligned by contract)
+  const bool vec = a.vec != 0;
   for (int64_t n0 = 0; n0 < N; n0 += 16) {
     const int cnt = (int)((N - n0) < 16 ? (N - n0) : 16);
     float h[16], An[16], Bv[16], Cv[16];
@@ -2546,11 +2549,12 @@ int launch_fwd_cfg(const ScanArgs& a, int64_t batch, int rule, bool gate, hipStr
   constexpr int CPB = (64 / LPC) * W;
   const dim3 grid((unsigned)((a.dim + CPB - 1) / CPB), (unsigned)batch);
   const size_t shmem = 2 * (size_t)CPB * (size_t)a.dstate * sizeof(float);
-  // the B/C tiles (static) and the carry and A rows (dynamic) must fit one CU's LDS
+  // the B/C tiles (static) and the carry and A rows (dynamic, at most
+  // kMaxDstate states) must fit one CU's LDS: a layout that cannot fails to
+  // compile rather than fault at launch
   constexpr size_t kTiles = 2 * (size_t)NT * LPC * (K + 4) * sizeof(float);
-  if (kTiles + shmem > kLdsBytes)
-    return fail(SSM_E_UNSUPPORTED, "dstate = %lld needs %zu bytes of LDS", (long long)a.dstate,
-                kTiles + shmem);
+  static_assert(kTiles + 2 * (size_t)CPB * kMaxDstate * sizeof(float) <= kLdsBytes,
+                "forward scan layout exceeds the LDS of one CU");
   with_rule(rule, [&](auto rt) {
     constexpr int R = decltype(rt)::value;
     if (gate) hipLaunchKernelGGL((scan_fwd_kernel<IO, LPC, K, W, NT, VEC, R, true>), grid, dim3(64 * W), shmem, s, a);
@@ -2889,6 +2893,8 @@ int ssm_state_update(float* state, const void* u, const void* delta, const float
     return fail(SSM_E_UNSUPPORTED, "dstate = %lld is outside 1..%lld", (long long)dstate,
                 (long long)kMaxDstate);
   if (!aligned16(state)) return fail(SSM_E_ALIGN, "state is not 16-byte aligned");
+  if (!aligned16(Bm)) return fail(SSM_E_ALIGN, "B is not 16-byte aligned");
+  if (!aligned16(Cm)) return fail(SSM_E_ALIGN, "C is not 16-byte aligned");
   const int64_t es = io_dtype == SSM_DTYPE_BF16 ? 2 : 4;
   const int64_t tok = batch * dim * es, bc = batch * dstate * es;
   const Span st_span{state, batch * dim * dstate * 4, "state"}, ys{y, tok, "y"};
@@ -2904,6 +2910,7 @@ int ssm_state_update(float* state, const void* u, const void* delta, const float
   a.state = state; a.u = u; a.delta = delta; a.A = A; a.Bm = Bm; a.Cm = Cm; a.Dskip = Dskip;
   a.z = z; a.delta_bias = delta_bias; a.y = y; a.batch = batch; a.dim = dim; a.dstate = dstate;
   a.softplus = delta_softplus ? 1 : 0;
+  a.vec = (dstate % 16 == 0 && aligned16(A)) ? 1 : 0;
   const int64_t threads = batch * dim;
   const dim3 grid((unsigned)((threads + 255) / 256));
   if (grid.x == 0 || (threads + 255) / 256 > 0x7fffffff)

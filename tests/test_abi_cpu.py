@@ -82,7 +82,7 @@ def step_args(**over):
 @pytest.mark.parametrize("over,status", [
     (dict(state=None), 1), (dict(y=None), 1), (dict(B=None), 1),
     (dict(dim=0), 2), (dict(io=5), 3), (dict(bbar=4), 3), (dict(N=100), 6),
-    (dict(state=1 * P + 4), 4),
+    (dict(state=1 * P + 4), 4), (dict(B=5 * P + 2), 4), (dict(C=6 * P + 8), 4),
     (dict(y=1 * P), 5), (dict(state=2 * P), 5),
 ])
 def test_state_update_validation(lib, over, status):

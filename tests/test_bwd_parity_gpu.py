@@ -6,15 +6,15 @@ Bounds: per-step gradients (du, ddelta, dz) and dh0 elementwise,
 over many steps or channels (dA, dB, dC, dD, ddelta_bias) are accumulated in
 float32 in an order that depends on scheduling; each element is bounded by
 the sum of the absolute values of its own terms, which the oracle returns:
-|gpu - oracle| <= 1e-4 * (1 + sum |term|) for both io dtypes (they are float32
-outputs formed without any bf16 rounding).
+|gpu - oracle| <= 1e-4 * (1 + sum |term|) for both io dtypes, plus 2^-8 |oracle|
+for dB and dC when they are stored in bf16 (their final rounding).
 tol = 1e-4 for float32 inputs, 2e-2 for bf16 inputs."""
 import numpy as np
 import pytest
 
 import oracle
 import workloads as wl
-from helpers import TOL, TOL_SUM, norm_err, sum_err, to_dev, to_np
+from helpers import Q_OUT, TOL, TOL_SUM, norm_err, sum_err, to_dev, to_np
 
 torch = pytest.importorskip("torch")
 
@@ -76,7 +76,9 @@ def compare(w, got, ref, label, channels=None, reduced=REDUCED):
     for k in reduced:
         if ref.get(k) is None or got.get(k) is None:
             continue
-        errs[k] = sum_err(to_np(got[k]).reshape(ref[k].shape), ref[k], ref[k + "_abs"])
+        # dB and dC are stored in the io dtype, the other sums in float32
+        q = Q_OUT[w.dtype] if k in ("dB", "dC") else 0.0
+        errs[k] = sum_err(to_np(got[k]).reshape(ref[k].shape), ref[k], ref[k + "_abs"], q)
     print(f"{label}: " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
     bad = {k: v for k, v in errs.items() if not v <= (TOL_SUM if k in reduced else tol)}
     assert not bad, bad
