@@ -297,6 +297,32 @@ int ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void* Bm, c
 int64_t ssm_ssd_workspace_size(int64_t batch, int64_t seqlen, int64_t ngroups, int64_t dstate);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * ssm_ssd_fwd with its workspace in a static scratch array of the library,
+ * ssm_ssd_scratch_bytes() = 32 MiB per GPU (held from the first call on that
+ * GPU until the process ends).  It allocates and frees nothing.  Arguments,
+ * layouts, results and errors are those of ssm_ssd_fwd, plus:
+ *  - SSM_E_SHAPE when ssm_ssd_workspace_size(batch, seqlen, ngroups, dstate)
+ *    exceeds the scratch (refused before any HIP call; the Mamba-2 2.7B layer
+ *    at batch 4, L 8192, N 128 needs 14.7 MB);
+ *  - SSM_E_HIP when hip_stream belongs to a device other than the current
+ *    one, or the scratch's address cannot be looked up.
+ * Every call on one GPU uses the same scratch: calls that overlap in time on
+ * one GPU (other streams, other threads) race and must be serialized by the
+ * caller.  Nothing in the scratch needs clearing between calls: each call
+ * writes all of it that it reads.
+ */
+int ssm_ssd_fwd_noalloc(const void* x, const void* dt, const float* A, const void* Bm,
+                        const void* Cm, const float* Dskip, const void* z, const float* dt_bias,
+                        int dt_softplus, const float* h0, void* y, float* final_state,
+                        int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                        int64_t ngroups, int64_t dstate, int io_dtype, void* hip_stream);
+
+/* Bytes of the static scratch that ssm_ssd_fwd_noalloc uses (per GPU). */
+int64_t ssm_ssd_scratch_bytes(void);
+
+/*
  * Time-invariant path: y = K * u + D u, the causal convolution of every
  * channel with its kernel K_k = C Abar^k Bbar (from ssm_lti_kernel), which is
  * what the recurrence computes when delta, B and C do not depend on the

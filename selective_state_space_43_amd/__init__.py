@@ -29,6 +29,9 @@ Entry points carry the C names:
       -> dict of gradients
   ssm_ssd_fwd(x, dt, A, B, C, nheads, ngroups, D=None, z=None, dt_bias=None,
               dt_softplus=True, h0=None) -> (y, final_state)      (Mamba-2 scan)
+  ssm_ssd_fwd_noalloc(x, dt, A, B, C, nheads, ngroups, y, ...) -> (y, final_state)
+      the same with the workspace in the library's static scratch: allocates
+      nothing (for callers that cannot allocate; ssm_ssd_scratch_bytes())
   selective_scan_fn(u, delta, A, B, C, D=None, z=None, delta_bias=None,
                     delta_softplus=False, h0=None, bbar="delta")
       -> (y, final_state), differentiable (torch.autograd): the forward's
@@ -48,8 +51,8 @@ from ._lib import (SSM_BBAR_DELTA_B, SSM_BBAR_ZOH_EXACT, SSM_DTYPE_BF16, SSM_DTY
                    ssm_status_str)
 from .binding import (ssm_causal_conv1d_bwd, ssm_causal_conv1d_fwd, ssm_causal_conv1d_update,
                       ssm_checkpoint_shape, ssm_lti_conv, ssm_lti_kernel,
-                      ssm_selective_scan_bwd, ssm_ssd_fwd,
-                      ssm_ssd_workspace_size,
+                      ssm_selective_scan_bwd, ssm_ssd_fwd, ssm_ssd_fwd_noalloc,
+                      ssm_ssd_scratch_bytes, ssm_ssd_workspace_size,
                       ssm_selective_scan_bwd_workspace_size, ssm_selective_scan_fwd,
                       ssm_state_update, selective_scan_fn, causal_conv1d_fn)
 
@@ -57,7 +60,8 @@ __all__ = [
     "ssm_selective_scan_fwd", "ssm_state_update", "ssm_lti_kernel", "ssm_lti_conv",
     "ssm_selective_scan_bwd", "ssm_checkpoint_shape", "selective_scan_fn", "causal_conv1d_fn",
     "ssm_selective_scan_bwd_workspace_size", "ssm_causal_conv1d_fwd", "ssm_causal_conv1d_update",
-    "ssm_causal_conv1d_bwd", "ssm_ssd_fwd", "ssm_ssd_workspace_size", "ssm_status_str",
+    "ssm_causal_conv1d_bwd", "ssm_ssd_fwd", "ssm_ssd_workspace_size", "ssm_ssd_fwd_noalloc",
+    "ssm_ssd_scratch_bytes", "ssm_status_str",
     "ssm_last_error", "ssm_abi_version", "SelscanError", "library_path", "lib",
     "SSM_DTYPE_F32", "SSM_DTYPE_BF16", "SSM_BBAR_DELTA_B", "SSM_BBAR_ZOH_EXACT",
 ]

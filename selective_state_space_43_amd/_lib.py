@@ -58,6 +58,11 @@ def lib() -> ctypes.CDLL:
         L.ssm_lti_conv_fft.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, vp]
         L.ssm_ssd_workspace_size.argtypes = [i64, i64, i64, i64]
         L.ssm_ssd_workspace_size.restype = i64
+        L.ssm_ssd_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp,
+                                          i64, i64, i64, i64, i64, i64, i32, vp]
+        L.ssm_ssd_fwd_noalloc.restype = i32
+        L.ssm_ssd_scratch_bytes.argtypes = []
+        L.ssm_ssd_scratch_bytes.restype = i64
         for f in (L.ssm_selective_scan_fwd, L.ssm_state_update, L.ssm_lti_kernel,
                   L.ssm_selective_scan_bwd, L.ssm_causal_conv1d_fwd, L.ssm_causal_conv1d_update,
                   L.ssm_causal_conv1d_bwd, L.ssm_ssd_fwd, L.ssm_lti_conv,

@@ -428,3 +428,44 @@ def ssm_ssd_fwd(x, dt, A, B, C, nheads, ngroups, D=None, z=None, dt_bias=None,
                                ngroups, N, SSM_DTYPE_BF16, _stream(dev))
     check(st, "ssm_ssd_fwd")
     return y, final_state
+
+
+def ssm_ssd_scratch_bytes():
+    """Size of the library's static scratch for ssm_ssd_fwd_noalloc."""
+    return int(lib().ssm_ssd_scratch_bytes())
+
+
+def ssm_ssd_fwd_noalloc(x, dt, A, B, C, nheads, ngroups, y, D=None, z=None, dt_bias=None,
+                        dt_softplus=True, h0=None, final_state=None):
+    """ssm_ssd_fwd with its workspace in the library's static scratch: nothing
+    is allocated, here or in the library (y and final_state are the
+    caller's).  Calls on one GPU share the scratch and must not overlap."""
+    _dev(x, "x", None)
+    dev = x.device
+    if x.dim() != 3 or x.dtype != torch.bfloat16:
+        raise TypeError("x must be [batch, nheads * headdim, L] bfloat16")
+    batch, hp, L = x.shape
+    if hp % nheads:
+        raise ValueError("x's channel count is not a multiple of nheads")
+    P = hp // nheads
+    if B.dim() != 3 or B.shape[1] % ngroups:
+        raise ValueError("B must be [batch, ngroups * dstate, L]")
+    N = B.shape[1] // ngroups
+    _io(dt, "dt", torch.bfloat16, (batch, nheads, L), dev)
+    _io(B, "B", torch.bfloat16, (batch, ngroups * N, L), dev)
+    _io(C, "C", torch.bfloat16, (batch, ngroups * N, L), dev)
+    _io(A, "A", torch.float32, (nheads,), dev)
+    _f32(D, "D", (nheads,), dev)
+    _f32(dt_bias, "dt_bias", (nheads,), dev)
+    if z is not None:
+        _io(z, "z", torch.bfloat16, (batch, hp, L), dev)
+    _f32(h0, "h0", (batch, nheads, P, N), dev)
+    _io(y, "y", torch.bfloat16, (batch, hp, L), dev)
+    _f32(final_state, "final_state", (batch, nheads, P, N), dev)
+    with torch.cuda.device(dev):
+        st = lib().ssm_ssd_fwd_noalloc(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                       _ptr(z), _ptr(dt_bias), int(bool(dt_softplus)), _ptr(h0),
+                                       _ptr(y), _ptr(final_state), batch, L, nheads, P, ngroups,
+                                       N, SSM_DTYPE_BF16, _stream(dev))
+    check(st, "ssm_ssd_fwd_noalloc")
+    return y, final_state

@@ -28,6 +28,7 @@
 #include <hip/hip_runtime.h>
 
 #include <stdarg.h>
+#include <mutex>
 #include <type_traits>
 #include <stdint.h>
 #include <stdio.h>
@@ -2765,6 +2766,54 @@ void launch_ssd(const SsdArgs& a, bool gate, hipStream_t s) {
 
 }  // namespace
 
+// ---------------------------------------------------------------- static scratch
+//
+// Device memory for ssm_ssd_fwd_noalloc, the Mamba-2 scan for callers that
+// cannot allocate: it holds the workspace that ssm_ssd_fwd takes from its
+// caller (token-major C and the C.B^T tiles), up to kSsdScratchBytes.  Every
+// GPU the library runs on holds its own copy until the process ends; all
+// calls on one GPU share it, so such calls must not overlap in time.
+constexpr int64_t kSsdScratchBytes = (int64_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[kSsdScratchBytes];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// The device address of `scratch` on the device that runs `stream` (which
+// must be the current device): looked up once per device with
+// hipGetSymbolAddress, with that device current.  In host code the array's
+// own name is not a device address and is never used.
+int scratch_address(hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SSM_E_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (stream) {
+    hipDevice_t sdev = -1;
+    e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess) return fail(SSM_E_HIP, "hipStreamGetDevice: %s", hipGetErrorString(e));
+    if ((int)sdev != dev)
+      return fail(SSM_E_HIP, "the stream belongs to device %d, the current device is %d",
+                  (int)sdev, dev);
+  }
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(SSM_E_HIP, "device %d is beyond the %d this library tracks", dev, kMaxScratchDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(SSM_E_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SSM_OK;
+}
+
+}  // namespace
+
 // ---------------------------------------------------------------- C ABI
 
 extern "C" {
@@ -3210,15 +3259,18 @@ int64_t ssm_ssd_workspace_size(int64_t batch, int64_t seqlen, int64_t ngroups, i
   return ssd_layout(batch, seqlen, ngroups, dstate).bytes;
 }
 
-int ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void* Bm, const void* Cm,
-                const float* Dskip, const void* z, const float* dt_bias, int dt_softplus,
-                const float* h0, void* y, float* final_state, void* workspace,
-                int64_t workspace_bytes, int64_t batch, int64_t seqlen, int64_t nheads,
-                int64_t headdim, int64_t ngroups, int64_t dstate, int io_dtype,
-                void* hip_stream) {
-  g_last_error[0] = 0;
+// The Mamba-2 scan: validation, then the launches.  `scratch_ws`: the
+// workspace is the static scratch (workspace is NULL on entry; its address
+// is looked up once the arguments are valid; it overlaps no tensor).
+static int ssd_fwd_run(const void* x, const void* dt, const float* A, const void* Bm,
+                       const void* Cm, const float* Dskip, const void* z, const float* dt_bias,
+                       int dt_softplus, const float* h0, void* y, float* final_state,
+                       void* workspace, int64_t workspace_bytes, int64_t batch, int64_t seqlen,
+                       int64_t nheads, int64_t headdim, int64_t ngroups, int64_t dstate,
+                       int io_dtype, void* hip_stream, bool scratch_ws) {
   const struct { const void* p; const char* name; } req[] = {
-      {x, "x"}, {dt, "dt"}, {A, "A"}, {Bm, "B"}, {Cm, "C"}, {y, "y"}, {workspace, "workspace"}};
+      {x, "x"}, {dt, "dt"}, {A, "A"}, {Bm, "B"}, {Cm, "C"}, {y, "y"},
+      {scratch_ws ? x : workspace, "workspace"}};
   for (const auto& r : req)
     if (!r.p) return fail(SSM_E_NULL, "%s is NULL", r.name);
   int st;
@@ -3244,10 +3296,15 @@ int ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void* Bm, c
   // this bound also keeps every buffer the scan kernel addresses (one group's B
   // rows, its C.B^T tiles, 32 channel rows) below 2^31 bytes
   if (lay.nchunks > 65535) return fail(SSM_E_SHAPE, "seqlen = %lld is too long", (long long)seqlen);
-  if (workspace_bytes < lay.bytes)
+  if (workspace_bytes < lay.bytes) {
+    if (scratch_ws)
+      return fail(SSM_E_SHAPE, "needs %lld bytes of scratch, the static scratch holds %lld",
+                  (long long)lay.bytes, (long long)workspace_bytes);
     return fail(SSM_E_SHAPE, "workspace holds %lld bytes, needs %lld", (long long)workspace_bytes,
                 (long long)lay.bytes);
-  if (!aligned16(workspace)) return fail(SSM_E_ALIGN, "workspace is not 16-byte aligned");
+  }
+  if (!scratch_ws && !aligned16(workspace))
+    return fail(SSM_E_ALIGN, "workspace is not 16-byte aligned");
   const int64_t seq = batch * nheads * headdim * seqlen * 2, bc = batch * ngroups * dstate * seqlen * 2;
   const int64_t stb = batch * nheads * headdim * dstate * 4;
   const Span ins[] = {{x, seq, "x"},        {dt, batch * nheads * seqlen * 2, "dt"},
@@ -3265,6 +3322,10 @@ int ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void* Bm, c
   }
   if (final_state && !aligned16(final_state))
     return fail(SSM_E_ALIGN, "final_state is not 16-byte aligned");
+  if (scratch_ws) {
+    const int st2 = scratch_address(static_cast<hipStream_t>(hip_stream), &workspace);
+    if (st2 != SSM_OK) return st2;
+  }
   SsdArgs a;
   memset(&a, 0, sizeof a);
   a.x = x; a.dt = dt; a.A = A; a.Bm = Bm; a.Cm = Cm; a.Dskip = Dskip; a.z = z; a.dt_bias = dt_bias;
@@ -3283,6 +3344,39 @@ int ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void* Bm, c
     default: launch_ssd<256>(a, gate, s); break;
   }
   return launch_status("ssm_ssd_fwd launch");
+}
+
+int ssm_ssd_fwd(const void* x, const void* dt, const float* A, const void* Bm, const void* Cm,
+                const float* Dskip, const void* z, const float* dt_bias, int dt_softplus,
+                const float* h0, void* y, float* final_state, void* workspace,
+                int64_t workspace_bytes, int64_t batch, int64_t seqlen, int64_t nheads,
+                int64_t headdim, int64_t ngroups, int64_t dstate, int io_dtype,
+                void* hip_stream) {
+  g_last_error[0] = 0;
+  return ssd_fwd_run(x, dt, A, Bm, Cm, Dskip, z, dt_bias, dt_softplus, h0, y, final_state,
+                     workspace, workspace_bytes, batch, seqlen, nheads, headdim, ngroups, dstate,
+                     io_dtype, hip_stream, false);
+}
+
+int64_t ssm_ssd_scratch_bytes(void) { return kSsdScratchBytes; }
+
+int ssm_ssd_fwd_noalloc(const void* x, const void* dt, const float* A, const void* Bm,
+                        const void* Cm, const float* Dskip, const void* z, const float* dt_bias,
+                        int dt_softplus, const float* h0, void* y, float* final_state,
+                        int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                        int64_t ngroups, int64_t dstate, int io_dtype, void* hip_stream) {
+  g_last_error[0] = 0;
+  // a size the scratch cannot hold is refused before any HIP call
+  if (batch > 0 && seqlen > 0 && ngroups > 0 && dstate > 0 && dstate <= 256 &&
+      product_ok(batch, ngroups, seqlen + kSsdT, dstate * 2)) {
+    const int64_t need = ssd_layout(batch, seqlen, ngroups, dstate).bytes;
+    if (need > kSsdScratchBytes)
+      return fail(SSM_E_SHAPE, "needs %lld bytes of scratch, the static scratch holds %lld",
+                  (long long)need, (long long)kSsdScratchBytes);
+  }
+  return ssd_fwd_run(x, dt, A, Bm, Cm, Dskip, z, dt_bias, dt_softplus, h0, y, final_state,
+                     nullptr, kSsdScratchBytes, batch, seqlen, nheads, headdim, ngroups, dstate,
+                     io_dtype, hip_stream, true);
 }
 
 int ssm_lti_conv(const float* K, const void* u, const float* Dskip, void* y, int64_t batch,

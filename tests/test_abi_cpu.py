@@ -241,6 +241,27 @@ def test_ssd_validation(lib, over, status):
     assert lib.ssm_ssd_fwd(*ssd_args(**over)) == status
 
 
+def test_ssd_noalloc_validation(lib):
+    """The allocation-free Mamba-2 entry point validates like ssm_ssd_fwd and
+    refuses a size beyond its static scratch before any HIP call."""
+    args = ssd_args()
+    noalloc = args[:12] + args[14:]  # no workspace and workspace size
+    assert lib.ssm_ssd_scratch_bytes() == 32 << 20
+    for pos, status in ((0, 1), (1, 1), (3, 1), (10, 1)):  # x, dt, B, y NULL
+        a = list(noalloc)
+        a[pos] = None
+        assert lib.ssm_ssd_fwd_noalloc(*a) == status
+    a = list(noalloc)
+    a[13] = 1 << 20  # seqlen: 16384 chunks of workspace for one sequence
+    assert lib.ssm_ssd_workspace_size(2, 1 << 20, 1, 128) > lib.ssm_ssd_scratch_bytes()
+    assert lib.ssm_ssd_fwd_noalloc(*a) == 2
+    import selective_state_space_43_amd as ssm
+    assert "static scratch" in ssm.ssm_last_error()
+    a = list(noalloc)
+    a[10] = 1 * P  # y on x
+    assert lib.ssm_ssd_fwd_noalloc(*a) == 5
+
+
 def test_lti_conv_validation(lib):
     f = lib.ssm_lti_conv
     assert f(None, 2 * P, None, 3 * P, 2, 4, 64, 1, None) == 1
