@@ -838,6 +838,10 @@ scan_bwd_main_kernel(const BwdArgs a) {
   __shared__ float4 sRed4[NW * 3 * 64 * SP / 4];  // [wave][ddt, du, yc][lane][step] partial sums
   __shared__ float4 sPrep4[3 * 64 * SP / 4];      // [delta, u, dy silu(z)][lane][step]
   __shared__ float sPar[NW * 3 * CPG * NT];      // per wave: A, state at chunk start, carry
+  // a group's per-channel sums, double-buffered by group parity: dA of the
+  // group's 4 channels x 16 states, and each wave's part of ddelta_bias and dD
+  __shared__ float sGdA[2][CPG][NT];
+  __shared__ float sGbD[2][2][NW][CPG];
   float* sRed = reinterpret_cast<float*>(sRed4);
   float* sPrep = reinterpret_cast<float*>(sPrep4);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -939,7 +943,7 @@ scan_bwd_main_kernel(const BwdArgs a) {
   // loads of group g + 2: a wait for those loads then finds the writes long
   // done instead of stalling on writes just issued.
   float p_du[2] = {0.0f, 0.0f}, p_dr[2] = {0.0f, 0.0f}, p_dz[2] = {0.0f, 0.0f};
-  float p_dA[4] = {0.0f, 0.0f, 0.0f, 0.0f}, p_db = 0.0f, p_dD = 0.0f;
+  float p_db = 0.0f, p_dD = 0.0f;
   int64_t p_d = -1;  // channel of the pending outputs (-1: none)
   // partial tiles (tile_mode 1, 2) leave their per-step sums in psum instead
   const bool partial = TILED && (a.tile_mode == 1 || a.tile_mode == 2);
@@ -979,15 +983,24 @@ scan_bwd_main_kernel(const BwdArgs a) {
         }
       }
     }
-    if (last) {
+  };
+  // The per-channel sums of group gp (dA, ddelta_bias, dD), gathered in LDS
+  // buffer bp, go out as contiguous runs of atomic adds: wave w adds channel
+  // w's dA over the tile's states; waves 0 and 1 add the group's four
+  // ddelta_bias and four dD, each summed over the four waves' parts.  (One
+  // atomic per lane and state, scattered over the channels, counted 32 bytes
+  // of memory writes each.)
+  auto issue_sums = [&](int64_t gp, int bp) {
+    const int64_t dp = gp * CPG + wave;
+    if (dp < a.dim && lane < nt) unsafeAtomicAdd(&a.dA[dp * N + n0 + lane], sGdA[bp][wave][lane]);
+    if (!partial && wave < 2 && lane < CPG) {
+      const int64_t dc = gp * CPG + lane;
+      float* dst = wave ? a.dD : a.ddelta_bias;
+      if (dst && dc < a.dim) {
+        float v = 0.0f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int n = wave + NW * j;
-        if (n < nt) unsafeAtomicAdd(&a.dA[p_d * N + n0 + n], p_dA[j]);
-      }
-      if (!partial) {
-        if (a.ddelta_bias) unsafeAtomicAdd(&a.ddelta_bias[p_d], p_db);
-        if (a.dD) unsafeAtomicAdd(&a.dD[p_d], p_dD);
+        for (int ww = 0; ww < NW; ++ww) v += sGbD[bp][wave][ww][lane];
+        unsafeAtomicAdd(&dst[dc], v);
       }
     }
   };
@@ -1027,6 +1040,8 @@ scan_bwd_main_kernel(const BwdArgs a) {
       *reinterpret_cast<float2*>(sPrep + (2 * 64 + lane) * SP + s0) = dyp;
     }
     __syncthreads();  // every wave's steps are in; the previous group's sums are read
+    if (g > g_begin) issue_sums(g - 1, (int)((g - 1) & 1));
+    const int gbuf = (int)(g & 1);
     // lb[i] (delta*B rule): sum over this wave's states of lambda_t B_t, from
     // which du and the input's part of ddelta follow once per step
     float dt[K], uu[K], w[K], dyc[K], yc[K], ddt[K], du[K], lb[K];
@@ -1143,7 +1158,7 @@ scan_bwd_main_kernel(const BwdArgs a) {
           mu = mun;
         }
         dAacc = row_sum16(dAacc);
-        p_dA[j] = dAacc;
+        if (last) sGdA[gbuf][row][n] = dAacc;
         if (ci == 0 && first && dvalid && a.dh0) a.dh0[ch * N + n0 + n] = mu;
       }
     }
@@ -1211,10 +1226,16 @@ scan_bwd_main_kernel(const BwdArgs a) {
       }
       p_db = row_sum16(dbacc);
       p_dD = row_sum16(dDacc);
+      if (last) {
+        sGbD[gbuf][0][wave][row] = p_db;
+        sGbD[gbuf][1][wave][row] = p_dD;
+      }
       p_d = d;
     }
   }
   flush();
+  __syncthreads();  // the last group's sums are in LDS
+  if (g_begin < g_end) issue_sums(g_end - 1, (int)((g_end - 1) & 1));
   // ---- this chunk's dB and dC from every channel the block visited
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
