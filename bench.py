@@ -411,10 +411,20 @@ def bench_lti(ssm, torch, dev, steps, warmup):
     ms_k = timed(lambda: ssm.ssm_lti_kernel(Ad, Bd, Cd, sd, w.seqlen, K=K))
     ms_d = timed(lambda: ssm.ssm_lti_conv(K, u, D=Dd, y=y))
     ms_f = timed(lambda: ssm.ssm_lti_conv(K, u, D=Dd, y=y, method="fft"))
+    # a longer sequence at the same batch and dim: the four-step transforms
+    # through the workspace (L 8192, M 16384 = 128 x 128 points)
+    Ll = 4 * w.seqlen
+    Kl = ssm.ssm_lti_kernel(Ad, Bd, Cd, sd, Ll)
+    ul = torch.randn((w.batch, w.dim, Ll), generator=torch.Generator().manual_seed(w.seed + 1)
+                     ).to(torch.bfloat16).to(dev)
+    yl = torch.empty_like(ul)
+    wsl = torch.empty(ssm.ssm_lti_conv_fft_workspace_size(w.dim, Ll), dtype=torch.uint8, device=dev)
+    ms_fl = timed(lambda: ssm.ssm_lti_conv(Kl, ul, D=Dd, y=yl, method="fft", workspace=wsl))
     return {"workload": f"LTI path: batch {w.batch}, dim {w.dim}, N {w.dstate}, L {w.seqlen}, "
                         "bf16 u and y",
             "kernel_ms": round(ms_k, 4), "conv_direct_ms": round(ms_d, 4),
-            "conv_fft_ms": round(ms_f, 4), "steps": steps}
+            "conv_fft_ms": round(ms_f, 4), "conv_fft_long_L": Ll,
+            "conv_fft_long_ms": round(ms_fl, 4), "steps": steps}
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0
@@ -627,7 +637,8 @@ def main(argv=None):
     if not args.no_lti:
         out["lti"] = bench_lti(ssm, torch, dev, 5, 1)
         print(f"[bench] lti: kernel {out['lti']['kernel_ms']} ms, conv direct "
-              f"{out['lti']['conv_direct_ms']} ms, fft {out['lti']['conv_fft_ms']} ms",
+              f"{out['lti']['conv_direct_ms']} ms, fft {out['lti']['conv_fft_ms']} ms, fft at L "
+              f"{out['lti']['conv_fft_long_L']} {out['lti']['conv_fft_long_ms']} ms",
               file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, x)

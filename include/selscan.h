@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 2
+#define SSM_ABI_VERSION 3
 
 typedef enum { SSM_DTYPE_F32 = 0, SSM_DTYPE_BF16 = 1 } ssm_dtype;
 
@@ -339,11 +339,21 @@ int ssm_lti_conv(const float* K, const void* u, const float* Dskip, void* y, int
  * "Recurrence and convolution": the precomputed kernel applied with an FFT in
  * O(L log L)): per channel, K and each sequence are zero-padded to a power of
  * two M >= 2 seqlen - 1, transformed, multiplied and transformed back, in
- * float32.  Arguments as for ssm_lti_conv; seqlen at most 4096
- * (SSM_E_UNSUPPORTED beyond: the direct sum takes any length).
+ * float32.  Arguments as for ssm_lti_conv, plus a workspace: up to seqlen
+ * 4096 the transforms stay in on-chip memory and workspace may be NULL; from
+ * 4097 to 2^20 they go through workspace, at least
+ * ssm_lti_conv_fft_workspace_size(dim, seqlen) bytes of device memory,
+ * 16-byte aligned, owned by the caller, not overlapping any argument (calls
+ * sharing it must not run concurrently).  seqlen beyond 2^20:
+ * SSM_E_UNSUPPORTED (the direct sum takes any length).
  */
-int ssm_lti_conv_fft(const float* K, const void* u, const float* Dskip, void* y, int64_t batch,
-                     int64_t dim, int64_t seqlen, int io_dtype, void* hip_stream);
+int ssm_lti_conv_fft(const float* K, const void* u, const float* Dskip, void* y, void* workspace,
+                     int64_t workspace_bytes, int64_t batch, int64_t dim, int64_t seqlen,
+                     int io_dtype, void* hip_stream);
+
+/* Bytes of workspace ssm_lti_conv_fft needs: 0 up to seqlen 4096, -1 if an
+ * extent is out of range. */
+int64_t ssm_lti_conv_fft_workspace_size(int64_t dim, int64_t seqlen);
 
 /* Static description of a status code (never NULL). */
 const char* ssm_status_str(int status);

@@ -50,7 +50,8 @@ from ._lib import (SSM_BBAR_DELTA_B, SSM_BBAR_ZOH_EXACT, SSM_DTYPE_BF16, SSM_DTY
                    SelscanError, library_path, lib, ssm_abi_version, ssm_last_error,
                    ssm_status_str)
 from .binding import (ssm_causal_conv1d_bwd, ssm_causal_conv1d_fwd, ssm_causal_conv1d_update,
-                      ssm_checkpoint_shape, ssm_lti_conv, ssm_lti_kernel,
+                      ssm_checkpoint_shape, ssm_lti_conv, ssm_lti_conv_fft_workspace_size,
+                      ssm_lti_kernel,
                       ssm_selective_scan_bwd, ssm_ssd_fwd, ssm_ssd_fwd_noalloc,
                       ssm_ssd_scratch_bytes, ssm_ssd_workspace_size,
                       ssm_selective_scan_bwd_workspace_size, ssm_selective_scan_fwd,
@@ -58,6 +59,7 @@ from .binding import (ssm_causal_conv1d_bwd, ssm_causal_conv1d_fwd, ssm_causal_c
 
 __all__ = [
     "ssm_selective_scan_fwd", "ssm_state_update", "ssm_lti_kernel", "ssm_lti_conv",
+    "ssm_lti_conv_fft_workspace_size",
     "ssm_selective_scan_bwd", "ssm_checkpoint_shape", "selective_scan_fn", "causal_conv1d_fn",
     "ssm_selective_scan_bwd_workspace_size", "ssm_causal_conv1d_fwd", "ssm_causal_conv1d_update",
     "ssm_causal_conv1d_bwd", "ssm_ssd_fwd", "ssm_ssd_workspace_size", "ssm_ssd_fwd_noalloc",

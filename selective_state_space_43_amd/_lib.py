@@ -7,7 +7,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SO = os.path.join(_HERE, "libselscan.so")
 
-ABI_VERSION = 2  # the SSM_ABI_VERSION these signatures follow
+ABI_VERSION = 3  # the SSM_ABI_VERSION these signatures follow
 SSM_DTYPE_F32, SSM_DTYPE_BF16 = 0, 1
 SSM_BBAR_DELTA_B, SSM_BBAR_ZOH_EXACT, SSM_DISC_EULER, SSM_DISC_BILINEAR = 0, 1, 2, 3
 STATUS_NAMES = {0: "SSM_OK", 1: "SSM_E_NULL", 2: "SSM_E_SHAPE", 3: "SSM_E_DTYPE",
@@ -55,7 +55,9 @@ def lib() -> ctypes.CDLL:
         L.ssm_ssd_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, i64,
                                   i64, i64, i64, i64, i64, i64, i32, vp]
         L.ssm_lti_conv.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, vp]
-        L.ssm_lti_conv_fft.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, vp]
+        L.ssm_lti_conv_fft.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp]
+        L.ssm_lti_conv_fft_workspace_size.argtypes = [i64, i64]
+        L.ssm_lti_conv_fft_workspace_size.restype = i64
         L.ssm_ssd_workspace_size.argtypes = [i64, i64, i64, i64]
         L.ssm_ssd_workspace_size.restype = i64
         L.ssm_ssd_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp,

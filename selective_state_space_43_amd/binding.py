@@ -155,9 +155,19 @@ def ssm_lti_kernel(A, Bv, Cv, delta, L, bbar="delta", K=None):
     return K
 
 
-def ssm_lti_conv(K, u, D=None, y=None, method="direct"):
+def ssm_lti_conv_fft_workspace_size(dim, seqlen):
+    """Bytes of workspace the FFT convolution needs (0 up to seqlen 4096)."""
+    n = lib().ssm_lti_conv_fft_workspace_size(dim, seqlen)
+    if n < 0:
+        raise ValueError("extents out of range")
+    return int(n)
+
+
+def ssm_lti_conv(K, u, D=None, y=None, method="direct", workspace=None):
     """y = K * u + D u per channel (causal): K [dim, L] float32, u [batch, dim, L].
-    method "direct" (the causal sum, any L) or "fft" (L up to 4096)."""
+    method "direct" (the causal sum, any L) or "fft" (L up to 2^20; past 4096
+    through a workspace of ssm_lti_conv_fft_workspace_size bytes, allocated
+    here unless given)."""
     if method not in ("direct", "fft"):
         raise ValueError(f"method {method!r}: expected 'direct' or 'fft'")
     _dev(u, "u", None)
@@ -171,9 +181,17 @@ def ssm_lti_conv(K, u, D=None, y=None, method="direct"):
         y = torch.empty_like(u)
     else:
         _io(y, "y", u.dtype, (batch, dim, L), dev)
-    fn = lib().ssm_lti_conv_fft if method == "fft" else lib().ssm_lti_conv
     with torch.cuda.device(dev):
-        st = fn(_ptr(K), _ptr(u), _ptr(D), _ptr(y), batch, dim, L, _IO[u.dtype], _stream(dev))
+        if method == "fft":
+            need = int(lib().ssm_lti_conv_fft_workspace_size(dim, L))  # -1: the call reports why
+            if workspace is None and need > 0:
+                workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+            nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+            st = lib().ssm_lti_conv_fft(_ptr(K), _ptr(u), _ptr(D), _ptr(y), _ptr(workspace), nbytes,
+                                        batch, dim, L, _IO[u.dtype], _stream(dev))
+        else:
+            st = lib().ssm_lti_conv(_ptr(K), _ptr(u), _ptr(D), _ptr(y), batch, dim, L,
+                                    _IO[u.dtype], _stream(dev))
     check(st, "ssm_lti_conv_fft" if method == "fft" else "ssm_lti_conv")
     return y
 

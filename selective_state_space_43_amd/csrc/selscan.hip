@@ -2502,6 +2502,221 @@ lti_conv_fft_kernel(const float* K, const void* u,
   }
 }
 
+// ---------------------------------------------------------------- LTI convolution by FFT, long sequences
+//
+// Past seqlen 4096 the transforms (M >= 2 seqlen - 1 points) no longer fit in
+// LDS, and one workgroup per channel computes them in four steps through a
+// workspace in HBM: with M = R x C (R <= 256, C <= 8192) and the padded
+// signal x read as an R x C matrix, x[r C + c],
+//
+//   X[kr + R kc] = sum_c W_C^{c kc} [ W_M^{c kr} sum_r W_R^{r kr} x[r C + c] ]
+//
+// (column DFTs of length R, a twiddle, row DFTs of length C; W_N =
+// exp(-2 pi i / N)).  The spectrum stays in [kr][kc] order: the kernel's and
+// the signal's are multiplied element by element in that order, and the
+// inverse takes the same steps backwards (row DFTs, the conjugate twiddle,
+// column DFTs; each inverse DFT as the conjugate of the forward DFT of the
+// conjugate), which returns natural order.  Every pass works on blocks of
+// 8192 points in LDS (CB columns of R points, or RB rows of C points) with
+// the batched radix-16 Stockham passes below; as in the in-LDS path the
+// sequences go two at a time, as the real and imaginary parts of one signal.
+
+// One radix-R Stockham pass over NB transforms of LEN points in LDS buffer s
+// (index i at s[i + i / 16]), in place: every thread reads its butterflies'
+// points, the block waits, then writes their results.
+template <int R, int LEN, int NB>
+__device__ __forceinline__ void fft_pass_lds(float2* s, int Ns) {
+  constexpr int BPT = LEN / R;      // butterflies per transform
+  constexpr int NBF = NB * BPT;
+  constexpr int IT = (NBF + 255) / 256;
+  float2 v[IT][R];
+  int base[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int j = (int)threadIdx.x + 256 * it;
+    if (NBF % 256 == 0 || j < NBF) {
+      const int t = j / BPT, jj = j % BPT, k = jj & (Ns - 1);
+#pragma unroll
+      for (int q = 0; q < R; ++q) {
+        const int i = t * LEN + jj + q * BPT;
+        v[it][q] = s[i + (i >> 4)];
+      }
+      if (Ns > 1) {
+        float sn, cs;
+        sincospif(-2.0f * (float)k / (float)(Ns * R), &sn, &cs);
+        const float2 w = make_float2(cs, sn);
+        float2 wq = w;
+#pragma unroll
+        for (int q = 1; q < R; ++q) {
+          v[it][q] = cmul(v[it][q], wq);
+          if (q + 1 < R) wq = cmul(wq, w);
+        }
+      }
+      dft_reg<R>(v[it]);
+      base[it] = t * LEN + (jj - k) * R + k;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int j = (int)threadIdx.x + 256 * it;
+    if (NBF % 256 == 0 || j < NBF) {
+#pragma unroll
+      for (int q = 0; q < R; ++q) {
+        const int i = base[it] + q * Ns;
+        s[i + (i >> 4)] = v[it][q];
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// NB forward DFTs of LEN points each, in place in LDS, natural order in and out
+template <int LEN, int NB>
+__device__ __forceinline__ void fft_lds(float2* s) {
+  constexpr int LG = LEN >= 8192 ? 13 : LEN >= 4096 ? 12 : LEN >= 2048 ? 11 : LEN >= 1024 ? 10
+                   : LEN >= 512 ? 9 : LEN >= 256 ? 8 : LEN >= 128 ? 7 : 6;
+  static_assert((1 << LG) == LEN, "LEN is a power of two, 64 .. 8192");
+  constexpr int P16 = LG / 4, REM = LG % 4;
+  int Ns = 1;
+#pragma unroll 1
+  for (int p = 0; p < P16; ++p) {
+    fft_pass_lds<16, LEN, NB>(s, Ns);
+    Ns *= 16;
+  }
+  if constexpr (REM != 0) fft_pass_lds<(1 << REM), LEN, NB>(s, Ns);
+}
+
+constexpr int kFftLongMaxLog2 = 21;  // M up to 2^21 points: seqlen up to 2^20
+
+// workspace of the long path: per channel the kernel's spectrum and one signal, M complex each
+__host__ __device__ constexpr int64_t fft_long_ws_per_channel(int lg) { return (int64_t)2 << lg; }
+
+template <typename IO, int LOG2R, int LOG2C>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+lti_conv_fft_long_kernel(const float* K, const void* u, const float* Dskip, void* y, float2* ws,
+                         int64_t batch, int64_t dim, int64_t L) {
+  constexpr int R = 1 << LOG2R, C = 1 << LOG2C;
+  constexpr int64_t M = (int64_t)R * C;
+  constexpr int PB = 8192;                       // points of an LDS block
+  constexpr int CB = PB / R < C ? PB / R : C;    // columns per column block
+  constexpr int RB = PB / C < R ? PB / C : R;    // rows per row block
+  constexpr int NPT = CB * R;                    // points of a column block
+  constexpr int NPR = RB * C;                    // points of a row block
+  __shared__ float2 s[PB + PB / 16];
+  auto P = [](int i) { return i + (i >> 4); };
+  const int64_t d = blockIdx.x;
+  float2* Ks = ws + d * fft_long_ws_per_channel(LOG2R + LOG2C);  // [kr][kc] spectrum of K
+  float2* Wk = Ks + M;                                            // work matrix
+  constexpr uint32_t ES = sizeof(IO);
+  auto ldv = [](Rsrc r, int64_t i) -> float {
+    if constexpr (ES == 2) return __uint_as_float(buf_ld16(r, (uint32_t)i * 2u, 0) << 16);
+    else return __uint_as_float(buf_ld32(r, (uint32_t)i * 4u, 0));
+  };
+  auto stv = [](Rsrc r, int64_t i, float v) {
+    if constexpr (ES == 2) buf_st16(__builtin_bit_cast(uint16_t, (__bf16)v), r, (uint32_t)i * 2u, 0);
+    else buf_st32(__float_as_uint(v), r, (uint32_t)i * 4u, 0);
+  };
+  // twiddle W_M^{e}, e = c kr < M, times v (sign -1: the conjugate)
+  auto twiddle = [](float2 v, int64_t e, float sign) {
+    float sn, cs;
+    sincospif(-2.0f * sign * (float)e / (float)M, &sn, &cs);
+    return cmul(v, make_float2(cs, sn));
+  };
+
+  // column DFTs + twiddle: x (point n read by get(n), zero at n >= L) -> Wk
+  auto column_forward = [&](auto get) {
+#pragma unroll 1
+    for (int c0 = 0; c0 < C; c0 += CB) {
+      for (int i = threadIdx.x; i < NPT; i += 256) {
+        const int r = i / CB, cc = i % CB;  // consecutive threads: consecutive columns
+        s[P(cc * R + r)] = get((int64_t)r * C + c0 + cc);
+      }
+      __syncthreads();
+      fft_lds<R, CB>(s);
+      for (int i = threadIdx.x; i < NPT; i += 256) {
+        const int kr = i / CB, cc = i % CB;
+        Wk[(int64_t)kr * C + c0 + cc] = twiddle(s[P(cc * R + kr)], (int64_t)(c0 + cc) * kr, 1.0f);
+      }
+      __syncthreads();
+    }
+  };
+
+  // the kernel's spectrum: its column pass, then row DFTs stored in Ks
+  {
+    const Rsrc rK = make_rsrc(K + d * L, L * 4);
+    column_forward([&](int64_t n) {
+      return make_float2(n < L ? __uint_as_float(buf_ld32(rK, (uint32_t)n * 4u, 0)) : 0.0f, 0.0f);
+    });
+#pragma unroll 1
+    for (int r0 = 0; r0 < R; r0 += RB) {
+      for (int i = threadIdx.x; i < NPR; i += 256) s[P(i)] = Wk[(int64_t)r0 * C + i];
+      __syncthreads();
+      fft_lds<C, RB>(s);
+      for (int i = threadIdx.x; i < NPR; i += 256) Ks[(int64_t)r0 * C + i] = s[P(i)];
+      __syncthreads();
+    }
+  }
+
+  const float Dd = Dskip ? Dskip[d] : 0.0f;
+  const float scale = 1.0f / (float)M;
+#pragma unroll 1
+  for (int64_t b = 0; b < batch; b += 2) {
+    const bool two = b + 1 < batch;
+    const int64_t row0 = (b * dim + d) * L, row1 = two ? ((b + 1) * dim + d) * L : row0;
+    const Rsrc rU0 = make_rsrc(static_cast<const char*>(u) + row0 * ES, L * ES);
+    const Rsrc rU1 = make_rsrc(static_cast<const char*>(u) + row1 * ES, two ? L * ES : 0);
+    const Rsrc rY0 = make_rsrc(static_cast<char*>(y) + row0 * ES, L * ES);
+    const Rsrc rY1 = make_rsrc(static_cast<char*>(y) + row1 * ES, two ? L * ES : 0);
+    // forward column pass of u_b + i u_{b+1} (points past L: the zero padding,
+    // read as zero through the extent L)
+    column_forward([&](int64_t n) {
+      return n < L ? make_float2(ldv(rU0, n), ldv(rU1, n)) : make_float2(0.0f, 0.0f);
+    });
+    // row DFTs, product with the kernel's spectrum, inverse row DFTs (as the
+    // conjugate of the DFT of the conjugate), conjugate twiddle
+#pragma unroll 1
+    for (int r0 = 0; r0 < R; r0 += RB) {
+      for (int i = threadIdx.x; i < NPR; i += 256) s[P(i)] = Wk[(int64_t)r0 * C + i];
+      __syncthreads();
+      fft_lds<C, RB>(s);
+      for (int i = threadIdx.x; i < NPR; i += 256) {
+        const float2 z = cmul(s[P(i)], Ks[(int64_t)r0 * C + i]);
+        s[P(i)] = make_float2(z.x, -z.y);
+      }
+      __syncthreads();
+      fft_lds<C, RB>(s);
+      for (int i = threadIdx.x; i < NPR; i += 256) {
+        const int rr = i / C, c = i % C;
+        const float2 v = s[P(i)];
+        Wk[(int64_t)r0 * C + i] = twiddle(make_float2(v.x, -v.y), (int64_t)c * (r0 + rr), -1.0f);
+      }
+      __syncthreads();
+    }
+    // inverse column DFTs; the real and imaginary parts are the two outputs
+#pragma unroll 1
+    for (int c0 = 0; c0 < C; c0 += CB) {
+      for (int i = threadIdx.x; i < NPT; i += 256) {
+        const int kr = i / CB, cc = i % CB;
+        const float2 v = Wk[(int64_t)kr * C + c0 + cc];
+        s[P(cc * R + kr)] = make_float2(v.x, -v.y);
+      }
+      __syncthreads();
+      fft_lds<R, CB>(s);
+      for (int i = threadIdx.x; i < NPT; i += 256) {
+        const int r = i / CB, cc = i % CB;
+        const int64_t n = (int64_t)r * C + c0 + cc;
+        if (n < L) {
+          const float2 v = s[P(cc * R + r)];  // conj of the result: (v.x, -v.y)
+          stv(rY0, n, fmaf(Dd, ldv(rU0, n), v.x * scale));
+          stv(rY1, n, fmaf(Dd, ldv(rU1, n), -v.y * scale));
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
 // ---------------------------------------------------------------- host side
 
 thread_local char g_last_error[512] = "";
@@ -3430,8 +3645,18 @@ int ssm_lti_conv(const float* K, const void* u, const float* Dskip, void* y, int
   return launch_status("ssm_lti_conv launch");
 }
 
-int ssm_lti_conv_fft(const float* K, const void* u, const float* Dskip, void* y, int64_t batch,
-                     int64_t dim, int64_t seqlen, int io_dtype, void* hip_stream) {
+int64_t ssm_lti_conv_fft_workspace_size(int64_t dim, int64_t seqlen) {
+  if (dim <= 0 || seqlen <= 0 || dim > ((int64_t)1 << 30)) return -1;
+  int lg = kFftMinLog2;
+  while ((int64_t(1) << lg) < 2 * seqlen - 1) ++lg;
+  if (lg <= kFftMaxLog2) return 0;
+  if (lg > kFftLongMaxLog2) return -1;
+  return dim * fft_long_ws_per_channel(lg) * (int64_t)sizeof(float2);
+}
+
+int ssm_lti_conv_fft(const float* K, const void* u, const float* Dskip, void* y, void* workspace,
+                     int64_t workspace_bytes, int64_t batch, int64_t dim, int64_t seqlen,
+                     int io_dtype, void* hip_stream) {
   g_last_error[0] = 0;
   if (!K) return fail(SSM_E_NULL, "K is NULL");
   if (!u) return fail(SSM_E_NULL, "u is NULL");
@@ -3446,15 +3671,30 @@ int ssm_lti_conv_fft(const float* K, const void* u, const float* Dskip, void* y,
     return fail(SSM_E_DTYPE, "io_dtype = %d is not SSM_DTYPE_F32 or SSM_DTYPE_BF16", io_dtype);
   int lg = kFftMinLog2;
   while ((int64_t(1) << lg) < 2 * seqlen - 1) ++lg;
-  if (lg > kFftMaxLog2)
+  if (lg > kFftLongMaxLog2)
     return fail(SSM_E_UNSUPPORTED, "seqlen = %lld: the FFT path takes seqlen up to %d",
-                (long long)seqlen, 1 << (kFftMaxLog2 - 1));
+                (long long)seqlen, 1 << (kFftLongMaxLog2 - 1));
+  const bool long_path = lg > kFftMaxLog2;
+  const int64_t ws_need = long_path ? dim * fft_long_ws_per_channel(lg) * (int64_t)sizeof(float2) : 0;
+  if (long_path) {
+    if (!workspace)
+      return fail(SSM_E_NULL, "workspace is NULL: seqlen = %lld needs %lld bytes of it",
+                  (long long)seqlen, (long long)ws_need);
+    if (workspace_bytes < ws_need)
+      return fail(SSM_E_SHAPE, "workspace holds %lld bytes, needs %lld", (long long)workspace_bytes,
+                  (long long)ws_need);
+    if (!aligned16(workspace)) return fail(SSM_E_ALIGN, "workspace is not 16-byte aligned");
+  }
   const int64_t es = io_dtype == SSM_DTYPE_BF16 ? 2 : 4;
   const Span ys{y, batch * dim * seqlen * es, "y"};
+  const Span ws{long_path ? workspace : nullptr, ws_need, "workspace"};
   const Span in[] = {{K, dim * seqlen * 4, "K"}, {u, batch * dim * seqlen * es, "u"},
                      {Dskip, dim * 4, "D"}};
-  for (const Span& s : in)
+  for (const Span& s : in) {
     if (overlaps(ys, s)) return fail(SSM_E_ALIAS, "y overlaps %s", s.name);
+    if (overlaps(ws, s)) return fail(SSM_E_ALIAS, "workspace overlaps %s", s.name);
+  }
+  if (overlaps(ws, ys)) return fail(SSM_E_ALIAS, "workspace overlaps y");
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   const bool bf = io_dtype == SSM_DTYPE_BF16;
   auto go = [&](auto lg_tag) {
@@ -3466,13 +3706,33 @@ int ssm_lti_conv_fft(const float* K, const void* u, const float* Dskip, void* y,
       hipLaunchKernelGGL((lti_conv_fft_kernel<float, LG>), dim3((unsigned)dim), dim3(256), 0, s,
                          K, u, Dskip, y, batch, dim, seqlen);
   };
+  // long path: M = R x C with R = 2^min(8, lg / 2), C = M / R <= 8192
+  auto go_long = [&](auto lg_tag) {
+    constexpr int LG = decltype(lg_tag)::value;
+    constexpr int LR = LG / 2 < 8 ? LG / 2 : 8, LC = LG - LR;
+    float2* w = static_cast<float2*>(workspace);
+    if (bf)
+      hipLaunchKernelGGL((lti_conv_fft_long_kernel<uint16_t, LR, LC>), dim3((unsigned)dim), dim3(256),
+                         0, s, K, u, Dskip, y, w, batch, dim, seqlen);
+    else
+      hipLaunchKernelGGL((lti_conv_fft_long_kernel<float, LR, LC>), dim3((unsigned)dim), dim3(256),
+                         0, s, K, u, Dskip, y, w, batch, dim, seqlen);
+  };
   switch (lg) {
     case 8: go(std::integral_constant<int, 8>{}); break;
     case 9: go(std::integral_constant<int, 9>{}); break;
     case 10: go(std::integral_constant<int, 10>{}); break;
     case 11: go(std::integral_constant<int, 11>{}); break;
     case 12: go(std::integral_constant<int, 12>{}); break;
-    default: go(std::integral_constant<int, 13>{}); break;
+    case 13: go(std::integral_constant<int, 13>{}); break;
+    case 14: go_long(std::integral_constant<int, 14>{}); break;
+    case 15: go_long(std::integral_constant<int, 15>{}); break;
+    case 16: go_long(std::integral_constant<int, 16>{}); break;
+    case 17: go_long(std::integral_constant<int, 17>{}); break;
+    case 18: go_long(std::integral_constant<int, 18>{}); break;
+    case 19: go_long(std::integral_constant<int, 19>{}); break;
+    case 20: go_long(std::integral_constant<int, 20>{}); break;
+    default: go_long(std::integral_constant<int, 21>{}); break;
   }
   return launch_status("ssm_lti_conv_fft launch");
 }

@@ -366,9 +366,67 @@ def test_lti_conv_fft_matches_oracle(ssm, dev, dt, L):
     assert worst <= TOL[dt]
 
 
-def test_lti_conv_fft_rejects_long_sequences(ssm, dev):
-    K = torch.zeros((1, 4097), dtype=torch.float32, device=dev)
-    u = torch.zeros((1, 1, 4097), dtype=torch.float32, device=dev)
+@pytest.mark.parametrize("dt,L", [("f32", 4097), ("bf16", 8192), ("f32", 16385), ("f32", 65536)])
+def test_lti_conv_fft_long_matches_oracle(ssm, dev, dt, L):
+    """Past 4096 steps the FFT goes through the workspace in four steps
+    (M = 16384 .. 131072: R x C = 128 x 128, 256 x 256, 256 x 512): one pair
+    of sequences on two channels against the oracle's direct causal sum."""
+    r = np.random.default_rng(200 + L)
+    batch, dim, N = 2, 2, 16
+    A = -np.exp(r.uniform(np.log(0.5), np.log(16), (dim, N)))
+    Bv, Cv = r.standard_normal((dim, N)), r.standard_normal((dim, N))
+    step = r.uniform(0.001, 0.02, dim)  # small steps: the kernel spans the whole sequence
+    K = oracle.lti_kernel(A, Bv, Cv, step, L, bbar="zoh").astype(np.float32)
+    Dv = r.standard_normal(dim).astype(np.float32)
+    u = r.standard_normal((batch, dim, L)).astype(np.float32)
+    if dt == "bf16":
+        u = wl.to_bf16_bits(u)
+    y = ssm.ssm_lti_conv(to_dev(K, dev), to_dev(u, dev), D=to_dev(Dv, dev), method="fft")
+    torch.cuda.synchronize()
+    uf = wl.bf16_bits_to_f32(u) if dt == "bf16" else u
+    worst = 0.0
+    for b in range(batch):
+        for d in range(dim):
+            yc = oracle.causal_conv(K[d].astype(np.float64), uf[b, d].astype(np.float64),
+                                    float(Dv[d]))
+            worst = max(worst, norm_err(to_np(y[b, d]), yc))
+    print(f"fft L={L} {dt}: {worst:.2e}", flush=True)
+    assert worst <= TOL[dt]
+
+
+def test_lti_conv_fft_longest_by_impulses(ssm, dev):
+    """The longest sequence the FFT path takes (L = 2^20, M = 2^21 = 256 x
+    8192) on inputs whose exact result is known at every step: a sum of a few
+    scaled impulses gives y = sum_j a_j K[t - t_j] + D u (superposition of
+    shifted kernels), computed by the oracle's arithmetic in float64 here."""
+    L = 1 << 20
+    r = np.random.default_rng(300)
+    dim, N = 2, 16
+    A = -np.exp(r.uniform(np.log(0.5), np.log(16), (dim, N)))
+    Bv, Cv = r.standard_normal((dim, N)), r.standard_normal((dim, N))
+    step = r.uniform(1e-5, 1e-4, dim)
+    K = oracle.lti_kernel(A, Bv, Cv, step, L, bbar="zoh").astype(np.float32)
+    Dv = r.standard_normal(dim).astype(np.float32)
+    u = np.zeros((2, dim, L), dtype=np.float32)
+    spikes = [(0, 1.5), (12345, -0.75), (L // 2, 2.0), (L - 3, 1.0)]
+    for t, a in spikes:
+        u[0, :, t] = a
+        u[1, :, L - 1 - t] = -a
+    y = ssm.ssm_lti_conv(to_dev(K, dev), to_dev(u, dev), D=to_dev(Dv, dev), method="fft")
+    torch.cuda.synchronize()
+    for b in range(2):
+        for d in range(dim):
+            ref = Dv[d].astype(np.float64) * u[b, d].astype(np.float64)
+            for t in np.nonzero(u[b, d])[0]:
+                ref[t:] += float(u[b, d, t]) * K[d, :L - t].astype(np.float64)
+            err = norm_err(to_np(y[b, d]), ref)
+            assert err <= TOL["f32"], (b, d, err)
+
+
+def test_lti_conv_fft_rejects_longer_sequences(ssm, dev):
+    L = (1 << 20) + 1
+    K = torch.zeros((1, L), dtype=torch.float32, device=dev)
+    u = torch.zeros((1, 1, L), dtype=torch.float32, device=dev)
     with pytest.raises(ssm.SelscanError, match="SSM_E_UNSUPPORTED"):
         ssm.ssm_lti_conv(K, u, method="fft")
 
