@@ -54,7 +54,7 @@ SCAN_SOURCE_END = b"// ---------------------------------------------------------
 
 def kernel_source_hash() -> str:
     """Hash of the forward scan's source: selscan.hip up to the backward
-    section (the helpers and scan_fwd_kernel); later kernels do not change
+    section (the helpers and both forward kernels); later kernels do not change
     the scan's traffic."""
     with open(KERNEL_SRC, "rb") as f:
         src = f.read()
@@ -577,7 +577,7 @@ def main(argv=None):
             "delta_bias": w.bias, "bbar": "delta*B", "parallelism": "single GPU",
         },
         "roofline": {
-            "kernel": "scan_fwd_kernel",
+            "kernel": "scan_fwd_pipe_kernel",
             "bound": "hbm",
             "achieved": round(hbm_gbps, 1),
             "peak": HBM_PEAK_GBPS,

@@ -23,6 +23,11 @@
 //    readout C_t . h_t.  The expanded state never leaves registers.
 //  * The chunk carry lives in LDS ([channels of the block][dstate]), so dstate
 //    is a runtime value.  Step size, softplus, D skip and silu gate are fused.
+//  * With 16 states, bf16 rows and many channels a second forward kernel runs
+//    the recurrence in time order inside each lane instead (no fold, scan or
+//    replay): lanes hold channels and states, the four waves of a workgroup
+//    hold consecutive time segments and hand their states on through LDS
+//    (scan_fwd_pipe_kernel below).
 //  * Everything is float32; bf16 inputs are widened exactly, y is rounded to
 //    bf16 with round-to-nearest-even (v_cvt_pk_bf16_f32).
 #include <hip/hip_runtime.h>
@@ -45,6 +50,11 @@
 #endif
 #ifndef SELSCAN_NT
 #define SELSCAN_NT 16  // states staged per LDS tile (16 lanes per channel)
+#endif
+#ifndef SELSCAN_PIPE_MIN_CHANNELS
+// launches with 16 states and at least this many channels use the
+// time-pipelined forward (one workgroup of four waves per 16 channels)
+#define SELSCAN_PIPE_MIN_CHANNELS 8192
 #endif
 #ifndef SELSCAN_WAVES_PER_EU
 // occupancy the register allocator must keep with 16 lanes per channel, for
@@ -154,6 +164,34 @@ struct Io<uint16_t> {  // bf16 bit patterns
     *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p) + i) = w;
   }
 };
+
+// Raw buffer accesses: a 32-bit byte offset from a base whose extent is
+// given, and reads past the extent return zero, so addresses need no clamps.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_ld128(Rsrc r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ uint2 buf_ld64(Rsrc r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+__device__ __forceinline__ uint32_t buf_ld16(Rsrc r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
+__device__ __forceinline__ void buf_st64(uint2 v, Rsrc r, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int, v), r, voff, soff, 0);
+}
+__device__ __forceinline__ void buf_st16(uint32_t v, Rsrc r, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v, r, voff, soff, 0);
+}
+__device__ __forceinline__ uint32_t buf_ld32(Rsrc r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+__device__ __forceinline__ void buf_st32(uint32_t v, Rsrc r, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, voff, soff, 0);
+}
 
 // ---------------------------------------------------------------- cross-lane
 
@@ -564,6 +602,356 @@ __global__ void __launch_bounds__(64 * W)
     // each channel's carry was written by its own wave; LDS is in order per wave
     for (int64_t n = seg; n < N; n += LPC)
       a.final_state[(b * a.dim + d) * N + n] = carry_row[n];
+  }
+}
+
+// ---------------------------------------------------------------- forward scan, time-pipelined (16 states)
+
+// Four consecutive bf16 elements of a row (one lane's steps), packed.
+struct Quad {
+  uint2 v;
+  __device__ float at(int i) const {
+    const uint32_t w = i < 2 ? v.x : v.y;
+    return (i & 1) ? bf_hi(w) : bf_lo(w);
+  }
+};
+
+// A quad of a row read through a buffer resource at byte offset voff + soff;
+// only its first n elements are read (n <= 0: none), the rest are zero.  VEC:
+// one aligned 8-byte load (L is a multiple of 8 and a quad starts at a
+// multiple of 4, so it lies wholly before the row's end or wholly past it).
+template <bool VEC>
+__device__ __forceinline__ void quad_load(Quad& q, Rsrc rs, uint32_t voff, uint32_t soff, int n) {
+  if (VEC) {
+    q.v = n >= 4 ? buf_ld64(rs, voff, soff) : make_uint2(0u, 0u);
+  } else {
+    uint32_t e[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) e[i] = i < n ? buf_ld16(rs, voff + 2 * i, soff) : 0u;
+    q.v = make_uint2(e[0] | (e[1] << 16), e[2] | (e[3] << 16));
+  }
+}
+
+// Makes the compiler treat a loaded quad as unknown until this point, so the
+// wait for its load stays here instead of moving up to the load.
+__device__ __forceinline__ void opaque(Quad& q) { asm volatile("" : "+v"(q.v.x), "+v"(q.v.y)); }
+
+// Orders this lane's LDS accesses before and after it for the compiler; the
+// hardware already runs one wave's LDS instructions in order, so this is what
+// lanes of one wave need to exchange data through LDS.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Forward scan for 16 states and bf16 rows in which every lane runs the
+// recurrence in time order over its own steps, with no fold, scan or replay:
+// each element costs its discretization, one state fma and one readout fma
+// (the recurrent form, "State-space models", section "Recurrence and
+// convolution"), against one more fma plus the scan for the kernel above.
+//
+// A workgroup holds 16 channels of one sequence and four waves; wave s owns
+// time segment s (16 steps) of every 64-step chunk.  In a wave, lane 16 r + c
+// holds channel c and the states n = 4 j + r, one after another (j = 0..3:
+// four "items" per chunk).  The waves form a ring over time: wave s runs item
+// (chunk t, j) from the state that wave s - 1 handed over for the same item
+// (for s = 0: wave 3, chunk t - 1) through an LDS slot, and counts its handed
+// items in LDS; a wave waits only for its predecessor's count (a bounded
+// spin), so the four segments of a chunk run concurrently, each one item
+// behind the other.  Each chunk's B and C rows of a segment are staged by the
+// wave that uses them.
+//
+// Per-step work (softplus step size, u weight, D u, gate) is done once per
+// (channel, step): lane (r, c) prepares steps 4 r .. 4 r + 3 of its channel's
+// segment of the next chunk during the items of this one, and the wave shares
+// them through LDS.  Each lane's readout sums over its own 4 states; after
+// the last item of a chunk the 4 rows are added through LDS, and lane (r, c)
+// finishes and stores steps 4 r .. 4 r + 3.
+//
+// Registers are held to 96 (five waves per SIMD: 20480 channels give exactly
+// five workgroups per CU) and LDS to 31 KiB per workgroup.
+
+// Which of the next chunk's 4 steps each item of the pipelined forward
+// prepares: item j does steps [kPipePrep[j], kPipePrep[j + 1]) (the first
+// item stages B and C, the last finishes the chunk).
+#ifndef SELSCAN_PIPE_PREP
+#define SELSCAN_PIPE_PREP 0, 0, 2, 4, 4
+#endif
+constexpr int kPipePrep[5] = {SELSCAN_PIPE_PREP};
+
+template <bool VEC, int RULE, bool GATE>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5)))
+    scan_fwd_pipe_kernel(const ScanArgs a) {
+  using IO = uint16_t;
+  static_assert(RULE != kRuleZoh, "exact ZOH needs more registers than five waves per SIMD leave");
+  constexpr int W = 4;      // waves = time segments of a chunk
+  constexpr int K = 16;     // steps per segment
+  constexpr int T = W * K;  // steps per chunk
+  constexpr int NS = 16;    // states
+  constexpr int KP = K + 4; // padded LDS rows (spreads banks)
+  static_assert(kCkptT % T == 0, "checkpoint blocks are whole chunks");
+  // per wave: the B and C rows of its segment, [2][NS][KP]; at the end of a
+  // chunk, the readout partial sums [4 step quads][64 lanes][4]
+  __shared__ float4 sWave[W][256];
+  // per wave: step sizes and u weights of its segment, [2][16 channels][KP]
+  __shared__ float4 sPrep[W][2 * 16 * KP / 4];
+  // state handed from wave s to wave s + 1, [s][j][lane] for the states
+  // n = 4 j + r of lane 16 r + c (the ring's dependences keep a slot from
+  // being rewritten before it is read; wave 3's slots start with the initial
+  // state), and the number of items each wave has handed over
+  __shared__ float sCarry[W][4][64];
+  __shared__ int sDone[W];
+  // A as [j][lane]
+  __shared__ float sA[4][64];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane >> 4, cl = lane & 15;
+  const int64_t b = blockIdx.y;
+  const int64_t d0 = (int64_t)blockIdx.x * 16;
+  const int64_t d = d0 + cl;
+  // lanes of a channel past `dim` compute on channel d0 and store nothing
+  const bool dvalid = d < a.dim;
+  const int64_t dc = dvalid ? d : d0;
+  const int64_t L = a.seqlen;
+  const int64_t nchunks = (L + T - 1) / T;
+  float* tile = reinterpret_cast<float*>(sWave[wave]);
+  float* prep = reinterpret_cast<float*>(sPrep[wave]);
+  const int seg0 = K * wave;  // first step of this wave's segment in a chunk
+  // Buffer resources over the rows of the workgroup's channels and of the
+  // sequence's B and C (the launcher checks that 16 L elements span less
+  // than 2^31 bytes): a lane adds its own byte offset, the chunk a uniform
+  // one.  Reads past a row's end within the last chunk are masked per lane.
+  constexpr int ES = sizeof(IO);
+  const int64_t seq_base = (b * a.dim + d0) * L;
+  const int64_t nrows = a.dim - d0 < 16 ? a.dim - d0 : 16;
+  const int seq_bytes = (int)(nrows * L * ES);
+  const Rsrc u_r = make_rsrc(static_cast<const IO*>(a.u) + seq_base, seq_bytes);
+  const Rsrc dl_r = make_rsrc(static_cast<const IO*>(a.delta) + seq_base, seq_bytes);
+  const Rsrc z_r = make_rsrc(GATE ? static_cast<const IO*>(a.z) + seq_base : nullptr, GATE ? seq_bytes : 0);
+  const Rsrc y_r = make_rsrc(static_cast<IO*>(a.y) + seq_base, seq_bytes);
+  const int bc_bytes = (int)(NS * L * ES);
+  const Rsrc B_r = make_rsrc(static_cast<const IO*>(a.Bm) + b * NS * L, bc_bytes);
+  const Rsrc C_r = make_rsrc(static_cast<const IO*>(a.Cm) + b * NS * L, bc_bytes);
+  const int qstep = seg0 + 4 * r;  // first step of this lane's quad in a chunk
+  const uint32_t seq_off = (uint32_t)(((dc - d0) * L + qstep) * ES);
+  const int st_n = lane >> 2, st_q = lane & 3;  // staging role: state, step quad
+  const int bstep = seg0 + 4 * st_q;
+  const uint32_t bc_off = (uint32_t)((st_n * L + bstep) * ES);
+
+  if (wave == 0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sA[j][lane] = a.A[dc * NS + 4 * j + r];
+  }
+  const float Dv = (a.Dskip && dvalid) ? a.Dskip[d] : 0.0f;
+  const float bias = (a.delta_bias && dvalid) ? a.delta_bias[d] : 0.0f;
+
+  // steps of chunk c before L (uniform, at most T), and the byte offset of
+  // the chunk
+  auto left = [&](int64_t c) { return (int)(L - c * T < T ? L - c * T : T); };
+  auto coff = [&](int64_t c) { return (uint32_t)(c * T * ES); };
+  // u and delta of the lane's quad of a chunk
+  struct Ud {
+    Quad u, dl;
+  };
+  auto load_ud = [&](Ud& q, int64_t c) {
+    const int n = left(c) - qstep;
+    quad_load<VEC>(q.u, u_r, seq_off, coff(c), n);
+    quad_load<VEC>(q.dl, dl_r, seq_off, coff(c), n);
+  };
+  Quad bq_raw, cq_raw;
+  auto load_bc = [&](int64_t c) {
+    const int n = left(c) - bstep;
+    quad_load<VEC>(bq_raw, B_r, bc_off, coff(c), n);
+    quad_load<VEC>(cq_raw, C_r, bc_off, coff(c), n);
+  };
+  // step size (log2 units) and u weight of step i of this lane's quad
+  auto prep_step = [&](const Ud& q, int i, int64_t c, float& dlo, float& wo) {
+    const float x = q.dl.at(i) + bias;
+    float v = a.softplus ? softplus_log2(x) : x * kLog2e;
+    v = qstep + i < left(c) ? v : 0.0f;  // identity step past the end
+    dlo = v;
+    wo = v * (q.u.at(i) * kLn2);  // delta u
+  };
+  // step i of the lane's quad, for the next chunk -> LDS (the wave has read
+  // this chunk's values into registers by then)
+  auto prep_store = [&](int i, float dlv, float wv) {
+    prep[cl * KP + 4 * r + i] = dlv;
+    prep[16 * KP + cl * KP + 4 * r + i] = wv;
+  };
+
+  // u of the chunk being finished (for D u), z of it, and u and delta of
+  // the next chunk (loaded during the last item of the chunk before)
+  Ud nxt{};
+  Quad cur_u{}, zq{};
+  {
+    Ud first;
+    load_ud(first, 0);
+    load_bc(0);
+    if (nchunks > 1) load_ud(nxt, 1);
+    cur_u = first.u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float dlv, wv;
+      prep_step(first, i, 0, dlv, wv);
+      prep_store(i, dlv, wv);
+    }
+  }
+  // states: [channel][NS] rows from (b, d0) on; checkpoints: [channel][nblk][NS]
+  const int64_t nblk = (L + kCkptT - 1) / kCkptT;
+  const int64_t st_base = (b * a.dim + d0) * NS;
+  const Rsrc fs_r = make_rsrc(a.final_state ? a.final_state + st_base : nullptr,
+                              a.final_state ? (int)(nrows * NS * 4) : 0);
+  const Rsrc ck_r = make_rsrc(a.ckpt ? a.ckpt + st_base * nblk : nullptr, a.ckpt ? (int)(nrows * nblk * NS * 4) : 0);
+  const uint32_t fs_off = (uint32_t)(((dc - d0) * NS + r) * 4);
+  const uint32_t ck_off = (uint32_t)(((dc - d0) * nblk * NS + r) * 4);
+  if (wave == W - 1) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      sCarry[W - 1][j][lane] = (a.h0 && dvalid) ? a.h0[(b * a.dim + d) * NS + 4 * j + r] : 0.0f;
+  }
+  if (threadIdx.x < W) sDone[threadIdx.x] = 0;
+  __syncthreads();
+  const int pred = (wave + W - 1) & (W - 1);  // the wave whose states this one continues
+
+  for (int64_t c = 0; c < nchunks; ++c) {
+    const bool more = c + 1 < nchunks;
+    // this chunk's B, C rows of the segment -> LDS; prefetch the next ones.
+    // The raw quads stay packed until here, so that the wait for their load
+    // (issued a chunk earlier) falls here.
+    {
+      opaque(bq_raw);
+      opaque(cq_raw);
+      float* dst = tile + st_n * KP + 4 * st_q;
+      *reinterpret_cast<float4*>(dst) = make_float4(bq_raw.at(0), bq_raw.at(1), bq_raw.at(2), bq_raw.at(3));
+      *reinterpret_cast<float4*>(dst + NS * KP) =
+          make_float4(cq_raw.at(0), cq_raw.at(1), cq_raw.at(2), cq_raw.at(3));
+    }
+    if (more) load_bc(c + 1);
+    if constexpr (GATE) quad_load<VEC>(zq, z_r, seq_off, coff(c), left(c) - qstep);
+    wave_lds_sync();
+    float dl[K], w[K], y[K];
+#pragma unroll
+    for (int i = 0; i < K; i += 4) {
+      const float4 p = *reinterpret_cast<const float4*>(prep + cl * KP + i);
+      const float4 q = *reinterpret_cast<const float4*>(prep + 16 * KP + cl * KP + i);
+      dl[i] = p.x; dl[i + 1] = p.y; dl[i + 2] = p.z; dl[i + 3] = p.w;
+      w[i] = q.x; w[i + 1] = q.y; w[i + 2] = q.z; w[i + 3] = q.w;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = 4 * j + r;
+      const int64_t item = 4 * c + j;
+      // wait until the predecessor has handed over this item's states: wave
+      // s - 1 the same item, wave 3 (for wave 0) the item one chunk back.
+      // The wait is bounded (2^23 sleeps, a fraction of a second); the
+      // waves of a workgroup are resident together, so it never runs out
+      // in a correct launch, and if it did the kernel would still end.
+      if (!(wave == 0 && c == 0)) {
+        const int need = (int)(wave == 0 ? item - 3 : item + 1);
+#pragma unroll 1
+        for (int spin = 0; spin < (1 << 23); ++spin) {
+          if (__builtin_amdgcn_readfirstlane(__hip_atomic_load(&sDone[pred], __ATOMIC_RELAXED,
+                                                               __HIP_MEMORY_SCOPE_WORKGROUP)) >= need)
+            break;
+          __builtin_amdgcn_s_sleep(1);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+      }
+      float h = sCarry[pred][j][lane];
+      if (a.ckpt && wave == 0 && (c & 1) == 0 && dvalid)
+        buf_st32(__float_as_uint(h), ck_r, ck_off, (uint32_t)(((c >> 1) * NS + 4 * j) * 4));
+      const float A = sA[j][lane];
+      const float* pb = tile + n * KP;
+      const float* pc = tile + NS * KP + n * KP;
+#pragma unroll
+      for (int i = 0; i < K; i += 4) {
+        // read B and C four steps at a time (not all up front: registers)
+        if (i > 0) asm volatile("" ::: "memory");
+        const float4 bb = *reinterpret_cast<const float4*>(pb + i);
+        const float4 cc = *reinterpret_cast<const float4*>(pc + i);
+        const float bq[4] = {bb.x, bb.y, bb.z, bb.w};
+        const float cq[4] = {cc.x, cc.y, cc.z, cc.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float dli = dl[i + q], wi = w[i + q];
+          float av, xv;
+          if constexpr (RULE == kRuleDeltaB) {
+            av = ex2(dli * A);
+            xv = wi * bq[q];
+          } else if constexpr (RULE == kRuleEuler) {
+            av = fmaf(dli * kLn2, A, 1.0f);
+            xv = wi * bq[q];
+          } else {  // bilinear
+            const float x = 0.5f * kLn2 * dli * A;  // delta A / 2
+            const float rr = rcp(1.0f - x);
+            av = (1.0f + x) * rr;
+            xv = wi * rr * bq[q];
+          }
+          h = fmaf(av, h, xv);
+          y[i + q] = j == 0 ? cq[q] * h : fmaf(cq[q], h, y[i + q]);
+        }
+      }
+      // keep the readout sums current item by item (the compiler would
+      // otherwise hold every state of the chunk until the last item)
+#pragma unroll
+      for (int i = 0; i < K; ++i) asm volatile("" : "+v"(y[i]));
+      sCarry[wave][j][lane] = h;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+      if (lane == 0) __hip_atomic_store(&sDone[wave], (int)(item + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      if (wave == W - 1 && !more && a.final_state && dvalid) buf_st32(__float_as_uint(h), fs_r, fs_off, 16 * j);
+      if (more) {
+        // the next chunk's step sizes and u weights, spread over the items
+        // that do not finish the chunk: steps [lo, hi) of the quad after
+        // item j
+        const int lo = kPipePrep[j], hi = kPipePrep[j + 1];
+        if (lo < hi && lo == kPipePrep[0]) {
+          opaque(nxt.u);
+          opaque(nxt.dl);
+        }
+#pragma unroll
+        for (int i = lo; i < hi; ++i) {
+          float dlv, wv;
+          prep_step(nxt, i, c + 1, dlv, wv);
+          prep_store(i, dlv, wv);
+        }
+      }
+      if (j == 3) {
+        // readout: add the 4 rows' partial sums, finish and store
+        wave_lds_sync();
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          sWave[wave][q * 64 + lane] = make_float4(y[4 * q], y[4 * q + 1], y[4 * q + 2], y[4 * q + 3]);
+        wave_lds_sync();
+        float4 s = sWave[wave][r * 64 + cl];
+#pragma unroll
+        for (int rr = 1; rr < 4; ++rr) {
+          const float4 p = sWave[wave][r * 64 + 16 * rr + cl];
+          s.x += p.x; s.y += p.y; s.z += p.z; s.w += p.w;
+        }
+        float o[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          o[i] = fmaf(Dv, cur_u.at(i), o[i]);
+          if constexpr (GATE) o[i] *= silu_f(zq.at(i));
+        }
+        const int nleft = left(c) - qstep;
+        if (dvalid) {
+          if (VEC && nleft >= 4) {
+            buf_st64(make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])), y_r, seq_off, coff(c));
+          } else if (!VEC) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              if (i >= nleft) break;
+              buf_st16(__builtin_bit_cast(uint16_t, (__bf16)o[i]), y_r, seq_off + 2 * i, coff(c));
+            }
+          }
+        }
+        cur_u = nxt.u;
+        if (c + 2 < nchunks) load_ud(nxt, c + 2);
+      }
+    }
   }
 }
 
@@ -1724,34 +2112,6 @@ __device__ __forceinline__ void split_bf16(float a, float b, uint32_t& hi, uint3
   lo = pk_bf16(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
 }
 
-// Raw buffer accesses: a 32-bit byte offset from a base whose extent is
-// given, and reads past the extent return zero, so addresses need no clamps.
-typedef __amdgpu_buffer_rsrc_t Rsrc;
-__device__ __forceinline__ Rsrc make_rsrc(const void* base, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ uint4 buf_ld128(Rsrc r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-}
-__device__ __forceinline__ uint2 buf_ld64(Rsrc r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
-}
-__device__ __forceinline__ uint32_t buf_ld16(Rsrc r, uint32_t voff, uint32_t soff) {
-  return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
-}
-__device__ __forceinline__ void buf_st64(uint2 v, Rsrc r, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int, v), r, voff, soff, 0);
-}
-__device__ __forceinline__ void buf_st16(uint32_t v, Rsrc r, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v, r, voff, soff, 0);
-}
-__device__ __forceinline__ uint32_t buf_ld32(Rsrc r, uint32_t voff, uint32_t soff) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
-}
-__device__ __forceinline__ void buf_st32(uint32_t v, Rsrc r, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_buffer_store_b32(v, r, voff, soff, 0);
-}
-
 // 8 (4) bf16 of a row at byte offset voff + soff: one 16-byte (8-byte) load
 // when rows are 16-byte aligned, else 2-byte loads
 template <bool ALIGNED>
@@ -2800,6 +3160,22 @@ int launch_fwd_cfg(const ScanArgs& a, int64_t batch, int rule, bool gate, hipStr
   return launch_status("ssm_selective_scan_fwd launch");
 }
 
+// The time-pipelined forward for 16 states and bf16 rows (one workgroup per
+// 16 channels).
+template <bool VEC>
+int launch_fwd_pipe(const ScanArgs& a, int64_t batch, int rule, bool gate, hipStream_t s) {
+  const dim3 grid((unsigned)((a.dim + 15) / 16), (unsigned)batch);
+  auto go = [&](auto rt) {
+    constexpr int R = decltype(rt)::value;
+    if (gate) hipLaunchKernelGGL((scan_fwd_pipe_kernel<VEC, R, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((scan_fwd_pipe_kernel<VEC, R, false>), grid, dim3(256), 0, s, a);
+  };
+  if (rule == kRuleEuler) go(std::integral_constant<int, kRuleEuler>{});
+  else if (rule == kRuleBilinear) go(std::integral_constant<int, kRuleBilinear>{});
+  else go(std::integral_constant<int, kRuleDeltaB>{});
+  return launch_status("ssm_selective_scan_fwd launch");
+}
+
 // Lane layout choice: 16 lanes per channel gives the shortest cross-lane scan;
 // wider groups are used when there are too few channels to give every SIMD of
 // the 256 CUs several waves.
@@ -2807,6 +3183,15 @@ template <typename IO, bool VEC>
 int launch_fwd_vec(const ScanArgs& a, int64_t batch, int rule, bool gate, hipStream_t s) {
   constexpr int K = SELSCAN_K, W = SELSCAN_W, NT = SELSCAN_NT;
   const int64_t channels = batch * a.dim;
+  // The pipelined kernel for bf16 sequences and the rules whose per-element
+  // work fits its registers (exact ZOH and float32 rows need more registers
+  // than five waves per SIMD leave; the fold-and-scan kernel is faster
+  // there).  It addresses a workgroup's 16 rows with 32-bit byte offsets.
+  if constexpr (std::is_same<IO, uint16_t>::value) {
+    if (rule != kRuleZoh && a.dstate == 16 && channels >= SELSCAN_PIPE_MIN_CHANNELS &&
+        16 * a.seqlen * (int64_t)sizeof(IO) < ((int64_t)1 << 31))
+      return launch_fwd_pipe<VEC>(a, batch, rule, gate, s);
+  }
   if (channels >= 4 * 4096) return launch_fwd_cfg<IO, 16, K, W, NT, VEC>(a, batch, rule, gate, s);
   // 32 lanes per channel: eight waves (16 channels) share each staged
   // 16-state B/C tile

@@ -112,9 +112,18 @@ def test_decode_1000_steps(ssm, dev):
 # ---------------------------------------------------------------- shapes, tails, modes
 
 # (batch, dim, N, L, dtype, gate, bias): the channel counts select each lane
-# layout (>= 16384 channels: 16 lanes per channel, >= 8192: 32, else 64); the
-# lengths cover one step, partial chunks, exact chunks and ragged tails.
+# layout (>= 16384 channels: 16 lanes per channel, >= 8192: 32, else 64; with
+# 16 states, bf16 rows and >= 8192 channels the time-pipelined kernel, one
+# workgroup per 16 channels, four 16-step segments per 64-step chunk); the
+# lengths cover one step, partial chunks, exact chunks and ragged tails, and
+# the dims partial 16-channel groups.
 CASES = [
+    (1, 8200, 16, 77, "bf16", True, True),
+    (2, 4104, 16, 136, "bf16", False, False),
+    (1, 8192, 16, 64, "bf16", True, False),
+    (1, 8192, 16, 1, "bf16", True, True),
+    (3, 2736, 16, 203, "bf16", True, True),
+    (1, 8208, 16, 1000, "bf16", False, True),
     (1, 3, 1, 1, "f32", False, False),
     (2, 5, 4, 7, "f32", True, True),
     (1, 37, 16, 255, "bf16", True, True),
@@ -171,6 +180,8 @@ RULE_CASES = [  # batch, dim, N, L
     (2, 24, 16, 600),
     (1, 8200, 4, 72),
     (2, 8200, 4, 41),
+    (1, 8200, 16, 77),
+    (2, 4104, 16, 200),
 ]
 
 
@@ -209,6 +220,26 @@ def test_h0_resume_in_place_equals_full_scan(ssm, dev):
     assert norm_err(to_np(f2).reshape(fr.shape), fr) <= TOL["f32"]
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_h0_resume_in_place_many_channels(ssm, dev, dt):
+    """The resume of a 16-state scan over 8200 channels (the pipelined kernel
+    for bf16 rows), cut at a step inside a chunk; the final state lands on h0."""
+    w, x = wl.custom(1, 8200, 16, 333, dtype=dt, gate=True, seed=53)
+    cut = 150
+
+    def part(lo, hi):
+        return {k: (np.ascontiguousarray(v[..., lo:hi]) if isinstance(v, np.ndarray) and v.ndim == 3 else v)
+                for k, v in x.items()}
+
+    y1, f1 = scan_gpu(ssm, part(0, cut), dev)
+    y2, f2 = scan_gpu(ssm, part(cut, 333), dev, h0=f1, final_state=f1)
+    torch.cuda.synchronize()
+    yr, fr = scan_oracle(oracle, x)
+    y = np.concatenate([to_np(y1), to_np(y2)], axis=-1).reshape(yr.shape)
+    assert norm_err(y, yr) <= TOL[dt]
+    assert norm_err(to_np(f2).reshape(fr.shape), fr) <= TOL[dt]
+
+
 def test_h0_from_oracle_state(ssm, dev):
     w, x = wl.custom(1, 30, 16, 500, dtype="bf16", gate=False, seed=61)
     h0 = np.random.default_rng(3).normal(0, 0.5, (1, 30, 16)).astype(np.float32)
@@ -219,8 +250,9 @@ def test_h0_from_oracle_state(ssm, dev):
     assert norm_err(to_np(fs).reshape(fr.shape), fr) <= TOL["bf16"]
 
 
-def test_repeat_runs_are_bitwise_identical(ssm, dev):
-    w, x = wl.custom(2, 512, 16, 2048, seed=71)
+@pytest.mark.parametrize("shape", [(2, 512, 16, 2048), (1, 8192, 16, 1000)])
+def test_repeat_runs_are_bitwise_identical(ssm, dev, shape):
+    w, x = wl.custom(*shape, seed=71)
     y1, f1 = scan_gpu(ssm, x, dev)
     y2, f2 = scan_gpu(ssm, x, dev)
     torch.cuda.synchronize()
