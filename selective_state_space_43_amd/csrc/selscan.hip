@@ -672,13 +672,6 @@ __device__ __forceinline__ void wave_lds_sync() {
 // Registers are held to 96 (five waves per SIMD: 20480 channels give exactly
 // five workgroups per CU) and LDS to 31 KiB per workgroup.
 
-// Which of the next chunk's 4 steps each item of the pipelined forward
-// prepares: item j does steps [kPipePrep[j], kPipePrep[j + 1]) (the first
-// item stages B and C, the last finishes the chunk).
-#ifndef SELSCAN_PIPE_PREP
-#define SELSCAN_PIPE_PREP 0, 0, 2, 4, 4
-#endif
-constexpr int kPipePrep[5] = {SELSCAN_PIPE_PREP};
 
 template <bool VEC, int RULE, bool GATE>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5)))
@@ -774,11 +767,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5)))
     dlo = v;
     wo = v * (q.u.at(i) * kLn2);  // delta u
   };
-  // step i of the lane's quad, for the next chunk -> LDS (the wave has read
-  // this chunk's values into registers by then)
-  auto prep_store = [&](int i, float dlv, float wv) {
-    prep[cl * KP + 4 * r + i] = dlv;
-    prep[16 * KP + cl * KP + 4 * r + i] = wv;
+  // steps i, i + 1 of the lane's quad, for the next chunk -> LDS (the wave
+  // has read this chunk's values into registers by then)
+  auto prep_pair = [&](const Ud& q, int i, int64_t c) {
+    float d0v, w0v, d1v, w1v;
+    prep_step(q, i, c, d0v, w0v);
+    prep_step(q, i + 1, c, d1v, w1v);
+    *reinterpret_cast<float2*>(prep + cl * KP + 4 * r + i) = make_float2(d0v, d1v);
+    *reinterpret_cast<float2*>(prep + 16 * KP + cl * KP + 4 * r + i) = make_float2(w0v, w1v);
   };
 
   // u of the chunk being finished (for D u), z of it, and u and delta of
@@ -791,12 +787,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5)))
     load_bc(0);
     if (nchunks > 1) load_ud(nxt, 1);
     cur_u = first.u;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float dlv, wv;
-      prep_step(first, i, 0, dlv, wv);
-      prep_store(i, dlv, wv);
-    }
+    prep_pair(first, 0, 0);
+    prep_pair(first, 2, 0);
   }
   // states: [channel][NS] rows from (b, d0) on; checkpoints: [channel][nblk][NS]
   const int64_t nblk = (L + kCkptT - 1) / kCkptT;
@@ -898,24 +890,20 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5)))
 #pragma unroll
       for (int i = 0; i < K; ++i) asm volatile("" : "+v"(y[i]));
       sCarry[wave][j][lane] = h;
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+      // one wave's LDS accesses complete in order, so the count lands after
+      // the state (a compiler fence keeps that order in the code; no wait)
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       if (lane == 0) __hip_atomic_store(&sDone[wave], (int)(item + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       if (wave == W - 1 && !more && a.final_state && dvalid) buf_st32(__float_as_uint(h), fs_r, fs_off, 16 * j);
-      if (more) {
-        // the next chunk's step sizes and u weights, spread over the items
-        // that do not finish the chunk: steps [lo, hi) of the quad after
-        // item j
-        const int lo = kPipePrep[j], hi = kPipePrep[j + 1];
-        if (lo < hi && lo == kPipePrep[0]) {
+      // the next chunk's step sizes and u weights: two steps after each of
+      // the middle items (the first item stages B and C, the last finishes
+      // the chunk; this balances the items)
+      if (more && (j == 1 || j == 2)) {
+        if (j == 1) {
           opaque(nxt.u);
           opaque(nxt.dl);
         }
-#pragma unroll
-        for (int i = lo; i < hi; ++i) {
-          float dlv, wv;
-          prep_step(nxt, i, c + 1, dlv, wv);
-          prep_store(i, dlv, wv);
-        }
+        prep_pair(nxt, 2 * (j - 1), c + 1);
       }
       if (j == 3) {
         // readout: add the 4 rows' partial sums, finish and store
