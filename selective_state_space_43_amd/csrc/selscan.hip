@@ -673,7 +673,9 @@ __device__ __forceinline__ void wave_lds_sync() {
 // five workgroups per CU) and LDS to 31 KiB per workgroup.
 
 
-template <bool VEC, int RULE, bool GATE>
+// CKPT: the checkpoint pass of the backward (states at every kCkptT-step
+// block start to a.ckpt, no output).
+template <bool VEC, int RULE, bool GATE, bool CKPT = false>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5)))
     scan_fwd_pipe_kernel(const ScanArgs a) {
   using IO = uint16_t;
@@ -757,7 +759,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5)))
   auto load_bc = [&](int64_t c) {
     const int n = left(c) - bstep;
     quad_load<VEC>(bq_raw, B_r, bc_off, coff(c), n);
-    quad_load<VEC>(cq_raw, C_r, bc_off, coff(c), n);
+    if constexpr (!CKPT) quad_load<VEC>(cq_raw, C_r, bc_off, coff(c), n);
   };
   // step size (log2 units) and u weight of step i of this lane's quad
   auto prep_step = [&](const Ud& q, int i, int64_t c, float& dlo, float& wo) {
@@ -817,11 +819,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5)))
       opaque(cq_raw);
       float* dst = tile + st_n * KP + 4 * st_q;
       *reinterpret_cast<float4*>(dst) = make_float4(bq_raw.at(0), bq_raw.at(1), bq_raw.at(2), bq_raw.at(3));
-      *reinterpret_cast<float4*>(dst + NS * KP) =
-          make_float4(cq_raw.at(0), cq_raw.at(1), cq_raw.at(2), cq_raw.at(3));
+      if constexpr (!CKPT)
+        *reinterpret_cast<float4*>(dst + NS * KP) =
+            make_float4(cq_raw.at(0), cq_raw.at(1), cq_raw.at(2), cq_raw.at(3));
     }
     if (more) load_bc(c + 1);
-    if constexpr (GATE) quad_load<VEC>(zq, z_r, seq_off, coff(c), left(c) - qstep);
+    if constexpr (GATE && !CKPT) quad_load<VEC>(zq, z_r, seq_off, coff(c), left(c) - qstep);
     wave_lds_sync();
     float dl[K], w[K], y[K];
 #pragma unroll
@@ -882,13 +885,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5)))
             xv = wi * rr * bq[q];
           }
           h = fmaf(av, h, xv);
-          y[i + q] = j == 0 ? cq[q] * h : fmaf(cq[q], h, y[i + q]);
+          if constexpr (!CKPT) y[i + q] = j == 0 ? cq[q] * h : fmaf(cq[q], h, y[i + q]);
         }
       }
       // keep the readout sums current item by item (the compiler would
       // otherwise hold every state of the chunk until the last item)
+      if constexpr (!CKPT) {
 #pragma unroll
-      for (int i = 0; i < K; ++i) asm volatile("" : "+v"(y[i]));
+        for (int i = 0; i < K; ++i) asm volatile("" : "+v"(y[i]));
+      }
       sCarry[wave][j][lane] = h;
       // one wave's LDS accesses complete in order, so the count lands after
       // the state (a compiler fence keeps that order in the code; no wait)
@@ -905,7 +910,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5)))
         }
         prep_pair(nxt, 2 * (j - 1), c + 1);
       }
-      if (j == 3) {
+      if (j == 3 && CKPT) {
+        if (c + 2 < nchunks) load_ud(nxt, c + 2);
+      } else if (j == 3) {
         // readout: add the 4 rows' partial sums, finish and store
         wave_lds_sync();
 #pragma unroll
@@ -2298,7 +2305,9 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(const SsdArgs a) {
   auto chunk = [&](int64_t c) {
     const int64_t t0 = c * T;
     const bool more = c + 1 < a.nchunks;
+#ifndef SSD_NO_TOPWAIT
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the operands of chunk c have arrived
+#endif
     if (c > 0) store_y(c - 1);
     // ---- 1. step sizes and running decay, lane l <-> step t0 + l
     float dtv = 0.0f;
@@ -2352,6 +2361,85 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(const SsdArgs a) {
     }
     if (more) fetch_g(c + 1, cur);
     __syncthreads();  // B: sX, sXw, sM ready
+#ifdef SSD_STATE_FIRST
+    // ---- 3b. state: S^T = exp(cs_63) S^T + B^T (w o X)
+    {
+      const float decay = ex2(cs_end);
+#pragma unroll
+      for (int q = 0; q < NBW; ++q)
+        if (wave + 4 * q < NB)
+#pragma unroll
+          for (int ns = 0; ns < 2; ++ns)
+#pragma unroll
+            for (int pb2 = 0; pb2 < 2; ++pb2) S[q][ns][pb2] *= decay;
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2) {
+#pragma unroll
+        for (int pb2 = 0; pb2 < 2; ++pb2) {
+          // w o X as the B operand: lane holds xw[s = 32 ks2 + (lane/16)*8 + j][p = pb2*16 + lane % 16]
+          const int xo = (pb2 * 16 + lane % 16) * XP + 32 * ks2 + (lane / 16) * 8;
+          const uint4 xw = *reinterpret_cast<const uint4*>(sXw + xo);
+          const uint4 xl = *reinterpret_cast<const uint4*>(sXwl + xo);
+#pragma unroll
+          for (int q = 0; q < NBW; ++q) {
+            if (wave + 4 * q < NB) {
+#pragma unroll
+              for (int ns = 0; ns < 2; ++ns) {
+                f32x4v_t& acc = S[q][ns][pb2];
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.bt[q][2 * ns + ks2]), as_bf16x8(xw), acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.bt[q][2 * ns + ks2]), as_bf16x8(xl), acc, 0, 0, 0);
+              }
+            }
+          }
+        }
+      }
+      if (more) fetch_b(c + 1, cur);
+    }
+    // ---- 3a. Y rows t in [16 wave, 16 wave + 16), channels p = pt*16 + lane % 16
+    {
+      f32x4v_t yv[2] = {{}, {}};
+#pragma unroll
+      for (int pt = 0; pt < 2; ++pt) {
+#pragma unroll
+        for (int k = 0; k < N / 32; ++k) {
+          const int off = (pt * 16 + lane % 16) * SP + 32 * k + (lane / 16) * 8;
+          const uint4 sv = *reinterpret_cast<const uint4*>(sS + off);
+          const uint4 sl = *reinterpret_cast<const uint4*>(sSl + off);
+          yv[pt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.ct[k]), as_bf16x8(sv), yv[pt], 0, 0, 0);
+          yv[pt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.ct[k]), as_bf16x8(sl), yv[pt], 0, 0, 0);
+        }
+      }
+      if (more) fetch_c(c + 1, cur);
+      const float4 ev = *reinterpret_cast<const float4*>(sE + ty);
+#pragma unroll
+      for (int pt = 0; pt < 2; ++pt) {
+        yv[pt][0] *= ev.x; yv[pt][1] *= ev.y; yv[pt][2] *= ev.z; yv[pt][3] *= ev.w;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          if (k == 0 || wave >= 2) {  // M is zero for s > t
+            const int mo = (16 * wave + lane % 16) * MP + 32 * k + (lane / 16) * 8;
+            const uint4 mv = *reinterpret_cast<const uint4*>(sM + mo);
+            const uint4 ml = *reinterpret_cast<const uint4*>(sMl + mo);
+            const uint4 xv = *reinterpret_cast<const uint4*>(sX + (pt * 16 + lane % 16) * XP + 32 * k + (lane / 16) * 8);
+            yv[pt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(mv), as_bf16x8(xv), yv[pt], 0, 0, 0);
+            yv[pt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ml), as_bf16x8(xv), yv[pt], 0, 0, 0);
+          }
+        }
+        // epilogue: channel p, steps ty .. ty + 3
+        const uint2 xr = *reinterpret_cast<const uint2*>(sX + (pt * 16 + lane % 16) * XP + ty);
+        float v[4] = {fmaf(Dh, bf_lo(xr.x), yv[pt][0]), fmaf(Dh, bf_hi(xr.x), yv[pt][1]),
+                      fmaf(Dh, bf_lo(xr.y), yv[pt][2]), fmaf(Dh, bf_hi(xr.y), yv[pt][3])};
+        if constexpr (GATE) {
+          v[0] *= silu_f(bf_lo(cur.zv[pt].x));
+          v[1] *= silu_f(bf_hi(cur.zv[pt].x));
+          v[2] *= silu_f(bf_lo(cur.zv[pt].y));
+          v[3] *= silu_f(bf_hi(cur.zv[pt].y));
+        }
+        ypend[pt] = make_uint2(pk_bf16(v[0], v[1]), pk_bf16(v[2], v[3]));
+      }
+      if (more) fetch_z(c + 1, cur);
+    }
+#else
     // ---- 3a. Y rows t in [16 wave, 16 wave + 16), channels p = pt*16 + lane % 16
     {
       f32x4v_t yv[2] = {{}, {}};
@@ -2429,6 +2517,7 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(const SsdArgs a) {
       }
       if (more) fetch_b(c + 1, cur);
     }
+#endif
     __syncthreads();  // C: every wave is done with sS (old state) and the step data
     write_state_bf16();
   };
@@ -3228,10 +3317,22 @@ int launch_bwd_typed(const ScanArgs& fa, BwdArgs ba, int64_t batch, hipStream_t 
   constexpr int K = kBwdK;
   const dim3 grid16((unsigned)((ba.dim + 15) / 16), (unsigned)batch);
   // 1. checkpoints: the state entering every kCkptT-step block (a forward
-  // pass over 256-step chunks), unless the caller brings the forward's
-  if (fa.ckpt)
-    hipLaunchKernelGGL((scan_fwd_kernel<IO, 16, 16, 4, 16, VEC, ZOH ? kRuleZoh : kRuleDeltaB, false, true>), grid16, dim3(256),
-                       2 * 16 * (size_t)ba.dstate * sizeof(float), s, fa);
+  // pass), unless the caller brings the forward's; the time-pipelined kernel
+  // where the forward would take it
+  if (fa.ckpt) {
+    bool piped = false;
+    if constexpr (std::is_same<IO, uint16_t>::value && !ZOH) {
+      if (ba.dstate == 16 && batch * ba.dim >= SELSCAN_PIPE_MIN_CHANNELS &&
+          16 * ba.seqlen * (int64_t)sizeof(IO) < ((int64_t)1 << 31)) {
+        hipLaunchKernelGGL((scan_fwd_pipe_kernel<VEC, kRuleDeltaB, false, true>),
+                           dim3((unsigned)((ba.dim + 15) / 16), (unsigned)batch), dim3(256), 0, s, fa);
+        piped = true;
+      }
+    }
+    if (!piped)
+      hipLaunchKernelGGL((scan_fwd_kernel<IO, 16, 16, 4, 16, VEC, ZOH ? kRuleZoh : kRuleDeltaB, false, true>), grid16, dim3(256),
+                         2 * 16 * (size_t)ba.dstate * sizeof(float), s, fa);
+  }
   // 2. adjoint carries at every block end (a reverse pass over 256-step chunks)
   if (ba.dstate <= 16)
     hipLaunchKernelGGL((scan_bwd_carry_kernel<IO, 16, VEC, GATE, false>), grid16, dim3(256), 0, s, ba);
