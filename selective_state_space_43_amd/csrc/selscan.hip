@@ -2559,13 +2559,12 @@ struct StepArgs {
   void* y;
   int64_t batch, dim, dstate;
   int softplus;
-  int vec;  // dstate % 16 == 0 and A 16-byte aligned: 16-byte accesses
+  int vec;  // dstate % 16 == 0 and A 16-byte aligned: the four-lane kernel
 };
 
-// One lane per channel: the lane streams its channel's whole state row
-// (N floats, 16-byte vectors) in and out, so a wave keeps 64 rows in flight
-// and neighbouring lanes read neighbouring rows.  A is read as float4s; B and
-// C (one row per sequence, shared by the wave's channels) as 16-byte vectors.
+// One lane per channel, for state rows that the four-lane kernel below does
+// not take (dstate not a multiple of 16, or A not 16-byte aligned): the lane
+// walks its channel's row element by element, 16 states at a time.
 template <typename IO, int RULE, bool GATE>
 __global__ void __launch_bounds__(256) state_update_kernel(const StepArgs a) {
   const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -2580,35 +2579,16 @@ __global__ void __launch_bounds__(256) state_update_kernel(const StepArgs a) {
   const float* Ar = a.A + d * N;
   const int64_t bc = b * N;
   float acc = 0.0f;
-  // 16 states at a time with vector accesses when rows allow it (the host
-  // checks the extent and the alignment of A; state, B and C bases are
-  // 16-byte aligned by contract)
-  const bool vec = a.vec != 0;
   for (int64_t n0 = 0; n0 < N; n0 += 16) {
     const int cnt = (int)((N - n0) < 16 ? (N - n0) : 16);
     float h[16], An[16], Bv[16], Cv[16];
-    if (vec) {
 #pragma unroll
-      for (int k = 0; k < 16; k += 4) {
-        const f32x4 s4 = *reinterpret_cast<const f32x4*>(st + n0 + k);
-        const float4 a4 = *reinterpret_cast<const float4*>(Ar + n0 + k);
-        h[k] = s4.x; h[k + 1] = s4.y; h[k + 2] = s4.z; h[k + 3] = s4.w;
-        An[k] = a4.x; An[k + 1] = a4.y; An[k + 2] = a4.z; An[k + 3] = a4.w;
-      }
-#pragma unroll
-      for (int k = 0; k < 16; k += Io<IO>::V) {
-        Io<IO>::ldv(a.Bm, bc + n0 + k, Bv + k);
-        Io<IO>::ldv(a.Cm, bc + n0 + k, Cv + k);
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const bool ok = k < cnt;
-        h[k] = ok ? st[n0 + k] : 0.0f;
-        An[k] = ok ? Ar[n0 + k] : 0.0f;
-        Bv[k] = ok ? Io<IO>::ld1(a.Bm, bc + n0 + k) : 0.0f;
-        Cv[k] = ok ? Io<IO>::ld1(a.Cm, bc + n0 + k) : 0.0f;
-      }
+    for (int k = 0; k < 16; ++k) {
+      const bool ok = k < cnt;
+      h[k] = ok ? st[n0 + k] : 0.0f;
+      An[k] = ok ? Ar[n0 + k] : 0.0f;
+      Bv[k] = ok ? Io<IO>::ld1(a.Bm, bc + n0 + k) : 0.0f;
+      Cv[k] = ok ? Io<IO>::ld1(a.Cm, bc + n0 + k) : 0.0f;
     }
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
@@ -2632,21 +2612,85 @@ __global__ void __launch_bounds__(256) state_update_kernel(const StepArgs a) {
       h[k] = fmaf(e, h[k], x);
       acc = fmaf(Cv[k], h[k], acc);
     }
-    if (vec) {
 #pragma unroll
-      for (int k = 0; k < 16; k += 4) {
-        const f32x4 v = {h[k], h[k + 1], h[k + 2], h[k + 3]};
-        *reinterpret_cast<f32x4*>(st + n0 + k) = v;
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < 16; ++k)
-        if (k < cnt) st[n0 + k] = h[k];
-    }
+    for (int k = 0; k < 16; ++k)
+      if (k < cnt) st[n0 + k] = h[k];
   }
   float yv = acc + (a.Dskip ? a.Dskip[d] : 0.0f) * uu;
   if constexpr (GATE) yv *= silu_f(Io<IO>::ld1(a.z, c));
   Io<IO>::st1(a.y, c, yv);
+}
+
+// Four lanes per channel (dstate a multiple of 16, A 16-byte aligned): lane q
+// of a channel owns states 4q .. 4q + 3 of every 16, so each of a wave's
+// 16-byte accesses to the state rows and to A covers 16 whole 64-byte rows;
+// the readout's four partial sums are added across the lane quad (DPP).  The
+// per-token work (step size, gate) is done by all four lanes.
+template <typename IO, int RULE, bool GATE>
+__global__ void __launch_bounds__(256) state_update4_kernel(const StepArgs a) {
+  const int64_t c = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 2;
+  const int q = threadIdx.x & 3;
+  if (c >= a.batch * a.dim) return;  // the four lanes of a channel leave together
+  const int64_t b = c / a.dim, d = c % a.dim;
+  const int64_t N = a.dstate;
+  const float uu = Io<IO>::ld1(a.u, c);
+  const float raw = Io<IO>::ld1(a.delta, c) + (a.delta_bias ? a.delta_bias[d] : 0.0f);
+  const float dl = a.softplus ? softplus_log2(raw) : raw * kLog2e;  // delta / ln 2
+  const float w = dl * kLn2 * uu;                                   // delta u
+  float* st = a.state + c * N + 4 * q;
+  const float* Ar = a.A + d * N + 4 * q;
+  const int64_t bc = b * N + 4 * q;
+  float acc = 0.0f;
+  for (int64_t n0 = 0; n0 < N; n0 += 16) {
+    const f32x4 s4 = *reinterpret_cast<const f32x4*>(st + n0);
+    const float4 a4 = *reinterpret_cast<const float4*>(Ar + n0);
+    float h[4] = {s4.x, s4.y, s4.z, s4.w};
+    const float An[4] = {a4.x, a4.y, a4.z, a4.w};
+    float Bv[4], Cv[4];
+    if constexpr (std::is_same<IO, uint16_t>::value) {
+      const uint2 bb = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.Bm) + bc + n0);
+      const uint2 cc = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.Cm) + bc + n0);
+      Bv[0] = bf_lo(bb.x); Bv[1] = bf_hi(bb.x); Bv[2] = bf_lo(bb.y); Bv[3] = bf_hi(bb.y);
+      Cv[0] = bf_lo(cc.x); Cv[1] = bf_hi(cc.x); Cv[2] = bf_lo(cc.y); Cv[3] = bf_hi(cc.y);
+    } else {
+      const float4 bb = *reinterpret_cast<const float4*>(static_cast<const float*>(a.Bm) + bc + n0);
+      const float4 cc = *reinterpret_cast<const float4*>(static_cast<const float*>(a.Cm) + bc + n0);
+      Bv[0] = bb.x; Bv[1] = bb.y; Bv[2] = bb.z; Bv[3] = bb.w;
+      Cv[0] = cc.x; Cv[1] = cc.y; Cv[2] = cc.z; Cv[3] = cc.w;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float e, x;
+      if constexpr (RULE == kRuleDeltaB) {
+        e = ex2(dl * An[k]);
+        x = w * Bv[k];
+      } else if constexpr (RULE == kRuleZoh) {
+        e = ex2(dl * An[k]);
+        const float coef = zoh_coef(dl * kLn2 * An[k], dl * kLn2, e, An[k] != 0.0f ? rcp(An[k]) : 0.0f);
+        x = coef * Bv[k] * uu;
+      } else if constexpr (RULE == kRuleEuler) {
+        e = fmaf(dl * kLn2, An[k], 1.0f);
+        x = w * Bv[k];
+      } else {
+        const float hx = 0.5f * kLn2 * dl * An[k];
+        const float r = rcp(1.0f - hx);
+        e = (1.0f + hx) * r;
+        x = w * r * Bv[k];
+      }
+      h[k] = fmaf(e, h[k], x);
+      acc = fmaf(Cv[k], h[k], acc);
+    }
+    const f32x4 v = {h[0], h[1], h[2], h[3]};
+    *reinterpret_cast<f32x4*>(st + n0) = v;
+  }
+  // the quad's four partial readouts: swap neighbours, then pairs
+  acc += dpp<0xB1, 0xf>(0.0f, acc);  // quad_perm [1, 0, 3, 2]
+  acc += dpp<0x4E, 0xf>(0.0f, acc);  // quad_perm [2, 3, 0, 1]
+  if (q == 0) {
+    float yv = acc + (a.Dskip ? a.Dskip[d] : 0.0f) * uu;
+    if constexpr (GATE) yv *= silu_f(Io<IO>::ld1(a.z, c));
+    Io<IO>::st1(a.y, c, yv);
+  }
 }
 
 // ---------------------------------------------------------------- LTI kernel
@@ -3670,7 +3714,8 @@ int ssm_state_update(float* state, const void* u, const void* delta, const float
   a.z = z; a.delta_bias = delta_bias; a.y = y; a.batch = batch; a.dim = dim; a.dstate = dstate;
   a.softplus = delta_softplus ? 1 : 0;
   a.vec = (dstate % 16 == 0 && aligned16(A)) ? 1 : 0;
-  const int64_t threads = batch * dim;
+  // one lane per channel, or four with 16-byte rows (a.vec)
+  const int64_t threads = batch * dim * (a.vec ? 4 : 1);
   const dim3 grid((unsigned)((threads + 255) / 256));
   if (grid.x == 0 || (threads + 255) / 256 > 0x7fffffff)
     return fail(SSM_E_SHAPE, "batch * dim too large for one launch");
@@ -3678,7 +3723,15 @@ int ssm_state_update(float* state, const void* u, const void* delta, const float
   const bool gate = z != nullptr;
   with_rule(bbar_mode, [&](auto rt) {
     constexpr int R = decltype(rt)::value;
-    if (io_dtype == SSM_DTYPE_BF16) {
+    if (a.vec) {
+      if (io_dtype == SSM_DTYPE_BF16) {
+        if (gate) hipLaunchKernelGGL((state_update4_kernel<uint16_t, R, true>), grid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((state_update4_kernel<uint16_t, R, false>), grid, dim3(256), 0, s, a);
+      } else {
+        if (gate) hipLaunchKernelGGL((state_update4_kernel<float, R, true>), grid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((state_update4_kernel<float, R, false>), grid, dim3(256), 0, s, a);
+      }
+    } else if (io_dtype == SSM_DTYPE_BF16) {
       if (gate) hipLaunchKernelGGL((state_update_kernel<uint16_t, R, true>), grid, dim3(256), 0, s, a);
       else hipLaunchKernelGGL((state_update_kernel<uint16_t, R, false>), grid, dim3(256), 0, s, a);
     } else {

@@ -304,6 +304,35 @@ def test_state_update_small_shapes(ssm, dev, dt, rule):
         assert norm_err(to_np(state).reshape(ref.shape), ref) <= TOL[dt]
 
 
+def test_state_update_unaligned_A_takes_the_one_lane_kernel(ssm, dev):
+    """16 states with A not 16-byte aligned (a view one float into a buffer):
+    the one-lane kernel instead of the four-lane one, same results."""
+    b, d, n = 2, 40, 16
+    w, x = wl.custom(b, d, n, 1, dtype="bf16", gate=True, seed=97)
+    col = {k: np.ascontiguousarray(v[..., 0]) for k, v in x.items()
+           if isinstance(v, np.ndarray) and v.ndim == 3}
+    s0 = np.random.default_rng(5).normal(0, 0.3, (b, d, n)).astype(np.float32)
+    ys = []
+    for shift in (0, 1):
+        buf = torch.zeros(d * n + 4, dtype=torch.float32, device=dev)
+        A = buf[shift:shift + d * n].view(d, n)
+        A.copy_(to_dev(x["A"], dev))
+        assert (A.data_ptr() % 16 == 0) == (shift == 0)
+        state = to_dev(s0, dev)
+        y = ssm.ssm_state_update(state, to_dev(col["u"], dev), to_dev(col["delta"], dev), A,
+                                 to_dev(col["B"], dev), to_dev(col["C"], dev),
+                                 D=to_dev(x["D"], dev), z=to_dev(col["z"], dev),
+                                 delta_bias=to_dev(x["delta_bias"], dev), delta_softplus=True)
+        torch.cuda.synchronize()
+        ref = s0.reshape(-1, n).astype(np.float64)
+        yr = oracle.state_update(ref, col["u"], col["delta"], x["A"], col["B"], col["C"],
+                                 D=x["D"], z=col["z"], delta_bias=x["delta_bias"],
+                                 delta_softplus=True)
+        assert norm_err(to_np(y).reshape(-1), yr) <= TOL["bf16"]
+        assert norm_err(to_np(state).reshape(ref.shape), ref) <= TOL["bf16"]
+        ys.append(to_np(y))
+
+
 # ---------------------------------------------------------------- LTI check path
 
 @pytest.mark.parametrize("bbar", ["delta", "zoh", "euler", "bilinear"])
