@@ -297,6 +297,29 @@ __device__ __forceinline__ float group_prev0(float v, bool first) {
   }
 }
 
+// Sum over the four 16-lane rows of a wave of eight values per lane.  permlane32_swap trades the upper half of its first operand for
+// the lower half of its second, permlane16_swap the odd rows of the first for
+// the even rows of the second; adding each swapped pair halves the rows to sum
+// while packing two values into one register.  On return row r of lo holds
+// the four-row sum of v[red_step(r)] and row r of hi that of v[4 + red_step(r)].
+__device__ __forceinline__ int red_step(int row) { return ((row & 1) << 1) | (row >> 1); }
+
+__device__ __forceinline__ void rows_sum8(const float* v, float& lo, float& hi) {
+  float s[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[2 * p]),
+                                                    __float_as_uint(v[2 * p + 1]), false, false);
+    s[p] = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+  }
+  const auto y0 = __builtin_amdgcn_permlane16_swap(__float_as_uint(s[0]), __float_as_uint(s[1]),
+                                                   false, false);
+  const auto y1 = __builtin_amdgcn_permlane16_swap(__float_as_uint(s[2]), __float_as_uint(s[3]),
+                                                   false, false);
+  lo = __uint_as_float(y0[0]) + __uint_as_float(y0[1]);
+  hi = __uint_as_float(y1[0]) + __uint_as_float(y1[1]);
+}
+
 // ---------------------------------------------------------------- forward scan
 
 // Raw (undecoded) storage of K consecutive elements.
@@ -666,11 +689,13 @@ __device__ __forceinline__ void wave_lds_sync() {
 // (channel, step): lane (r, c) prepares steps 4 r .. 4 r + 3 of its channel's
 // segment of the next chunk during the items of this one, and the wave shares
 // them through LDS.  Each lane's readout sums over its own 4 states; after
-// the last item of a chunk the 4 rows are added through LDS, and lane (r, c)
-// finishes and stores steps 4 r .. 4 r + 3.
+// the last item of a chunk the 4 rows are added with lane swaps, lane (r, c)
+// finishes steps 4 r .. 4 r + 3 into an LDS copy of the chunk's y, and the
+// last wave stores the chunk's y rows whole (128 bytes each) once every wave
+// has written its segment, so no line of y is written in pieces.
 //
 // Registers are held to 96 (five waves per SIMD: 20480 channels give exactly
-// five workgroups per CU) and LDS to 31 KiB per workgroup.
+// five workgroups per CU) and LDS to 30 KiB per workgroup.
 
 
 // CKPT: the checkpoint pass of the backward (states at every kCkptT-step
@@ -686,9 +711,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5)))
   constexpr int NS = 16;    // states
   constexpr int KP = K + 4; // padded LDS rows (spreads banks)
   static_assert(kCkptT % T == 0, "checkpoint blocks are whole chunks");
-  // per wave: the B and C rows of its segment, [2][NS][KP]; at the end of a
-  // chunk, the readout partial sums [4 step quads][64 lanes][4]
-  __shared__ float4 sWave[W][256];
+  // per wave: the B and C rows of its segment, [2][NS][KP]
+  __shared__ float4 sWave[W][2 * NS * KP / 4];
+  // the chunk's y as bf16, [chunk parity][16 channels][64 steps + 8 pad],
+  // stored to HBM as whole 128-byte rows by the last wave
+  __shared__ __align__(16) uint16_t sY[2][16][T + 8];
   // per wave: step sizes and u weights of its segment, [2][16 channels][KP]
   __shared__ float4 sPrep[W][2 * 16 * KP / 4];
   // state handed from wave s to wave s + 1, [s][j][lane] for the states
@@ -730,10 +757,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5)))
   const Rsrc B_r = make_rsrc(static_cast<const IO*>(a.Bm) + b * NS * L, bc_bytes);
   const Rsrc C_r = make_rsrc(static_cast<const IO*>(a.Cm) + b * NS * L, bc_bytes);
   const int qstep = seg0 + 4 * r;  // first step of this lane's quad in a chunk
-  const uint32_t seq_off = (uint32_t)(((dc - d0) * L + qstep) * ES);
-  const int st_n = lane >> 2, st_q = lane & 3;  // staging role: state, step quad
-  const int bstep = seg0 + 4 * st_q;
-  const uint32_t bc_off = (uint32_t)((st_n * L + bstep) * ES);
+  // Lane (r, c) reads its quad of channel c's rows and, for the staging of
+  // the B and C tile, the same quad of state c's rows: one offset.  Rows of
+  // channels past `dim` lie past the resource's extent and read as zero.
+  const uint32_t seq_off = (uint32_t)((cl * L + qstep) * ES);
 
   if (wave == 0) {
 #pragma unroll
@@ -757,9 +784,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5)))
   };
   Quad bq_raw, cq_raw;
   auto load_bc = [&](int64_t c) {
-    const int n = left(c) - bstep;
-    quad_load<VEC>(bq_raw, B_r, bc_off, coff(c), n);
-    if constexpr (!CKPT) quad_load<VEC>(cq_raw, C_r, bc_off, coff(c), n);
+    const int n = left(c) - qstep;
+    quad_load<VEC>(bq_raw, B_r, seq_off, coff(c), n);
+    if constexpr (!CKPT) quad_load<VEC>(cq_raw, C_r, seq_off, coff(c), n);
   };
   // step size (log2 units) and u weight of step i of this lane's quad
   auto prep_step = [&](const Ud& q, int i, int64_t c, float& dlo, float& wo) {
@@ -768,6 +795,28 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5)))
     v = qstep + i < left(c) ? v : 0.0f;  // identity step past the end
     dlo = v;
     wo = v * (q.u.at(i) * kLn2);  // delta u
+  };
+  // chunk cc's y rows from sY to HBM: lane 4 k + q writes steps 16 q .. 16 q
+  // + 15 of channel k, so four lanes cover one 128-byte row
+  auto store_y = [&](int64_t cc) {
+    const int sch = lane >> 2, sq = lane & 3;
+    if (d0 + sch >= a.dim) return;
+    const uint16_t* src = &sY[cc & 1][sch][16 * sq];
+    const int n = left(cc) - 16 * sq;  // steps of this piece before L
+    const uint32_t off = (uint32_t)((sch * L + 16 * sq) * ES);
+    if (VEC) {
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+        if (n >= 8 * (h2 + 1))
+          __builtin_amdgcn_raw_buffer_store_b128(
+              __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int,
+                                 *reinterpret_cast<const uint4*>(src + 8 * h2)),
+              y_r, off + 16 * h2, coff(cc), 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (i < n) buf_st16(src[i], y_r, off + 2 * i, coff(cc));
+    }
   };
   // steps i, i + 1 of the lane's quad, for the next chunk -> LDS (the wave
   // has read this chunk's values into registers by then)
@@ -817,7 +866,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5)))
     {
       opaque(bq_raw);
       opaque(cq_raw);
-      float* dst = tile + st_n * KP + 4 * st_q;
+      float* dst = tile + cl * KP + 4 * r;
       *reinterpret_cast<float4*>(dst) = make_float4(bq_raw.at(0), bq_raw.at(1), bq_raw.at(2), bq_raw.at(3));
       if constexpr (!CKPT)
         *reinterpret_cast<float4*>(dst + NS * KP) =
@@ -855,6 +904,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5)))
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
       }
       float h = sCarry[pred][j][lane];
+      if constexpr (!CKPT) {
+        // the last wave stores the previous chunk's y: every wave finished it
+        // before handing over this chunk's first item
+        if (j == 0 && wave == W - 1 && c > 0) store_y(c - 1);
+      }
       if (a.ckpt && wave == 0 && (c & 1) == 0 && dvalid)
         buf_st32(__float_as_uint(h), ck_r, ck_off, (uint32_t)(((c >> 1) * NS + 4 * j) * 4));
       const float A = sA[j][lane];
@@ -914,39 +968,38 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5)))
         if (c + 2 < nchunks) load_ud(nxt, c + 2);
       } else if (j == 3) {
         // readout: add the 4 rows' partial sums, finish and store
-        wave_lds_sync();
+        float o[4];
+        // across the rows with lane swaps: rows_sum8 leaves in row r the sums
+        // of v[red_step(r)] and v[4 + red_step(r)]; red_step is its own
+        // inverse, so feeding v[red_step(k)] = y[4 k + i] puts step 4 r + i
+        // of the sum in row r
+        {
+          float va[8], vb[8];
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          sWave[wave][q * 64 + lane] = make_float4(y[4 * q], y[4 * q + 1], y[4 * q + 2], y[4 * q + 3]);
-        wave_lds_sync();
-        float4 s = sWave[wave][r * 64 + cl];
-#pragma unroll
-        for (int rr = 1; rr < 4; ++rr) {
-          const float4 p = sWave[wave][r * 64 + 16 * rr + cl];
-          s.x += p.x; s.y += p.y; s.z += p.z; s.w += p.w;
+          for (int k = 0; k < 4; ++k) {
+            va[red_step(k)] = y[4 * k];
+            va[4 + red_step(k)] = y[4 * k + 1];
+            vb[red_step(k)] = y[4 * k + 2];
+            vb[4 + red_step(k)] = y[4 * k + 3];
+          }
+          rows_sum8(va, o[0], o[1]);
+          rows_sum8(vb, o[2], o[3]);
         }
-        float o[4] = {s.x, s.y, s.z, s.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           o[i] = fmaf(Dv, cur_u.at(i), o[i]);
           if constexpr (GATE) o[i] *= silu_f(zq.at(i));
         }
-        const int nleft = left(c) - qstep;
-        if (dvalid) {
-          if (VEC && nleft >= 4) {
-            buf_st64(make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])), y_r, seq_off, coff(c));
-          } else if (!VEC) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              if (i >= nleft) break;
-              buf_st16(__builtin_bit_cast(uint16_t, (__bf16)o[i]), y_r, seq_off + 2 * i, coff(c));
-            }
-          }
-        }
+        *reinterpret_cast<uint2*>(&sY[c & 1][cl][qstep]) =
+            make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
         cur_u = nxt.u;
         if (c + 2 < nchunks) load_ud(nxt, c + 2);
       }
     }
+  }
+  if constexpr (!CKPT) {
+    __syncthreads();  // every wave has finished the last chunk
+    if (wave == W - 1) store_y(nchunks - 1);
   }
 }
 
@@ -1046,29 +1099,6 @@ __device__ __forceinline__ float row_sum16(float v) {
   return v;
 }
 
-// Sum over the four 16-lane rows of a wave (four channels) of eight values
-// per lane.  permlane32_swap trades the upper half of its first operand for
-// the lower half of its second, permlane16_swap the odd rows of the first for
-// the even rows of the second; adding each swapped pair halves the rows to sum
-// while packing two values into one register.  On return row r of lo holds
-// the four-row sum of v[red_step(r)] and row r of hi that of v[4 + red_step(r)].
-__device__ __forceinline__ int red_step(int row) { return ((row & 1) << 1) | (row >> 1); }
-
-__device__ __forceinline__ void rows_sum8(const float* v, float& lo, float& hi) {
-  float s[4];
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[2 * p]),
-                                                    __float_as_uint(v[2 * p + 1]), false, false);
-    s[p] = __uint_as_float(x[0]) + __uint_as_float(x[1]);
-  }
-  const auto y0 = __builtin_amdgcn_permlane16_swap(__float_as_uint(s[0]), __float_as_uint(s[1]),
-                                                   false, false);
-  const auto y1 = __builtin_amdgcn_permlane16_swap(__float_as_uint(s[2]), __float_as_uint(s[3]),
-                                                   false, false);
-  lo = __uint_as_float(y0[0]) + __uint_as_float(y0[1]);
-  hi = __uint_as_float(y1[0]) + __uint_as_float(y1[1]);
-}
 
 template <typename IO, int K, bool VEC, bool GATE, bool TILED>
 __global__ void __launch_bounds__(256) scan_bwd_carry_kernel(const BwdArgs a) {
