@@ -2335,9 +2335,7 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(const SsdArgs a) {
   auto chunk = [&](int64_t c) {
     const int64_t t0 = c * T;
     const bool more = c + 1 < a.nchunks;
-#ifndef SSD_NO_TOPWAIT
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the operands of chunk c have arrived
-#endif
     if (c > 0) store_y(c - 1);
     // ---- 1. step sizes and running decay, lane l <-> step t0 + l
     float dtv = 0.0f;
@@ -2391,85 +2389,6 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(const SsdArgs a) {
     }
     if (more) fetch_g(c + 1, cur);
     __syncthreads();  // B: sX, sXw, sM ready
-#ifdef SSD_STATE_FIRST
-    // ---- 3b. state: S^T = exp(cs_63) S^T + B^T (w o X)
-    {
-      const float decay = ex2(cs_end);
-#pragma unroll
-      for (int q = 0; q < NBW; ++q)
-        if (wave + 4 * q < NB)
-#pragma unroll
-          for (int ns = 0; ns < 2; ++ns)
-#pragma unroll
-            for (int pb2 = 0; pb2 < 2; ++pb2) S[q][ns][pb2] *= decay;
-#pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2) {
-#pragma unroll
-        for (int pb2 = 0; pb2 < 2; ++pb2) {
-          // w o X as the B operand: lane holds xw[s = 32 ks2 + (lane/16)*8 + j][p = pb2*16 + lane % 16]
-          const int xo = (pb2 * 16 + lane % 16) * XP + 32 * ks2 + (lane / 16) * 8;
-          const uint4 xw = *reinterpret_cast<const uint4*>(sXw + xo);
-          const uint4 xl = *reinterpret_cast<const uint4*>(sXwl + xo);
-#pragma unroll
-          for (int q = 0; q < NBW; ++q) {
-            if (wave + 4 * q < NB) {
-#pragma unroll
-              for (int ns = 0; ns < 2; ++ns) {
-                f32x4v_t& acc = S[q][ns][pb2];
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.bt[q][2 * ns + ks2]), as_bf16x8(xw), acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.bt[q][2 * ns + ks2]), as_bf16x8(xl), acc, 0, 0, 0);
-              }
-            }
-          }
-        }
-      }
-      if (more) fetch_b(c + 1, cur);
-    }
-    // ---- 3a. Y rows t in [16 wave, 16 wave + 16), channels p = pt*16 + lane % 16
-    {
-      f32x4v_t yv[2] = {{}, {}};
-#pragma unroll
-      for (int pt = 0; pt < 2; ++pt) {
-#pragma unroll
-        for (int k = 0; k < N / 32; ++k) {
-          const int off = (pt * 16 + lane % 16) * SP + 32 * k + (lane / 16) * 8;
-          const uint4 sv = *reinterpret_cast<const uint4*>(sS + off);
-          const uint4 sl = *reinterpret_cast<const uint4*>(sSl + off);
-          yv[pt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.ct[k]), as_bf16x8(sv), yv[pt], 0, 0, 0);
-          yv[pt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.ct[k]), as_bf16x8(sl), yv[pt], 0, 0, 0);
-        }
-      }
-      if (more) fetch_c(c + 1, cur);
-      const float4 ev = *reinterpret_cast<const float4*>(sE + ty);
-#pragma unroll
-      for (int pt = 0; pt < 2; ++pt) {
-        yv[pt][0] *= ev.x; yv[pt][1] *= ev.y; yv[pt][2] *= ev.z; yv[pt][3] *= ev.w;
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          if (k == 0 || wave >= 2) {  // M is zero for s > t
-            const int mo = (16 * wave + lane % 16) * MP + 32 * k + (lane / 16) * 8;
-            const uint4 mv = *reinterpret_cast<const uint4*>(sM + mo);
-            const uint4 ml = *reinterpret_cast<const uint4*>(sMl + mo);
-            const uint4 xv = *reinterpret_cast<const uint4*>(sX + (pt * 16 + lane % 16) * XP + 32 * k + (lane / 16) * 8);
-            yv[pt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(mv), as_bf16x8(xv), yv[pt], 0, 0, 0);
-            yv[pt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ml), as_bf16x8(xv), yv[pt], 0, 0, 0);
-          }
-        }
-        // epilogue: channel p, steps ty .. ty + 3
-        const uint2 xr = *reinterpret_cast<const uint2*>(sX + (pt * 16 + lane % 16) * XP + ty);
-        float v[4] = {fmaf(Dh, bf_lo(xr.x), yv[pt][0]), fmaf(Dh, bf_hi(xr.x), yv[pt][1]),
-                      fmaf(Dh, bf_lo(xr.y), yv[pt][2]), fmaf(Dh, bf_hi(xr.y), yv[pt][3])};
-        if constexpr (GATE) {
-          v[0] *= silu_f(bf_lo(cur.zv[pt].x));
-          v[1] *= silu_f(bf_hi(cur.zv[pt].x));
-          v[2] *= silu_f(bf_lo(cur.zv[pt].y));
-          v[3] *= silu_f(bf_hi(cur.zv[pt].y));
-        }
-        ypend[pt] = make_uint2(pk_bf16(v[0], v[1]), pk_bf16(v[2], v[3]));
-      }
-      if (more) fetch_z(c + 1, cur);
-    }
-#else
     // ---- 3a. Y rows t in [16 wave, 16 wave + 16), channels p = pt*16 + lane % 16
     {
       f32x4v_t yv[2] = {{}, {}};
@@ -2547,7 +2466,6 @@ __global__ void __launch_bounds__(256) ssd_fwd_kernel(const SsdArgs a) {
       }
       if (more) fetch_b(c + 1, cur);
     }
-#endif
     __syncthreads();  // C: every wave is done with sS (old state) and the step data
     write_state_bf16();
   };
