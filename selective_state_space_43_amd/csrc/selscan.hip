@@ -100,6 +100,14 @@ __device__ __forceinline__ float softplus_log2(float x) {
   return x > 15.0f ? xl : l;
 }
 
+// softplus(x) in natural units with the compensation of softplus_log2.
+__device__ __forceinline__ float softplus_nat(float x) {
+  const float e = ex2(x * kLog2e);
+  const float u = 1.0f + e;
+  const float l = fmaf((u - 1.0f) - e, u - 2.0f, lg2(u) * kLn2);
+  return x > 15.0f ? x : l;
+}
+
 // silu(z) = z * sigmoid(z)
 __device__ __forceinline__ float silu_f(float z) { return z * rcp(1.0f + ex2(-z * kLog2e)); }
 
@@ -737,7 +745,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5)))
   const bool dvalid = d < a.dim;
   const int64_t dc = dvalid ? d : d0;
   const int64_t L = a.seqlen;
-  const int64_t nchunks = (L + T - 1) / T;
+  const int nchunks = (int)((L + T - 1) / T);  // L < 2^26 (launcher)
   float* tile = reinterpret_cast<float*>(sWave[wave]);
   float* prep = reinterpret_cast<float*>(sPrep[wave]);
   const int seg0 = K * wave;  // first step of this wave's segment in a chunk
@@ -762,47 +770,56 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5)))
   // channels past `dim` lie past the resource's extent and read as zero.
   const uint32_t seq_off = (uint32_t)((cl * L + qstep) * ES);
 
+  // A, for the delta*B rule in log2 units (step sizes are kept in natural
+  // units, so that Abar = exp2(delta A log2 e) and delta u take one multiply each)
   if (wave == 0) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) sA[j][lane] = a.A[dc * NS + 4 * j + r];
+    for (int j = 0; j < 4; ++j) {
+      const float Av = a.A[dc * NS + 4 * j + r];
+      sA[j][lane] = RULE == kRuleDeltaB ? Av * kLog2e : Av;
+    }
   }
   const float Dv = (a.Dskip && dvalid) ? a.Dskip[d] : 0.0f;
   const float bias = (a.delta_bias && dvalid) ? a.delta_bias[d] : 0.0f;
 
   // steps of chunk c before L (uniform, at most T), and the byte offset of
-  // the chunk
-  auto left = [&](int64_t c) { return (int)(L - c * T < T ? L - c * T : T); };
-  auto coff = [&](int64_t c) { return (uint32_t)(c * T * ES); };
+  // the chunk.  The chunk body below comes in two forms: FULL for chunks c
+  // with c + 2 < L / T (this chunk and the two it loads ahead hold T steps,
+  // so no lane masks its loads or steps), and the general one for the rest.
+  auto left = [&](int c) { return (int)(L - (int64_t)c * T < T ? L - (int64_t)c * T : T); };
+  auto coff = [&](int c) { return (uint32_t)c * (uint32_t)(T * ES); };
+  // elements of the lane's quad before L in chunk c
+  auto quad_n = [&](int c, auto full) { return decltype(full)::value ? 4 : left(c) - qstep; };
   // u and delta of the lane's quad of a chunk
   struct Ud {
     Quad u, dl;
   };
-  auto load_ud = [&](Ud& q, int64_t c) {
-    const int n = left(c) - qstep;
+  auto load_ud = [&](Ud& q, int c, auto full) {
+    const int n = quad_n(c, full);
     quad_load<VEC>(q.u, u_r, seq_off, coff(c), n);
     quad_load<VEC>(q.dl, dl_r, seq_off, coff(c), n);
   };
   Quad bq_raw, cq_raw;
-  auto load_bc = [&](int64_t c) {
-    const int n = left(c) - qstep;
+  auto load_bc = [&](int c, auto full) {
+    const int n = quad_n(c, full);
     quad_load<VEC>(bq_raw, B_r, seq_off, coff(c), n);
     if constexpr (!CKPT) quad_load<VEC>(cq_raw, C_r, seq_off, coff(c), n);
   };
-  // step size (log2 units) and u weight of step i of this lane's quad
-  auto prep_step = [&](const Ud& q, int i, int64_t c, float& dlo, float& wo) {
+  // step size (natural units) and u weight of step i of this lane's quad
+  auto prep_step = [&](const Ud& q, int i, int c, auto full, float& dlo, float& wo) {
     const float x = q.dl.at(i) + bias;
-    float v = a.softplus ? softplus_log2(x) : x * kLog2e;
-    v = qstep + i < left(c) ? v : 0.0f;  // identity step past the end
+    float v = a.softplus ? softplus_nat(x) : x;
+    if constexpr (!decltype(full)::value) v = qstep + i < left(c) ? v : 0.0f;  // identity step past the end
     dlo = v;
-    wo = v * (q.u.at(i) * kLn2);  // delta u
+    wo = v * q.u.at(i);  // delta u
   };
   // chunk cc's y rows from sY to HBM: lane 4 k + q writes steps 16 q .. 16 q
   // + 15 of channel k, so four lanes cover one 128-byte row
-  auto store_y = [&](int64_t cc) {
+  auto store_y = [&](int cc, auto full) {
     const int sch = lane >> 2, sq = lane & 3;
     if (d0 + sch >= a.dim) return;
     const uint16_t* src = &sY[cc & 1][sch][16 * sq];
-    const int n = left(cc) - 16 * sq;  // steps of this piece before L
+    const int n = decltype(full)::value ? 16 : left(cc) - 16 * sq;  // steps of this piece before L
     const uint32_t off = (uint32_t)((sch * L + 16 * sq) * ES);
     if (VEC) {
 #pragma unroll
@@ -820,26 +837,27 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5)))
   };
   // steps i, i + 1 of the lane's quad, for the next chunk -> LDS (the wave
   // has read this chunk's values into registers by then)
-  auto prep_pair = [&](const Ud& q, int i, int64_t c) {
+  auto prep_pair = [&](const Ud& q, int i, int c, auto full) {
     float d0v, w0v, d1v, w1v;
-    prep_step(q, i, c, d0v, w0v);
-    prep_step(q, i + 1, c, d1v, w1v);
+    prep_step(q, i, c, full, d0v, w0v);
+    prep_step(q, i + 1, c, full, d1v, w1v);
     *reinterpret_cast<float2*>(prep + cl * KP + 4 * r + i) = make_float2(d0v, d1v);
     *reinterpret_cast<float2*>(prep + 16 * KP + cl * KP + 4 * r + i) = make_float2(w0v, w1v);
   };
 
   // u of the chunk being finished (for D u), z of it, and u and delta of
   // the next chunk (loaded during the last item of the chunk before)
+  const std::false_type general{};
   Ud nxt{};
   Quad cur_u{}, zq{};
   {
     Ud first;
-    load_ud(first, 0);
-    load_bc(0);
-    if (nchunks > 1) load_ud(nxt, 1);
+    load_ud(first, 0, general);
+    load_bc(0, general);
+    if (nchunks > 1) load_ud(nxt, 1, general);
     cur_u = first.u;
-    prep_pair(first, 0, 0);
-    prep_pair(first, 2, 0);
+    prep_pair(first, 0, 0, general);
+    prep_pair(first, 2, 0, general);
   }
   // states: [channel][NS] rows from (b, d0) on; checkpoints: [channel][nblk][NS]
   const int64_t nblk = (L + kCkptT - 1) / kCkptT;
@@ -858,8 +876,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5)))
   __syncthreads();
   const int pred = (wave + W - 1) & (W - 1);  // the wave whose states this one continues
 
-  for (int64_t c = 0; c < nchunks; ++c) {
-    const bool more = c + 1 < nchunks;
+  auto chunk = [&](const int c, auto full) {
+    constexpr bool FULL = decltype(full)::value;
+    const bool more = FULL || c + 1 < nchunks;
+    const bool more2 = FULL || c + 2 < nchunks;
     // this chunk's B, C rows of the segment -> LDS; prefetch the next ones.
     // The raw quads stay packed until here, so that the wait for their load
     // (issued a chunk earlier) falls here.
@@ -872,8 +892,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5)))
         *reinterpret_cast<float4*>(dst + NS * KP) =
             make_float4(cq_raw.at(0), cq_raw.at(1), cq_raw.at(2), cq_raw.at(3));
     }
-    if (more) load_bc(c + 1);
-    if constexpr (GATE && !CKPT) quad_load<VEC>(zq, z_r, seq_off, coff(c), left(c) - qstep);
+    if (more) load_bc(c + 1, full);
+    if constexpr (GATE && !CKPT) quad_load<VEC>(zq, z_r, seq_off, coff(c), quad_n(c, full));
     wave_lds_sync();
     float dl[K], w[K], y[K];
 #pragma unroll
@@ -886,14 +906,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5)))
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int n = 4 * j + r;
-      const int64_t item = 4 * c + j;
+      const int item = 4 * c + j;
       // wait until the predecessor has handed over this item's states: wave
       // s - 1 the same item, wave 3 (for wave 0) the item one chunk back.
       // The wait is bounded (2^23 sleeps, a fraction of a second); the
       // waves of a workgroup are resident together, so it never runs out
       // in a correct launch, and if it did the kernel would still end.
       if (!(wave == 0 && c == 0)) {
-        const int need = (int)(wave == 0 ? item - 3 : item + 1);
+        const int need = wave == 0 ? item - 3 : item + 1;
 #pragma unroll 1
         for (int spin = 0; spin < (1 << 23); ++spin) {
           if (__builtin_amdgcn_readfirstlane(__hip_atomic_load(&sDone[pred], __ATOMIC_RELAXED,
@@ -907,7 +927,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5)))
       if constexpr (!CKPT) {
         // the last wave stores the previous chunk's y: every wave finished it
         // before handing over this chunk's first item
-        if (j == 0 && wave == W - 1 && c > 0) store_y(c - 1);
+        if (j == 0 && wave == W - 1 && c > 0) store_y(c - 1, full);
       }
       if (a.ckpt && wave == 0 && (c & 1) == 0 && dvalid)
         buf_st32(__float_as_uint(h), ck_r, ck_off, (uint32_t)(((c >> 1) * NS + 4 * j) * 4));
@@ -930,10 +950,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5)))
             av = ex2(dli * A);
             xv = wi * bq[q];
           } else if constexpr (RULE == kRuleEuler) {
-            av = fmaf(dli * kLn2, A, 1.0f);
+            av = fmaf(dli, A, 1.0f);
             xv = wi * bq[q];
           } else {  // bilinear
-            const float x = 0.5f * kLn2 * dli * A;  // delta A / 2
+            const float x = 0.5f * dli * A;  // delta A / 2
             const float rr = rcp(1.0f - x);
             av = (1.0f + x) * rr;
             xv = wi * rr * bq[q];
@@ -952,7 +972,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5)))
       // one wave's LDS accesses complete in order, so the count lands after
       // the state (a compiler fence keeps that order in the code; no wait)
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      if (lane == 0) __hip_atomic_store(&sDone[wave], (int)(item + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      if (lane == 0) __hip_atomic_store(&sDone[wave], item + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       if (wave == W - 1 && !more && a.final_state && dvalid) buf_st32(__float_as_uint(h), fs_r, fs_off, 16 * j);
       // the next chunk's step sizes and u weights: two steps after each of
       // the middle items (the first item stages B and C, the last finishes
@@ -962,10 +982,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5)))
           opaque(nxt.u);
           opaque(nxt.dl);
         }
-        prep_pair(nxt, 2 * (j - 1), c + 1);
+        prep_pair(nxt, 2 * (j - 1), c + 1, full);
       }
       if (j == 3 && CKPT) {
-        if (c + 2 < nchunks) load_ud(nxt, c + 2);
+        if (more2) load_ud(nxt, c + 2, full);
       } else if (j == 3) {
         // readout: add the 4 rows' partial sums, finish and store
         float o[4];
@@ -993,13 +1013,18 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5)))
         *reinterpret_cast<uint2*>(&sY[c & 1][cl][qstep]) =
             make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
         cur_u = nxt.u;
-        if (c + 2 < nchunks) load_ud(nxt, c + 2);
+        if (more2) load_ud(nxt, c + 2, full);
       }
     }
-  }
+  };
+  // chunks whose loads ahead are all whole, then the rest
+  const int nmain = (int)(L / T) - 2;
+  int c = 0;
+  for (; c < nmain; ++c) chunk(c, std::true_type{});
+  for (; c < nchunks; ++c) chunk(c, general);
   if constexpr (!CKPT) {
     __syncthreads();  // every wave has finished the last chunk
-    if (wave == W - 1) store_y(nchunks - 1);
+    if (wave == W - 1) store_y(nchunks - 1, general);
   }
 }
 
