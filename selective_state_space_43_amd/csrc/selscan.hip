@@ -128,9 +128,12 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// Two floats to bf16 (round to nearest even), lo in the low half: one
+// conversion of the pair.
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const __bf16 a = (__bf16)lo, b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2v){lo, hi}, bf16x2v));
 }
 
 template <typename IO>
@@ -816,6 +819,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5)))
   // chunk cc's y rows from sY to HBM: lane 4 k + q writes steps 16 q .. 16 q
   // + 15 of channel k, so four lanes cover one 128-byte row
   auto store_y = [&](int cc, auto full) {
+    cc = __builtin_amdgcn_readfirstlane(cc);  // uniform: keeps the offset scalar
     const int sch = lane >> 2, sq = lane & 3;
     if (d0 + sch >= a.dim) return;
     const uint16_t* src = &sY[cc & 1][sch][16 * sq];
@@ -908,11 +912,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5)))
       const int n = 4 * j + r;
       const int item = 4 * c + j;
       // wait until the predecessor has handed over this item's states: wave
-      // s - 1 the same item, wave 3 (for wave 0) the item one chunk back.
+      // s - 1 the same item, wave 3 (for wave 0) the item one chunk back
+      // (in chunk 0 wave 0 needs at most 0 items: its slots hold h0).
       // The wait is bounded (2^23 sleeps, a fraction of a second); the
       // waves of a workgroup are resident together, so it never runs out
       // in a correct launch, and if it did the kernel would still end.
-      if (!(wave == 0 && c == 0)) {
+      {
         const int need = wave == 0 ? item - 3 : item + 1;
 #pragma unroll 1
         for (int spin = 0; spin < (1 << 23); ++spin) {
