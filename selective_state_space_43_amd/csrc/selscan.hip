@@ -1246,6 +1246,197 @@ __global__ void __launch_bounds__(256) scan_bwd_carry_kernel(const BwdArgs a) {
   }
 }
 
+// The carry pass for 16 states and bf16 rows, time-pipelined like the
+// forward's scan_fwd_pipe_kernel: every lane runs the adjoint recurrence
+// (the form above: lambda_t = dyc_t C_t + mu_{t+1}, mu_t = Abar_t lambda_t,
+// backwards in t) over its own steps, with no fold and no scan.  Lane
+// 16 r + c holds channel c and the states 4 j + r (items j = 0..3); the four
+// waves are the 16-step segments of every 64-step chunk taken from the end
+// (wave s runs steps 48 - 16 s .. 63 - 16 s), the chunks run from the last
+// to the first, and mu passes from wave s to wave s + 1 (from wave 3 to wave
+// 0 of the chunk before) through LDS slots with counted items, as in the
+// forward.  Two chunks make a checkpoint block: mu at the first step of an
+// even chunk is the carry of the block before it, and the last block's
+// carry is the final-state gradient.  The per-step values (step size,
+// dy silu(z)) of a lane's four steps of the next chunk are formed during
+// this one and shared through LDS.
+template <bool VEC, bool GATE>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5)))
+    scan_bwd_carry_pipe_kernel(const BwdArgs a) {
+  using IO = uint16_t;
+  constexpr int W = 4, K = 16, T = W * K, NS = 16, KP = K + 4;
+  static_assert(kCkptT == 2 * T, "a checkpoint block is two chunks");
+  __shared__ float4 sWave[W][NS * KP / 4];      // per wave: C rows of its segment
+  __shared__ float4 sPrep[W][2 * 16 * KP / 4];  // per wave: step sizes, dy silu(z)
+  __shared__ float sCarry[W][4][64];            // mu handed from wave s to s + 1
+  __shared__ int sDone[W];
+  __shared__ float sA[4][64];                   // A log2 e as [j][lane]
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane >> 4, cl = lane & 15;
+  const int64_t b = blockIdx.y;
+  const int64_t d0 = (int64_t)blockIdx.x * 16;
+  const int64_t d = d0 + cl;
+  const bool dvalid = d < a.dim;
+  const int64_t dc = dvalid ? d : d0;
+  const int64_t L = a.seqlen;
+  const int nchunks = (int)((L + T - 1) / T);  // L < 2^26 (launcher)
+  const int64_t nblk = a.chunks;               // checkpoint blocks
+  float* tile = reinterpret_cast<float*>(sWave[wave]);
+  float* prep = reinterpret_cast<float*>(sPrep[wave]);
+  const int seg0 = K * (W - 1 - wave);  // first step of this wave's segment in a chunk
+  constexpr int ES = sizeof(IO);
+  const int64_t seq_base = (b * a.dim + d0) * L;
+  const int64_t nrows = a.dim - d0 < 16 ? a.dim - d0 : 16;
+  const int seq_bytes = (int)(nrows * L * ES);
+  const Rsrc dy_r = make_rsrc(static_cast<const IO*>(a.dy) + seq_base, seq_bytes);
+  const Rsrc dl_r = make_rsrc(static_cast<const IO*>(a.delta) + seq_base, seq_bytes);
+  const Rsrc z_r = make_rsrc(GATE ? static_cast<const IO*>(a.z) + seq_base : nullptr, GATE ? seq_bytes : 0);
+  const Rsrc C_r = make_rsrc(static_cast<const IO*>(a.Cm) + b * NS * L, (int)(NS * L * ES));
+  const int qstep = seg0 + 4 * r;  // first step of this lane's quad in a chunk
+  // lane (r, c): its quad of channel c's rows and, for the C tile, of state c's row
+  const uint32_t seq_off = (uint32_t)((cl * L + qstep) * ES);
+  // carries: [channel][nblk][NS] rows from (b, d0) on
+  const Rsrc cy_r = make_rsrc(a.carry + (b * a.dim + d0) * nblk * NS, (int)(nrows * nblk * NS * 4));
+  const uint32_t cy_off = (uint32_t)(((dc - d0) * nblk * NS + r) * 4);
+
+  if (wave == 0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sA[j][lane] = a.A[dc * NS + 4 * j + r] * kLog2e;
+  }
+  const float bias = (a.delta_bias && dvalid) ? a.delta_bias[d] : 0.0f;
+
+  // The chunk body comes in two forms: FULL for whole chunks (every chunk
+  // but the last, and the last when 64 divides L), whose steps need no lane
+  // masks, and the general one.  The look-ahead loads are of whole chunks
+  // and are issued unmasked in every chunk (near the start they read chunk
+  // 0 again, in bounds and unused), so that the number of memory operations
+  // after each load is the same on every path and the wait for a load does
+  // not have to drain the younger ones.
+  auto left = [&](int c) { return (int)(L - (int64_t)c * T < T ? L - (int64_t)c * T : T); };
+  auto coff = [&](int c) { return (uint32_t)c * (uint32_t)(T * ES); };
+  auto quad_n = [&](int c, auto full) { return decltype(full)::value ? 4 : left(c) - qstep; };
+  struct Raw {
+    Quad dy, dl, z;
+  };
+  auto load_raw = [&](Raw& q, int c, auto full) {
+    const int n = quad_n(c, full);
+    quad_load<VEC>(q.dy, dy_r, seq_off, coff(c), n);
+    quad_load<VEC>(q.dl, dl_r, seq_off, coff(c), n);
+    if constexpr (GATE) quad_load<VEC>(q.z, z_r, seq_off, coff(c), n);
+  };
+  Quad cq_raw;
+  auto load_c = [&](int c, auto full) { quad_load<VEC>(cq_raw, C_r, seq_off, coff(c), quad_n(c, full)); };
+  // steps i, i + 1 of the lane's quad of chunk c -> LDS: the step size
+  // (natural units; zero past L, an identity step) and dy silu(z)
+  auto prep_pair = [&](const Raw& q, int i, int c, auto full) {
+    float v[2], g[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const float x = q.dl.at(i + k) + bias;
+      float s = a.softplus ? softplus_nat(x) : x;
+      if constexpr (!decltype(full)::value) s = qstep + i + k < left(c) ? s : 0.0f;
+      v[k] = s;
+      g[k] = GATE ? q.dy.at(i + k) * silu_f(q.z.at(i + k)) : q.dy.at(i + k);
+    }
+    *reinterpret_cast<float2*>(prep + cl * KP + 4 * r + i) = make_float2(v[0], v[1]);
+    *reinterpret_cast<float2*>(prep + 16 * KP + cl * KP + 4 * r + i) = make_float2(g[0], g[1]);
+  };
+
+  const std::false_type general{};
+  const int clast = nchunks - 1;
+  Raw nxt{};
+  {
+    Raw first;
+    load_raw(first, clast, general);
+    load_c(clast, general);
+    load_raw(nxt, clast > 0 ? clast - 1 : 0, std::true_type{});
+    prep_pair(first, 0, clast, general);
+    prep_pair(first, 2, clast, general);
+  }
+  if (wave == W - 1) {
+    // mu entering the last step is the final-state gradient; it is also the
+    // last block's carry
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float mu = (a.dfinal && dvalid) ? a.dfinal[(b * a.dim + d) * NS + 4 * j + r] : 0.0f;
+      sCarry[W - 1][j][lane] = mu;
+      if (dvalid) buf_st32(__float_as_uint(mu), cy_r, cy_off, (uint32_t)(((nblk - 1) * NS + 4 * j) * 4));
+    }
+  }
+  if (threadIdx.x < W) sDone[threadIdx.x] = 0;
+  __syncthreads();
+  const int pred = (wave + W - 1) & (W - 1);
+
+  // chunk c, the p-th processed
+  auto chunk = [&](const int c, const int p, auto full) {
+    {
+      opaque(cq_raw);
+      *reinterpret_cast<float4*>(tile + cl * KP + 4 * r) =
+          make_float4(cq_raw.at(0), cq_raw.at(1), cq_raw.at(2), cq_raw.at(3));
+    }
+    load_c(c > 0 ? c - 1 : 0, std::true_type{});
+    wave_lds_sync();
+    float dl[K], g[K];
+#pragma unroll
+    for (int i = 0; i < K; i += 4) {
+      const float4 pv = *reinterpret_cast<const float4*>(prep + cl * KP + i);
+      const float4 qv = *reinterpret_cast<const float4*>(prep + 16 * KP + cl * KP + i);
+      dl[i] = pv.x; dl[i + 1] = pv.y; dl[i + 2] = pv.z; dl[i + 3] = pv.w;
+      g[i] = qv.x; g[i + 1] = qv.y; g[i + 2] = qv.z; g[i + 3] = qv.w;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int item = 4 * p + j;
+      // the predecessor's hand-over of this item (bounded wait, as in the
+      // forward; in the first chunk wave 0 needs none: its slots hold dfinal)
+      {
+        const int need = wave == 0 ? item - 3 : item + 1;
+#pragma unroll 1
+        for (int spin = 0; spin < (1 << 23); ++spin) {
+          if (__builtin_amdgcn_readfirstlane(__hip_atomic_load(&sDone[pred], __ATOMIC_RELAXED,
+                                                               __HIP_MEMORY_SCOPE_WORKGROUP)) >= need)
+            break;
+          __builtin_amdgcn_s_sleep(1);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+      }
+      float mu = sCarry[pred][j][lane];
+      const float A = sA[j][lane];
+      const float* pc = tile + (4 * j + r) * KP;
+#pragma unroll
+      for (int i = K - 4; i >= 0; i -= 4) {
+        const float4 cc = *reinterpret_cast<const float4*>(pc + i);
+        const float cq[4] = {cc.x, cc.y, cc.z, cc.w};
+#pragma unroll
+        for (int q = 3; q >= 0; --q) {
+          const float lam = fmaf(g[i + q], cq[q], mu);
+          mu = ex2(dl[i + q] * A) * lam;
+        }
+      }
+      sCarry[wave][j][lane] = mu;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      if (lane == 0) __hip_atomic_store(&sDone[wave], item + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      // mu at the first step of an even chunk c >= 2: the carry of block c / 2 - 1
+      if (wave == W - 1 && (c & 1) == 0 && c >= 2 && dvalid)
+        buf_st32(__float_as_uint(mu), cy_r, cy_off, (uint32_t)(((c / 2 - 1) * NS + 4 * j) * 4));
+      if (j == 1 || j == 2) {
+        if (j == 1) {
+          opaque(nxt.dy);
+          opaque(nxt.dl);
+          if constexpr (GATE) opaque(nxt.z);
+        }
+        if (c >= 1) prep_pair(nxt, 2 * (j - 1), c - 1, std::true_type{});  // chunk c - 1 is whole
+      }
+      if (j == 3) load_raw(nxt, c > 1 ? c - 2 : 0, std::true_type{});
+    }
+  };
+  if (L % T == 0) chunk(clast, 0, std::true_type{});
+  else chunk(clast, 0, general);
+  for (int c = clast - 1, p = 1; c >= 0; --c, ++p) chunk(c, p, std::true_type{});
+}
+
 // Two consecutive elements starting at an even index (4- or 8-byte aligned).
 template <typename IO>
 struct Pair;
@@ -3355,11 +3546,22 @@ int launch_bwd_typed(const ScanArgs& fa, BwdArgs ba, int64_t batch, hipStream_t 
       hipLaunchKernelGGL((scan_fwd_kernel<IO, 16, 16, 4, 16, VEC, ZOH ? kRuleZoh : kRuleDeltaB, false, true>), grid16, dim3(256),
                          2 * 16 * (size_t)ba.dstate * sizeof(float), s, fa);
   }
-  // 2. adjoint carries at every block end (a reverse pass over 256-step chunks)
-  if (ba.dstate <= 16)
+  // 2. adjoint carries at every block end (a reverse pass; time-pipelined
+  // where the forward is)
+  bool piped = false;
+  if constexpr (std::is_same<IO, uint16_t>::value) {
+    if (ba.dstate == 16 && batch * ba.dim >= SELSCAN_PIPE_MIN_CHANNELS &&
+        16 * ba.seqlen * (int64_t)sizeof(IO) < ((int64_t)1 << 31)) {
+      hipLaunchKernelGGL((scan_bwd_carry_pipe_kernel<VEC, GATE>), grid16, dim3(256), 0, s, ba);
+      piped = true;
+    }
+  }
+  if (piped) {
+  } else if (ba.dstate <= 16) {
     hipLaunchKernelGGL((scan_bwd_carry_kernel<IO, 16, VEC, GATE, false>), grid16, dim3(256), 0, s, ba);
-  else
+  } else {
     hipLaunchKernelGGL((scan_bwd_carry_kernel<IO, 16, VEC, GATE, true>), grid16, dim3(256), 0, s, ba);
+  }
   // 3. gradients, every (sequence, chunk) independently; groups of 4 channels
   const int64_t ngroups = (ba.dim + 3) / 4;
   const int64_t cells = ngroups * ba.chunks * batch;

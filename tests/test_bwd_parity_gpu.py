@@ -118,6 +118,13 @@ BWD_CASES = [
     (2, 20, 64, 260, "bf16", True, True, "delta"),
     (1, 17, 48, 129, "bf16", False, True, "zoh"),
     (1, 8, 17, 77, "f32", True, True, "delta"),
+    # 8192 channels and more with 16 states and bf16 rows: the time-pipelined
+    # checkpoint and carry passes (a ragged last chunk of 64 steps and block of
+    # 128, odd L: the element-wise loads, dim not a multiple of 16)
+    (1, 8200, 16, 77, "bf16", True, True, "delta"),
+    (2, 4104, 16, 200, "bf16", False, False, "zoh"),
+    (1, 8192, 16, 384, "bf16", True, False, "delta"),
+    (3, 2740, 16, 203, "bf16", True, True, "zoh"),
 ]
 
 
