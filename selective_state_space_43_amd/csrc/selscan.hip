@@ -502,6 +502,66 @@ __global__ void __launch_bounds__(64 * W)
     }
   };
 
+  // PREF (the layouts with 32 and 64 lanes per channel, whose occupancy the
+  // grid limits to one or two workgroups per CU; vectorised rows): the next
+  // B/C tile is loaded into registers while the current one is computed,
+  // instead of between two barriers where every wave of the workgroup waits
+  // for it.  The loads are unconditional (a vector past L reads its row's
+  // start instead; rows are whole vectors long) and the vectors past L are
+  // zeroed when the tile is written to LDS, so the number of memory
+  // operations is the same on every path and the compiler's wait for the
+  // tile covers only older ones.
+  constexpr bool PREF = LPC >= 32 && VEC && !CKPT;
+  uint4 pre[PREF ? ITEMS : 1];
+  int64_t pre_t0 = 0;  // first step of the prefetched tile's chunk
+  auto tile_nt = [&](int64_t n0) { return (int)((N - n0) < NT ? (N - n0) : NT); };
+  auto fetch_bc = [&](int64_t t0, int64_t n0) __attribute__((always_inline)) {
+    const int nt = tile_nt(n0);
+    pre_t0 = t0;
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k) {
+      // items past the tile (a last tile of fewer states) load item 0's vector
+      const int item0 = threadIdx.x + k * NTH;
+      const int item = item0 < 2 * nt * TV ? item0 : 0;
+      const int tensor = item / (nt * TV);
+      const int r = item % (nt * TV);
+      const int nl = r / TV, tloc = (r % TV) * V;
+      const int64_t rowp = bcrow + (n0 + nl) * L;
+      const int64_t t = t0 + tloc < L ? t0 + tloc : 0;
+      pre[k] = *reinterpret_cast<const uint4*>(static_cast<const IO*>(tensor ? a.Cm : a.Bm) + rowp + t);
+    }
+  };
+  auto put_bc = [&](int64_t n0) __attribute__((always_inline)) {
+    const int nt = tile_nt(n0);
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k) {
+      const int item = threadIdx.x + k * NTH;
+      if (item < 2 * nt * TV) {
+        const int tensor = item / (nt * TV);
+        const int r = item % (nt * TV);
+        const int nl = r / TV, tloc = (r % TV) * V;
+        Run<IO, V> rv;
+        const bool in = pre_t0 + tloc < L;
+        const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
+        __builtin_memcpy(&rv.v[0], in ? &pre[k] : &z4, sizeof(uint4));
+        float v[V];
+        rv.unpack(v);
+        float* dst = (tensor ? sC : sB) + (nl * LPC + tloc / K) * KP + tloc % K;
+#pragma unroll
+        for (int q = 0; q < V; q += 4)
+          *reinterpret_cast<float4*>(dst + q) = make_float4(v[q], v[q + 1], v[q + 2], v[q + 3]);
+      }
+    }
+  };
+  // write the prefetched tile (t0, n0) and fetch the one after it: the next
+  // states of the chunk, else the next chunk's first (past L: not read)
+  auto put_and_fetch = [&](int64_t t0, int64_t n0) __attribute__((always_inline)) {
+    put_bc(n0);
+    asm volatile("" ::: "memory");  // the new loads stay after the old tile is consumed
+    if (n0 + NT < N) fetch_bc(t0, n0 + NT);
+    else fetch_bc(t0 + T < L ? t0 + T : t0, 0);
+  };
+
   // One chunk of T timesteps.  FULL: the chunk lies inside [0, L) and N is a
   // multiple of NT, so no step or state needs masking.
   auto chunk = [&](int64_t t0, auto full_tag) {
@@ -513,13 +573,17 @@ __global__ void __launch_bounds__(64 * W)
     float dl[K], w[K], y[K], ul[K];
     float S = 0.0f;
     // issue this chunk's sequence loads first: they complete while the first
-    // B/C tile is staged
+    // B/C tile is staged.  With PREF every lane loads (lanes of channels past
+    // `dim` read channel 0's row and store nothing), so that the number of
+    // loads is fixed and the wait for the prefetched tile need not cover them.
+    const bool lv = PREF ? true : dvalid;
     Run<IO, K> ru, rd, rz;
-    run_load<IO, K, VEC, FULL>(ru, a.u, row, tl, L, dvalid);
-    run_load<IO, K, VEC, FULL>(rd, a.delta, row, tl, L, dvalid);
-    if constexpr (GATE) run_load<IO, K, VEC, FULL>(rz, a.z, row, tl, L, dvalid);
+    run_load<IO, K, VEC, FULL>(ru, a.u, row, tl, L, lv);
+    run_load<IO, K, VEC, FULL>(rd, a.delta, row, tl, L, lv);
+    if constexpr (GATE) run_load<IO, K, VEC, FULL>(rz, a.z, row, tl, L, lv);
     __syncthreads();  // every wave is done with the previous chunk's last tile
-    stage_bc(t0, 0, (int)(N < NT ? N : NT), full_tag);
+    if constexpr (PREF) put_and_fetch(t0, 0);
+    else stage_bc(t0, 0, (int)(N < NT ? N : NT), full_tag);
     __syncthreads();
     {
       float raw[K];
@@ -609,7 +673,8 @@ __global__ void __launch_bounds__(64 * W)
     for (int64_t n0 = 0; n0 < N; n0 += NT) {
       if (n0 > 0) {
         __syncthreads();  // every wave is done with the previous tile
-        stage_bc(t0, n0, (int)((N - n0) < NT ? (N - n0) : NT), full_tag);
+        if constexpr (PREF) put_and_fetch(t0, n0);
+        else stage_bc(t0, n0, (int)((N - n0) < NT ? (N - n0) : NT), full_tag);
         __syncthreads();
       }
       const int nt = FULL ? NT : (int)((N - n0) < NT ? (N - n0) : NT);
@@ -626,6 +691,7 @@ __global__ void __launch_bounds__(64 * W)
     run_store<IO, K, VEC, FULL>(a.y, row, tl, L, dvalid, y);
   };
 
+  if constexpr (PREF) fetch_bc(0, 0);
   int64_t t0 = 0;
   if (N % NT == 0) {
     for (; t0 + T <= L; t0 += T) chunk(t0, std::true_type{});
