@@ -503,7 +503,8 @@ __global__ void __launch_bounds__(64 * W)
   };
 
   // PREF (the layouts with 32 and 64 lanes per channel, whose occupancy the
-  // grid limits to one or two workgroups per CU; vectorised rows): the next
+  // grid limits to one or two workgroups per CU; vectorised bf16 rows: a
+  // float32 tile is twice the registers, which spill there): the next
   // B/C tile is loaded into registers while the current one is computed,
   // instead of between two barriers where every wave of the workgroup waits
   // for it.  The loads are unconditional (a vector past L reads its row's
@@ -511,7 +512,7 @@ __global__ void __launch_bounds__(64 * W)
   // zeroed when the tile is written to LDS, so the number of memory
   // operations is the same on every path and the compiler's wait for the
   // tile covers only older ones.
-  constexpr bool PREF = LPC >= 32 && VEC && !CKPT;
+  constexpr bool PREF = LPC >= 32 && VEC && !CKPT && sizeof(IO) == 2;
   uint4 pre[PREF ? ITEMS : 1];
   int64_t pre_t0 = 0;  // first step of the prefetched tile's chunk
   auto tile_nt = [&](int64_t n0) { return (int)((N - n0) < NT ? (N - n0) : NT); };
