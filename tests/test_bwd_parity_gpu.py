@@ -151,12 +151,16 @@ def test_bwd_no_h0_no_dfinal(ssm, dev):
     _case(ssm, dev, w, x, with_h0=False, with_dfinal=False, label="no h0 / dfinal")
 
 
-def test_bwd_no_softplus(ssm, dev):
-    # raw steps used as they are: keep them positive
-    w, x = wl.custom(1, 32, 16, 300, dtype="f32", bias=False, delta_mean=0.3, delta_std=0.05,
+@pytest.mark.parametrize("shape", [(1, 32, 16, 300, "f32"), (1, 8200, 16, 200, "bf16")],
+                         ids=["f32", "bf16_pipelined"])
+def test_bwd_no_softplus(ssm, dev, shape):
+    # raw steps used as they are: keep them positive (the bf16 shape takes the
+    # time-pipelined checkpoint and carry passes)
+    b, d, n, L, dt = shape
+    w, x = wl.custom(b, d, n, L, dtype=dt, bias=False, delta_mean=0.3, delta_std=0.05,
                      seed=5300)
     x["delta_softplus"] = False
-    _case(ssm, dev, w, x, label="no softplus")
+    _case(ssm, dev, w, x, label=f"no softplus {dt}")
 
 
 def test_bwd_optional_outputs_absent(ssm, dev):

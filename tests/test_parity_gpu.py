@@ -135,6 +135,12 @@ CASES = [
     (2, 8192, 4, 72, "bf16", True, True),
     (1, 16384, 2, 40, "bf16", True, True),
     (4, 4100, 3, 33, "f32", True, True),
+    # the 32- and 64-lane layouts with bf16 rows load the next B/C tile while
+    # computing the current one: several whole chunks (1024 / 512 steps), a
+    # ragged last chunk and a last tile of fewer states
+    (1, 40, 16, 2504, "bf16", True, True),
+    (1, 24, 24, 3080, "bf16", False, True),
+    (2, 4100, 12, 1096, "bf16", True, False),
 ]
 
 
@@ -195,11 +201,16 @@ def test_discretization_rules(ssm, dev, rule, dt, case):
     _check(ssm, dev, w, x, bbar=rule, label=f"{rule} {dt} {case}")
 
 
-def test_no_softplus_positive_raw_step(ssm, dev):
-    w, x = wl.custom(1, 20, 8, 300, dtype="f32", gate=False, bias=False, seed=41)
-    x["delta"] = np.abs(x["delta"]) * np.float32(0.1)
+@pytest.mark.parametrize("shape", [(1, 20, 8, 300, "f32"), (1, 8200, 16, 300, "bf16"),
+                                   (1, 40, 16, 2504, "bf16")],
+                         ids=["f32", "bf16_pipelined", "bf16_64_lanes"])
+def test_no_softplus_positive_raw_step(ssm, dev, shape):
+    # raw steps used as they are: N(0.1, 0.02), positive
+    b, d, n, L, dt = shape
+    w, x = wl.custom(b, d, n, L, dtype=dt, gate=dt == "bf16", bias=False, delta_mean=0.1,
+                     delta_std=0.02, seed=41)
     x["delta_softplus"] = False
-    _check(ssm, dev, w, x, label="raw step")
+    _check(ssm, dev, w, x, label=f"raw step {dt}")
 
 
 def test_h0_resume_in_place_equals_full_scan(ssm, dev):
