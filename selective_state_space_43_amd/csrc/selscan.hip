@@ -1377,8 +1377,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5)))
   // The chunk body comes in two forms: FULL for whole chunks (every chunk
   // but the last, and the last when 64 divides L), whose steps need no lane
   // masks, and the general one.  The look-ahead loads are of whole chunks
-  // and are issued unmasked in every chunk (near the start they read chunk
-  // 0 again, in bounds and unused), so that the number of memory operations
+  // and are issued unmasked in every chunk (in the last chunks processed,
+  // the sequence's first, they read chunk 0 again: in bounds, unused), so
+  // that the number of memory operations
   // after each load is the same on every path and the wait for a load does
   // not have to drain the younger ones.
   auto left = [&](int c) { return (int)(L - (int64_t)c * T < T ? L - (int64_t)c * T : T); };
