@@ -282,9 +282,9 @@ def bench_bwd(ssm, torch, w, x, dev, steps, warmup):
     """The backward pass (ssm_selective_scan_bwd: checkpointed forward, adjoint
     carries, gradients) on the same inputs with a seeded upstream gradient.
     Every gradient is produced; the workspace is allocated once outside the
-    timed region.  Timed standalone (the backward recomputes its checkpoints)
-    and as a training step: a forward that writes checkpoints followed by a
-    backward that takes them."""
+    timed region.  Timed standalone (the backward recomputes its checkpoints),
+    as a training step (a forward that writes checkpoints followed by a
+    backward that takes them), and as that backward alone."""
     g = wl.grad_inputs(w)
     u, dl, A, B, C = (to_dev(x[k], dev) for k in ("u", "delta", "A", "B", "C"))
     D, z, bias = to_dev(x["D"], dev), to_dev(x["z"], dev), to_dev(x["delta_bias"], dev)
@@ -320,8 +320,14 @@ def bench_bwd(ssm, torch, w, x, dev, steps, warmup):
         torch.cuda.synchronize()
         return a.elapsed_time(b) / steps
 
+    def bwd_from_checkpoints():
+        return ssm.ssm_selective_scan_bwd(u, dl, A, B, C, dy, D=D, z=z, delta_bias=bias,
+                                          delta_softplus=True, workspace=ws, want_dh0=True,
+                                          checkpoints=ck)
+
     ms = timed(step)
     ms_train = timed(train_step)
+    ms_ckpt = timed(bwd_from_checkpoints)  # ck holds the forward's checkpoints by now
     es = 2 if w.dtype == "bf16" else 4
     seq = w.batch * w.dim * w.seqlen * es
     bc = w.batch * w.dstate * w.seqlen * es
@@ -339,6 +345,8 @@ def bench_bwd(ssm, torch, w, x, dev, steps, warmup):
         "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
         "train_step_ms": round(ms_train, 4),
         "train_step": "forward writing checkpoints, then the backward taking them",
+        "ms_from_checkpoints": round(ms_ckpt, 4),
+        "from_checkpoints": "the backward alone, given the forward's checkpoints (no checkpoint pass)",
         "steps": steps,
     }
 
