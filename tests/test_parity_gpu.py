@@ -315,6 +315,34 @@ def test_state_update_small_shapes(ssm, dev, dt, rule):
         assert norm_err(to_np(state).reshape(ref.shape), ref) <= TOL[dt]
 
 
+@pytest.mark.parametrize("rule", ["delta", "zoh", "euler", "bilinear"])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_state_update_many_channels(ssm, dev, dt, rule):
+    """Over 2^18 channels in one step for every rule and io type, on the
+    four-lane kernel: channel counts that leave the last workgroup partly
+    filled, and 32 states (two 16-state blocks per channel) without the gate."""
+    for (b, d, n, gate) in [(3, 87383, 16, True), (2, 131101, 32, False)]:
+        assert b * d >= 1 << 18
+        w, x = wl.custom(b, d, n, 1, dtype=dt, gate=gate, seed=93 + n)
+        col = {k: np.ascontiguousarray(v[..., 0]) for k, v in x.items()
+               if isinstance(v, np.ndarray) and v.ndim == 3}
+        s0 = np.random.default_rng(n + 7).normal(0, 0.3, (b, d, n)).astype(np.float32)
+        state = to_dev(s0, dev)
+        z = col.get("z") if gate else None
+        y = ssm.ssm_state_update(state, to_dev(col["u"], dev), to_dev(col["delta"], dev),
+                                 to_dev(x["A"], dev), to_dev(col["B"], dev), to_dev(col["C"], dev),
+                                 D=to_dev(x["D"], dev), z=None if z is None else to_dev(z, dev),
+                                 delta_bias=to_dev(x["delta_bias"], dev), delta_softplus=True,
+                                 bbar=rule)
+        torch.cuda.synchronize()
+        ref = s0.reshape(-1, n).astype(np.float64)
+        yr = oracle.state_update(ref, col["u"], col["delta"], x["A"], col["B"], col["C"],
+                                 D=x["D"], z=z, delta_bias=x["delta_bias"],
+                                 delta_softplus=True, bbar=rule)
+        assert norm_err(to_np(y).reshape(-1), yr) <= TOL[dt], (b, d, n)
+        assert norm_err(to_np(state).reshape(ref.shape), ref) <= TOL[dt], (b, d, n)
+
+
 def test_state_update_unaligned_A_takes_the_one_lane_kernel(ssm, dev):
     """16 states with A not 16-byte aligned (a view one float into a buffer):
     the one-lane kernel instead of the four-lane one, same results."""
