@@ -2863,22 +2863,26 @@ __global__ void __launch_bounds__(256) state_update_kernel(const StepArgs a) {
 // 16-byte accesses to the state rows and to A covers 16 whole 64-byte rows;
 // the readout's four partial sums are added across the lane quad (DPP).  The
 // per-token work (step size, gate) is done by all four lanes.
-template <typename IO, int RULE, bool GATE>
+// OFF32 (every element index of the state and of A below 2^31, checked by
+// the launcher): the channel split and the element offsets take 32-bit
+// arithmetic, in place of 64-bit divisions, products and adds per lane.
+template <typename IO, int RULE, bool GATE, bool OFF32>
 __global__ void __launch_bounds__(256) state_update4_kernel(const StepArgs a) {
-  const int64_t c = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 2;
+  using Ix = typename std::conditional<OFF32, uint32_t, int64_t>::type;
+  const Ix c = (Ix)(((int64_t)blockIdx.x * 256 + threadIdx.x) >> 2);
   const int q = threadIdx.x & 3;
-  if (c >= a.batch * a.dim) return;  // the four lanes of a channel leave together
-  const int64_t b = c / a.dim, d = c % a.dim;
-  const int64_t N = a.dstate;
+  if ((int64_t)c >= a.batch * a.dim) return;  // the four lanes of a channel leave together
+  const Ix dim = (Ix)a.dim, N = (Ix)a.dstate;
+  const Ix b = c / dim, d = c - b * dim;
   const float uu = Io<IO>::ld1(a.u, c);
   const float raw = Io<IO>::ld1(a.delta, c) + (a.delta_bias ? a.delta_bias[d] : 0.0f);
   const float dl = a.softplus ? softplus_log2(raw) : raw * kLog2e;  // delta / ln 2
   const float w = dl * kLn2 * uu;                                   // delta u
   float* st = a.state + c * N + 4 * q;
   const float* Ar = a.A + d * N + 4 * q;
-  const int64_t bc = b * N + 4 * q;
+  const Ix bc = b * N + 4 * q;
   float acc = 0.0f;
-  for (int64_t n0 = 0; n0 < N; n0 += 16) {
+  for (Ix n0 = 0; n0 < N; n0 += 16) {
     const f32x4 s4 = *reinterpret_cast<const f32x4*>(st + n0);
     const float4 a4 = *reinterpret_cast<const float4*>(Ar + n0);
     float h[4] = {s4.x, s4.y, s4.z, s4.w};
@@ -3972,13 +3976,22 @@ int ssm_state_update(float* state, const void* u, const void* delta, const float
   with_rule(bbar_mode, [&](auto rt) {
     constexpr int R = decltype(rt)::value;
     if (a.vec) {
-      if (io_dtype == SSM_DTYPE_BF16) {
-        if (gate) hipLaunchKernelGGL((state_update4_kernel<uint16_t, R, true>), grid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((state_update4_kernel<uint16_t, R, false>), grid, dim3(256), 0, s, a);
-      } else {
-        if (gate) hipLaunchKernelGGL((state_update4_kernel<float, R, true>), grid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((state_update4_kernel<float, R, false>), grid, dim3(256), 0, s, a);
-      }
+      // 32-bit element offsets: the largest is a state or A element index
+      const bool off32 = batch * dim * dstate < ((int64_t)1 << 31) && dim * dstate < ((int64_t)1 << 31);
+      auto go = [&](auto io, auto gt, auto o32) {
+        hipLaunchKernelGGL((state_update4_kernel<decltype(io), R, decltype(gt)::value, decltype(o32)::value>),
+                           grid, dim3(256), 0, s, a);
+      };
+      auto go_off = [&](auto io, auto gt) {
+        if (off32) go(io, gt, std::true_type{});
+        else go(io, gt, std::false_type{});
+      };
+      auto go_gate = [&](auto io) {
+        if (gate) go_off(io, std::true_type{});
+        else go_off(io, std::false_type{});
+      };
+      if (io_dtype == SSM_DTYPE_BF16) go_gate(uint16_t{});
+      else go_gate(float{});
     } else if (io_dtype == SSM_DTYPE_BF16) {
       if (gate) hipLaunchKernelGGL((state_update_kernel<uint16_t, R, true>), grid, dim3(256), 0, s, a);
       else hipLaunchKernelGGL((state_update_kernel<uint16_t, R, false>), grid, dim3(256), 0, s, a);
