@@ -1938,24 +1938,34 @@ scan_bwd_main_kernel(const BwdArgs a) {
   flush();
   __syncthreads();  // the last group's sums are in LDS
   if (g_begin < g_end) issue_sums(g_end - 1, (int)((g_end - 1) & 1));
-  // ---- this chunk's dB and dC from every channel the block visited
+  // ---- this chunk's dB and dC from every channel the block visited.
+  // After the row sums, lane (seg, row) holds steps seg K + red_row (lo) and
+  // seg K + red_row + 4 (hi).  The hi values are rotated by half a row
+  // (segments seg and seg +- 8 trade them), so that the first atomic of each
+  // tensor covers segments 0..7 and the second segments 8..15, each as whole
+  // 32-byte runs of eight steps (two atomics per sector otherwise).
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int n = wave + NW * j;
-    const int64_t t = t0 + seg * K + red_row;
     if (n < nt) {
       float* pBn = a.accB + (b * N + n0 + n) * L;
       float* pCn = a.accC + (b * N + n0 + n) * L;
       float bl, bh, cl, chh;
       rows_sum8(accB[j], bl, bh);
       rows_sum8(accC[j], cl, chh);
-      if (t < L) {
-        unsafeAtomicAdd(pBn + t, bl);
-        unsafeAtomicAdd(pCn + t, cl);
+      const float bh8 = dpp<0x128, 0xf>(0.0f, bh);   // row_ror:8: segment seg -+ 8's hi
+      const float ch8 = dpp<0x128, 0xf>(0.0f, chh);
+      const bool low = seg < 8;
+      // first atomic: segments 0..7; second: segments 8..15
+      const int64_t ta = t0 + (low ? seg * K + red_row : (seg - 8) * K + red_row + 4);
+      const int64_t tb = t0 + (low ? (seg + 8) * K + red_row + 4 : seg * K + red_row);
+      if (ta < L) {
+        unsafeAtomicAdd(pBn + ta, low ? bl : bh8);
+        unsafeAtomicAdd(pCn + ta, low ? cl : ch8);
       }
-      if (t + 4 < L) {
-        unsafeAtomicAdd(pBn + t + 4, bh);
-        unsafeAtomicAdd(pCn + t + 4, chh);
+      if (tb < L) {
+        unsafeAtomicAdd(pBn + tb, low ? bh8 : bl);
+        unsafeAtomicAdd(pCn + tb, low ? ch8 : cl);
       }
     }
   }
