@@ -100,13 +100,21 @@ __device__ __forceinline__ float softplus_log2(float x) {
   return x > 15.0f ? xl : l;
 }
 
-// softplus(x) in natural units with the compensation of softplus_log2.
-__device__ __forceinline__ float softplus_nat(float x) {
-  const float e = ex2(x * kLog2e);
+// softplus(raw + bias) / ln 2 from xl = (raw + bias) / ln 2 (formed by the
+// caller as one fma), with the compensation of softplus_log2 and its factor
+// (u - 2) / ln 2 as one fma.
+__device__ __forceinline__ float softplus_xl(float xl) {
+  const float e = ex2(xl);
   const float u = 1.0f + e;
-  const float l = fmaf((u - 1.0f) - e, u - 2.0f, lg2(u) * kLn2);
-  return x > 15.0f ? x : l;
+  const float l = fmaf((u - 1.0f) - e, fmaf(u, kLog2e, -2.0f * kLog2e), lg2(u));
+  return xl > 15.0f * kLog2e ? xl : l;
 }
+
+// silu(z) ln 2: the ln 2 goes into the reciprocal's argument for free.
+__device__ __forceinline__ float silu_ln2(float z) {
+  return z * rcp(fmaf(ex2(-z * kLog2e), kLog2e, kLog2e));
+}
+
 
 // silu(z) = z * sigmoid(z)
 __device__ __forceinline__ float silu_f(float z) { return z * rcp(1.0f + ex2(-z * kLog2e)); }
@@ -118,6 +126,15 @@ __device__ __forceinline__ float silu_f(float z) { return z * rcp(1.0f + ex2(-z 
 __device__ __forceinline__ float zoh_coef(float r, float delta, float e, float rA) {
   const float p = delta * fmaf(r, fmaf(r, fmaf(r, 1.0f / 24, 1.0f / 6), 0.5f), 1.0f);
   return fabsf(r) < 0.03125f ? p : (e - 1.0f) * rA;
+}
+
+// The same coefficient divided by ln 2, from log2-unit arguments: t = delta A
+// / ln 2, dl = delta / ln 2, e = exp2(t) and rAl = 1 / (A ln 2) (0 when A =
+// 0); the series is the one above with r = t ln 2 and the same cut.
+__device__ __forceinline__ float zoh_coef_l2(float t, float dl, float e, float rAl) {
+  constexpr float c1 = 0.5f * kLn2, c2 = kLn2 * kLn2 / 6, c3 = kLn2 * kLn2 * kLn2 / 24;
+  const float p = dl * fmaf(t, fmaf(t, fmaf(t, c3, c2), c1), 1.0f);
+  return fabsf(t) < 0.03125f * kLog2e ? p : (e - 1.0f) * rAl;
 }
 
 // ---------------------------------------------------------------- io
@@ -467,12 +484,15 @@ __global__ void __launch_bounds__(64 * W)
   for (int64_t i = threadIdx.x; i < CPB * N; i += NTH) {
     const int64_t c = i / N, n = i % N;
     const bool ok = d0 + c < a.dim;
-    sCarry[i] = (a.h0 && ok) ? a.h0[(b * a.dim + d0 + c) * N + n] : 0.0f;
+    const float h0v = (a.h0 && ok) ? a.h0[(b * a.dim + d0 + c) * N + n] : 0.0f;
+    sCarry[i] = h0v * kLog2e;  // h / ln 2 (below)
     sA[i] = ok ? a.A[(d0 + c) * N + n] : 0.0f;
+    // the checkpoint of block 0 is h0 itself
+    if (a.ckpt && ok) a.ckpt[(b * a.dim + d0 + c) * ((L + kCkptT - 1) / kCkptT) * N + n] = h0v;
   }
-  // y accumulates D u with u kept as u ln 2 (see below)
+  // y accumulates (D u + C h) / ln 2 (see below)
   const float Dl = ((a.Dskip && dvalid) ? a.Dskip[d] : 0.0f) * kLog2e;
-  const float bias = (a.delta_bias && dvalid) ? a.delta_bias[d] : 0.0f;
+  const float bias = ((a.delta_bias && dvalid) ? a.delta_bias[d] : 0.0f) * kLog2e;  // bias / ln 2
   float* carry_row = sCarry + chb * N;
   const float* a_row = sA + chb * N;
 
@@ -568,9 +588,12 @@ __global__ void __launch_bounds__(64 * W)
   auto chunk = [&](int64_t t0, auto full_tag) {
     constexpr bool FULL = decltype(full_tag)::value;
     const int64_t tl = t0 + seg * K;
-    // Step sizes are kept in log2 units, dl = delta / ln 2, so that
-    // Abar = exp(delta A) = exp2(dl A) with A in natural units, and u is
-    // kept as ul = u ln 2 so that delta u = dl ul.
+    // Step sizes are kept in log2 units, dl = delta / ln 2 (from the raw
+    // step by one fma), so that Abar = exp(delta A) = exp2(dl A) with A in
+    // natural units.  The u weight dl u = delta u / ln 2 scales the whole
+    // recurrence: lanes, carries and the readout hold h / ln 2 and y / ln 2,
+    // converted where a state enters (h0) or leaves (final state,
+    // checkpoints) and once per output step (for free inside the gate).
     float dl[K], w[K], y[K], ul[K];
     float S = 0.0f;
     // issue this chunk's sequence loads first: they complete while the first
@@ -592,10 +615,9 @@ __global__ void __launch_bounds__(64 * W)
       rd.unpack(raw);
 #pragma unroll
       for (int i = 0; i < K; ++i) {
-        const float x = raw[i] + bias;
-        float v = a.softplus ? softplus_log2(x) : x * kLog2e;
+        const float xl = fmaf(raw[i], kLog2e, bias);  // (raw + bias) / ln 2
+        float v = a.softplus ? softplus_xl(xl) : xl;
         if constexpr (!FULL) v = (tl + i < L) ? v : 0.0f;  // identity step past the end
-        ul[i] *= kLn2;
         dl[i] = v;
         w[i] = v * ul[i];
         y[i] = Dl * ul[i];
@@ -610,7 +632,7 @@ __global__ void __launch_bounds__(64 * W)
       const float* pb = sB + (j * LPC + seg) * KP;
       const float* pc = sC + (j * LPC + seg) * KP;
       float av[K], xv[K];
-      const float rA = (RULE == kRuleZoh && An != 0.0f) ? rcp(An) : 0.0f;
+      const float rA = (RULE == kRuleZoh && An != 0.0f) ? rcp(An * kLn2) : 0.0f;  // 1 / (A ln 2)
 #pragma unroll
       for (int i = 0; i < K; i += 4) {
         const float4 bb = *reinterpret_cast<const float4*>(pb + i);
@@ -623,7 +645,7 @@ __global__ void __launch_bounds__(64 * W)
           } else if constexpr (RULE == kRuleZoh) {
             const float t = dl[i + q] * An;  // delta A / ln 2
             av[i + q] = ex2(t);
-            xv[i + q] = zoh_coef(t * kLn2, dl[i + q] * kLn2, av[i + q], rA) * bq[q] * (ul[i + q] * kLog2e);
+            xv[i + q] = zoh_coef_l2(t, dl[i + q], av[i + q], rA) * bq[q] * ul[i + q];  // / ln 2, as h
           } else if constexpr (RULE == kRuleEuler) {
             av[i + q] = fmaf(dl[i + q] * kLn2, An, 1.0f);
             xv[i + q] = w[i + q] * bq[q];
@@ -656,8 +678,8 @@ __global__ void __launch_bounds__(64 * W)
       if (seg == LPC - 1) carry_row[n] = H;
       static_assert(!CKPT || (kCkptT % K == 0 && T % kCkptT == 0), "checkpoints fall on lane starts");
       if constexpr (kCkptT % K == 0 && T % kCkptT == 0) {
-        if (a.ckpt && dvalid && (seg * K) % kCkptT == 0 && tl < L)
-          a.ckpt[((b * a.dim + d) * ((L + kCkptT - 1) / kCkptT) + tl / kCkptT) * N + n] = h;
+        if (a.ckpt && dvalid && (seg * K) % kCkptT == 0 && tl < L && tl > 0)  // block 0's: above
+          a.ckpt[((b * a.dim + d) * ((L + kCkptT - 1) / kCkptT) + tl / kCkptT) * N + n] = h * kLn2;
       }
 #pragma unroll
       for (int i = 0; i < K; i += 4) {
@@ -687,7 +709,10 @@ __global__ void __launch_bounds__(64 * W)
       float zz[K];
       rz.unpack(zz);
 #pragma unroll
-      for (int i = 0; i < K; ++i) y[i] *= silu_f(zz[i]);
+      for (int i = 0; i < K; ++i) y[i] *= silu_ln2(zz[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < K; ++i) y[i] *= kLn2;
     }
     run_store<IO, K, VEC, FULL>(a.y, row, tl, L, dvalid, y);
   };
@@ -702,7 +727,7 @@ __global__ void __launch_bounds__(64 * W)
   if (a.final_state && dvalid) {
     // each channel's carry was written by its own wave; LDS is in order per wave
     for (int64_t n = seg; n < N; n += LPC)
-      a.final_state[(b * a.dim + d) * N + n] = carry_row[n];
+      a.final_state[(b * a.dim + d) * N + n] = carry_row[n] * kLn2;
   }
 }
 
@@ -840,17 +865,22 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5)))
   // channels past `dim` lie past the resource's extent and read as zero.
   const uint32_t seq_off = (uint32_t)((cl * L + qstep) * ES);
 
-  // A, for the delta*B rule in log2 units (step sizes are kept in natural
-  // units, so that Abar = exp2(delta A log2 e) and delta u take one multiply each)
+  // Step sizes are kept in log2 units (dl = delta / ln 2, from the raw step
+  // by one fma), so that Abar = exp2(dl A) for the delta*B rule; A is held
+  // as A ln 2 for the other rules, whose formulas take delta A.  The u weight
+  // dl u = delta u / ln 2 then scales the whole recurrence: the lanes carry
+  // h / ln 2, which is converted where a state enters (h0) or leaves (final
+  // state, checkpoints), and the readout sum is multiplied by ln 2 once per
+  // step, for free inside the gate's reciprocal.
   if (wave == 0) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float Av = a.A[dc * NS + 4 * j + r];
-      sA[j][lane] = RULE == kRuleDeltaB ? Av * kLog2e : Av;
+      sA[j][lane] = RULE == kRuleDeltaB ? Av : Av * kLn2;
     }
   }
-  const float Dv = (a.Dskip && dvalid) ? a.Dskip[d] : 0.0f;
-  const float bias = (a.delta_bias && dvalid) ? a.delta_bias[d] : 0.0f;
+  const float Dv = (a.Dskip && dvalid) ? a.Dskip[d] * kLog2e : 0.0f;  // D / ln 2
+  const float bias = (a.delta_bias && dvalid) ? a.delta_bias[d] * kLog2e : 0.0f;  // bias / ln 2
 
   // steps of chunk c before L (uniform, at most T), and the byte offset of
   // the chunk.  The chunk body below comes in two forms: FULL for chunks c
@@ -875,10 +905,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5)))
     quad_load<VEC>(bq_raw, B_r, seq_off, coff(c), n);
     if constexpr (!CKPT) quad_load<VEC>(cq_raw, C_r, seq_off, coff(c), n);
   };
-  // step size (natural units) and u weight of step i of this lane's quad
+  // step size (log2 units) and u weight of step i of this lane's quad
   auto prep_step = [&](const Ud& q, int i, int c, auto full, float& dlo, float& wo) {
-    const float x = q.dl.at(i) + bias;
-    float v = a.softplus ? softplus_nat(x) : x;
+    const float xl = fmaf(q.dl.at(i), kLog2e, bias);  // (raw + bias) / ln 2
+    float v = a.softplus ? softplus_xl(xl) : xl;
     if constexpr (!decltype(full)::value) v = qstep + i < left(c) ? v : 0.0f;  // identity step past the end
     dlo = v;
     wo = v * q.u.at(i);  // delta u
@@ -940,8 +970,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5)))
   const uint32_t ck_off = (uint32_t)(((dc - d0) * nblk * NS + r) * 4);
   if (wave == W - 1) {
 #pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float h0v = (a.h0 && dvalid) ? a.h0[(b * a.dim + d) * NS + 4 * j + r] : 0.0f;
+      sCarry[W - 1][j][lane] = h0v * kLog2e;  // h0 / ln 2
+    }
+  }
+  if (a.ckpt && wave == 0 && dvalid) {  // the state entering block 0, exactly h0
+#pragma unroll
     for (int j = 0; j < 4; ++j)
-      sCarry[W - 1][j][lane] = (a.h0 && dvalid) ? a.h0[(b * a.dim + d) * NS + 4 * j + r] : 0.0f;
+      buf_st32(__float_as_uint(a.h0 ? a.h0[(b * a.dim + d) * NS + 4 * j + r] : 0.0f), ck_r, ck_off, 16 * j);
   }
   if (threadIdx.x < W) sDone[threadIdx.x] = 0;
   __syncthreads();
@@ -1001,8 +1038,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5)))
         // before handing over this chunk's first item
         if (j == 0 && wave == W - 1 && c > 0) store_y(c - 1, full);
       }
-      if (a.ckpt && wave == 0 && (c & 1) == 0 && dvalid)
-        buf_st32(__float_as_uint(h), ck_r, ck_off, (uint32_t)(((c >> 1) * NS + 4 * j) * 4));
+      if (a.ckpt && wave == 0 && (c & 1) == 0 && c > 0 && dvalid)  // block 0's is h0 (below)
+        buf_st32(__float_as_uint(h * kLn2), ck_r, ck_off, (uint32_t)(((c >> 1) * NS + 4 * j) * 4));
       const float A = sA[j][lane];
       const float* pb = tile + n * KP;
       const float* pc = tile + NS * KP + n * KP;
@@ -1045,7 +1082,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5)))
       // the state (a compiler fence keeps that order in the code; no wait)
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       if (lane == 0) __hip_atomic_store(&sDone[wave], item + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      if (wave == W - 1 && !more && a.final_state && dvalid) buf_st32(__float_as_uint(h), fs_r, fs_off, 16 * j);
+      if (wave == W - 1 && !more && a.final_state && dvalid) buf_st32(__float_as_uint(h * kLn2), fs_r, fs_off, 16 * j);
       // the next chunk's step sizes and u weights: two steps after each of
       // the middle items (the first item stages B and C, the last finishes
       // the chunk; this balances the items)
@@ -1078,9 +1115,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5)))
           rows_sum8(vb, o[2], o[3]);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 4; ++i) {  // (sum + D u / ln 2) ln 2, gated
           o[i] = fmaf(Dv, cur_u.at(i), o[i]);
-          if constexpr (GATE) o[i] *= silu_f(zq.at(i));
+          o[i] *= GATE ? silu_ln2(zq.at(i)) : kLn2;
         }
         *reinterpret_cast<uint2*>(&sY[c & 1][cl][qstep]) =
             make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
@@ -1337,7 +1374,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5)))
   __shared__ float4 sPrep[W][2 * 16 * KP / 4];  // per wave: step sizes, dy silu(z)
   __shared__ float sCarry[W][4][64];            // mu handed from wave s to s + 1
   __shared__ int sDone[W];
-  __shared__ float sA[4][64];                   // A log2 e as [j][lane]
+  __shared__ float sA[4][64];                   // A as [j][lane]
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1370,9 +1407,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5)))
 
   if (wave == 0) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) sA[j][lane] = a.A[dc * NS + 4 * j + r] * kLog2e;
+    for (int j = 0; j < 4; ++j) sA[j][lane] = a.A[dc * NS + 4 * j + r];
   }
-  const float bias = (a.delta_bias && dvalid) ? a.delta_bias[d] : 0.0f;
+  const float bias = ((a.delta_bias && dvalid) ? a.delta_bias[d] : 0.0f) * kLog2e;  // bias / ln 2
 
   // The chunk body comes in two forms: FULL for whole chunks (every chunk
   // but the last, and the last when 64 divides L), whose steps need no lane
@@ -1396,14 +1433,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5)))
   };
   Quad cq_raw;
   auto load_c = [&](int c, auto full) { quad_load<VEC>(cq_raw, C_r, seq_off, coff(c), quad_n(c, full)); };
-  // steps i, i + 1 of the lane's quad of chunk c -> LDS: the step size
-  // (natural units; zero past L, an identity step) and dy silu(z)
+  // steps i, i + 1 of the lane's quad of chunk c -> LDS: the step size in
+  // log2 units (dl = delta / ln 2 from the raw step by one fma, so that Abar
+  // = exp2(dl A); zero past L, an identity step) and dy silu(z)
   auto prep_pair = [&](const Raw& q, int i, int c, auto full) {
     float v[2], g[2];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const float x = q.dl.at(i + k) + bias;
-      float s = a.softplus ? softplus_nat(x) : x;
+      const float xl = fmaf(q.dl.at(i + k), kLog2e, bias);  // (raw + bias) / ln 2
+      float s = a.softplus ? softplus_xl(xl) : xl;
       if constexpr (!decltype(full)::value) s = qstep + i + k < left(c) ? s : 0.0f;
       v[k] = s;
       g[k] = GATE ? q.dy.at(i + k) * silu_f(q.z.at(i + k)) : q.dy.at(i + k);
