@@ -3294,17 +3294,17 @@ lti_conv_fft_kernel(const float* K, const void* u,
 // One radix-R Stockham pass over NB transforms of LEN points in LDS buffer s
 // (index i at s[i + i / 16]), in place: every thread reads its butterflies'
 // points, the block waits, then writes their results.
-template <int R, int LEN, int NB>
+template <int R, int LEN, int NB, int NTH = 256>
 __device__ __forceinline__ void fft_pass_lds(float2* s, int Ns) {
   constexpr int BPT = LEN / R;      // butterflies per transform
   constexpr int NBF = NB * BPT;
-  constexpr int IT = (NBF + 255) / 256;
+  constexpr int IT = (NBF + NTH - 1) / NTH;
   float2 v[IT][R];
   int base[IT];
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
-    const int j = (int)threadIdx.x + 256 * it;
-    if (NBF % 256 == 0 || j < NBF) {
+    const int j = (int)threadIdx.x + NTH * it;
+    if (NBF % NTH == 0 || j < NBF) {
       const int t = j / BPT, jj = j % BPT, k = jj & (Ns - 1);
 #pragma unroll
       for (int q = 0; q < R; ++q) {
@@ -3329,8 +3329,8 @@ __device__ __forceinline__ void fft_pass_lds(float2* s, int Ns) {
   __syncthreads();
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
-    const int j = (int)threadIdx.x + 256 * it;
-    if (NBF % 256 == 0 || j < NBF) {
+    const int j = (int)threadIdx.x + NTH * it;
+    if (NBF % NTH == 0 || j < NBF) {
 #pragma unroll
       for (int q = 0; q < R; ++q) {
         const int i = base[it] + q * Ns;
@@ -3341,26 +3341,94 @@ __device__ __forceinline__ void fft_pass_lds(float2* s, int Ns) {
   __syncthreads();
 }
 
-// NB forward DFTs of LEN points each, in place in LDS, natural order in and out
-template <int LEN, int NB>
+// NB forward DFTs of LEN points each, in place in LDS, natural order in and
+// out, by a workgroup of NTH threads
+template <int LEN, int NB, int NTH = 256>
 __device__ __forceinline__ void fft_lds(float2* s) {
-  constexpr int LG = LEN >= 8192 ? 13 : LEN >= 4096 ? 12 : LEN >= 2048 ? 11 : LEN >= 1024 ? 10
-                   : LEN >= 512 ? 9 : LEN >= 256 ? 8 : LEN >= 128 ? 7 : 6;
-  static_assert((1 << LG) == LEN, "LEN is a power of two, 64 .. 8192");
+  constexpr int LG = LEN >= 16384 ? 14 : LEN >= 8192 ? 13 : LEN >= 4096 ? 12 : LEN >= 2048 ? 11
+                   : LEN >= 1024 ? 10 : LEN >= 512 ? 9 : LEN >= 256 ? 8 : LEN >= 128 ? 7 : 6;
+  static_assert((1 << LG) == LEN, "LEN is a power of two, 64 .. 16384");
   constexpr int P16 = LG / 4, REM = LG % 4;
   int Ns = 1;
 #pragma unroll 1
   for (int p = 0; p < P16; ++p) {
-    fft_pass_lds<16, LEN, NB>(s, Ns);
+    fft_pass_lds<16, LEN, NB, NTH>(s, Ns);
     Ns *= 16;
   }
-  if constexpr (REM != 0) fft_pass_lds<(1 << REM), LEN, NB>(s, Ns);
+  if constexpr (REM != 0) fft_pass_lds<(1 << REM), LEN, NB, NTH>(s, Ns);
 }
 
 constexpr int kFftLongMaxLog2 = 21;  // M up to 2^21 points: seqlen up to 2^20
+constexpr int kFftMidLog2 = 14;      // M = 16384 (seqlen 4097 .. 8192): one transform in LDS
 
 // workspace of the long path: per channel the kernel's spectrum and one signal, M complex each
 __host__ __device__ constexpr int64_t fft_long_ws_per_channel(int lg) { return (int64_t)2 << lg; }
+
+// LTI convolution for M = 16384 points: every transform is one in-place FFT
+// of the whole signal in LDS (139 KB: one workgroup per CU), so the signal
+// makes no trips through HBM between passes; only the kernel's spectrum is
+// kept in the workspace (written once per channel, read once per pair of
+// sequences), since registers cannot hold it at this size.  Otherwise as the
+// in-LDS path above: two sequences as the real and imaginary parts of one
+// signal, the product with the kernel's spectrum conjugated, and the
+// inverse as the conjugate of the forward transform of the conjugate.
+template <typename IO>
+__global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4)))
+lti_conv_fft_mid_kernel(const float* K, const void* u, const float* Dskip, void* y, float2* ws,
+                        int64_t batch, int64_t dim, int64_t L) {
+  constexpr int M = 1 << kFftMidLog2, NTH = 1024;
+  __shared__ float2 s[M + M / 16];
+  auto P = [](int i) { return i + (i >> 4); };
+  const int64_t d = blockIdx.x;
+  float2* Ks = ws + d * fft_long_ws_per_channel(kFftMidLog2);
+  constexpr uint32_t ES = sizeof(IO);
+  auto ldv = [](Rsrc r, int i) -> float {
+    if constexpr (ES == 2) return __uint_as_float(buf_ld16(r, (uint32_t)i * 2u, 0) << 16);
+    else return __uint_as_float(buf_ld32(r, (uint32_t)i * 4u, 0));
+  };
+  auto stv = [](Rsrc r, int i, float v) {
+    if constexpr (ES == 2) buf_st16(__builtin_bit_cast(uint16_t, (__bf16)v), r, (uint32_t)i * 2u, 0);
+    else buf_st32(__float_as_uint(v), r, (uint32_t)i * 4u, 0);
+  };
+  // the kernel's spectrum (points past L read as zero through the extent)
+  {
+    const Rsrc rK = make_rsrc(K + d * L, L * 4);
+    for (int i = threadIdx.x; i < M; i += NTH)
+      s[P(i)] = make_float2(__uint_as_float(buf_ld32(rK, (uint32_t)i * 4u, 0)), 0.0f);
+    __syncthreads();
+    fft_lds<M, 1, NTH>(s);
+    for (int i = threadIdx.x; i < M; i += NTH) Ks[i] = s[P(i)];
+  }
+  const float Dd = Dskip ? Dskip[d] : 0.0f;
+  const float scale = 1.0f / (float)M;
+#pragma unroll 1
+  for (int64_t b = 0; b < batch; b += 2) {
+    const bool two = b + 1 < batch;
+    // sequence b + 1 absent: an empty extent reads zeros and drops the writes
+    const int64_t row0 = (b * dim + d) * L, row1 = two ? ((b + 1) * dim + d) * L : row0;
+    const Rsrc rU0 = make_rsrc(static_cast<const char*>(u) + row0 * ES, L * ES);
+    const Rsrc rU1 = make_rsrc(static_cast<const char*>(u) + row1 * ES, two ? L * ES : 0);
+    const Rsrc rY0 = make_rsrc(static_cast<char*>(y) + row0 * ES, L * ES);
+    const Rsrc rY1 = make_rsrc(static_cast<char*>(y) + row1 * ES, two ? L * ES : 0);
+    __syncthreads();  // every thread is done with the buffer's previous contents
+    for (int i = threadIdx.x; i < M; i += NTH) s[P(i)] = make_float2(ldv(rU0, i), ldv(rU1, i));
+    __syncthreads();
+    fft_lds<M, 1, NTH>(s);
+    // each thread multiplies the points it then transforms back into place
+    for (int i = threadIdx.x; i < M; i += NTH) {
+      const float2 z = cmul(s[P(i)], Ks[i]);
+      s[P(i)] = make_float2(z.x, -z.y);
+    }
+    __syncthreads();
+    fft_lds<M, 1, NTH>(s);
+    for (int i = threadIdx.x; i < L; i += NTH) {
+      const float2 v = s[P(i)];
+      stv(rY0, i, fmaf(Dd, ldv(rU0, i), v.x * scale));
+      stv(rY1, i, fmaf(Dd, ldv(rU1, i), -v.y * scale));
+    }
+  }
+}
+
 
 template <typename IO, int LOG2R, int LOG2C>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
@@ -4561,7 +4629,14 @@ int ssm_lti_conv_fft(const float* K, const void* u, const float* Dskip, void* y,
     case 11: go(std::integral_constant<int, 11>{}); break;
     case 12: go(std::integral_constant<int, 12>{}); break;
     case 13: go(std::integral_constant<int, 13>{}); break;
-    case 14: go_long(std::integral_constant<int, 14>{}); break;
+    case 14:  // one in-LDS transform per signal (kernel spectrum in the workspace)
+      if (bf)
+        hipLaunchKernelGGL((lti_conv_fft_mid_kernel<uint16_t>), dim3((unsigned)dim), dim3(1024), 0, s,
+                           K, u, Dskip, y, static_cast<float2*>(workspace), batch, dim, seqlen);
+      else
+        hipLaunchKernelGGL((lti_conv_fft_mid_kernel<float>), dim3((unsigned)dim), dim3(1024), 0, s,
+                           K, u, Dskip, y, static_cast<float2*>(workspace), batch, dim, seqlen);
+      break;
     case 15: go_long(std::integral_constant<int, 15>{}); break;
     case 16: go_long(std::integral_constant<int, 16>{}); break;
     case 17: go_long(std::integral_constant<int, 17>{}); break;

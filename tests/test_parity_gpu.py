@@ -466,13 +466,16 @@ def test_lti_conv_fft_matches_oracle(ssm, dev, dt, L):
     assert worst <= TOL[dt]
 
 
-@pytest.mark.parametrize("dt,L", [("f32", 4097), ("bf16", 8192), ("f32", 16385), ("f32", 65536)])
-def test_lti_conv_fft_long_matches_oracle(ssm, dev, dt, L):
-    """Past 4096 steps the FFT goes through the workspace in four steps
-    (M = 16384 .. 131072: R x C = 128 x 128, 256 x 256, 256 x 512): one pair
-    of sequences on two channels against the oracle's direct causal sum."""
+@pytest.mark.parametrize("dt,L,batch", [("f32", 4097, 2), ("bf16", 8192, 2), ("f32", 6000, 3),
+                                         ("f32", 16385, 2), ("f32", 65536, 2)])
+def test_lti_conv_fft_long_matches_oracle(ssm, dev, dt, L, batch):
+    """Past 4096 steps: M = 16384 (L up to 8192) as one in-LDS transform per
+    signal with the kernel's spectrum in the workspace, longer sequences
+    through the workspace in four steps (M = 32768 .. 131072: R x C = 128 x
+    256, 256 x 512); pairs of sequences (an odd batch leaves one alone) on
+    two channels against the oracle's direct causal sum."""
     r = np.random.default_rng(200 + L)
-    batch, dim, N = 2, 2, 16
+    dim, N = 2, 16
     A = -np.exp(r.uniform(np.log(0.5), np.log(16), (dim, N)))
     Bv, Cv = r.standard_normal((dim, N)), r.standard_normal((dim, N))
     step = r.uniform(0.001, 0.02, dim)  # small steps: the kernel spans the whole sequence
