@@ -444,8 +444,9 @@ def bench_lti(ssm, torch, dev, steps, warmup):
     ms_k = timed(lambda: ssm.ssm_lti_kernel(Ad, Bd, Cd, sd, w.seqlen, K=K))
     ms_d = timed(lambda: ssm.ssm_lti_conv(K, u, D=Dd, y=y))
     ms_f = timed(lambda: ssm.ssm_lti_conv(K, u, D=Dd, y=y, method="fft"))
-    # a longer sequence at the same batch and dim: the four-step transforms
-    # through the workspace (L 8192, M 16384 = 128 x 128 points)
+    # longer sequences at the same batch and dim: L 8192 (M 16384, one
+    # in-LDS transform per signal) and L 65536 (M 131072 = 256 x 512, the
+    # four-step transforms through the workspace)
     Ll = 4 * w.seqlen
     Kl = ssm.ssm_lti_kernel(Ad, Bd, Cd, sd, Ll)
     ul = torch.randn((w.batch, w.dim, Ll), generator=torch.Generator().manual_seed(w.seed + 1)
@@ -453,11 +454,21 @@ def bench_lti(ssm, torch, dev, steps, warmup):
     yl = torch.empty_like(ul)
     wsl = torch.empty(ssm.ssm_lti_conv_fft_workspace_size(w.dim, Ll), dtype=torch.uint8, device=dev)
     ms_fl = timed(lambda: ssm.ssm_lti_conv(Kl, ul, D=Dd, y=yl, method="fft", workspace=wsl))
+    del Kl, ul, yl, wsl
+    Lx = 32 * w.seqlen
+    Kx = ssm.ssm_lti_kernel(Ad, Bd, Cd, sd, Lx)
+    ux = torch.randn((w.batch, w.dim, Lx), generator=torch.Generator().manual_seed(w.seed + 2)
+                     ).to(torch.bfloat16).to(dev)
+    yx = torch.empty_like(ux)
+    wsx = torch.empty(ssm.ssm_lti_conv_fft_workspace_size(w.dim, Lx), dtype=torch.uint8, device=dev)
+    ms_fx = timed(lambda: ssm.ssm_lti_conv(Kx, ux, D=Dd, y=yx, method="fft", workspace=wsx))
+    del Kx, ux, yx, wsx
     return {"workload": f"LTI path: batch {w.batch}, dim {w.dim}, N {w.dstate}, L {w.seqlen}, "
                         "bf16 u and y",
             "kernel_ms": round(ms_k, 4), "conv_direct_ms": round(ms_d, 4),
             "conv_fft_ms": round(ms_f, 4), "conv_fft_long_L": Ll,
-            "conv_fft_long_ms": round(ms_fl, 4), "steps": steps}
+            "conv_fft_long_ms": round(ms_fl, 4), "conv_fft_longer_L": Lx,
+            "conv_fft_longer_ms": round(ms_fx, 4), "steps": steps}
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0
@@ -672,7 +683,8 @@ def main(argv=None):
         out["lti"] = bench_lti(ssm, torch, dev, 5, 1)
         print(f"[bench] lti: kernel {out['lti']['kernel_ms']} ms, conv direct "
               f"{out['lti']['conv_direct_ms']} ms, fft {out['lti']['conv_fft_ms']} ms, fft at L "
-              f"{out['lti']['conv_fft_long_L']} {out['lti']['conv_fft_long_ms']} ms",
+              f"{out['lti']['conv_fft_long_L']} {out['lti']['conv_fft_long_ms']} ms, fft at L "
+              f"{out['lti']['conv_fft_longer_L']} {out['lti']['conv_fft_longer_ms']} ms",
               file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, x)

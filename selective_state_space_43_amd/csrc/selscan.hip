@@ -3430,13 +3430,16 @@ lti_conv_fft_mid_kernel(const float* K, const void* u, const float* Dskip, void*
 }
 
 
+// 512 threads, two workgroups per CU (four waves per SIMD): with 256 threads
+// the in-place passes waited on LDS latency.
 template <typename IO, int LOG2R, int LOG2C>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4)))
 lti_conv_fft_long_kernel(const float* K, const void* u, const float* Dskip, void* y, float2* ws,
                          int64_t batch, int64_t dim, int64_t L) {
   constexpr int R = 1 << LOG2R, C = 1 << LOG2C;
   constexpr int64_t M = (int64_t)R * C;
   constexpr int PB = 8192;                       // points of an LDS block
+  constexpr int NTH = 512;                       // threads: one radix-16 butterfly each per pass
   constexpr int CB = PB / R < C ? PB / R : C;    // columns per column block
   constexpr int RB = PB / C < R ? PB / C : R;    // rows per row block
   constexpr int NPT = CB * R;                    // points of a column block
@@ -3466,13 +3469,13 @@ lti_conv_fft_long_kernel(const float* K, const void* u, const float* Dskip, void
   auto column_forward = [&](auto get) {
 #pragma unroll 1
     for (int c0 = 0; c0 < C; c0 += CB) {
-      for (int i = threadIdx.x; i < NPT; i += 256) {
+      for (int i = threadIdx.x; i < NPT; i += NTH) {
         const int r = i / CB, cc = i % CB;  // consecutive threads: consecutive columns
         s[P(cc * R + r)] = get((int64_t)r * C + c0 + cc);
       }
       __syncthreads();
-      fft_lds<R, CB>(s);
-      for (int i = threadIdx.x; i < NPT; i += 256) {
+      fft_lds<R, CB, NTH>(s);
+      for (int i = threadIdx.x; i < NPT; i += NTH) {
         const int kr = i / CB, cc = i % CB;
         Wk[(int64_t)kr * C + c0 + cc] = twiddle(s[P(cc * R + kr)], (int64_t)(c0 + cc) * kr, 1.0f);
       }
@@ -3488,10 +3491,10 @@ lti_conv_fft_long_kernel(const float* K, const void* u, const float* Dskip, void
     });
 #pragma unroll 1
     for (int r0 = 0; r0 < R; r0 += RB) {
-      for (int i = threadIdx.x; i < NPR; i += 256) s[P(i)] = Wk[(int64_t)r0 * C + i];
+      for (int i = threadIdx.x; i < NPR; i += NTH) s[P(i)] = Wk[(int64_t)r0 * C + i];
       __syncthreads();
-      fft_lds<C, RB>(s);
-      for (int i = threadIdx.x; i < NPR; i += 256) Ks[(int64_t)r0 * C + i] = s[P(i)];
+      fft_lds<C, RB, NTH>(s);
+      for (int i = threadIdx.x; i < NPR; i += NTH) Ks[(int64_t)r0 * C + i] = s[P(i)];
       __syncthreads();
     }
   }
@@ -3515,16 +3518,16 @@ lti_conv_fft_long_kernel(const float* K, const void* u, const float* Dskip, void
     // conjugate of the DFT of the conjugate), conjugate twiddle
 #pragma unroll 1
     for (int r0 = 0; r0 < R; r0 += RB) {
-      for (int i = threadIdx.x; i < NPR; i += 256) s[P(i)] = Wk[(int64_t)r0 * C + i];
+      for (int i = threadIdx.x; i < NPR; i += NTH) s[P(i)] = Wk[(int64_t)r0 * C + i];
       __syncthreads();
-      fft_lds<C, RB>(s);
-      for (int i = threadIdx.x; i < NPR; i += 256) {
+      fft_lds<C, RB, NTH>(s);
+      for (int i = threadIdx.x; i < NPR; i += NTH) {
         const float2 z = cmul(s[P(i)], Ks[(int64_t)r0 * C + i]);
         s[P(i)] = make_float2(z.x, -z.y);
       }
       __syncthreads();
-      fft_lds<C, RB>(s);
-      for (int i = threadIdx.x; i < NPR; i += 256) {
+      fft_lds<C, RB, NTH>(s);
+      for (int i = threadIdx.x; i < NPR; i += NTH) {
         const int rr = i / C, c = i % C;
         const float2 v = s[P(i)];
         Wk[(int64_t)r0 * C + i] = twiddle(make_float2(v.x, -v.y), (int64_t)c * (r0 + rr), -1.0f);
@@ -3534,14 +3537,14 @@ lti_conv_fft_long_kernel(const float* K, const void* u, const float* Dskip, void
     // inverse column DFTs; the real and imaginary parts are the two outputs
 #pragma unroll 1
     for (int c0 = 0; c0 < C; c0 += CB) {
-      for (int i = threadIdx.x; i < NPT; i += 256) {
+      for (int i = threadIdx.x; i < NPT; i += NTH) {
         const int kr = i / CB, cc = i % CB;
         const float2 v = Wk[(int64_t)kr * C + c0 + cc];
         s[P(cc * R + kr)] = make_float2(v.x, -v.y);
       }
       __syncthreads();
-      fft_lds<R, CB>(s);
-      for (int i = threadIdx.x; i < NPT; i += 256) {
+      fft_lds<R, CB, NTH>(s);
+      for (int i = threadIdx.x; i < NPT; i += NTH) {
         const int r = i / CB, cc = i % CB;
         const int64_t n = (int64_t)r * C + c0 + cc;
         if (n < L) {
@@ -4616,10 +4619,10 @@ int ssm_lti_conv_fft(const float* K, const void* u, const float* Dskip, void* y,
     constexpr int LR = LG / 2 < 8 ? LG / 2 : 8, LC = LG - LR;
     float2* w = static_cast<float2*>(workspace);
     if (bf)
-      hipLaunchKernelGGL((lti_conv_fft_long_kernel<uint16_t, LR, LC>), dim3((unsigned)dim), dim3(256),
+      hipLaunchKernelGGL((lti_conv_fft_long_kernel<uint16_t, LR, LC>), dim3((unsigned)dim), dim3(512),
                          0, s, K, u, Dskip, y, w, batch, dim, seqlen);
     else
-      hipLaunchKernelGGL((lti_conv_fft_long_kernel<float, LR, LC>), dim3((unsigned)dim), dim3(256),
+      hipLaunchKernelGGL((lti_conv_fft_long_kernel<float, LR, LC>), dim3((unsigned)dim), dim3(512),
                          0, s, K, u, Dskip, y, w, batch, dim, seqlen);
   };
   switch (lg) {
