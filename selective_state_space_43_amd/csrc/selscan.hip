@@ -3364,23 +3364,32 @@ constexpr int kFftMidLog2 = 14;      // M = 16384 (seqlen 4097 .. 8192): one tra
 // workspace of the long path: per channel the kernel's spectrum and one signal, M complex each
 __host__ __device__ constexpr int64_t fft_long_ws_per_channel(int lg) { return (int64_t)2 << lg; }
 
-// LTI convolution for M = 16384 points: every transform is one in-place FFT
-// of the whole signal in LDS (139 KB: one workgroup per CU), so the signal
-// makes no trips through HBM between passes; only the kernel's spectrum is
-// kept in the workspace (written once per channel, read once per pair of
-// sequences), since registers cannot hold it at this size.  Otherwise as the
-// in-LDS path above: two sequences as the real and imaginary parts of one
-// signal, the product with the kernel's spectrum conjugated, and the
-// inverse as the conjugate of the forward transform of the conjugate.
-template <typename IO>
+// LTI convolution for M = 8192 and 16384 points: every transform is one
+// in-place FFT of the whole signal in LDS by 1024 threads (four waves per
+// SIMD; one workgroup per CU), so the signal makes no trips through HBM
+// between passes and no pass waits on a single wave's LDS latency.  The
+// kernel's spectrum sits beside the signal in LDS for M = 8192 (2 x 69.6
+// KB) and in the workspace for M = 16384 (written once per channel, read
+// once per pair of sequences), since neither LDS nor registers hold it there.
+// Otherwise as the in-LDS path above: two sequences as the real and imaginary
+// parts of one signal, the product with the kernel's spectrum conjugated, and
+// the inverse as the conjugate of the forward transform of the conjugate.
+template <typename IO, int LOG2M>
 __global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4)))
 lti_conv_fft_mid_kernel(const float* K, const void* u, const float* Dskip, void* y, float2* ws,
                         int64_t batch, int64_t dim, int64_t L) {
-  constexpr int M = 1 << kFftMidLog2, NTH = 1024;
+  static_assert(LOG2M == 13 || LOG2M == kFftMidLog2, "M = 8192 or 16384");
+  constexpr int M = 1 << LOG2M, NTH = 1024;
+  constexpr bool KS_LDS = LOG2M == 13;
   __shared__ float2 s[M + M / 16];
+  __shared__ float2 sk[KS_LDS ? M + M / 16 : 1];
   auto P = [](int i) { return i + (i >> 4); };
   const int64_t d = blockIdx.x;
-  float2* Ks = ws + d * fft_long_ws_per_channel(kFftMidLog2);
+  float2* Ks = KS_LDS ? nullptr : ws + d * fft_long_ws_per_channel(LOG2M);
+  auto ks = [&](int i) -> float2& {
+    if constexpr (KS_LDS) return sk[P(i)];
+    else return Ks[i];
+  };
   constexpr uint32_t ES = sizeof(IO);
   auto ldv = [](Rsrc r, int i) -> float {
     if constexpr (ES == 2) return __uint_as_float(buf_ld16(r, (uint32_t)i * 2u, 0) << 16);
@@ -3397,7 +3406,7 @@ lti_conv_fft_mid_kernel(const float* K, const void* u, const float* Dskip, void*
       s[P(i)] = make_float2(__uint_as_float(buf_ld32(rK, (uint32_t)i * 4u, 0)), 0.0f);
     __syncthreads();
     fft_lds<M, 1, NTH>(s);
-    for (int i = threadIdx.x; i < M; i += NTH) Ks[i] = s[P(i)];
+    for (int i = threadIdx.x; i < M; i += NTH) ks(i) = s[P(i)];
   }
   const float Dd = Dskip ? Dskip[d] : 0.0f;
   const float scale = 1.0f / (float)M;
@@ -3416,7 +3425,7 @@ lti_conv_fft_mid_kernel(const float* K, const void* u, const float* Dskip, void*
     fft_lds<M, 1, NTH>(s);
     // each thread multiplies the points it then transforms back into place
     for (int i = threadIdx.x; i < M; i += NTH) {
-      const float2 z = cmul(s[P(i)], Ks[i]);
+      const float2 z = cmul(s[P(i)], ks(i));
       s[P(i)] = make_float2(z.x, -z.y);
     }
     __syncthreads();
@@ -4631,13 +4640,20 @@ int ssm_lti_conv_fft(const float* K, const void* u, const float* Dskip, void* y,
     case 10: go(std::integral_constant<int, 10>{}); break;
     case 11: go(std::integral_constant<int, 11>{}); break;
     case 12: go(std::integral_constant<int, 12>{}); break;
-    case 13: go(std::integral_constant<int, 13>{}); break;
+    case 13:  // one in-LDS transform per signal, the kernel's spectrum beside it
+      if (bf)
+        hipLaunchKernelGGL((lti_conv_fft_mid_kernel<uint16_t, 13>), dim3((unsigned)dim), dim3(1024), 0, s,
+                           K, u, Dskip, y, nullptr, batch, dim, seqlen);
+      else
+        hipLaunchKernelGGL((lti_conv_fft_mid_kernel<float, 13>), dim3((unsigned)dim), dim3(1024), 0, s,
+                           K, u, Dskip, y, nullptr, batch, dim, seqlen);
+      break;
     case 14:  // one in-LDS transform per signal (kernel spectrum in the workspace)
       if (bf)
-        hipLaunchKernelGGL((lti_conv_fft_mid_kernel<uint16_t>), dim3((unsigned)dim), dim3(1024), 0, s,
+        hipLaunchKernelGGL((lti_conv_fft_mid_kernel<uint16_t, 14>), dim3((unsigned)dim), dim3(1024), 0, s,
                            K, u, Dskip, y, static_cast<float2*>(workspace), batch, dim, seqlen);
       else
-        hipLaunchKernelGGL((lti_conv_fft_mid_kernel<float>), dim3((unsigned)dim), dim3(1024), 0, s,
+        hipLaunchKernelGGL((lti_conv_fft_mid_kernel<float, 14>), dim3((unsigned)dim), dim3(1024), 0, s,
                            K, u, Dskip, y, static_cast<float2*>(workspace), batch, dim, seqlen);
       break;
     case 15: go_long(std::integral_constant<int, 15>{}); break;
