@@ -457,8 +457,8 @@ def bench_lti(ssm, torch, dev, steps, warmup):
     del Kl, ul, yl, wsl
     Lx = 32 * w.seqlen
     Kx = ssm.ssm_lti_kernel(Ad, Bd, Cd, sd, Lx)
-    ux = torch.randn((w.batch, w.dim, Lx), generator=torch.Generator().manual_seed(w.seed + 2)
-                     ).to(torch.bfloat16).to(dev)
+    ux = torch.randn((w.batch, w.dim, Lx), device=dev,  # drawn on the GPU: 805 M values
+                     generator=torch.Generator(device=dev).manual_seed(w.seed + 2)).to(torch.bfloat16)
     yx = torch.empty_like(ux)
     wsx = torch.empty(ssm.ssm_lti_conv_fft_workspace_size(w.dim, Lx), dtype=torch.uint8, device=dev)
     ms_fx = timed(lambda: ssm.ssm_lti_conv(Kx, ux, D=Dd, y=yx, method="fft", workspace=wsx))
